@@ -1,0 +1,158 @@
+/*
+ * splitzip.h -- C ABI of the MI355X (gfx950) SplitZip BF16 KV-cache codec.
+ *
+ * The method is the one the SplitZip explainers describe ("SplitZip: Ultra
+ * Fast Lossless KV Compression for Disaggregated LLM Serving", gist.science
+ * pages for arXiv 2605.01708, French and Japanese): every BF16 word is split
+ * into sign, exponent and mantissa (section "1. La structure de la Note");
+ * the 16 most frequent exponents of the tensor get fixed 4-bit codes, two
+ * codes per byte, and every other exponent is written as a (position,
+ * exponent) escape record (section "3. La strategie SplitZip"); decoding
+ * looks the codes up, recombines them with sign and mantissa and overwrites
+ * the escaped slots (section "4. Pourquoi est-ce rapide ?"); the round trip
+ * is bit-exact (section "Les Resultats").
+ *
+ * Container produced by sz_encode (little-endian, no padding):
+ *   off 0    u32  magic 0x564B5A53 (bytes 'S' 'Z' 'K' 'V')
+ *   off 4    u16  version 1
+ *   off 6    u16  element type 1 (bf16)
+ *   off 8    u64  N, number of elements
+ *   off 16   u64  E, number of escapes
+ *   off 24   u64  total bytes = 176 + ceil(N/2) + N + 5E
+ *   off 32   u64  seg_end[16]: number of escapes whose position is below
+ *                 (s+1) * 2^32 (escape positions are stored modulo 2^32)
+ *   off 160  u8   codebook[16]: code c -> exponent; codes are ranks by count
+ *                 (descending), equal counts ordered by exponent (ascending)
+ *   off 176  u8   nibbles[ceil(N/2)]: element 2j in the low nibble of byte j,
+ *                 element 2j+1 in the high nibble; escaped elements hold 0
+ *   +        u8   sm[N]: sign in bit 7, mantissa in bits 6..0
+ *   +        u32  pos_lo[E]: escape positions mod 2^32, strictly ascending
+ *   +        u8   exp[E]: the exponent of each escape
+ *
+ * Conventions for every call below:
+ *   - Pointers named d_* are device pointers (hipMalloc or a PyTorch CUDA
+ *     tensor) owned by the caller; the library keeps none of them after the
+ *     stream work completes.  BF16 and container pointers must be 16-byte
+ *     aligned; workspaces 256-byte aligned.
+ *   - Calls are asynchronous on `stream` and never synchronise the host.
+ *     The return value reports errors found on the host before anything is
+ *     launched (nothing is launched then), or SZ_ERR_HIP for a failed
+ *     launch or allocation.  Results are valid once the stream work is done.
+ *   - Calls on different streams may run concurrently if they use different
+ *     buffers.
+ */
+#ifndef SPLITZIP_H
+#define SPLITZIP_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SZ_HEADER_BYTES 160u
+#define SZ_CODEBOOK_BYTES 16u
+#define SZ_PREFIX_BYTES 176u
+#define SZ_MAX_ELEMENTS (1ull << 36)
+
+typedef enum {
+    SZ_OK = 0,
+    SZ_ERR_INVALID_ARGUMENT = 1, /* NULL or misaligned pointer, overlap, bad workspace */
+    SZ_ERR_CAPACITY = 2,         /* destination smaller than sz_max_compressed_size(n) */
+    SZ_ERR_TOO_LARGE = 3,        /* n > SZ_MAX_ELEMENTS */
+    SZ_ERR_CORRUPT = 4,          /* container inconsistent with n or with itself */
+    SZ_ERR_HIP = 5               /* a HIP launch or allocation failed */
+} sz_status;
+
+/* Upper bound of the container size for n elements: 176 + ceil(n/2) + n +
+ * 5*floor(15n/16), since the 16 most frequent of 256 exponents always cover
+ * at least n/16 elements.  Returns 0 when n > SZ_MAX_ELEMENTS.  Host-only,
+ * touches no device. */
+uint64_t sz_max_compressed_size(uint64_t n_elements);
+
+/* Bytes of device workspace the staged encode calls need for n elements
+ * (at most about 2.2 MB).  Host-only. */
+uint64_t sz_workspace_size(uint64_t n_elements);
+
+/* Compress n BF16 words at d_src into the container format above at d_dst.
+ * SplitZip explainer section "3. La strategie SplitZip" (top-16 exponent
+ * codebook, 4-bit codes two per byte, escape records for the rest).
+ *   d_src             n little-endian BF16 words (any bit patterns)
+ *   d_dst             container buffer, dst_capacity bytes; must be at least
+ *                     sz_max_compressed_size(n) (else SZ_ERR_CAPACITY); only
+ *                     the first `total bytes` of the container are written
+ *   d_compressed_size optional device u64 that receives the container size
+ *                     (the same value is stored at container offset 24)
+ * Allocates its workspace (sz_workspace_size(n)) from a library-owned,
+ * stream-ordered device memory pool and returns it on the same stream. */
+sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
+                    uint64_t dst_capacity, uint64_t *d_compressed_size,
+                    hipStream_t stream);
+
+/* Decompress a container of src_bytes bytes into n BF16 words at d_dst,
+ * bit-exactly.  SplitZip explainer section "4. Pourquoi est-ce rapide ?"
+ * (code -> exponent lookup, recombination with sign and mantissa, escaped
+ * slots overwritten).
+ *   src_bytes   must equal the container's total size: the host derives E
+ *               from it, so no device read is needed before launching
+ *   d_status    optional device i32: SZ_OK, or SZ_ERR_CORRUPT when the
+ *               header or an escape position fails a check on the device
+ *               (d_dst content is then unspecified, but no write ever leaves
+ *               d_dst[0..n))
+ * Host-side SZ_ERR_CORRUPT: src_bytes < 176 + ceil(n/2) + n, or the rest is
+ * not a multiple of 5 bytes, or implies more than floor(15n/16) escapes. */
+sz_status sz_decode(const void *d_src, uint64_t src_bytes, void *d_dst,
+                    uint64_t n_elements, int32_t *d_status, hipStream_t stream);
+
+/* ---- staged form: the same kernels, one call per pass ------------------
+ * sz_encode = sz_encode_histogram; sz_encode_codebook; sz_encode_pack on one
+ * stream with one workspace of at least sz_workspace_size(n) bytes that the
+ * caller owns and does not touch in between.  sz_decode = sz_decode_unpack;
+ * sz_decode_scatter.  Out-of-order use cannot write outside the caller's
+ * buffers, but yields an unspecified container. */
+
+/* Pass 1, exponent histogram (explainer section "2. La decouverte
+ * secrete": the exponents are highly repetitive): one 256-bin count per
+ * fixed-size chunk of the input, into the workspace. */
+sz_status sz_encode_histogram(const void *d_src, uint64_t n_elements,
+                              void *d_workspace, uint64_t workspace_bytes,
+                              hipStream_t stream);
+
+/* Pass 2, top-16 selection (section "3. La strategie SplitZip", shortcut
+ * bullet): merges the chunk counts, ranks the 256 exponents, writes the
+ * header and codebook to d_dst, the escape offset of every chunk to the
+ * workspace and the container size to *d_compressed_size (optional). */
+sz_status sz_encode_codebook(uint64_t n_elements, void *d_workspace,
+                             uint64_t workspace_bytes, void *d_dst,
+                             uint64_t dst_capacity, uint64_t *d_compressed_size,
+                             hipStream_t stream);
+
+/* Pass 3, packing (same section, packing and rare-value bullets): 4-bit
+ * codes two per byte, sign|mantissa bytes, and the escape records of each
+ * chunk written to their final slots in ascending position order. */
+sz_status sz_encode_pack(const void *d_src, uint64_t n_elements,
+                         const void *d_workspace, uint64_t workspace_bytes,
+                         void *d_dst, uint64_t dst_capacity, hipStream_t stream);
+
+/* Decode pass 1: header check (sets *d_status to SZ_OK or SZ_ERR_CORRUPT)
+ * and every word rebuilt from its code and its sign|mantissa byte. */
+sz_status sz_decode_unpack(const void *d_src, uint64_t src_bytes, void *d_dst,
+                           uint64_t n_elements, int32_t *d_status,
+                           hipStream_t stream);
+
+/* Decode pass 2: every escape record overwrites the exponent of its slot;
+ * a position >= n or not above the previous one raises *d_status to
+ * SZ_ERR_CORRUPT and is skipped.  Launches nothing when E = 0. */
+sz_status sz_decode_scatter(const void *d_src, uint64_t src_bytes, void *d_dst,
+                            uint64_t n_elements, int32_t *d_status,
+                            hipStream_t stream);
+
+/* Static English text for a status code (never NULL). */
+const char *sz_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITZIP_H */

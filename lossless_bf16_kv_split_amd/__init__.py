@@ -1,0 +1,188 @@
+"""MI355X-native SplitZip BF16 KV-cache codec: Python binding.
+
+A thin ctypes layer over ``libsplitzip.so`` (hand-written HIP for gfx950,
+C ABI declared in ``include/splitzip.h``).  The functions named ``sz_*`` are
+the C entry points with the same names and arguments; they only marshal
+arguments (a torch tensor's data pointer, or a raw integer device pointer,
+and the current torch stream by default) and turn a non-zero status into
+``SplitZipError``.  Every step of the codec runs in the library's kernels;
+PyTorch only provides device memory and streams.
+
+``encode`` and ``decode`` are conveniences that allocate their outputs with
+torch and call the entry points.
+
+The method follows the SplitZip explainers (gist.science, arXiv 2605.01708):
+top-16 exponent codebook with 4-bit codes two per byte, sign|mantissa bytes,
+and (position, exponent) escapes for the remaining exponents (section
+"3. La strategie SplitZip"), decoded by lookup, recombination and escape
+overwrite (section "4. Pourquoi est-ce rapide ?").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "SplitZipError", "lib_path", "sz_max_compressed_size", "sz_workspace_size", "sz_encode",
+    "sz_decode", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
+    "sz_decode_unpack", "sz_decode_scatter", "sz_status_string", "encode", "decode",
+    "PREFIX_BYTES", "MAX_ELEMENTS",
+]
+
+PREFIX_BYTES = 176
+MAX_ELEMENTS = 1 << 36
+
+SZ_OK = 0
+SZ_ERR_INVALID_ARGUMENT = 1
+SZ_ERR_CAPACITY = 2
+SZ_ERR_TOO_LARGE = 3
+SZ_ERR_CORRUPT = 4
+SZ_ERR_HIP = 5
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_HERE, "libsplitzip.so")
+
+
+class SplitZipError(RuntimeError):
+    def __init__(self, status: int, call: str):
+        super().__init__(f"{call}: {sz_status_string(status)} (status {status})")
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(lib_path):
+        raise ImportError(
+            f"{lib_path} is missing: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(lib_path)
+    u64, p, i32 = ctypes.c_uint64, ctypes.c_void_p, ctypes.c_int
+    L.sz_max_compressed_size.argtypes = [u64]
+    L.sz_max_compressed_size.restype = u64
+    L.sz_workspace_size.argtypes = [u64]
+    L.sz_workspace_size.restype = u64
+    L.sz_encode.argtypes = [p, u64, p, u64, p, p]
+    L.sz_decode.argtypes = [p, u64, p, u64, p, p]
+    L.sz_encode_histogram.argtypes = [p, u64, p, u64, p]
+    L.sz_encode_codebook.argtypes = [u64, p, u64, p, u64, p, p]
+    L.sz_encode_pack.argtypes = [p, u64, p, u64, p, u64, p]
+    L.sz_decode_unpack.argtypes = [p, u64, p, u64, p, p]
+    L.sz_decode_scatter.argtypes = [p, u64, p, u64, p, p]
+    for name in ("sz_encode", "sz_decode", "sz_encode_histogram", "sz_encode_codebook",
+                 "sz_encode_pack", "sz_decode_unpack", "sz_decode_scatter"):
+        getattr(L, name).restype = i32
+    L.sz_status_string.argtypes = [i32]
+    L.sz_status_string.restype = ctypes.c_char_p
+    return L
+
+
+_lib = _load()
+
+
+def _ptr(x) -> int | None:
+    """Device pointer of a tensor, or an integer pointer as given (None = NULL)."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, call: str) -> None:
+    if status != SZ_OK:
+        raise SplitZipError(status, call)
+
+
+def sz_status_string(status: int) -> str:
+    return _lib.sz_status_string(status).decode()
+
+
+def sz_max_compressed_size(n_elements: int) -> int:
+    return int(_lib.sz_max_compressed_size(n_elements))
+
+
+def sz_workspace_size(n_elements: int) -> int:
+    return int(_lib.sz_workspace_size(n_elements))
+
+
+def sz_encode(src, n_elements: int, dst, dst_capacity: int, d_compressed_size=None,
+              stream=None) -> None:
+    _check(_lib.sz_encode(_ptr(src), n_elements, _ptr(dst), dst_capacity,
+                          _ptr(d_compressed_size), _stream(stream)), "sz_encode")
+
+
+def sz_decode(src, src_bytes: int, dst, n_elements: int, d_status=None, stream=None) -> None:
+    _check(_lib.sz_decode(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
+                          _stream(stream)), "sz_decode")
+
+
+def sz_encode_histogram(src, n_elements: int, workspace, workspace_bytes: int,
+                        stream=None) -> None:
+    _check(_lib.sz_encode_histogram(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
+                                    _stream(stream)), "sz_encode_histogram")
+
+
+def sz_encode_codebook(n_elements: int, workspace, workspace_bytes: int, dst,
+                       dst_capacity: int, d_compressed_size=None, stream=None) -> None:
+    _check(_lib.sz_encode_codebook(n_elements, _ptr(workspace), workspace_bytes, _ptr(dst),
+                                   dst_capacity, _ptr(d_compressed_size), _stream(stream)),
+           "sz_encode_codebook")
+
+
+def sz_encode_pack(src, n_elements: int, workspace, workspace_bytes: int, dst,
+                   dst_capacity: int, stream=None) -> None:
+    _check(_lib.sz_encode_pack(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
+                               _ptr(dst), dst_capacity, _stream(stream)), "sz_encode_pack")
+
+
+def sz_decode_unpack(src, src_bytes: int, dst, n_elements: int, d_status=None,
+                     stream=None) -> None:
+    _check(_lib.sz_decode_unpack(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
+                                 _stream(stream)), "sz_decode_unpack")
+
+
+def sz_decode_scatter(src, src_bytes: int, dst, n_elements: int, d_status=None,
+                      stream=None) -> None:
+    _check(_lib.sz_decode_scatter(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
+                                  _stream(stream)), "sz_decode_scatter")
+
+
+# ---- conveniences (torch allocates; the library computes) -----------------
+
+def encode(x, stream=None):
+    """Compress a CUDA tensor of BF16 (or 16-bit integer) words; returns the
+    container as a uint8 CUDA tensor trimmed to its exact size (this reads
+    the size back, so it synchronises the stream)."""
+    import torch
+    if x.element_size() != 2 or not x.is_cuda:
+        raise ValueError("encode expects a CUDA tensor of 16-bit elements")
+    x = x.contiguous()
+    n = x.numel()
+    cap = sz_max_compressed_size(n)
+    dst = torch.empty(cap, dtype=torch.uint8, device=x.device)
+    size = torch.zeros(1, dtype=torch.int64, device=x.device)
+    sz_encode(x, n, dst, cap, size, stream)
+    return dst[: int(size.item())]
+
+
+def decode(container, n_elements: int, dtype=None, stream=None, check: bool = True):
+    """Decompress a uint8 CUDA container into ``n_elements`` words (bfloat16
+    unless ``dtype`` says otherwise).  With ``check`` the device status is
+    read back (synchronising) and a corrupt container raises."""
+    import torch
+    out = torch.empty(n_elements, dtype=dtype or torch.bfloat16, device=container.device)
+    status = torch.zeros(1, dtype=torch.int32, device=container.device)
+    sz_decode(container, container.numel(), out, n_elements, status, stream)
+    if check:
+        st = int(status.item())
+        if st != SZ_OK:
+            raise SplitZipError(st, "sz_decode (device check)")
+    return out

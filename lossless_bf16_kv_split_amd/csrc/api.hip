@@ -1,0 +1,209 @@
+// api.hip -- extern "C" entry points of libsplitzip.so (declared, with their
+// argument contracts, in include/splitzip.h).
+//
+// Host side only: argument checks that need no device access, the chunk
+// plan, a library-owned stream-ordered memory pool for sz_encode's
+// workspace, and the kernel launch sequences.  No call synchronises the host.
+#include "splitzip.h"
+#include "sz_internal.h"
+
+#include <mutex>
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+std::mutex g_mutex;
+hipMemPool_t g_pools[kMaxDevices] = {};
+int g_num_cus[kMaxDevices] = {};
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+bool overlap(const void* a, uint64_t a_bytes, const void* b, uint64_t b_bytes) {
+    if (a_bytes == 0 || b_bytes == 0) return false;
+    const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+    return a0 < b0 + b_bytes && b0 < a0 + a_bytes;
+}
+
+int current_device() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return -1;
+    return dev;
+}
+
+int num_cus(int dev) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_num_cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        g_num_cus[dev] = v;
+    }
+    return g_num_cus[dev];
+}
+
+// A private pool, so that sz_encode neither changes the process-wide
+// default pool nor returns its workspace to the driver after every call.
+hipMemPool_t pool_for(int dev) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_pools[dev] == nullptr) {
+        hipMemPoolProps props = {};
+        props.allocType = hipMemAllocationTypePinned;
+        props.handleTypes = hipMemHandleTypeNone;
+        props.location.type = hipMemLocationTypeDevice;
+        props.location.id = dev;
+        hipMemPool_t pool = nullptr;
+        if (hipMemPoolCreate(&pool, &props) != hipSuccess) return nullptr;
+        uint64_t keep = UINT64_MAX;
+        (void)hipMemPoolSetAttribute(pool, hipMemPoolAttrReleaseThreshold, &keep);
+        g_pools[dev] = pool;
+    }
+    return g_pools[dev];
+}
+
+sz_status check_encode_args(const void* src, uint64_t n, const void* dst, uint64_t cap) {
+    if (n > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (dst == nullptr || (n > 0 && src == nullptr)) return SZ_ERR_INVALID_ARGUMENT;
+    if (!aligned(dst, 16) || (n > 0 && !aligned(src, 16))) return SZ_ERR_INVALID_ARGUMENT;
+    if (cap < sz_max_compressed_size(n)) return SZ_ERR_CAPACITY;
+    if (overlap(src, 2 * n, dst, cap)) return SZ_ERR_INVALID_ARGUMENT;
+    return SZ_OK;
+}
+
+sz_status check_workspace(const void* ws, uint64_t ws_bytes, const sz::EncodePlan& p) {
+    if (ws == nullptr || !aligned(ws, 256) || ws_bytes < p.ws_bytes) return SZ_ERR_INVALID_ARGUMENT;
+    return SZ_OK;
+}
+
+// Host-side container checks for decode; derives the escape count E from
+// the container size alone (total = 176 + ceil(n/2) + n + 5E).
+sz_status check_decode_args(const void* src, uint64_t src_bytes, const void* dst, uint64_t n,
+                            uint64_t* e_out) {
+    if (n > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (src == nullptr || (n > 0 && dst == nullptr)) return SZ_ERR_INVALID_ARGUMENT;
+    if (!aligned(src, 16) || (n > 0 && !aligned(dst, 16))) return SZ_ERR_INVALID_ARGUMENT;
+    const uint64_t fixed = sz::container_bytes(n, 0);
+    if (src_bytes < fixed || (src_bytes - fixed) % 5 != 0) return SZ_ERR_CORRUPT;
+    const uint64_t e = (src_bytes - fixed) / 5;
+    if (e > (15 * n) / 16) return SZ_ERR_CORRUPT;
+    if (overlap(src, src_bytes, dst, 2 * n)) return SZ_ERR_INVALID_ARGUMENT;
+    *e_out = e;
+    return SZ_OK;
+}
+
+sz_status hip_status(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+uint64_t sz_max_compressed_size(uint64_t n) {
+    if (n > SZ_MAX_ELEMENTS) return 0;
+    return sz::container_bytes(n, (15 * n) / 16);
+}
+
+uint64_t sz_workspace_size(uint64_t n) {
+    if (n > SZ_MAX_ELEMENTS) return 0;
+    return sz::plan_encode(n).ws_bytes;
+}
+
+sz_status sz_encode_histogram(const void* d_src, uint64_t n, void* d_workspace,
+                              uint64_t workspace_bytes, hipStream_t stream) {
+    if (n > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (n > 0 && (d_src == nullptr || !aligned(d_src, 16))) return SZ_ERR_INVALID_ARGUMENT;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
+    return hip_status(sz::launch_histogram(static_cast<const uint16_t*>(d_src), p,
+                                           static_cast<uint8_t*>(d_workspace), stream));
+}
+
+sz_status sz_encode_codebook(uint64_t n, void* d_workspace, uint64_t workspace_bytes, void* d_dst,
+                             uint64_t dst_capacity, uint64_t* d_compressed_size,
+                             hipStream_t stream) {
+    if (n > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (d_dst == nullptr || !aligned(d_dst, 16)) return SZ_ERR_INVALID_ARGUMENT;
+    if (dst_capacity < sz_max_compressed_size(n)) return SZ_ERR_CAPACITY;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
+    return hip_status(sz::launch_codebook(p, static_cast<uint8_t*>(d_workspace),
+                                          static_cast<uint8_t*>(d_dst), d_compressed_size,
+                                          stream));
+}
+
+sz_status sz_encode_pack(const void* d_src, uint64_t n, const void* d_workspace,
+                         uint64_t workspace_bytes, void* d_dst, uint64_t dst_capacity,
+                         hipStream_t stream) {
+    if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    return hip_status(sz::launch_pack(static_cast<const uint16_t*>(d_src), p,
+                                      static_cast<const uint8_t*>(d_workspace),
+                                      static_cast<uint8_t*>(d_dst), dst_capacity, num_cus(dev),
+                                      stream));
+}
+
+sz_status sz_encode(const void* d_src, uint64_t n, void* d_dst, uint64_t dst_capacity,
+                    uint64_t* d_compressed_size, hipStream_t stream) {
+    if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    hipMemPool_t pool = pool_for(dev);
+    if (pool == nullptr) return SZ_ERR_HIP;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    void* ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, p.ws_bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    sz_status st = hip_status(sz::launch_histogram(static_cast<const uint16_t*>(d_src), p, w, stream));
+    if (st == SZ_OK)
+        st = hip_status(sz::launch_codebook(p, w, static_cast<uint8_t*>(d_dst), d_compressed_size,
+                                            stream));
+    if (st == SZ_OK)
+        st = hip_status(sz::launch_pack(static_cast<const uint16_t*>(d_src), p, w,
+                                        static_cast<uint8_t*>(d_dst), dst_capacity, num_cus(dev),
+                                        stream));
+    if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
+    return st;
+}
+
+sz_status sz_decode_unpack(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
+                           int32_t* d_status, hipStream_t stream) {
+    uint64_t e = 0;
+    if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    return hip_status(sz::launch_unpack(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
+                                        static_cast<uint16_t*>(d_dst), d_status, num_cus(dev),
+                                        stream));
+}
+
+sz_status sz_decode_scatter(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
+                            int32_t* d_status, hipStream_t stream) {
+    uint64_t e = 0;
+    if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
+    return hip_status(sz::launch_scatter(static_cast<const uint8_t*>(d_src), n, e,
+                                         static_cast<uint16_t*>(d_dst), d_status, stream));
+}
+
+sz_status sz_decode(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
+                    int32_t* d_status, hipStream_t stream) {
+    sz_status st = sz_decode_unpack(d_src, src_bytes, d_dst, n, d_status, stream);
+    if (st != SZ_OK) return st;
+    return sz_decode_scatter(d_src, src_bytes, d_dst, n, d_status, stream);
+}
+
+const char* sz_status_string(int status) {
+    switch (status) {
+        case SZ_OK: return "ok";
+        case SZ_ERR_INVALID_ARGUMENT: return "invalid argument (null, misaligned, overlapping or bad workspace)";
+        case SZ_ERR_CAPACITY: return "destination capacity below sz_max_compressed_size(n)";
+        case SZ_ERR_TOO_LARGE: return "more than 2^36 elements";
+        case SZ_ERR_CORRUPT: return "corrupt or inconsistent container";
+        case SZ_ERR_HIP: return "HIP launch or allocation failed";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,423 @@
+// encode.hip -- the three encode passes of the SplitZip BF16 codec on gfx950.
+//
+//   histogram  one workgroup per chunk: 256-bin exponent counts in LDS
+//              (replicated sub-histograms against same-address conflicts),
+//              written out as one row per chunk
+//   codebook   merge the rows, rank the 256 exponents (count desc, value
+//              asc), write header + codebook, and turn every chunk's row
+//              into its exact escape count and first escape slot
+//   pack       one workgroup per chunk: 16-byte loads, 256-entry exponent
+//              -> code table in LDS, 4-bit codes two per byte, sign|mantissa
+//              bytes, ballot/popcount escape ranks, escapes written straight
+//              to their final slots in ascending position order
+//
+// Method: SplitZip explainers (gist.science, arXiv 2605.01708), sections
+// "2. La decouverte secrete" (exponents repeat), "3. La strategie SplitZip"
+// (top-16 list, fixed 4-bit codes two per byte, rare exponents as
+// (position, exponent) notes) and "4. Pourquoi est-ce rapide ?" (fixed-size
+// codes make every output slot known in advance).
+#include "sz_internal.h"
+
+namespace sz {
+
+// ---------------------------------------------------------------- plan
+
+EncodePlan plan_encode(uint64_t n) {
+    EncodePlan p;
+    p.n = n;
+    uint32_t c = kMinChunkLog2;
+    while (c < 40 && ((n + (1ull << c) - 1) >> c) > kMaxChunks) c++;
+    p.chunk_log2 = c;
+    p.chunks = (uint32_t)((n + (1ull << c) - 1) >> c);
+    p.partials = (p.chunks + kRowsPerPartial - 1) / kRowsPerPartial;
+    auto align = [](uint64_t x) { return (x + 255) & ~255ull; };
+    p.rows_off = 0;
+    p.partial_off = align(p.rows_off + (uint64_t)p.chunks * 256 * 4);
+    p.base_off = align(p.partial_off + (uint64_t)p.partials * 256 * 8);
+    p.ws_bytes = align(p.base_off + (uint64_t)p.chunks * 8);
+    if (p.ws_bytes == 0) p.ws_bytes = 256;
+    return p;
+}
+
+// ---------------------------------------------------------------- pass 1
+
+constexpr int kHistThreads = 256;
+constexpr int kHistCopies = 8;    // sub-histograms per workgroup
+constexpr int kHistPitch = 257;   // odd pitch: copies of one bin sit in different banks
+
+__device__ __forceinline__ void hist_add(uint32_t* h, uint32_t e) {
+    __hip_atomic_fetch_add(h + e, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
+// Two BF16 words per dword: exponents are bits 14..7 and 30..23.
+__device__ __forceinline__ void hist_dword(uint32_t* h, uint32_t d) {
+    hist_add(h, (d >> 7) & 0xFFu);
+    hist_add(h, (d >> 23) & 0xFFu);
+}
+
+__device__ __forceinline__ void hist_uint4(uint32_t* h, const uint4& v) {
+    hist_dword(h, v.x);
+    hist_dword(h, v.y);
+    hist_dword(h, v.z);
+    hist_dword(h, v.w);
+}
+
+__global__ __launch_bounds__(kHistThreads) void k_histogram(const uint16_t* __restrict__ src,
+                                                            uint64_t n, uint32_t chunk_log2,
+                                                            uint32_t* __restrict__ rows) {
+    __shared__ uint32_t h[kHistCopies * kHistPitch];
+    for (int i = threadIdx.x; i < kHistCopies * kHistPitch; i += kHistThreads) h[i] = 0;
+    __syncthreads();
+
+    const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
+    const uint64_t end = min(begin + (1ull << chunk_log2), n);
+    uint32_t* mine = h + (threadIdx.x % kHistCopies) * kHistPitch;
+
+    // 8 words per 16-byte load; four loads in flight per thread
+    const uint4* v = reinterpret_cast<const uint4*>(src + begin);
+    const uint32_t groups = (uint32_t)((end - begin) >> 3);
+    uint32_t g = threadIdx.x;
+    for (; g + 3 * kHistThreads < groups; g += 4 * kHistThreads) {
+        const uint4 a = v[g];
+        const uint4 b = v[g + kHistThreads];
+        const uint4 c = v[g + 2 * kHistThreads];
+        const uint4 d = v[g + 3 * kHistThreads];
+        hist_uint4(mine, a);
+        hist_uint4(mine, b);
+        hist_uint4(mine, c);
+        hist_uint4(mine, d);
+    }
+    for (; g < groups; g += kHistThreads) hist_uint4(mine, v[g]);
+    // fewer than 8 words left at the very end of the input
+    for (uint64_t i = begin + ((uint64_t)groups << 3) + threadIdx.x; i < end; i += kHistThreads)
+        hist_add(mine, (src[i] >> 7) & 0xFFu);
+    __syncthreads();
+
+    for (int bin = threadIdx.x; bin < 256; bin += kHistThreads) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < kHistCopies; c++) s += h[c * kHistPitch + bin];
+        rows[(uint64_t)blockIdx.x * 256 + bin] = s;
+    }
+}
+
+hipError_t launch_histogram(const uint16_t* src, const EncodePlan& p, uint8_t* ws,
+                            hipStream_t stream) {
+    if (p.chunks == 0) return hipSuccess;
+    k_histogram<<<p.chunks, kHistThreads, 0, stream>>>(
+        src, p.n, p.chunk_log2, reinterpret_cast<uint32_t*>(ws + p.rows_off));
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pass 2
+
+// Merge kRowsPerPartial chunk rows per workgroup; thread = exponent bin.
+__global__ __launch_bounds__(256) void k_merge_rows(const uint32_t* __restrict__ rows,
+                                                    uint32_t chunks,
+                                                    uint64_t* __restrict__ partial) {
+    const uint32_t bin = threadIdx.x;
+    const uint32_t r0 = blockIdx.x * kRowsPerPartial;
+    const uint32_t r1 = min(r0 + kRowsPerPartial, chunks);
+    uint64_t s = 0;
+    for (uint32_t r = r0; r < r1; r++) s += rows[(uint64_t)r * 256 + bin];
+    partial[(uint64_t)blockIdx.x * 256 + bin] = s;
+}
+
+constexpr int kSelectThreads = 1024;
+constexpr int kSelectWaves = kSelectThreads / 64;
+
+__device__ __forceinline__ uint64_t wave_inclusive_sum(uint64_t v) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint64_t o = __shfl_up(v, d, 64);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+// One workgroup.  chunk_base[b] receives the number of escapes in chunks
+// before b, which is where chunk b's escape records start.
+__global__ __launch_bounds__(kSelectThreads) void k_select(
+    uint64_t n, uint32_t chunk_log2, uint32_t chunks, uint32_t partials,
+    const uint32_t* __restrict__ rows, const uint64_t* __restrict__ partial,
+    uint64_t* __restrict__ chunk_base, uint8_t* __restrict__ dst, uint64_t* d_size) {
+    __shared__ uint64_t part[4][256];
+    __shared__ uint64_t hist[256];
+    __shared__ uint32_t rank_part[4][256];
+    __shared__ uint32_t codebook[16];
+    __shared__ uint64_t wave_sum[kSelectWaves];
+    __shared__ uint64_t wave_off[kSelectWaves];
+    __shared__ uint64_t base_lds[kMaxChunks];
+
+    const int t = threadIdx.x;
+    const int bin = t & 255;
+    const int grp = t >> 8;  // 0..3
+    if (t < 16) codebook[t] = 0;
+
+    // exponent histogram of the whole tensor
+    uint64_t s = 0;
+    for (uint32_t q = grp; q < partials; q += 4) s += partial[(uint64_t)q * 256 + bin];
+    part[grp][bin] = s;
+    __syncthreads();
+    if (t < 256) hist[t] = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+    __syncthreads();
+
+    // rank(x) = #{y : h[y] > h[x] or (h[y] == h[x] and y < x)}; group g
+    // counts over y in [64g, 64g + 64)
+    {
+        const uint64_t hx = hist[bin];
+        uint32_t r = 0;
+        for (int y = grp * 64; y < grp * 64 + 64; y++) {
+            const uint64_t hy = hist[y];
+            r += (hy > hx) || (hy == hx && y < bin);
+        }
+        rank_part[grp][bin] = r;
+    }
+    __syncthreads();
+    if (t < 256) {
+        const uint32_t r = rank_part[0][t] + rank_part[1][t] + rank_part[2][t] + rank_part[3][t];
+        if (r < 16) codebook[r] = (uint32_t)t;
+    }
+    __syncthreads();
+
+    // escapes of chunks 2t and 2t+1 = chunk length - elements whose
+    // exponent is in the codebook
+    uint64_t esc[2] = {0, 0};
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+        const uint32_t b = 2 * t + j;
+        if (b < chunks) {
+            const uint64_t start = (uint64_t)b << chunk_log2;
+            const uint64_t len = min(1ull << chunk_log2, n - start);
+            const uint32_t* row = rows + (uint64_t)b * 256;
+            uint64_t kept = 0;
+#pragma unroll
+            for (int c = 0; c < 16; c++) kept += row[codebook[c] & 255u];
+            esc[j] = len - kept;
+        }
+    }
+
+    // exclusive scan of the per-chunk escape counts over the workgroup
+    const uint64_t mine = esc[0] + esc[1];
+    const uint64_t incl = wave_inclusive_sum(mine);
+    const int lane = t & 63, wave = t >> 6;
+    if (lane == 63) wave_sum[wave] = incl;
+    __syncthreads();
+    if (t == 0) {
+        uint64_t run = 0;
+        for (int w = 0; w < kSelectWaves; w++) {
+            wave_off[w] = run;
+            run += wave_sum[w];
+        }
+    }
+    __syncthreads();
+    const uint64_t excl = wave_off[wave] + incl - mine;
+    if (2 * t < chunks) {
+        chunk_base[2 * t] = excl;
+        base_lds[2 * t] = excl;
+    }
+    if (2 * t + 1 < chunks) {
+        chunk_base[2 * t + 1] = excl + esc[0];
+        base_lds[2 * t + 1] = excl + esc[0];
+    }
+    const uint64_t E = wave_off[kSelectWaves - 1] + wave_sum[kSelectWaves - 1];
+    __syncthreads();
+    const uint64_t total = kPrefixBytes + (n + 1) / 2 + n + 5 * E;
+    if (t == 0) {
+        *reinterpret_cast<uint32_t*>(dst + 0) = kMagic;
+        *reinterpret_cast<uint16_t*>(dst + 4) = kVersion;
+        *reinterpret_cast<uint16_t*>(dst + 6) = kElementBf16;
+        *reinterpret_cast<uint64_t*>(dst + 8) = n;
+        *reinterpret_cast<uint64_t*>(dst + 16) = E;
+        *reinterpret_cast<uint64_t*>(dst + 24) = total;
+        if (d_size) *d_size = total;
+    }
+    if (t < 16) {
+        // seg_end[t]: escapes below element (t+1) * 2^32 -- a chunk boundary,
+        // because chunks are powers of two no larger than 2^32
+        const uint64_t boundary_chunk = (uint64_t)(t + 1) << (32 - chunk_log2);
+        const uint64_t v = boundary_chunk < chunks ? base_lds[boundary_chunk] : E;
+        *reinterpret_cast<uint64_t*>(dst + 32 + 8 * t) = v;
+        dst[kHeaderBytes + t] = (uint8_t)codebook[t];
+    }
+}
+
+hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst, uint64_t* d_size,
+                           hipStream_t stream) {
+    const uint32_t* rows = reinterpret_cast<const uint32_t*>(ws + p.rows_off);
+    uint64_t* partial = reinterpret_cast<uint64_t*>(ws + p.partial_off);
+    if (p.partials > 0)
+        k_merge_rows<<<p.partials, 256, 0, stream>>>(rows, p.chunks, partial);
+    k_select<<<1, kSelectThreads, 0, stream>>>(p.n, p.chunk_log2, p.chunks, p.partials, rows,
+                                               partial,
+                                               reinterpret_cast<uint64_t*>(ws + p.base_off),
+                                               dst, d_size);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- pass 3
+
+constexpr int kPackThreads = 256;
+constexpr int kPackWaves = kPackThreads / 64;
+constexpr uint32_t kPackTile = kPackThreads * 8;  // words per workgroup step
+static_assert((1u << kMinChunkLog2) % kPackTile == 0, "chunks hold whole tiles");
+static_assert(kPackThreads == 256, "one LUT entry per thread");
+static_assert(2 * kSelectThreads >= kMaxChunks, "two chunks per select thread");
+
+// Rank of this lane's bits among lower lanes: popcount of mask below lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+template <bool kAlignedSm>
+__global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restrict__ src,
+                                                      uint64_t n, uint32_t chunk_log2,
+                                                      const uint64_t* __restrict__ chunk_base,
+                                                      uint8_t* __restrict__ dst,
+                                                      uint64_t dst_capacity) {
+    __shared__ uint8_t lut[256];            // exponent -> code, 0x10 = escape
+    __shared__ uint32_t wave_escapes[2][kPackWaves];
+
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
+    lut[t] = 0x10;
+    __syncthreads();
+    if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
+    __syncthreads();
+
+    const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
+    const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
+    // never write an escape record outside the caller's buffer, whatever
+    // the workspace and header hold: slots below E, and all 5E escape bytes
+    // inside the buffer
+    const uint64_t slot_limit =
+        (dst_capacity >= esc_off && E <= (dst_capacity - esc_off) / 5) ? E : 0;
+    uint8_t* nib = dst + kPrefixBytes;
+    uint8_t* sm = nib + (n + 1) / 2;
+    uint8_t* esc_pos = dst + esc_off;
+    uint8_t* esc_exp = esc_pos + 4 * E;
+    const bool pos_aligned = (esc_off & 3) == 0;
+
+    const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
+    const uint64_t end = min(begin + (1ull << chunk_log2), n);
+    uint64_t slot_base = chunk_base[blockIdx.x];
+
+    int parity = 0;
+    for (uint64_t t0 = begin; t0 < end; t0 += kPackTile, parity ^= 1) {
+        const uint64_t i0 = t0 + (uint64_t)t * 8;
+        const uint32_t valid = i0 + 8 <= end ? 8u : (i0 < end ? (uint32_t)(end - i0) : 0u);
+
+        uint32_t w[4] = {0, 0, 0, 0};
+        if (valid == 8) {
+            const uint4 v = *reinterpret_cast<const uint4*>(src + i0);
+            w[0] = v.x;
+            w[1] = v.y;
+            w[2] = v.z;
+            w[3] = v.w;
+        } else {
+            for (uint32_t k = 0; k < valid; k++) w[k >> 1] |= (uint32_t)src[i0 + k] << (16 * (k & 1));
+        }
+
+        uint32_t nibbles = 0, mask = 0, sm_lo = 0, sm_hi = 0, ex_lo = 0, ex_hi = 0;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            const uint32_t word = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
+            const uint32_t e = (word >> 7) & 0xFFu;
+            uint32_t code = lut[e];
+            if ((uint32_t)k >= valid) code = 0;
+            nibbles |= (code & 0xFu) << (4 * k);
+            mask |= (code >> 4) << k;
+            const uint32_t s = ((word >> 8) & 0x80u) | (word & 0x7Fu);
+            if (k < 4) {
+                sm_lo |= s << (8 * k);
+                ex_lo |= e << (8 * k);
+            } else {
+                sm_hi |= s << (8 * (k - 4));
+                ex_hi |= e << (8 * (k - 4));
+            }
+        }
+
+        if (valid == 8) {
+            *reinterpret_cast<uint32_t*>(nib + i0 / 2) = nibbles;
+            if (kAlignedSm) {
+                *reinterpret_cast<uint2*>(sm + i0) = make_uint2(sm_lo, sm_hi);
+            } else {
+#pragma unroll
+                for (int k = 0; k < 8; k++)
+                    sm[i0 + k] = (uint8_t)((k < 4 ? sm_lo >> (8 * k) : sm_hi >> (8 * (k - 4))) & 0xFF);
+            }
+        } else if (valid > 0) {
+            for (uint32_t j = 0; j < (valid + 1) / 2; j++)
+                nib[i0 / 2 + j] = (uint8_t)((nibbles >> (8 * j)) & 0xFF);
+            for (uint32_t k = 0; k < valid; k++)
+                sm[i0 + k] = (uint8_t)((k < 4 ? sm_lo >> (8 * k) : sm_hi >> (8 * (k - 4))) & 0xFF);
+        }
+
+        // Escape ranks: a lane has at most 8 escapes, so four ballots on the
+        // bits of its count give the exclusive prefix over the wave.
+        const uint32_t cnt = __popc(mask);
+        const uint64_t b0 = __ballot(cnt & 1u);
+        const uint64_t b1 = __ballot(cnt & 2u);
+        const uint64_t b2 = __ballot(cnt & 4u);
+        const uint64_t b3 = __ballot(cnt & 8u);
+        const uint32_t lane_prefix =
+            lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3);
+        if (lane == 0)
+            wave_escapes[parity][wave] = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) +
+                                         8 * __popcll(b3);
+        __syncthreads();
+        uint32_t before = 0, tile_total = 0;
+#pragma unroll
+        for (int v = 0; v < kPackWaves; v++) {
+            const uint32_t x = wave_escapes[parity][v];
+            before += v < wave ? x : 0u;
+            tile_total += x;
+        }
+
+        if (mask) {
+            uint64_t slot = slot_base + before + lane_prefix;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                if ((mask >> k) & 1u) {
+                    if (slot < slot_limit) {
+                        const uint32_t pos = (uint32_t)((i0 + k) & 0xFFFFFFFFull);
+                        if (pos_aligned) {
+                            *reinterpret_cast<uint32_t*>(esc_pos + 4 * slot) = pos;
+                        } else {
+                            esc_pos[4 * slot + 0] = (uint8_t)(pos & 0xFF);
+                            esc_pos[4 * slot + 1] = (uint8_t)((pos >> 8) & 0xFF);
+                            esc_pos[4 * slot + 2] = (uint8_t)((pos >> 16) & 0xFF);
+                            esc_pos[4 * slot + 3] = (uint8_t)(pos >> 24);
+                        }
+                        esc_exp[slot] =
+                            (uint8_t)((k < 4 ? ex_lo >> (8 * k) : ex_hi >> (8 * (k - 4))) & 0xFF);
+                    }
+                    slot++;
+                }
+            }
+        }
+        slot_base += tile_total;
+    }
+}
+
+hipError_t launch_pack(const uint16_t* src, const EncodePlan& p, const uint8_t* ws,
+                       uint8_t* dst, uint64_t dst_capacity, int /*num_cus*/,
+                       hipStream_t stream) {
+    if (p.chunks == 0) return hipSuccess;
+    const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
+    // the sign|mantissa stream starts at 176 + ceil(n/2): 16-byte aligned
+    // exactly when n is a multiple of 32
+    const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
+    if (aligned)
+        k_pack<true><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base, dst,
+                                                            dst_capacity);
+    else
+        k_pack<false><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base, dst,
+                                                             dst_capacity);
+    return hipGetLastError();
+}
+
+}  // namespace sz

@@ -1,0 +1,56 @@
+// sz_internal.h -- shared between the kernel and API translation units of
+// libsplitzip.so (not installed, not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sz {
+
+constexpr uint32_t kHeaderBytes = 160;
+constexpr uint32_t kPrefixBytes = 176;  // header + 16-byte codebook
+constexpr uint32_t kMagic = 0x564B5A53u;
+constexpr uint16_t kVersion = 1;
+constexpr uint16_t kElementBf16 = 1;
+constexpr uint64_t kMaxElements = 1ull << 36;
+
+// Encoding works on power-of-two chunks of the input.  The histogram pass
+// counts exponents per chunk, the codebook pass turns those counts into the
+// exact number of escapes of every chunk (and so into each chunk's first
+// escape slot), and the pack pass lets one workgroup stream one chunk.
+// A chunk is at least two pack tiles and the grid at most kMaxChunks.
+constexpr uint32_t kMinChunkLog2 = 12;
+constexpr uint32_t kMaxChunks = 2048;
+constexpr uint32_t kRowsPerPartial = 32;  // chunk rows merged per reduce block
+
+struct EncodePlan {
+    uint64_t n = 0;
+    uint32_t chunk_log2 = kMinChunkLog2;
+    uint32_t chunks = 0;    // G = ceil(n / 2^chunk_log2)
+    uint32_t partials = 0;  // ceil(G / kRowsPerPartial)
+    // workspace layout, byte offsets (256-byte aligned regions)
+    uint64_t rows_off = 0;     // u32[G][256]   per-chunk exponent counts
+    uint64_t partial_off = 0;  // u64[P][256]   merged counts
+    uint64_t base_off = 0;     // u64[G]        first escape slot of each chunk
+    uint64_t ws_bytes = 0;
+};
+
+EncodePlan plan_encode(uint64_t n);
+
+inline uint64_t container_bytes(uint64_t n, uint64_t e) {
+    return kPrefixBytes + (n + 1) / 2 + n + 5 * e;
+}
+
+// Launchers (asynchronous on `stream`; return the launch status).
+hipError_t launch_histogram(const uint16_t* src, const EncodePlan& p, uint8_t* ws,
+                            hipStream_t stream);
+hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst,
+                           uint64_t* d_size, hipStream_t stream);
+hipError_t launch_pack(const uint16_t* src, const EncodePlan& p, const uint8_t* ws,
+                       uint8_t* dst, uint64_t dst_capacity, int num_cus, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
+                         uint16_t* dst, int32_t* status, int num_cus, hipStream_t stream);
+hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* dst,
+                          int32_t* status, hipStream_t stream);
+
+}  // namespace sz

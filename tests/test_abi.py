@@ -1,0 +1,127 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/splitzip.h declares, and its host-only logic (size bounds,
+argument checks that return before anything touches a device) behaves as
+the header states.  No kernel is launched here."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "splitzip.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sz_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def sz():
+    import lossless_bf16_kv_split_amd as m
+    return m
+
+
+def test_header_declares_the_codec_calls():
+    names = declared_functions()
+    for must in ("sz_max_compressed_size", "sz_encode", "sz_decode"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(sz):
+    out = subprocess.run(["nm", "-D", "--defined-only", sz.lib_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sz_\w+)", out))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    for n in declared_functions():
+        assert hasattr(sz._lib, n)
+
+
+def test_no_oracle_in_product_library(sz):
+    out = subprocess.run(["nm", "-D", sz.lib_path], capture_output=True, text=True,
+                         check=True).stdout
+    assert "szref" not in out
+    deps = subprocess.run(["ldd", sz.lib_path], capture_output=True, text=True).stdout
+    assert "szref" not in deps
+
+
+def test_max_compressed_size_matches_closed_form(sz):
+    for n in list(range(0, 100)) + [1 << 20, (1 << 29) + 1, 1 << 36]:
+        assert sz.sz_max_compressed_size(n) == 176 + (n + 1) // 2 + n + 5 * ((15 * n) // 16)
+        assert sz.sz_max_compressed_size(n) == oracle.max_compressed_size(n)
+    assert sz.sz_max_compressed_size((1 << 36) + 1) == 0
+
+
+def test_workspace_is_small(sz):
+    assert sz.sz_workspace_size(0) > 0
+    for n in (1, 4096, 1 << 21, 1 << 29, 5 << 30, 1 << 36):
+        ws = sz.sz_workspace_size(n)
+        assert 0 < ws <= 2304 * 1024, (n, ws)
+    assert sz.sz_workspace_size((1 << 36) + 1) == 0
+
+
+def test_status_strings(sz):
+    for s in range(6):
+        assert sz.sz_status_string(s)
+    assert sz.sz_status_string(99) == "unknown status"
+
+
+# Fake device addresses: the calls below must reject them on the host, before
+# any HIP call, so they are never dereferenced.
+A = 0x7F0000000000
+MIS = A + 2
+
+
+def status_of(fn, *args):
+    try:
+        fn(*args)
+    except Exception as e:  # SplitZipError
+        return e.status
+    return 0
+
+
+def test_encode_host_checks(sz):
+    cap = sz.sz_max_compressed_size(1000)
+    assert status_of(sz.sz_encode, A, (1 << 36) + 1, A + (1 << 40), 1 << 62, None, 0) == 3
+    assert status_of(sz.sz_encode, A, 1000, None, cap, None, 0) == 1
+    assert status_of(sz.sz_encode, None, 1000, A + (1 << 30), cap, None, 0) == 1
+    assert status_of(sz.sz_encode, MIS, 1000, A + (1 << 30), cap, None, 0) == 1
+    assert status_of(sz.sz_encode, A, 1000, A + (1 << 30) + 8, cap, None, 0) == 1
+    assert status_of(sz.sz_encode, A, 1000, A + (1 << 30), cap - 1, None, 0) == 2
+    assert status_of(sz.sz_encode, A, 1000, A + 1024, cap, None, 0) == 1      # overlap
+
+
+def test_decode_host_checks(sz):
+    n = 1000
+    fixed = 176 + (n + 1) // 2 + n
+    B = A + (1 << 30)
+    assert status_of(sz.sz_decode, A, fixed, B, (1 << 36) + 1, None, 0) == 3
+    assert status_of(sz.sz_decode, None, fixed, B, n, None, 0) == 1
+    assert status_of(sz.sz_decode, A, fixed, None, n, None, 0) == 1
+    assert status_of(sz.sz_decode, MIS, fixed, B, n, None, 0) == 1
+    assert status_of(sz.sz_decode, A, fixed - 1, B, n, None, 0) == 4          # too short
+    assert status_of(sz.sz_decode, A, fixed + 3, B, n, None, 0) == 4          # not 5E
+    too_many = fixed + 5 * ((15 * n) // 16 + 1)
+    assert status_of(sz.sz_decode, A, too_many, B, n, None, 0) == 4
+    assert status_of(sz.sz_decode, A, fixed, A + 64, n, None, 0) == 1         # overlap
+    for fn in (sz.sz_decode_unpack, sz.sz_decode_scatter):
+        assert status_of(fn, A, fixed - 1, B, n, None, 0) == 4
+
+
+def test_staged_host_checks(sz):
+    n = 1 << 20
+    ws = sz.sz_workspace_size(n)
+    cap = sz.sz_max_compressed_size(n)
+    W, D = A + (1 << 32), A + (1 << 33)
+    assert status_of(sz.sz_encode_histogram, A, n, W, ws - 1, 0) == 1        # small workspace
+    assert status_of(sz.sz_encode_histogram, A, n, W + 16, ws, 0) == 1       # misaligned
+    assert status_of(sz.sz_encode_histogram, A, n, None, ws, 0) == 1
+    assert status_of(sz.sz_encode_codebook, n, W, ws, D, cap - 1, None, 0) == 2
+    assert status_of(sz.sz_encode_codebook, n, W, ws - 256, D, cap, None, 0) == 1
+    assert status_of(sz.sz_encode_pack, A, n, W, ws, D, cap - 1, 0) == 2
+    assert status_of(sz.sz_encode_pack, A, n, None, ws, D, cap, 0) == 1

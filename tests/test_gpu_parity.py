@@ -1,0 +1,319 @@
+"""GPU parity: the HIP codec against the CPU oracle, through the C ABI.
+
+Bit-exact everywhere (the codec is integer-only): the compressed container
+must equal the oracle's byte for byte, and decoding must give back every
+input bit.  Both directions of cross-decoding are checked (GPU decode of the
+oracle's container, oracle decode of the GPU's container).  Full-size
+workloads are compared in full; the 10.7 GB one against the oracle's stored
+SHA-256 (tests/golden/workload_digests.json, written by
+tests/golden/make_workload_digests.py from the oracle alone)."""
+import hashlib
+import json
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import kvgen
+import oracle
+import szformat
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a ROCm device"
+    t.cuda.set_device(0)
+    return t
+
+
+@pytest.fixture(scope="module")
+def sz(torch):
+    import lossless_bf16_kv_split_amd as m
+    return m
+
+
+def to_dev(torch, words: np.ndarray):
+    return torch.from_numpy(np.ascontiguousarray(words).view(np.int16)).cuda()
+
+
+def gpu_encode(torch, sz, x, n):
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sz.sz_encode(x, n, dst, cap, size)
+    total = int(size.item())
+    return dst[:total]
+
+
+GUARD = 64
+SENTINEL = 0x5A5A
+
+
+def gpu_decode(torch, sz, container_dev, n):
+    """Decode into a buffer with GUARD sentinel words after element n; returns
+    (words tensor of n, device status, guard intact)."""
+    out = torch.full((n + GUARD,), SENTINEL, dtype=torch.int16, device="cuda")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    sz.sz_decode(container_dev, container_dev.numel(), out, n, status)
+    torch.cuda.synchronize()
+    guard_ok = bool((out[n:] == SENTINEL).all().item())
+    return out[:n], int(status.item()), guard_ok
+
+
+# ---- inputs -------------------------------------------------------------------
+
+def make_words(kind: str, n: int, seed: int) -> np.ndarray:
+    rng = np.random.default_rng([seed, n, len(kind)])
+    if kind == "kv":
+        return kvgen.small_kv(n, seed)
+    if kind == "random":          # every exponent: escape heavy
+        return rng.integers(0, 65536, n, dtype=np.uint16)
+    if kind == "narrow":          # fewer than 16 distinct exponents
+        e = rng.choice(np.array([3, 77, 126, 127, 200], dtype=np.uint16), n)
+        return ((rng.integers(0, 2, n, dtype=np.uint16) << 15) | (e << 7) |
+                rng.integers(0, 128, n, dtype=np.uint16)).astype(np.uint16)
+    if kind == "wide40":          # exponents uniform over 40 values
+        e = rng.integers(100, 140, n, dtype=np.uint16)
+        return ((rng.integers(0, 2, n, dtype=np.uint16) << 15) | (e << 7) |
+                rng.integers(0, 128, n, dtype=np.uint16)).astype(np.uint16)
+    if kind == "ties":            # 20 exponents, equal counts: tie-break decides
+        e = (np.arange(n) % 20 + 110).astype(np.uint16)
+        rng.shuffle(e)
+        return ((e << 7) | rng.integers(0, 128, n, dtype=np.uint16)).astype(np.uint16)
+    if kind == "special":         # zeros, subnormals, Inf, NaN mixed into KV
+        w = kvgen.small_kv(n, seed)
+        pick = rng.integers(0, 8, n)
+        pay = rng.integers(1, 128, n, dtype=np.uint16)
+        sign = (rng.integers(0, 2, n, dtype=np.uint16) << 15).astype(np.uint16)
+        w = np.where(pick == 0, sign, w)
+        w = np.where(pick == 1, sign | pay, w)
+        w = np.where(pick == 2, sign | 0x7F80, w)
+        w = np.where(pick == 3, sign | 0x7F80 | pay, w)
+        return w.astype(np.uint16)
+    raise KeyError(kind)
+
+
+SIZES = [0, 1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257,
+         1000, 2047, 2048, 2049, 4095, 4096, 4097, 8191, 8192, 8193, 12345, 65535, 65536,
+         65537, (1 << 20) - 1, (1 << 20) + 1, 3 * (1 << 20) + 17]
+KINDS = ["kv", "random", "narrow", "wide40", "ties", "special"]
+
+
+def check_case(torch, sz, words: np.ndarray, label: str):
+    n = words.size
+    say(label, "n =", n)
+    want = oracle.encode(words)
+    x = to_dev(torch, words) if n else torch.empty(0, dtype=torch.int16, device="cuda")
+    got_dev = gpu_encode(torch, sz, x, n)
+    got = got_dev.cpu().numpy()
+    assert got.size == want.size, (label, got.size, want.size)
+    if not np.array_equal(got, want):
+        bad = np.nonzero(got != want)[0]
+        raise AssertionError(f"{label}: {bad.size} container bytes differ, first at {bad[:8]}")
+    # GPU decode of the GPU container, GPU decode of the oracle container
+    y, st, guard = gpu_decode(torch, sz, got_dev, n)
+    assert st == 0 and guard, (label, st, guard)
+    assert torch.equal(y, x), label
+    y2, st2, guard2 = gpu_decode(torch, sz, torch.from_numpy(want).cuda(), n)
+    assert st2 == 0 and guard2 and torch.equal(y2, x), label
+    # oracle decode of the GPU container
+    assert np.array_equal(oracle.decode(got, n), words), label
+
+
+@pytest.mark.parametrize("kind", KINDS)
+def test_small_sizes(torch, sz, kind):
+    for i, n in enumerate(SIZES):
+        check_case(torch, sz, make_words(kind, n, 1000 + i), f"{kind}")
+
+
+def test_every_pattern(torch, sz):
+    words = np.arange(65536, dtype=np.uint16)
+    check_case(torch, sz, words, "all 65536 patterns")
+    rng = np.random.default_rng(5)
+    check_case(torch, sz, rng.permutation(np.tile(words, 7)), "all patterns x7 shuffled")
+
+
+def test_worked_example(torch, sz):
+    with open(os.path.join(GOLDEN, "worked_example_escape.json")) as f:
+        g = json.load(f)
+    words = np.array(g["words"], dtype=np.uint16)
+    check_case(torch, sz, words, "worked example")
+    got = gpu_encode(torch, sz, to_dev(torch, words), words.size).cpu().numpy()
+    r = szformat.read(got)
+    assert [[int(p), int(e)] for p, e in zip(r.positions, r.exps)] == g["expected_escapes"]
+
+
+def test_many_chunks_ragged(torch, sz):
+    # more than 2048 minimum-size chunks: larger chunks, a ragged last chunk
+    for n in (2048 * 4096 + 123, 2 * 2048 * 8192 + 77):
+        check_case(torch, sz, make_words("kv", n, 7), "many chunks kv")
+    check_case(torch, sz, make_words("wide40", 2048 * 4096 + 5, 8), "many chunks wide40")
+
+
+def sha256(a: np.ndarray) -> str:
+    h = hashlib.sha256()
+    mv = memoryview(np.ascontiguousarray(a).reshape(-1).view(np.uint8))
+    for i in range(0, len(mv), 1 << 28):
+        h.update(mv[i:i + (1 << 28)])
+    return h.hexdigest()
+
+
+def digests():
+    with open(os.path.join(GOLDEN, "workload_digests.json")) as f:
+        return json.load(f)
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["single_layer_kv", "llama3_8b_kv_8k", "escape_heavy",
+                                  "special_values"])
+def test_workload_full(torch, sz, name):
+    say("workload", name)
+    words = kvgen.generate(name)
+    d = digests()[name]
+    assert sha256(words) == d["input_sha256"], "input generator drifted"
+    x = to_dev(torch, words)
+    got_dev = gpu_encode(torch, sz, x, words.size)
+    got = got_dev.cpu().numpy()
+    want = oracle.encode(words)
+    assert got.size == want.size == d["container_bytes"]
+    assert np.array_equal(got, want), f"{name}: container differs from the oracle"
+    assert sha256(got) == d["container_sha256"]
+    y, st, guard = gpu_decode(torch, sz, got_dev, words.size)
+    assert st == 0 and guard and torch.equal(y, x)
+    del y
+    assert np.array_equal(oracle.decode(got, words.size), words)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(1100)
+def test_workload_70b_32k(torch, sz):
+    """10.7 GB, more than 2^32 elements: two position segments."""
+    name = "llama3_70b_kv_32k"
+    d = digests()[name]
+    say("workload", name, "generate")
+    words = kvgen.generate(name)
+    assert words.size > (1 << 32)
+    assert sha256(words) == d["input_sha256"], "input generator drifted"
+    say("upload")
+    x = to_dev(torch, words)
+    del words
+    say("encode")
+    got_dev = gpu_encode(torch, sz, x, x.numel())
+    assert got_dev.numel() == d["container_bytes"]
+    say("header")
+    head = got_dev[:176].cpu().numpy()
+    r = szformat.read(np.concatenate([head, np.zeros(0, np.uint8)]))
+    assert r.e == d["escapes"]
+    assert r.codebook.tolist() == d["codebook"]
+    assert r.seg_end.tolist() == d["seg_end"]
+    say("digest")
+    assert sha256(got_dev.cpu().numpy()) == d["container_sha256"]
+    say("decode")
+    y, st, guard = gpu_decode(torch, sz, got_dev, x.numel())
+    assert st == 0 and guard
+    assert torch.equal(y, x)
+
+
+def test_staged_calls_match_encode(torch, sz):
+    words = kvgen.generate("single_layer_kv")
+    n = words.size
+    x = to_dev(torch, words)
+    ws_bytes = sz.sz_workspace_size(n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sz.sz_encode_histogram(x, n, ws, ws_bytes)
+    sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
+    sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap)
+    staged = dst[: int(size.item())].cpu().numpy()
+    assert np.array_equal(staged, oracle.encode(words))
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    c = dst[: int(size.item())]
+    sz.sz_decode_unpack(c, c.numel(), out, n, status)
+    sz.sz_decode_scatter(c, c.numel(), out, n, status)
+    assert int(status.item()) == 0 and torch.equal(out, x)
+
+
+def test_deterministic_and_streams(torch, sz):
+    words = kvgen.generate("escape_heavy")[: 1 << 24]
+    n = words.size
+    x = to_dev(torch, words)
+    first = gpu_encode(torch, sz, x, n).clone()
+    for _ in range(5):
+        assert torch.equal(gpu_encode(torch, sz, x, n), first)
+    # two encodes at once on two streams
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    cap = sz.sz_max_compressed_size(n)
+    d1 = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    d2 = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    for _ in range(3):
+        sz.sz_encode(x, n, d1, cap, None, s1)
+        sz.sz_encode(x, n, d2, cap, None, s2)
+    torch.cuda.synchronize()
+    m = first.numel()
+    assert torch.equal(d1[:m], first) and torch.equal(d2[:m], first)
+
+
+def test_corrupt_containers_flagged_on_device(torch, sz):
+    rng = np.random.default_rng(16)
+    n = 5000
+    words = ((rng.integers(0, 2, n) << 15) | (rng.integers(90, 130, n) << 7) |
+             rng.integers(0, 128, n)).astype(np.uint16)
+    good = oracle.encode(words)
+    r = szformat.read(good)
+    assert r.e > 10
+    esc = 176 + (n + 1) // 2 + n
+
+    def status(c):
+        _, st, guard = gpu_decode(torch, sz, torch.from_numpy(c).cuda(), n)
+        assert guard, "decode wrote past element n"
+        return st
+
+    assert status(good) == 0
+    cases = {
+        "magic": (0, good[0] ^ 1), "version": (4, 2), "type": (6, 2), "n": (8, good[8] ^ 1),
+        "e": (16, good[16] ^ 1), "total": (24, good[24] ^ 1), "seg_end0": (32, 0),
+        "seg_end1": (40, good[40] + 1),
+    }
+    for what, (off, val) in cases.items():
+        c = good.copy()
+        c[off] = val
+        assert status(c) == 4, what
+    for what, pos in {"pos >= n": n, "pos = 2^32 - 1": 0xFFFFFFFF}.items():
+        c = good.copy()
+        c[esc + 4 * 3:esc + 4 * 4] = np.frombuffer(np.uint32(pos).tobytes(), np.uint8)
+        assert status(c) == 4, what
+    c = good.copy()
+    c[esc:esc + 4], c[esc + 4:esc + 8] = good[esc + 4:esc + 8].copy(), good[esc:esc + 4].copy()
+    assert status(c) == 4, "not ascending"
+
+
+def test_host_errors_with_real_buffers(torch, sz):
+    n = 4096
+    x = torch.zeros(n, dtype=torch.int16, device="cuda")
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.sz_encode(x, n, dst, cap - 1)
+    assert e.value.status == 2
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.sz_encode(x[1:], n - 1, dst, cap)
+    assert e.value.status == 1
+    c = sz.encode(x)
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.sz_decode(c, c.numel() - 1, x, n)
+    assert e.value.status == 4

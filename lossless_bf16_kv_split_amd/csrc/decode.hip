@@ -19,48 +19,57 @@ constexpr int kUnpackThreads = 256;
 constexpr int kScatterThreads = 256;
 constexpr int32_t kStatusCorrupt = 4;
 
-// The 16-byte codebook held in registers as two 64-bit halves.
-struct Codebook {
-    uint64_t lo;  // codes 0..7
-    uint64_t hi;  // codes 8..15
-};
-
-__device__ __forceinline__ Codebook load_codebook(const uint8_t* src) {
-    const uint4 v = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
-    return Codebook{(uint64_t)v.x | ((uint64_t)v.y << 32), (uint64_t)v.z | ((uint64_t)v.w << 32)};
+// v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value
+// {hi (bytes 4..7), lo (bytes 0..3)}.
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
 }
 
-// exponent of code c (0..15); the half is chosen with a mask rather than a
-// branch or select so that the codebook stays in registers
-__device__ __forceinline__ uint32_t codebook_exponent(Codebook cb, uint32_t c) {
-    const uint64_t take_hi = 0ull - (uint64_t)((c >> 3) & 1u);
-    const uint64_t half = cb.lo ^ ((cb.lo ^ cb.hi) & take_hi);
-    return (uint32_t)(half >> (8 * (c & 7u))) & 0xFFu;
+// bitwise select: bits of a where m is set, bits of b elsewhere (v_bfi_b32)
+__device__ __forceinline__ uint32_t bitselect(uint32_t m, uint32_t a, uint32_t b) {
+    return (m & a) | (~m & b);
 }
 
-// sign in bit 7 and mantissa in bits 6..0 of sm, exponent between them
+// Four 4-bit codes, one per byte of x, to their four exponent bytes; the
+// 16-byte codebook sits in four registers cb0..cb3.  Codes 0..7 come from
+// cb0:cb1, codes 8..15 from cb2:cb3, chosen per byte by bit 3 of the code.
+__device__ __forceinline__ uint32_t lookup4(uint32_t x, uint4 cb) {
+    const uint32_t sel = x & 0x07070707u;
+    const uint32_t lo = perm(cb.y, cb.x, sel);
+    const uint32_t hi = perm(cb.w, cb.z, sel);
+    const uint32_t bit3 = (x >> 3) & 0x01010101u;
+    return bitselect((bit3 << 8) - bit3, hi, lo);  // 0xFF in every byte with bit 3 set
+}
+
+// Eight words from one dword of codes (element 2j in the low nibble of byte
+// j) and eight sign|mantissa bytes s0 (elements 0..3), s1 (4..7).  Per
+// byte lane: high byte of the word = sign | exponent >> 1, low byte =
+// (exponent & 1) << 7 | mantissa; then the two byte streams are interleaved.
+__device__ __forceinline__ uint4 decode8(uint32_t codes, uint32_t s0, uint32_t s1, uint4 cb) {
+    const uint32_t even = lookup4(codes & 0x0F0F0F0Fu, cb);         // elements 0,2,4,6
+    const uint32_t odd = lookup4((codes >> 4) & 0x0F0F0F0Fu, cb);   // elements 1,3,5,7
+    const uint32_t e0 = perm(odd, even, 0x05010400u);               // elements 0..3
+    const uint32_t e1 = perm(odd, even, 0x07030602u);               // elements 4..7
+    const uint32_t h0 = bitselect(0x80808080u, s0, e0 >> 1);
+    const uint32_t l0 = bitselect(0x80808080u, e0 << 7, s0);
+    const uint32_t h1 = bitselect(0x80808080u, s1, e1 >> 1);
+    const uint32_t l1 = bitselect(0x80808080u, e1 << 7, s1);
+    return make_uint4(perm(h0, l0, 0x05010400u), perm(h0, l0, 0x07030602u),
+                      perm(h1, l1, 0x05010400u), perm(h1, l1, 0x07030602u));
+}
+
+// one word, for the last n % 8 elements
 __device__ __forceinline__ uint32_t recombine(uint32_t sm, uint32_t e) {
     return ((sm & 0x80u) << 8) | (e << 7) | (sm & 0x7Fu);
 }
 
-// Two words from one nibble byte (low nibble = first word) and two
-// sign|mantissa bytes (low byte = first word); returns them as one dword.
-__device__ __forceinline__ uint32_t word_pair(uint32_t code_byte, uint32_t sm_pair,
-                                              Codebook cb) {
-    const uint32_t lo = recombine(sm_pair & 0xFFu, codebook_exponent(cb, code_byte & 0xFu));
-    const uint32_t hi =
-        recombine((sm_pair >> 8) & 0xFFu, codebook_exponent(cb, (code_byte >> 4) & 0xFu));
-    return lo | (hi << 16);
+__device__ __forceinline__ uint32_t codebook_byte(uint4 cb, uint32_t c) {
+    return lookup4(c, cb) & 0xFFu;
 }
 
 __device__ __forceinline__ uint32_t load4_unaligned(const uint8_t* q) {
     return (uint32_t)q[0] | ((uint32_t)q[1] << 8) | ((uint32_t)q[2] << 16) |
            ((uint32_t)q[3] << 24);
-}
-
-__device__ __forceinline__ uint4 load16_unaligned(const uint8_t* q) {
-    return make_uint4(load4_unaligned(q), load4_unaligned(q + 4), load4_unaligned(q + 8),
-                      load4_unaligned(q + 12));
 }
 
 __device__ bool header_ok(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e) {
@@ -91,40 +100,46 @@ __global__ __launch_bounds__(kUnpackThreads) void k_unpack(const uint8_t* __rest
     if (blockIdx.x == 0 && threadIdx.x == 0 && status)
         *status = header_ok(src, src_bytes, n, e) ? 0 : kStatusCorrupt;
 
-    const Codebook cb = load_codebook(src);
+    const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
     const uint8_t* nib = src + kPrefixBytes;
     const uint8_t* sm = nib + (n + 1) / 2;
 
-    const uint64_t groups = n / 16;  // 16 words per thread step
+    // 8 words per thread step: 4 code bytes + 8 sm bytes in, 16 bytes out
+    const uint64_t groups = n / 8;
     const uint64_t stride = (uint64_t)gridDim.x * kUnpackThreads;
     for (uint64_t g = (uint64_t)blockIdx.x * kUnpackThreads + threadIdx.x; g < groups; g += stride) {
-        const uint2 c = *reinterpret_cast<const uint2*>(nib + 8 * g);
-        const uint4 s = kAlignedSm ? *reinterpret_cast<const uint4*>(sm + 16 * g)
-                                   : load16_unaligned(sm + 16 * g);
-        uint4* dst = reinterpret_cast<uint4*>(out + 16 * g);
-        dst[0] = make_uint4(word_pair(c.x, s.x, cb), word_pair(c.x >> 8, s.x >> 16, cb),
-                            word_pair(c.x >> 16, s.y, cb), word_pair(c.x >> 24, s.y >> 16, cb));
-        dst[1] = make_uint4(word_pair(c.y, s.z, cb), word_pair(c.y >> 8, s.z >> 16, cb),
-                            word_pair(c.y >> 16, s.w, cb), word_pair(c.y >> 24, s.w >> 16, cb));
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(nib + 4 * g);
+        uint32_t s0, s1;
+        if (kAlignedSm) {
+            const uint2 v = *reinterpret_cast<const uint2*>(sm + 8 * g);
+            s0 = v.x;
+            s1 = v.y;
+        } else {
+            s0 = load4_unaligned(sm + 8 * g);
+            s1 = load4_unaligned(sm + 8 * g + 4);
+        }
+        *reinterpret_cast<uint4*>(out + 8 * g) = decode8(codes, s0, s1, cb);
     }
 
-    // the last n % 16 words
+    // the last n % 8 words
     if (blockIdx.x == gridDim.x - 1) {
-        for (uint64_t i = groups * 16 + threadIdx.x; i < n; i += kUnpackThreads) {
+        for (uint64_t i = groups * 8 + threadIdx.x; i < n; i += kUnpackThreads) {
             const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
-            out[i] = (uint16_t)recombine(sm[i], codebook_exponent(cb, code));
+            out[i] = (uint16_t)recombine(sm[i], codebook_byte(cb, code));
         }
     }
 }
 
 hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                          uint16_t* dst, int32_t* status, int num_cus, hipStream_t stream) {
-    const uint64_t groups = n / 16;
+    const uint64_t groups = n / 8;
     uint64_t blocks = (groups + kUnpackThreads - 1) / kUnpackThreads;
-    const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * 8;
+    // four workgroups per CU: measured fastest for this read 1.5 / write 2
+    // byte stream (more resident waves only add DRAM page conflicts)
+    const uint64_t cap = (uint64_t)(num_cus > 0 ? num_cus : 256) * 4;
     if (blocks > cap) blocks = cap;
     if (blocks == 0) blocks = 1;  // header check and tail still run
-    const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 15) == 0;
+    const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
     if (aligned)
         k_unpack<true><<<(uint32_t)blocks, kUnpackThreads, 0, stream>>>(src, src_bytes, n, e,
                                                                        dst, status);
@@ -158,7 +173,6 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(const uint8_t* __re
     const uint64_t k = (uint64_t)blockIdx.x * kScatterThreads + threadIdx.x;
     if (k >= e) return;
     const uint64_t* seg_end = reinterpret_cast<const uint64_t*>(src + 32);
-    const uint8_t* sm = src + kPrefixBytes + (n + 1) / 2;
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
     const uint8_t* pos_lo = src + esc_off;
     const uint8_t* exps = pos_lo + 4 * e;
@@ -173,7 +187,10 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(const uint8_t* __re
                                    __HIP_MEMORY_SCOPE_AGENT);
         return;
     }
-    out[p] = (uint16_t)recombine(sm[p], exps[k]);
+    // the unpack pass already wrote sign and mantissa: replace the exponent
+    // field in place (reading the word's own line, not the sm stream's)
+    const uint32_t w = out[p];
+    out[p] = (uint16_t)((w & 0x807Fu) | ((uint32_t)exps[k] << 7));
 }
 
 hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* dst,

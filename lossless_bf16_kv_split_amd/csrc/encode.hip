@@ -42,7 +42,10 @@ EncodePlan plan_encode(uint64_t n) {
 // ---------------------------------------------------------------- pass 1
 
 constexpr int kHistThreads = 256;
-constexpr int kHistCopies = 8;    // sub-histograms per workgroup
+// Sub-histograms per workgroup, lane i adding into copy i % 32.  KV
+// exponents crowd into a few bins, so fewer copies serialise on same-address
+// LDS atomics; from 16 copies up the pass runs at the speed of its loads.
+constexpr int kHistCopies = 32;
 constexpr int kHistPitch = 257;   // odd pitch: copies of one bin sit in different banks
 
 __device__ __forceinline__ void hist_add(uint32_t* h, uint32_t e) {
@@ -119,7 +122,15 @@ __global__ __launch_bounds__(256) void k_merge_rows(const uint32_t* __restrict__
     const uint32_t r0 = blockIdx.x * kRowsPerPartial;
     const uint32_t r1 = min(r0 + kRowsPerPartial, chunks);
     uint64_t s = 0;
-    for (uint32_t r = r0; r < r1; r++) s += rows[(uint64_t)r * 256 + bin];
+    uint32_t r = r0;
+    for (; r + 8 <= r1; r += 8) {  // eight loads in flight per thread
+        uint32_t v[8];
+#pragma unroll
+        for (int j = 0; j < 8; j++) v[j] = rows[(uint64_t)(r + j) * 256 + bin];
+#pragma unroll
+        for (int j = 0; j < 8; j++) s += v[j];
+    }
+    for (; r < r1; r++) s += rows[(uint64_t)r * 256 + bin];
     partial[(uint64_t)blockIdx.x * 256 + bin] = s;
 }
 
@@ -143,7 +154,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     const uint32_t* __restrict__ rows, const uint64_t* __restrict__ partial,
     uint64_t* __restrict__ chunk_base, uint8_t* __restrict__ dst, uint64_t* d_size) {
     __shared__ uint64_t part[4][256];
-    __shared__ uint64_t hist[256];
+    __shared__ uint64_t key[256];
     __shared__ uint32_t rank_part[4][256];
     __shared__ uint32_t codebook[16];
     __shared__ uint64_t wave_sum[kSelectWaves];
@@ -157,21 +168,28 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 
     // exponent histogram of the whole tensor
     uint64_t s = 0;
-    for (uint32_t q = grp; q < partials; q += 4) s += partial[(uint64_t)q * 256 + bin];
+    uint32_t q = grp;
+    for (; q + 12 < partials; q += 16) {  // four loads in flight per thread
+        uint64_t v[4];
+#pragma unroll
+        for (int j = 0; j < 4; j++) v[j] = partial[(uint64_t)(q + 4 * j) * 256 + bin];
+#pragma unroll
+        for (int j = 0; j < 4; j++) s += v[j];
+    }
+    for (; q < partials; q += 4) s += partial[(uint64_t)q * 256 + bin];
     part[grp][bin] = s;
     __syncthreads();
-    if (t < 256) hist[t] = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+    // key(x) = count << 8 | (255 - x): "more frequent, then smaller exponent"
+    // becomes one unsigned comparison (counts stay below 2^37)
+    if (t < 256) key[t] = ((part[0][t] + part[1][t] + part[2][t] + part[3][t]) << 8) | (255u - t);
     __syncthreads();
 
-    // rank(x) = #{y : h[y] > h[x] or (h[y] == h[x] and y < x)}; group g
-    // counts over y in [64g, 64g + 64)
+    // rank(x) = #{y : key(y) > key(x)}; group g counts over y in [64g, 64g + 64)
     {
-        const uint64_t hx = hist[bin];
+        const uint64_t kx = key[bin];
         uint32_t r = 0;
-        for (int y = grp * 64; y < grp * 64 + 64; y++) {
-            const uint64_t hy = hist[y];
-            r += (hy > hx) || (hy == hx && y < bin);
-        }
+#pragma unroll 16
+        for (int y = grp * 64; y < grp * 64 + 64; y++) r += key[y] > kx ? 1u : 0u;
         rank_part[grp][bin] = r;
     }
     __syncthreads();
@@ -183,6 +201,9 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 
     // escapes of chunks 2t and 2t+1 = chunk length - elements whose
     // exponent is in the codebook
+    uint32_t cb[16];
+#pragma unroll
+    for (int c = 0; c < 16; c++) cb[c] = codebook[c] & 255u;
     uint64_t esc[2] = {0, 0};
 #pragma unroll
     for (int j = 0; j < 2; j++) {
@@ -191,9 +212,12 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
             const uint64_t start = (uint64_t)b << chunk_log2;
             const uint64_t len = min(1ull << chunk_log2, n - start);
             const uint32_t* row = rows + (uint64_t)b * 256;
+            uint32_t v[16];
+#pragma unroll
+            for (int c = 0; c < 16; c++) v[c] = row[cb[c]];
             uint64_t kept = 0;
 #pragma unroll
-            for (int c = 0; c < 16; c++) kept += row[codebook[c] & 255u];
+            for (int c = 0; c < 16; c++) kept += v[c];
             esc[j] = len - kept;
         }
     }
@@ -258,17 +282,98 @@ hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst, uint6
 
 // ---------------------------------------------------------------- pass 3
 
-constexpr int kPackThreads = 256;
+// 16 waves per workgroup and 8192-word tiles: measured fastest for this
+// read 2 / write 1.5 byte stream (fewer, longer concurrent streams).
+constexpr int kPackThreads = 1024;
 constexpr int kPackWaves = kPackThreads / 64;
 constexpr uint32_t kPackTile = kPackThreads * 8;  // words per workgroup step
 static_assert((1u << kMinChunkLog2) % kPackTile == 0, "chunks hold whole tiles");
-static_assert(kPackThreads == 256, "one LUT entry per thread");
+static_assert(kPackThreads >= 256, "one LUT entry per thread");
 static_assert(2 * kSelectThreads >= kMaxChunks, "two chunks per select thread");
 
 // Rank of this lane's bits among lower lanes: popcount of mask below lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Split 8 BF16 words (two per dword, little-endian) into 8 sign|mantissa
+// bytes and 8 exponent bytes, 4 per dword, element k in byte k % 4.
+// v_perm gathers the high and low bytes of 4 words; the sign is bit 7 of
+// the high byte, the mantissa bits 6..0 of the low byte, the exponent the
+// high byte's low 7 bits above the low byte's bit 7.
+__device__ __forceinline__ void split8(const uint32_t w[4], uint32_t& sm_lo, uint32_t& sm_hi,
+                                       uint32_t& ex_lo, uint32_t& ex_hi) {
+    const uint32_t hi0 = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u);
+    const uint32_t lo0 = __builtin_amdgcn_perm(w[1], w[0], 0x06040200u);
+    const uint32_t hi1 = __builtin_amdgcn_perm(w[3], w[2], 0x07050301u);
+    const uint32_t lo1 = __builtin_amdgcn_perm(w[3], w[2], 0x06040200u);
+    sm_lo = (hi0 & 0x80808080u) | (lo0 & 0x7F7F7F7Fu);
+    sm_hi = (hi1 & 0x80808080u) | (lo1 & 0x7F7F7F7Fu);
+    ex_lo = ((hi0 << 1) & 0xFEFEFEFEu) | ((lo0 >> 7) & 0x01010101u);
+    ex_hi = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
+}
+
+__device__ __forceinline__ uint32_t byte_of(uint32_t lo, uint32_t hi, int k) {
+    return ((k < 4 ? lo : hi) >> (8 * (k & 3))) & 0xFFu;
+}
+
+// Escape records of one pack tile go to their final slots: a lane holds at
+// most 8 escapes, so four ballots on the bits of its count give its
+// exclusive prefix within the wave; wave totals meet in LDS.
+struct EscapeOut {
+    uint8_t* pos;        // u32 positions (mod 2^32)
+    uint8_t* exp;        // u8 exponents
+    uint64_t limit;      // slots below this may be written
+    bool pos_aligned;    // pos is 4-byte aligned
+};
+
+__device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t i0, uint32_t ex_lo,
+                                                  uint32_t ex_hi, uint64_t slot_base,
+                                                  uint32_t (*wave_escapes)[kPackWaves],
+                                                  int parity, const EscapeOut& out) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const uint32_t cnt = __popc(mask);
+    const uint64_t b0 = __ballot(cnt & 1u);
+    const uint64_t b1 = __ballot(cnt & 2u);
+    const uint64_t b2 = __ballot(cnt & 4u);
+    const uint64_t b3 = __ballot(cnt & 8u);
+    const uint32_t lane_prefix =
+        lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3);
+    if (lane == 0)
+        wave_escapes[parity][wave] =
+            __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3);
+    __syncthreads();
+    uint32_t before = 0, tile_total = 0;
+#pragma unroll
+    for (int v = 0; v < kPackWaves; v++) {
+        const uint32_t x = wave_escapes[parity][v];
+        before += v < wave ? x : 0u;
+        tile_total += x;
+    }
+    if (mask) {
+        uint64_t slot = slot_base + before + lane_prefix;
+#pragma unroll
+        for (int k = 0; k < 8; k++) {
+            if ((mask >> k) & 1u) {
+                if (slot < out.limit) {
+                    const uint32_t pos = (uint32_t)((i0 + k) & 0xFFFFFFFFull);
+                    if (out.pos_aligned) {
+                        *reinterpret_cast<uint32_t*>(out.pos + 4 * slot) = pos;
+                    } else {
+                        out.pos[4 * slot + 0] = (uint8_t)(pos & 0xFF);
+                        out.pos[4 * slot + 1] = (uint8_t)((pos >> 8) & 0xFF);
+                        out.pos[4 * slot + 2] = (uint8_t)((pos >> 16) & 0xFF);
+                        out.pos[4 * slot + 3] = (uint8_t)(pos >> 24);
+                    }
+                    out.exp[slot] = (uint8_t)byte_of(ex_lo, ex_hi, k);
+                }
+                slot++;
+            }
+        }
+    }
+    return tile_total;
 }
 
 template <bool kAlignedSm>
@@ -281,9 +386,7 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restric
     __shared__ uint32_t wave_escapes[2][kPackWaves];
 
     const int t = threadIdx.x;
-    const int lane = t & 63;
-    const int wave = t >> 6;
-    lut[t] = 0x10;
+    if (t < 256) lut[t] = 0x10;
     __syncthreads();
     if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
     __syncthreads();
@@ -293,113 +396,69 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restric
     // never write an escape record outside the caller's buffer, whatever
     // the workspace and header hold: slots below E, and all 5E escape bytes
     // inside the buffer
-    const uint64_t slot_limit =
-        (dst_capacity >= esc_off && E <= (dst_capacity - esc_off) / 5) ? E : 0;
+    EscapeOut esc;
+    esc.pos = dst + esc_off;
+    esc.exp = esc.pos + 4 * E;
+    esc.limit = (dst_capacity >= esc_off && E <= (dst_capacity - esc_off) / 5) ? E : 0;
+    esc.pos_aligned = (esc_off & 3) == 0;
     uint8_t* nib = dst + kPrefixBytes;
     uint8_t* sm = nib + (n + 1) / 2;
-    uint8_t* esc_pos = dst + esc_off;
-    uint8_t* esc_exp = esc_pos + 4 * E;
-    const bool pos_aligned = (esc_off & 3) == 0;
 
     const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
     const uint64_t end = min(begin + (1ull << chunk_log2), n);
     uint64_t slot_base = chunk_base[blockIdx.x];
 
     int parity = 0;
-    for (uint64_t t0 = begin; t0 < end; t0 += kPackTile, parity ^= 1) {
+    uint64_t t0 = begin;
+    // whole tiles: no per-word checks
+    for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
         const uint64_t i0 = t0 + (uint64_t)t * 8;
-        const uint32_t valid = i0 + 8 <= end ? 8u : (i0 < end ? (uint32_t)(end - i0) : 0u);
-
-        uint32_t w[4] = {0, 0, 0, 0};
-        if (valid == 8) {
-            const uint4 v = *reinterpret_cast<const uint4*>(src + i0);
-            w[0] = v.x;
-            w[1] = v.y;
-            w[2] = v.z;
-            w[3] = v.w;
-        } else {
-            for (uint32_t k = 0; k < valid; k++) w[k >> 1] |= (uint32_t)src[i0 + k] << (16 * (k & 1));
-        }
-
-        uint32_t nibbles = 0, mask = 0, sm_lo = 0, sm_hi = 0, ex_lo = 0, ex_hi = 0;
+        const uint4 v = *reinterpret_cast<const uint4*>(src + i0);
+        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        uint32_t sm_lo, sm_hi, ex_lo, ex_hi;
+        split8(w, sm_lo, sm_hi, ex_lo, ex_hi);
+        uint32_t nibbles = 0, mask = 0;
 #pragma unroll
         for (int k = 0; k < 8; k++) {
-            const uint32_t word = (w[k >> 1] >> (16 * (k & 1))) & 0xFFFFu;
-            const uint32_t e = (word >> 7) & 0xFFu;
-            uint32_t code = lut[e];
-            if ((uint32_t)k >= valid) code = 0;
+            const uint32_t code = lut[byte_of(ex_lo, ex_hi, k)];
             nibbles |= (code & 0xFu) << (4 * k);
             mask |= (code >> 4) << k;
-            const uint32_t s = ((word >> 8) & 0x80u) | (word & 0x7Fu);
-            if (k < 4) {
-                sm_lo |= s << (8 * k);
-                ex_lo |= e << (8 * k);
-            } else {
-                sm_hi |= s << (8 * (k - 4));
-                ex_hi |= e << (8 * (k - 4));
-            }
         }
-
-        if (valid == 8) {
-            *reinterpret_cast<uint32_t*>(nib + i0 / 2) = nibbles;
-            if (kAlignedSm) {
-                *reinterpret_cast<uint2*>(sm + i0) = make_uint2(sm_lo, sm_hi);
-            } else {
+        *reinterpret_cast<uint32_t*>(nib + i0 / 2) = nibbles;
+        if (kAlignedSm) {
+            *reinterpret_cast<uint2*>(sm + i0) = make_uint2(sm_lo, sm_hi);
+        } else {
 #pragma unroll
-                for (int k = 0; k < 8; k++)
-                    sm[i0 + k] = (uint8_t)((k < 4 ? sm_lo >> (8 * k) : sm_hi >> (8 * (k - 4))) & 0xFF);
-            }
-        } else if (valid > 0) {
-            for (uint32_t j = 0; j < (valid + 1) / 2; j++)
-                nib[i0 / 2 + j] = (uint8_t)((nibbles >> (8 * j)) & 0xFF);
-            for (uint32_t k = 0; k < valid; k++)
-                sm[i0 + k] = (uint8_t)((k < 4 ? sm_lo >> (8 * k) : sm_hi >> (8 * (k - 4))) & 0xFF);
+            for (int k = 0; k < 8; k++) sm[i0 + k] = (uint8_t)byte_of(sm_lo, sm_hi, k);
         }
-
-        // Escape ranks: a lane has at most 8 escapes, so four ballots on the
-        // bits of its count give the exclusive prefix over the wave.
-        const uint32_t cnt = __popc(mask);
-        const uint64_t b0 = __ballot(cnt & 1u);
-        const uint64_t b1 = __ballot(cnt & 2u);
-        const uint64_t b2 = __ballot(cnt & 4u);
-        const uint64_t b3 = __ballot(cnt & 8u);
-        const uint32_t lane_prefix =
-            lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3);
-        if (lane == 0)
-            wave_escapes[parity][wave] = __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) +
-                                         8 * __popcll(b3);
-        __syncthreads();
-        uint32_t before = 0, tile_total = 0;
-#pragma unroll
-        for (int v = 0; v < kPackWaves; v++) {
-            const uint32_t x = wave_escapes[parity][v];
-            before += v < wave ? x : 0u;
-            tile_total += x;
+        slot_base += write_escapes(mask, i0, ex_lo, ex_hi, slot_base, wave_escapes, parity, esc);
+    }
+    // the ragged last tile of the input (last chunk only)
+    if (t0 < end) {
+        const uint64_t i0 = t0 + (uint64_t)t * 8;
+        const uint32_t valid = i0 + 8 <= end ? 8u : (i0 < end ? (uint32_t)(end - i0) : 0u);
+        uint64_t lo4 = 0, hi4 = 0;  // words 0..3 and 4..7
+        for (uint32_t k = 0; k < valid; k++) {
+            const uint64_t word = src[i0 + k];
+            if (k < 4)
+                lo4 |= word << (16 * k);
+            else
+                hi4 |= word << (16 * (k - 4));
         }
-
-        if (mask) {
-            uint64_t slot = slot_base + before + lane_prefix;
-#pragma unroll
-            for (int k = 0; k < 8; k++) {
-                if ((mask >> k) & 1u) {
-                    if (slot < slot_limit) {
-                        const uint32_t pos = (uint32_t)((i0 + k) & 0xFFFFFFFFull);
-                        if (pos_aligned) {
-                            *reinterpret_cast<uint32_t*>(esc_pos + 4 * slot) = pos;
-                        } else {
-                            esc_pos[4 * slot + 0] = (uint8_t)(pos & 0xFF);
-                            esc_pos[4 * slot + 1] = (uint8_t)((pos >> 8) & 0xFF);
-                            esc_pos[4 * slot + 2] = (uint8_t)((pos >> 16) & 0xFF);
-                            esc_pos[4 * slot + 3] = (uint8_t)(pos >> 24);
-                        }
-                        esc_exp[slot] =
-                            (uint8_t)((k < 4 ? ex_lo >> (8 * k) : ex_hi >> (8 * (k - 4))) & 0xFF);
-                    }
-                    slot++;
-                }
-            }
+        const uint32_t w[4] = {(uint32_t)lo4, (uint32_t)(lo4 >> 32), (uint32_t)hi4,
+                               (uint32_t)(hi4 >> 32)};
+        uint32_t sm_lo, sm_hi, ex_lo, ex_hi;
+        split8(w, sm_lo, sm_hi, ex_lo, ex_hi);
+        uint32_t nibbles = 0, mask = 0;
+        for (uint32_t k = 0; k < valid; k++) {
+            const uint32_t code = lut[byte_of(ex_lo, ex_hi, k)];
+            nibbles |= (code & 0xFu) << (4 * k);
+            mask |= (code >> 4) << k;
         }
-        slot_base += tile_total;
+        for (uint32_t j = 0; j < (valid + 1) / 2; j++)
+            nib[i0 / 2 + j] = (uint8_t)((nibbles >> (8 * j)) & 0xFF);
+        for (uint32_t k = 0; k < valid; k++) sm[i0 + k] = (uint8_t)byte_of(sm_lo, sm_hi, k);
+        write_escapes(mask, i0, ex_lo, ex_hi, slot_base, wave_escapes, parity, esc);
     }
 }
 

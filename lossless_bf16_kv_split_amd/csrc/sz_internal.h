@@ -18,8 +18,8 @@ constexpr uint64_t kMaxElements = 1ull << 36;
 // counts exponents per chunk, the codebook pass turns those counts into the
 // exact number of escapes of every chunk (and so into each chunk's first
 // escape slot), and the pack pass lets one workgroup stream one chunk.
-// A chunk is at least two pack tiles and the grid at most kMaxChunks.
-constexpr uint32_t kMinChunkLog2 = 12;
+// A chunk holds whole pack tiles and the grid is at most kMaxChunks.
+constexpr uint32_t kMinChunkLog2 = 13;
 constexpr uint32_t kMaxChunks = 2048;
 constexpr uint32_t kRowsPerPartial = 32;  // chunk rows merged per reduce block
 

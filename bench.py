@@ -1,10 +1,12 @@
 """Benchmark of the SplitZip BF16 codec on one MI355X.
 
 One step = the whole hot path over one tensor already resident in HBM:
-exponent histogram -> top-16 codebook -> pack (encode), then unpack ->
-escape scatter (decode).  Every pass is bracketed by HIP events on the
-stream the kernels run on, so each kernel's average duration is measured
-inside the timed region.  Prints ONE JSON line.
+exponent histogram -> top-16 codebook -> pack (encode), then decode (unpack
+with the escape overwrite in the same pass).  Every pass is bracketed by HIP
+events on the stream the kernels run on, so each kernel's average duration
+is measured inside the timed region.  The two-pass decode (unpack, then
+escape scatter) is timed as well, after the timed region.  Prints ONE JSON
+line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_8b_kv_8k]
 
@@ -35,9 +37,12 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["lossless_bf16_kv_split_amd/csrc/encode.hip",
                   "lossless_bf16_kv_split_amd/csrc/decode.hip",
                   "lossless_bf16_kv_split_amd/csrc/sz_internal.h"]
-PASSES = ["histogram", "codebook", "pack", "unpack", "scatter"]
-KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_rows+k_select",
-                "pack": "k_pack", "unpack": "k_unpack", "scatter": "k_scatter"}
+ENCODE_PASSES = ["histogram", "codebook", "pack"]
+KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select",
+                "pack": "k_pack", "fused": "k_decode_fused", "unpack": "k_unpack",
+                "scatter": "k_scatter"}
+# sz_decode runs the single pass when more than one word in this many escapes
+FUSED_DECODE_DENSITY = 128
 
 
 def kernel_source_hash() -> str:
@@ -56,8 +61,9 @@ def algorithmic_bytes(n: int, e: int) -> dict:
         "histogram": 2 * n,                        # read every word once
         "codebook": 0,                             # O(chunks) metadata only
         "pack": 2 * n + nib + sm + esc + pre,      # read words, write container
+        "fused": pre + nib + sm + esc + 2 * n,     # read container, write words once
         "unpack": pre + nib + sm + 2 * n,          # read codes + sm, write words
-        "scatter": esc + 3 * e,                    # read records; sm read + word write per escape
+        "scatter": esc + 4 * e,                    # read records; read + rewrite each escaped word
     }
 
 
@@ -157,65 +163,89 @@ def main() -> int:
     container = dst[:total]
     e = int.from_bytes(container[16:24].cpu().numpy().tobytes(), "little")
 
-    def step(ev=None):
+    # the decode passes sz_decode runs for this container (same rule)
+    dense = e > n // FUSED_DECODE_DENSITY
+    decode_passes = ["fused"] if dense else ["unpack", "scatter"]
+    other_passes = ["unpack", "scatter"] if dense else ["fused"]
+    passes = ENCODE_PASSES + decode_passes
+
+    def run_pass(p, dst_words):
+        if p == "histogram":
+            sz.sz_encode_histogram(x, n, ws, ws_bytes, stream)
+        elif p == "codebook":
+            sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size, stream)
+        elif p == "pack":
+            sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap, stream)
+        elif p == "fused":
+            sz.sz_decode_fused(container, total, dst_words, n, status, stream)
+        elif p == "unpack":
+            sz.sz_decode_unpack(container, total, dst_words, n, status, stream)
+        elif p == "scatter":
+            sz.sz_decode_scatter(container, total, dst_words, n, status, stream)
+
+    def step(seq, dst_words, ev=None):
+        for i, p in enumerate(seq):
+            if ev:
+                ev[i].record(stream)
+            run_pass(p, dst_words)
         if ev:
-            ev[0].record(stream)
-        sz.sz_encode_histogram(x, n, ws, ws_bytes, stream)
-        if ev:
-            ev[1].record(stream)
-        sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size, stream)
-        if ev:
-            ev[2].record(stream)
-        sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap, stream)
-        if ev:
-            ev[3].record(stream)
-        sz.sz_decode_unpack(container, total, out, n, status, stream)
-        if ev:
-            ev[4].record(stream)
-        sz.sz_decode_scatter(container, total, out, n, status, stream)
-        if ev:
-            ev[5].record(stream)
+            ev[len(seq)].record(stream)
 
     for _ in range(args.warmup):
-        step()
+        step(passes, out)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    def new_events(k):
+        return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(args.steps)]
+
+    events = new_events(len(passes) + 1)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        step(events[k])
+        step(passes, out, events[k])
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
 
-    per = {p: [] for p in PASSES}
-    for ev in events:
-        for i, p in enumerate(PASSES):
-            per[p].append(ev[i].elapsed_time(ev[i + 1]))
-    avg_ms = {p: sum(v) / len(v) for p, v in per.items()}
+    avg_ms = {}
+    for i, p in enumerate(passes):
+        avg_ms[p] = sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps
 
     # the timed work is correct: same container, exact round trip
     ok = bool(torch.equal(out, x)) and int(status.item()) == 0 and int(size.item()) == total
 
+    # the other decode form, after the timed region; each run follows an
+    # encode, as in the step
+    out2 = torch.empty_like(out)
+    other_ev = new_events(len(other_passes) + 1)
+    for k in range(args.steps):
+        step(ENCODE_PASSES, out2)
+        step(other_passes, out2, other_ev[k])
+    torch.cuda.synchronize()
+    for i, p in enumerate(other_passes):
+        avg_ms[p] = sum(ev[i].elapsed_time(ev[i + 1]) for ev in other_ev) / args.steps
+    ok = ok and bool(torch.equal(out2, x)) and int(status.item()) == 0
+    del out2
+
     alg = algorithmic_bytes(n, e)
     kernels = {}
-    for p in PASSES:
+    for p in passes + other_passes:
         ms = avg_ms[p]
         gbps = alg[p] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
         kernels[p] = {"kernel": KERNEL_NAMES[p], "avg_ms": round(ms, 5),
                       "alg_bytes": alg[p], "GBps": round(gbps, 1),
                       "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
-    enc_ms = avg_ms["histogram"] + avg_ms["codebook"] + avg_ms["pack"]
-    dec_ms = avg_ms["unpack"] + avg_ms["scatter"]
+    enc_ms = sum(avg_ms[p] for p in ENCODE_PASSES)
+    dec_ms = sum(avg_ms[p] for p in decode_passes)
+    other_dec_ms = sum(avg_ms[p] for p in other_passes)
     enc_alg = alg["histogram"] + alg["pack"]
-    dec_alg = alg["unpack"] + (5 * e)
+    dec_alg = alg["fused"]  # container in, words out: the same for either form
     ms_per_step = total_ms / args.steps
 
-    dominant = max(["histogram", "pack", "unpack", "scatter"], key=lambda p: avg_ms[p])
+    dominant = max([p for p in passes if p != "codebook"], key=lambda p: avg_ms[p])
     ach = kernels[dominant]["GBps"]
     traffic = load_traffic(KERNEL_NAMES[dominant], w.name)
 
@@ -252,6 +282,8 @@ def main() -> int:
         "decode_GBps": round(2 * n / (dec_ms * 1e-3) / 1e9, 2),
         "encode_frac_hbm": round(enc_alg / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "decode_frac_hbm": round(dec_alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "decode_form": "single pass" if dense else "unpack + escape scatter",
+        "other_decode_form_GBps": round(2 * n / (other_dec_ms * 1e-3) / 1e9, 2),
         "ratio": round(2 * n / total, 5),
         "escapes": e,
         "container_bytes": total,

@@ -93,7 +93,9 @@ sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
 /* Decompress a container of src_bytes bytes into n BF16 words at d_dst,
  * bit-exactly.  SplitZip explainer section "4. Pourquoi est-ce rapide ?"
  * (code -> exponent lookup, recombination with sign and mantissa, escaped
- * slots overwritten).
+ * slots overwritten).  With many escapes (more than one word in 128) it runs
+ * as one pass that overwrites the escaped exponents before each word is
+ * stored; otherwise as the two staged passes below.  Same result either way.
  *   src_bytes   must equal the container's total size: the host derives E
  *               from it, so no device read is needed before launching
  *   d_status    optional device i32: SZ_OK, or SZ_ERR_CORRUPT when the
@@ -108,9 +110,10 @@ sz_status sz_decode(const void *d_src, uint64_t src_bytes, void *d_dst,
 /* ---- staged form: the same kernels, one call per pass ------------------
  * sz_encode = sz_encode_histogram; sz_encode_codebook; sz_encode_pack on one
  * stream with one workspace of at least sz_workspace_size(n) bytes that the
- * caller owns and does not touch in between.  sz_decode = sz_decode_unpack;
- * sz_decode_scatter.  Out-of-order use cannot write outside the caller's
- * buffers, but yields an unspecified container. */
+ * caller owns and does not touch in between.  sz_decode_unpack followed by
+ * sz_decode_scatter gives the same words and status as sz_decode.
+ * Out-of-order use cannot write outside the caller's buffers, but yields an
+ * unspecified result. */
 
 /* Pass 1, exponent histogram (explainer section "2. La decouverte
  * secrete": the exponents are highly repetitive): one 256-bin count per
@@ -141,12 +144,22 @@ sz_status sz_decode_unpack(const void *d_src, uint64_t src_bytes, void *d_dst,
                            uint64_t n_elements, int32_t *d_status,
                            hipStream_t stream);
 
-/* Decode pass 2: every escape record overwrites the exponent of its slot;
- * a position >= n or not above the previous one raises *d_status to
- * SZ_ERR_CORRUPT and is skipped.  Launches nothing when E = 0. */
+/* Decode pass 2: every escape record overwrites the exponent field of the
+ * word pass 1 wrote at its position; a position >= n or not above the
+ * previous one raises *d_status to SZ_ERR_CORRUPT and is skipped.  Launches
+ * nothing when E = 0. */
 sz_status sz_decode_scatter(const void *d_src, uint64_t src_bytes, void *d_dst,
                             uint64_t n_elements, int32_t *d_status,
                             hipStream_t stream);
+
+/* Decode in a single pass whatever the escape density: each workgroup
+ * finds its range's escape records by a 64-way search over the sorted
+ * positions, stages them in LDS and overwrites the escaped exponents before
+ * the words are stored (explainer section "4. Pourquoi est-ce rapide ?").
+ * Same arguments, result and status as sz_decode, which picks this form
+ * for escape-dense containers. */
+sz_status sz_decode_fused(const void *d_src, uint64_t src_bytes, void *d_dst,
+                          uint64_t n_elements, int32_t *d_status, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char *sz_status_string(int status);

@@ -189,9 +189,29 @@ sz_status sz_decode_scatter(const void* d_src, uint64_t src_bytes, void* d_dst, 
 
 sz_status sz_decode(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
                     int32_t* d_status, hipStream_t stream) {
-    sz_status st = sz_decode_unpack(d_src, src_bytes, d_dst, n, d_status, stream);
+    uint64_t e = 0;
+    if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
+    const uint8_t* src = static_cast<const uint8_t*>(d_src);
+    uint16_t* dst = static_cast<uint16_t*>(d_dst);
+    if (e > n / sz::kFusedDecodeDensity) {
+        // escape-dense: patch escaped exponents before each word is stored
+        return hip_status(sz::launch_decode_fused(src, src_bytes, n, e, dst, d_status, stream));
+    }
+    // escape-sparse: stream every word out, then rewrite the few escaped ones
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    sz_status st = hip_status(sz::launch_unpack(src, src_bytes, n, e, dst, d_status, num_cus(dev),
+                                                stream));
     if (st != SZ_OK) return st;
-    return sz_decode_scatter(d_src, src_bytes, d_dst, n, d_status, stream);
+    return hip_status(sz::launch_scatter(src, n, e, dst, d_status, stream));
+}
+
+sz_status sz_decode_fused(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
+                          int32_t* d_status, hipStream_t stream) {
+    uint64_t e = 0;
+    if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
+    return hip_status(sz::launch_decode_fused(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
+                                              static_cast<uint16_t*>(d_dst), d_status, stream));
 }
 
 const char* sz_status_string(int status) {

@@ -41,21 +41,32 @@ __device__ __forceinline__ uint32_t lookup4(uint32_t x, uint4 cb) {
     return bitselect((bit3 << 8) - bit3, hi, lo);  // 0xFF in every byte with bit 3 set
 }
 
-// Eight words from one dword of codes (element 2j in the low nibble of byte
-// j) and eight sign|mantissa bytes s0 (elements 0..3), s1 (4..7).  Per
-// byte lane: high byte of the word = sign | exponent >> 1, low byte =
-// (exponent & 1) << 7 | mantissa; then the two byte streams are interleaved.
-__device__ __forceinline__ uint4 decode8(uint32_t codes, uint32_t s0, uint32_t s1, uint4 cb) {
+// Exponent bytes of eight words from one dword of codes (element 2j in the
+// low nibble of byte j): e0 holds elements 0..3, e1 elements 4..7.
+__device__ __forceinline__ void exponents8(uint32_t codes, uint4 cb, uint32_t& e0, uint32_t& e1) {
     const uint32_t even = lookup4(codes & 0x0F0F0F0Fu, cb);         // elements 0,2,4,6
     const uint32_t odd = lookup4((codes >> 4) & 0x0F0F0F0Fu, cb);   // elements 1,3,5,7
-    const uint32_t e0 = perm(odd, even, 0x05010400u);               // elements 0..3
-    const uint32_t e1 = perm(odd, even, 0x07030602u);               // elements 4..7
+    e0 = perm(odd, even, 0x05010400u);
+    e1 = perm(odd, even, 0x07030602u);
+}
+
+// Eight words from their exponent bytes (e0, e1) and sign|mantissa bytes
+// (s0 elements 0..3, s1 elements 4..7).  Per byte lane: high byte of the
+// word = sign | exponent >> 1, low byte = (exponent & 1) << 7 | mantissa;
+// the two byte streams are then interleaved into words.
+__device__ __forceinline__ uint4 words8(uint32_t e0, uint32_t e1, uint32_t s0, uint32_t s1) {
     const uint32_t h0 = bitselect(0x80808080u, s0, e0 >> 1);
     const uint32_t l0 = bitselect(0x80808080u, e0 << 7, s0);
     const uint32_t h1 = bitselect(0x80808080u, s1, e1 >> 1);
     const uint32_t l1 = bitselect(0x80808080u, e1 << 7, s1);
     return make_uint4(perm(h0, l0, 0x05010400u), perm(h0, l0, 0x07030602u),
                       perm(h1, l1, 0x05010400u), perm(h1, l1, 0x07030602u));
+}
+
+__device__ __forceinline__ uint4 decode8(uint32_t codes, uint32_t s0, uint32_t s1, uint4 cb) {
+    uint32_t e0, e1;
+    exponents8(codes, cb, e0, e1);
+    return words8(e0, e1, s0, s1);
 }
 
 // one word, for the last n % 8 elements
@@ -198,6 +209,278 @@ hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* 
     if (e == 0) return hipSuccess;
     const uint64_t blocks = (e + kScatterThreads - 1) / kScatterThreads;
     k_scatter<<<(uint32_t)blocks, kScatterThreads, 0, stream>>>(src, n, e, dst, status);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
+// Fused decode: unpack and escape overwrite in one pass, so every word is
+// written once.  One workgroup per power-of-two range of words.
+
+#ifndef SZ_FUSED_THREADS
+#define SZ_FUSED_THREADS 512
+#endif
+#ifndef SZ_FUSED_BATCH_PER_THREAD
+#define SZ_FUSED_BATCH_PER_THREAD 4
+#endif
+constexpr int kFusedThreads = SZ_FUSED_THREADS;
+constexpr uint32_t kFusedTile = kFusedThreads * 8;   // words per workgroup step
+constexpr int kBatchPerThread = SZ_FUSED_BATCH_PER_THREAD;
+static_assert(kBatchPerThread >= 1 && kBatchPerThread <= 4, "prefetched exponents share one register");
+constexpr uint32_t kBatch = kFusedThreads * kBatchPerThread;  // escape records in LDS
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+
+// Escape positions: low 32 bits stored, segment from the header's seg_end
+// (kept in LDS; with n <= 2^32 every escape is in segment 0).
+struct EscapeReader {
+    const uint8_t* pos_lo;
+    const uint8_t* exps;
+    const uint64_t* seg_end;  // LDS copy of the header table
+    bool one_segment;
+    bool aligned;
+
+    __device__ uint64_t position(uint64_t k) const {
+        uint64_t seg = 0;
+        if (!one_segment) {
+#pragma unroll
+            for (int s = 0; s < 16; s++) seg += seg_end[s] <= k ? 1u : 0u;
+        }
+        uint32_t lo;
+        if (aligned) {
+            lo = reinterpret_cast<const uint32_t*>(pos_lo)[k];
+        } else {
+            lo = load4_unaligned(pos_lo + 4 * k);
+        }
+        return (seg << 32) | lo;
+    }
+};
+
+// First k in [0, e] whose position is >= target, for one wavefront: every
+// step probes 64 evenly spaced records and keeps the bracket where the
+// predicate turns true, so the interval shrinks on every step and the loop
+// ends on any input (sorted input gives the exact lower bound).
+__device__ uint64_t wave_lower_bound(const EscapeReader& r, uint64_t e, uint64_t target) {
+    const uint64_t lane = threadIdx.x & 63;
+    uint64_t lo = 0, hi = e;
+    while (hi - lo > 64) {
+        const uint64_t step = (hi - lo + 63) / 64;
+        const uint64_t k = lo + lane * step;
+        const bool ge = k < hi ? r.position(k) >= target : true;
+        const uint64_t m = __ballot(ge);
+        const uint64_t f = m ? (uint64_t)(__ffsll((long long)m) - 1) : 64;
+        const uint64_t new_hi = f < 64 ? min(hi, lo + f * step) : hi;
+        const uint64_t new_lo = f > 0 ? lo + (f - 1) * step + 1 : lo;
+        lo = new_lo;
+        hi = new_hi;
+    }
+    const uint64_t k = lo + lane;
+    const bool ge = k < hi ? r.position(k) >= target : true;
+    const uint64_t m = __ballot(ge);
+    return m ? min(lo + (uint64_t)(__ffsll((long long)m) - 1), hi) : hi;
+}
+
+// a value every lane holds, moved to scalar registers
+__device__ __forceinline__ uint64_t uniform64(uint64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// bits 0..3 of x -> bytes 0..3 set to 0xFF or 0x00
+__device__ __forceinline__ uint32_t bits_to_bytes(uint32_t x) {
+    const uint32_t spread = ((x & 0xFu) * 0x00204081u) & 0x01010101u;
+    return (spread << 8) - spread;
+}
+
+__global__ void k_status_clear(int32_t* status) { *status = 0; }
+
+template <bool kAlignedSm>
+__global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
+    const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e,
+    uint32_t range_log2, uint16_t* __restrict__ out, int32_t* status) {
+    __shared__ uint32_t batch_pos[kBatch];            // offsets from the range start
+    __shared__ uint8_t batch_exp[kBatch];
+    __shared__ uint8_t patch_exp[2][kFusedTile];      // exponent of each escaped word
+    __shared__ uint32_t patch_bits[2][kFusedTile / 32];
+    __shared__ uint64_t bounds[2];
+    __shared__ uint64_t seg_table[16];
+    __shared__ int bad;
+
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    if (t == 0) bad = 0;
+    if (blockIdx.x == 0 && t == 0 && !header_ok(src, src_bytes, n, e)) bad = 1;
+
+    const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
+    const uint8_t* nib = src + kPrefixBytes;
+    const uint8_t* sm = nib + (n + 1) / 2;
+    const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
+    EscapeReader rd;
+    rd.pos_lo = src + esc_off;
+    rd.exps = rd.pos_lo + 4 * e;
+    rd.aligned = (esc_off & 3) == 0;
+    rd.one_segment = n <= (1ull << 32);
+    rd.seg_end = seg_table;
+    if (t < 16) seg_table[t] = reinterpret_cast<const uint64_t*>(src + 32)[t];
+    __syncthreads();
+
+    const uint64_t begin = min((uint64_t)blockIdx.x << range_log2, n);
+    const uint64_t end = min(begin + (1ull << range_log2), n);
+
+    // escapes of this range: [k_lo, k_hi)
+    if (wave < 2) {
+        const uint64_t b = wave_lower_bound(rd, e, wave == 0 ? begin : end);
+        if ((t & 63) == 0) bounds[wave] = b;
+    }
+    __syncthreads();
+    const uint64_t k_lo = uniform64(bounds[0]);
+    const uint64_t k_hi = uniform64(bounds[1] > k_lo ? bounds[1] : k_lo);
+    if (t == 0 && blockIdx.x == gridDim.x - 1 && bounds[1] != e) bad = 1;  // positions >= n
+
+    // batch of escape records in LDS, the next batch prefetched in registers
+    uint64_t kb = k_lo;
+    uint32_t cnt = (uint32_t)min((uint64_t)kBatch, k_hi - kb);
+    uint64_t next_kb = kb + cnt;
+    uint32_t pre_off[kBatchPerThread];   // offset from begin, or kNoSlot
+    uint32_t pre_exp = 0;                // the records' exponents, one per byte
+    bool pre_first_ok = true;            // first record of the batch above its predecessor
+
+    auto fetch = [&](uint64_t base) {
+        pre_exp = 0;
+#pragma unroll
+        for (int i = 0; i < kBatchPerThread; i++) {
+            const uint64_t k = base + (uint64_t)(t + i * kFusedThreads);
+            pre_off[i] = kNoSlot;
+            if (k < k_hi) {
+                const uint64_t p = rd.position(k);
+                if (p >= begin && p < end) pre_off[i] = (uint32_t)(p - begin);
+                pre_exp |= (uint32_t)rd.exps[k] << (8 * i);
+                if (i == 0 && t == 0 && k > 0) pre_first_ok = p > rd.position(k - 1);
+            }
+        }
+    };
+    // install the fetched records (batch starting at kb, cnt records), then
+    // check they ascend: against the neighbour, and the first against the
+    // record before the batch; a record outside the range is corrupt too
+    auto install = [&]() {
+#pragma unroll
+        for (int i = 0; i < kBatchPerThread; i++) {
+            const uint32_t q = t + i * kFusedThreads;
+            if (q < cnt) {
+                batch_pos[q] = pre_off[i];
+                batch_exp[q] = (uint8_t)(pre_exp >> (8 * i));
+                if (pre_off[i] == kNoSlot) bad = 1;
+            }
+        }
+        if (t == 0 && cnt > 0 && !pre_first_ok) bad = 1;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kBatchPerThread; i++) {
+            const uint32_t q = t + i * kFusedThreads;
+            if (q > 0 && q < cnt && !(batch_pos[q] > batch_pos[q - 1])) bad = 1;
+        }
+    };
+
+    fetch(kb);
+    install();
+    fetch(next_kb);
+
+    // A tile's codes and sign|mantissa bytes are loaded one tile ahead, so
+    // the loads stay in flight across this tile's barriers and patching.
+    auto load_tile = [&](uint64_t i0, uint32_t& codes, uint32_t& s0, uint32_t& s1) {
+        if (i0 + 8 <= end) {
+            codes = *reinterpret_cast<const uint32_t*>(nib + i0 / 2);
+            if (kAlignedSm) {
+                const uint2 v = *reinterpret_cast<const uint2*>(sm + i0);
+                s0 = v.x;
+                s1 = v.y;
+            } else {
+                s0 = load4_unaligned(sm + i0);
+                s1 = load4_unaligned(sm + i0 + 4);
+            }
+        }
+    };
+    uint32_t codes = 0, s0 = 0, s1 = 0;
+    load_tile(begin + (uint64_t)t * 8, codes, s0, s1);
+
+    int parity = 0;
+    for (uint64_t t0 = begin; t0 < end; t0 += kFusedTile, parity ^= 1) {
+        const uint64_t i0 = t0 + (uint64_t)t * 8;
+        const bool full = i0 + 8 <= end;
+        uint32_t next_codes = 0, next_s0 = 0, next_s1 = 0;
+        if (t0 + kFusedTile < end) load_tile(i0 + kFusedTile, next_codes, next_s0, next_s1);
+        for (int q = t; q < (int)(kFusedTile / 32); q += kFusedThreads) patch_bits[parity][q] = 0;
+        __syncthreads();
+
+        // mark this tile's escapes; refill the batch while it ends inside the tile
+        const uint32_t off0 = (uint32_t)(t0 - begin);
+        while (true) {
+#pragma unroll
+            for (int i = 0; i < kBatchPerThread; i++) {
+                const uint32_t q = t + i * kFusedThreads;
+                if (q < cnt) {
+                    const uint32_t d = batch_pos[q] - off0;
+                    if (d < kFusedTile) {
+                        patch_exp[parity][d] = batch_exp[q];
+                        atomicOr(&patch_bits[parity][d >> 5], 1u << (d & 31));
+                    }
+                }
+            }
+            const bool more = kb + cnt < k_hi;
+            const bool ends_here = cnt == 0 || batch_pos[cnt - 1] - off0 < kFusedTile ||
+                                   batch_pos[cnt - 1] < off0;
+            if (!(more && ends_here)) break;
+            __syncthreads();
+            kb = next_kb;
+            cnt = (uint32_t)min((uint64_t)kBatch, k_hi - kb);
+            next_kb = kb + cnt;
+            install();
+            fetch(next_kb);
+        }
+        __syncthreads();
+
+        // patch the exponents of escaped words, then rebuild the words
+        const uint32_t present = (patch_bits[parity][t >> 2] >> (8 * (t & 3))) & 0xFFu;
+        if (full) {
+            uint32_t e0, e1;
+            exponents8(codes, cb, e0, e1);
+            if (present) {
+                const uint2 pe = *reinterpret_cast<const uint2*>(&patch_exp[parity][8 * t]);
+                e0 = bitselect(bits_to_bytes(present), pe.x, e0);
+                e1 = bitselect(bits_to_bytes(present >> 4), pe.y, e1);
+            }
+            *reinterpret_cast<uint4*>(out + i0) = words8(e0, e1, s0, s1);
+        } else {
+            for (uint32_t k = 0; k < 8 && i0 + k < end; k++) {
+                const uint64_t i = i0 + k;
+                const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
+                const uint32_t ex = (present >> k) & 1u ? patch_exp[parity][8 * t + k]
+                                                        : codebook_byte(cb, code);
+                out[i] = (uint16_t)recombine(sm[i], ex);
+            }
+        }
+        codes = next_codes;
+        s0 = next_s0;
+        s1 = next_s1;
+    }
+    __syncthreads();
+    if (t == 0 && bad && status)
+        __hip_atomic_fetch_max(status, kStatusCorrupt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
+                               uint16_t* dst, int32_t* status, hipStream_t stream) {
+    uint32_t r = 13;
+    while (r < 40 && ((n + (1ull << r) - 1) >> r) > 2048) r++;
+    uint64_t blocks = (n + (1ull << r) - 1) >> r;
+    if (blocks == 0) blocks = 1;  // the header check still runs
+    if (status) k_status_clear<<<1, 1, 0, stream>>>(status);
+    const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
+    if (aligned)
+        k_decode_fused<true><<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(src, src_bytes, n, e,
+                                                                            r, dst, status);
+    else
+        k_decode_fused<false><<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(src, src_bytes, n,
+                                                                             e, r, dst, status);
     return hipGetLastError();
 }
 

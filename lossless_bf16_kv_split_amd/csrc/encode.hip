@@ -2,9 +2,9 @@
 //
 //   histogram  one workgroup per chunk: 256-bin exponent counts in LDS
 //              (replicated sub-histograms against same-address conflicts),
-//              written out as one row per chunk
-//   codebook   merge the rows, rank the 256 exponents (count desc, value
-//              asc), write header + codebook, and turn every chunk's row
+//              written out bin-major, counts[bin][chunk]
+//   codebook   merge the counts, rank the 256 exponents (count desc, value
+//              asc), write header + codebook, and turn every chunk's counts
 //              into its exact escape count and first escape slot
 //   pack       one workgroup per chunk: 16-byte loads, 256-entry exponent
 //              -> code table in LDS, 4-bit codes two per byte, sign|mantissa
@@ -29,13 +29,11 @@ EncodePlan plan_encode(uint64_t n) {
     while (c < 40 && ((n + (1ull << c) - 1) >> c) > kMaxChunks) c++;
     p.chunk_log2 = c;
     p.chunks = (uint32_t)((n + (1ull << c) - 1) >> c);
-    p.partials = (p.chunks + kRowsPerPartial - 1) / kRowsPerPartial;
     auto align = [](uint64_t x) { return (x + 255) & ~255ull; };
-    p.rows_off = 0;
-    p.partial_off = align(p.rows_off + (uint64_t)p.chunks * 256 * 4);
-    p.base_off = align(p.partial_off + (uint64_t)p.partials * 256 * 8);
+    p.counts_off = 0;
+    p.hist_off = align(p.counts_off + (uint64_t)p.chunks * 256 * 4);
+    p.base_off = align(p.hist_off + 256 * 8);
     p.ws_bytes = align(p.base_off + (uint64_t)p.chunks * 8);
-    if (p.ws_bytes == 0) p.ws_bytes = 256;
     return p;
 }
 
@@ -65,9 +63,12 @@ __device__ __forceinline__ void hist_uint4(uint32_t* h, const uint4& v) {
     hist_dword(h, v.w);
 }
 
+// counts[bin * chunks + chunk]: bin-major, so that the codebook pass reads
+// every bin's counts, and each chunk's 16 codebook counts, coalesced
 __global__ __launch_bounds__(kHistThreads) void k_histogram(const uint16_t* __restrict__ src,
                                                             uint64_t n, uint32_t chunk_log2,
-                                                            uint32_t* __restrict__ rows) {
+                                                            uint32_t chunks,
+                                                            uint32_t* __restrict__ counts) {
     __shared__ uint32_t h[kHistCopies * kHistPitch];
     for (int i = threadIdx.x; i < kHistCopies * kHistPitch; i += kHistThreads) h[i] = 0;
     __syncthreads();
@@ -100,7 +101,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const uint16_t* __re
         uint32_t s = 0;
 #pragma unroll
         for (int c = 0; c < kHistCopies; c++) s += h[c * kHistPitch + bin];
-        rows[(uint64_t)blockIdx.x * 256 + bin] = s;
+        counts[(uint64_t)bin * chunks + blockIdx.x] = s;
     }
 }
 
@@ -108,30 +109,42 @@ hipError_t launch_histogram(const uint16_t* src, const EncodePlan& p, uint8_t* w
                             hipStream_t stream) {
     if (p.chunks == 0) return hipSuccess;
     k_histogram<<<p.chunks, kHistThreads, 0, stream>>>(
-        src, p.n, p.chunk_log2, reinterpret_cast<uint32_t*>(ws + p.rows_off));
+        src, p.n, p.chunk_log2, p.chunks, reinterpret_cast<uint32_t*>(ws + p.counts_off));
     return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- pass 2
 
-// Merge kRowsPerPartial chunk rows per workgroup; thread = exponent bin.
-__global__ __launch_bounds__(256) void k_merge_rows(const uint32_t* __restrict__ rows,
-                                                    uint32_t chunks,
-                                                    uint64_t* __restrict__ partial) {
-    const uint32_t bin = threadIdx.x;
-    const uint32_t r0 = blockIdx.x * kRowsPerPartial;
-    const uint32_t r1 = min(r0 + kRowsPerPartial, chunks);
-    uint64_t s = 0;
-    uint32_t r = r0;
-    for (; r + 8 <= r1; r += 8) {  // eight loads in flight per thread
-        uint32_t v[8];
+// hist[bin] = sum over chunks of counts[bin][chunk]; one workgroup per bin,
+// every load coalesced and in flight at once.
+constexpr int kMergeThreads = 256;
+constexpr uint32_t kMergePerThread = kMaxChunks / kMergeThreads;
+
+__global__ __launch_bounds__(kMergeThreads) void k_merge_counts(const uint32_t* __restrict__ counts,
+                                                               uint32_t chunks,
+                                                               uint64_t* __restrict__ hist) {
+    __shared__ uint64_t wave_sum[kMergeThreads / 64];
+    const uint32_t bin = blockIdx.x;
+    const uint32_t t = threadIdx.x;
+    const uint32_t* row = counts + (uint64_t)bin * chunks;
+    uint32_t v[kMergePerThread];
 #pragma unroll
-        for (int j = 0; j < 8; j++) v[j] = rows[(uint64_t)(r + j) * 256 + bin];
-#pragma unroll
-        for (int j = 0; j < 8; j++) s += v[j];
+    for (uint32_t j = 0; j < kMergePerThread; j++) {
+        const uint32_t c = t + j * kMergeThreads;
+        v[j] = c < chunks ? row[c] : 0u;
     }
-    for (; r < r1; r++) s += rows[(uint64_t)r * 256 + bin];
-    partial[(uint64_t)blockIdx.x * 256 + bin] = s;
+    uint64_t s = 0;
+#pragma unroll
+    for (uint32_t j = 0; j < kMergePerThread; j++) s += v[j];
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) s += __shfl_down(s, d, 64);
+    if ((t & 63) == 0) wave_sum[t >> 6] = s;
+    __syncthreads();
+    if (t == 0) {
+        uint64_t total = 0;
+        for (int w = 0; w < kMergeThreads / 64; w++) total += wave_sum[w];
+        hist[bin] = total;
+    }
 }
 
 constexpr int kSelectThreads = 1024;
@@ -150,10 +163,9 @@ __device__ __forceinline__ uint64_t wave_inclusive_sum(uint64_t v) {
 // One workgroup.  chunk_base[b] receives the number of escapes in chunks
 // before b, which is where chunk b's escape records start.
 __global__ __launch_bounds__(kSelectThreads) void k_select(
-    uint64_t n, uint32_t chunk_log2, uint32_t chunks, uint32_t partials,
-    const uint32_t* __restrict__ rows, const uint64_t* __restrict__ partial,
-    uint64_t* __restrict__ chunk_base, uint8_t* __restrict__ dst, uint64_t* d_size) {
-    __shared__ uint64_t part[4][256];
+    uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
+    const uint64_t* __restrict__ hist, uint64_t* __restrict__ chunk_base,
+    uint8_t* __restrict__ dst, uint64_t* d_size) {
     __shared__ uint64_t key[256];
     __shared__ uint32_t rank_part[4][256];
     __shared__ uint32_t codebook[16];
@@ -166,22 +178,9 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     const int grp = t >> 8;  // 0..3
     if (t < 16) codebook[t] = 0;
 
-    // exponent histogram of the whole tensor
-    uint64_t s = 0;
-    uint32_t q = grp;
-    for (; q + 12 < partials; q += 16) {  // four loads in flight per thread
-        uint64_t v[4];
-#pragma unroll
-        for (int j = 0; j < 4; j++) v[j] = partial[(uint64_t)(q + 4 * j) * 256 + bin];
-#pragma unroll
-        for (int j = 0; j < 4; j++) s += v[j];
-    }
-    for (; q < partials; q += 4) s += partial[(uint64_t)q * 256 + bin];
-    part[grp][bin] = s;
-    __syncthreads();
     // key(x) = count << 8 | (255 - x): "more frequent, then smaller exponent"
     // becomes one unsigned comparison (counts stay below 2^37)
-    if (t < 256) key[t] = ((part[0][t] + part[1][t] + part[2][t] + part[3][t]) << 8) | (255u - t);
+    if (t < 256) key[t] = (hist[t] << 8) | (255u - t);
     __syncthreads();
 
     // rank(x) = #{y : key(y) > key(x)}; group g counts over y in [64g, 64g + 64)
@@ -204,6 +203,18 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     uint32_t cb[16];
 #pragma unroll
     for (int c = 0; c < 16; c++) cb[c] = codebook[c] & 255u;
+    // chunks 2t and 2t+1: their 16 codebook counts, coalesced across threads
+    // (bin-major layout), all in flight at once
+    uint32_t v[2][16];
+#pragma unroll
+    for (int c = 0; c < 16; c++) {
+        const uint32_t* row = counts + (uint64_t)cb[c] * chunks;
+#pragma unroll
+        for (int j = 0; j < 2; j++) {
+            const uint32_t b = 2 * t + j;
+            v[j][c] = b < chunks ? row[b] : 0u;
+        }
+    }
     uint64_t esc[2] = {0, 0};
 #pragma unroll
     for (int j = 0; j < 2; j++) {
@@ -211,13 +222,9 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
         if (b < chunks) {
             const uint64_t start = (uint64_t)b << chunk_log2;
             const uint64_t len = min(1ull << chunk_log2, n - start);
-            const uint32_t* row = rows + (uint64_t)b * 256;
-            uint32_t v[16];
-#pragma unroll
-            for (int c = 0; c < 16; c++) v[c] = row[cb[c]];
             uint64_t kept = 0;
 #pragma unroll
-            for (int c = 0; c < 16; c++) kept += v[c];
+            for (int c = 0; c < 16; c++) kept += v[j][c];
             esc[j] = len - kept;
         }
     }
@@ -269,12 +276,10 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
 
 hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst, uint64_t* d_size,
                            hipStream_t stream) {
-    const uint32_t* rows = reinterpret_cast<const uint32_t*>(ws + p.rows_off);
-    uint64_t* partial = reinterpret_cast<uint64_t*>(ws + p.partial_off);
-    if (p.partials > 0)
-        k_merge_rows<<<p.partials, 256, 0, stream>>>(rows, p.chunks, partial);
-    k_select<<<1, kSelectThreads, 0, stream>>>(p.n, p.chunk_log2, p.chunks, p.partials, rows,
-                                               partial,
+    const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + p.counts_off);
+    uint64_t* hist = reinterpret_cast<uint64_t*>(ws + p.hist_off);
+    k_merge_counts<<<256, kMergeThreads, 0, stream>>>(counts, p.chunks, hist);
+    k_select<<<1, kSelectThreads, 0, stream>>>(p.n, p.chunk_log2, p.chunks, counts, hist,
                                                reinterpret_cast<uint64_t*>(ws + p.base_off),
                                                dst, d_size);
     return hipGetLastError();
@@ -410,11 +415,16 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restric
 
     int parity = 0;
     uint64_t t0 = begin;
-    // whole tiles: no per-word checks
+    // whole tiles, no per-word checks; each tile's words are loaded one tile
+    // ahead so the loads stay in flight across this tile's barrier
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (t0 + kPackTile <= end) v = *reinterpret_cast<const uint4*>(src + t0 + (uint64_t)t * 8);
     for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
         const uint64_t i0 = t0 + (uint64_t)t * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(src + i0);
+        uint4 v_next = make_uint4(0, 0, 0, 0);
+        if (t0 + 2 * kPackTile <= end) v_next = *reinterpret_cast<const uint4*>(src + i0 + kPackTile);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+        v = v_next;
         uint32_t sm_lo, sm_hi, ex_lo, ex_hi;
         split8(w, sm_lo, sm_hi, ex_lo, ex_hi);
         uint32_t nibbles = 0, mask = 0;

@@ -21,21 +21,24 @@ constexpr uint64_t kMaxElements = 1ull << 36;
 // A chunk holds whole pack tiles and the grid is at most kMaxChunks.
 constexpr uint32_t kMinChunkLog2 = 13;
 constexpr uint32_t kMaxChunks = 2048;
-constexpr uint32_t kRowsPerPartial = 32;  // chunk rows merged per reduce block
 
 struct EncodePlan {
     uint64_t n = 0;
     uint32_t chunk_log2 = kMinChunkLog2;
     uint32_t chunks = 0;    // G = ceil(n / 2^chunk_log2)
-    uint32_t partials = 0;  // ceil(G / kRowsPerPartial)
     // workspace layout, byte offsets (256-byte aligned regions)
-    uint64_t rows_off = 0;     // u32[G][256]   per-chunk exponent counts
-    uint64_t partial_off = 0;  // u64[P][256]   merged counts
+    uint64_t counts_off = 0;   // u32[256][G]   exponent counts, bin-major
+    uint64_t hist_off = 0;     // u64[256]      exponent counts of the whole input
     uint64_t base_off = 0;     // u64[G]        first escape slot of each chunk
     uint64_t ws_bytes = 0;
 };
 
 EncodePlan plan_encode(uint64_t n);
+
+// sz_decode patches escapes inside the unpack pass when more than one word
+// in kFusedDecodeDensity is an escape; below that, a separate in-place rewrite of
+// the few escaped words costs less than the fused pass's bookkeeping.
+constexpr uint64_t kFusedDecodeDensity = 128;
 
 inline uint64_t container_bytes(uint64_t n, uint64_t e) {
     return kPrefixBytes + (n + 1) / 2 + n + 5 * e;
@@ -52,5 +55,7 @@ hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uin
                          uint16_t* dst, int32_t* status, int num_cus, hipStream_t stream);
 hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* dst,
                           int32_t* status, hipStream_t stream);
+hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
+                               uint16_t* dst, int32_t* status, hipStream_t stream);
 
 }  // namespace sz

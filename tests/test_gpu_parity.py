@@ -60,12 +60,22 @@ GUARD = 64
 SENTINEL = 0x5A5A
 
 
-def gpu_decode(torch, sz, container_dev, n):
+DECODE_FORMS = ("auto", "fused", "staged")
+
+
+def gpu_decode(torch, sz, container_dev, n, form="auto"):
     """Decode into a buffer with GUARD sentinel words after element n; returns
-    (words tensor of n, device status, guard intact)."""
+    (words tensor of n, device status, guard intact).  form: "auto" is
+    sz_decode, "fused" the single pass, "staged" unpack then escape scatter."""
     out = torch.full((n + GUARD,), SENTINEL, dtype=torch.int16, device="cuda")
     status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    sz.sz_decode(container_dev, container_dev.numel(), out, n, status)
+    if form == "staged":
+        sz.sz_decode_unpack(container_dev, container_dev.numel(), out, n, status)
+        sz.sz_decode_scatter(container_dev, container_dev.numel(), out, n, status)
+    elif form == "fused":
+        sz.sz_decode_fused(container_dev, container_dev.numel(), out, n, status)
+    else:
+        sz.sz_decode(container_dev, container_dev.numel(), out, n, status)
     torch.cuda.synchronize()
     guard_ok = bool((out[n:] == SENTINEL).all().item())
     return out[:n], int(status.item()), guard_ok
@@ -121,10 +131,12 @@ def check_case(torch, sz, words: np.ndarray, label: str):
     if not np.array_equal(got, want):
         bad = np.nonzero(got != want)[0]
         raise AssertionError(f"{label}: {bad.size} container bytes differ, first at {bad[:8]}")
-    # GPU decode of the GPU container, GPU decode of the oracle container
-    y, st, guard = gpu_decode(torch, sz, got_dev, n)
-    assert st == 0 and guard, (label, st, guard)
-    assert torch.equal(y, x), label
+    # GPU decode (every form) of the GPU container, GPU decode of the oracle
+    # container
+    for form in DECODE_FORMS:
+        y, st, guard = gpu_decode(torch, sz, got_dev, n, form)
+        assert st == 0 and guard, (label, form, st, guard)
+        assert torch.equal(y, x), (label, form)
     y2, st2, guard2 = gpu_decode(torch, sz, torch.from_numpy(want).cuda(), n)
     assert st2 == 0 and guard2 and torch.equal(y2, x), label
     # oracle decode of the GPU container
@@ -189,9 +201,10 @@ def test_workload_full(torch, sz, name):
     assert got.size == want.size == d["container_bytes"]
     assert np.array_equal(got, want), f"{name}: container differs from the oracle"
     assert sha256(got) == d["container_sha256"]
-    y, st, guard = gpu_decode(torch, sz, got_dev, words.size)
-    assert st == 0 and guard and torch.equal(y, x)
-    del y
+    for form in DECODE_FORMS:
+        y, st, guard = gpu_decode(torch, sz, got_dev, words.size, form)
+        assert st == 0 and guard and torch.equal(y, x), (name, form)
+        del y
     assert np.array_equal(oracle.decode(got, words.size), words)
 
 
@@ -279,9 +292,13 @@ def test_corrupt_containers_flagged_on_device(torch, sz):
     esc = 176 + (n + 1) // 2 + n
 
     def status(c):
-        _, st, guard = gpu_decode(torch, sz, torch.from_numpy(c).cuda(), n)
-        assert guard, "decode wrote past element n"
-        return st
+        sts = []
+        for form in DECODE_FORMS:
+            _, st, guard = gpu_decode(torch, sz, torch.from_numpy(c).cuda(), n, form)
+            assert guard, "decode wrote past element n"
+            sts.append(st)
+        assert len(set(sts)) == 1, sts
+        return sts[0]
 
     assert status(good) == 0
     cases = {
@@ -300,6 +317,29 @@ def test_corrupt_containers_flagged_on_device(torch, sz):
     c = good.copy()
     c[esc:esc + 4], c[esc + 4:esc + 8] = good[esc + 4:esc + 8].copy(), good[esc:esc + 4].copy()
     assert status(c) == 4, "not ascending"
+    c = good.copy()
+    last = esc + 4 * (r.e - 1)
+    c[last:last + 4] = c[last - 4:last]
+    assert status(c) == 4, "last repeats"
+
+
+def test_corrupt_escapes_many_ranges(torch, sz):
+    """Escape-dense input over many decode ranges and record batches: an
+    out-of-order record deep inside is flagged by both decode forms, and
+    neither writes past the output."""
+    n = 3 * 8192 * 7 + 5
+    words = make_words("wide40", n, 21)
+    good = oracle.encode(words)
+    r = szformat.read(good)
+    assert r.e > 4096 * 3
+    esc = 176 + (n + 1) // 2 + n
+    for k in (1, 4095, 4096, 4097, r.e // 2, r.e - 1):
+        c = good.copy()
+        a, b = esc + 4 * (k - 1), esc + 4 * k
+        c[a:a + 4], c[b:b + 4] = good[b:b + 4].copy(), good[a:a + 4].copy()
+        for form in DECODE_FORMS:
+            _, st, guard = gpu_decode(torch, sz, torch.from_numpy(c).cuda(), n, form)
+            assert guard and st == 4, (k, form, st)
 
 
 def test_host_errors_with_real_buffers(torch, sz):

@@ -43,6 +43,18 @@ def _u(buf: np.ndarray, off: int, width: int) -> int:
     return int.from_bytes(buf[off:off + width].tobytes(), "little")
 
 
+def read_header(container) -> dict:
+    """The fixed 176-byte prefix only: header fields and codebook."""
+    b = np.ascontiguousarray(container, dtype=np.uint8).reshape(-1)
+    assert b.size >= PREFIX
+    return {
+        "magic": _u(b, 0, 4), "version": _u(b, 4, 2), "elem_type": _u(b, 6, 2),
+        "n": _u(b, 8, 8), "e": _u(b, 16, 8), "total": _u(b, 24, 8),
+        "seg_end": [_u(b, 32 + 8 * s, 8) for s in range(16)],
+        "codebook": [int(v) for v in b[160:176]],
+    }
+
+
 def read(container) -> Container:
     b = np.ascontiguousarray(container, dtype=np.uint8).reshape(-1)
     n = _u(b, 8, 8)

@@ -225,17 +225,20 @@ def test_workload_70b_32k(torch, sz):
     got_dev = gpu_encode(torch, sz, x, x.numel())
     assert got_dev.numel() == d["container_bytes"]
     say("header")
-    head = got_dev[:176].cpu().numpy()
-    r = szformat.read(np.concatenate([head, np.zeros(0, np.uint8)]))
-    assert r.e == d["escapes"]
-    assert r.codebook.tolist() == d["codebook"]
-    assert r.seg_end.tolist() == d["seg_end"]
+    h = szformat.read_header(got_dev[:176].cpu().numpy())
+    assert h["magic"] == szformat.MAGIC and h["n"] == d["n"]
+    assert h["e"] == d["escapes"] and h["total"] == d["container_bytes"]
+    assert h["codebook"] == d["codebook"]
+    assert h["seg_end"] == d["seg_end"]
+    assert h["seg_end"][0] < h["e"], "escapes on both sides of 2^32 expected"
     say("digest")
     assert sha256(got_dev.cpu().numpy()) == d["container_sha256"]
-    say("decode")
-    y, st, guard = gpu_decode(torch, sz, got_dev, x.numel())
-    assert st == 0 and guard
-    assert torch.equal(y, x)
+    for form in DECODE_FORMS:
+        say("decode", form)
+        y, st, guard = gpu_decode(torch, sz, got_dev, x.numel(), form)
+        assert st == 0 and guard, (form, st, guard)
+        assert torch.equal(y, x), form
+        del y
 
 
 def test_staged_calls_match_encode(torch, sz):

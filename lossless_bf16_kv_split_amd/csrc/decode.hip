@@ -129,7 +129,9 @@ __global__ __launch_bounds__(kUnpackThreads) void k_unpack(const uint8_t* __rest
             s0 = load4_unaligned(sm + 8 * g);
             s1 = load4_unaligned(sm + 8 * g + 4);
         }
-        *reinterpret_cast<uint4*>(out + 8 * g) = decode8(codes, s0, s1, cb);
+        // non-temporal: the words are not kept dirty in the caches, so later
+        // kernels do not pay for writing them back
+        store_streaming(reinterpret_cast<uint4*>(out + 8 * g), decode8(codes, s0, s1, cb));
     }
 
     // the last n % 8 words

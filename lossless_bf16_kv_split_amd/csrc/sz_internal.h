@@ -35,6 +35,19 @@ struct EncodePlan {
 
 EncodePlan plan_encode(uint64_t n);
 
+// 16-byte non-temporal load and store (global_load/store with the nt bit)
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 load_streaming(const uint4* p) {
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ void store_streaming(uint4* p, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+}
+
 // sz_decode patches escapes inside the unpack pass when more than one word
 // in kFusedDecodeDensity is an escape; below that, a separate in-place rewrite of
 // the few escaped words costs less than the fused pass's bookkeeping.

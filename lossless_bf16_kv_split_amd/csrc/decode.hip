@@ -269,7 +269,7 @@ __device__ uint64_t wave_lower_bound(const EscapeReader& r, uint64_t e, uint64_t
         const bool ge = k < hi ? r.position(k) >= target : true;
         const uint64_t m = __ballot(ge);
         const uint64_t f = m ? (uint64_t)(__ffsll((long long)m) - 1) : 64;
-        const uint64_t new_hi = f < 64 ? min(hi, lo + f * step) : hi;
+        const uint64_t new_hi = f < 64 ? min_u64(hi, lo + f * step) : hi;
         const uint64_t new_lo = f > 0 ? lo + (f - 1) * step + 1 : lo;
         lo = new_lo;
         hi = new_hi;
@@ -277,7 +277,7 @@ __device__ uint64_t wave_lower_bound(const EscapeReader& r, uint64_t e, uint64_t
     const uint64_t k = lo + lane;
     const bool ge = k < hi ? r.position(k) >= target : true;
     const uint64_t m = __ballot(ge);
-    return m ? min(lo + (uint64_t)(__ffsll((long long)m) - 1), hi) : hi;
+    return m ? min_u64(lo + (uint64_t)(__ffsll((long long)m) - 1), hi) : hi;
 }
 
 // a value every lane holds, moved to scalar registers
@@ -325,8 +325,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
     if (t < 16) seg_table[t] = reinterpret_cast<const uint64_t*>(src + 32)[t];
     __syncthreads();
 
-    const uint64_t begin = min((uint64_t)blockIdx.x << range_log2, n);
-    const uint64_t end = min(begin + (1ull << range_log2), n);
+    const uint64_t begin = min_u64((uint64_t)blockIdx.x << range_log2, n);
+    const uint64_t end = min_u64(begin + (uint64_t{1} << range_log2), n);
 
     // escapes of this range: [k_lo, k_hi)
     if (wave < 2) {
@@ -340,7 +340,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
 
     // batch of escape records in LDS, the next batch prefetched in registers
     uint64_t kb = k_lo;
-    uint32_t cnt = (uint32_t)min((uint64_t)kBatch, k_hi - kb);
+    uint32_t cnt = (uint32_t)min_u64(kBatch, k_hi - kb);
     uint64_t next_kb = kb + cnt;
     uint32_t pre_off[kBatchPerThread];   // offset from begin, or kNoSlot
     uint32_t pre_exp = 0;                // the records' exponents, one per byte
@@ -433,7 +433,7 @@ __global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
             if (!(more && ends_here)) break;
             __syncthreads();
             kb = next_kb;
-            cnt = (uint32_t)min((uint64_t)kBatch, k_hi - kb);
+            cnt = (uint32_t)min_u64(kBatch, k_hi - kb);
             next_kb = kb + cnt;
             install();
             fetch(next_kb);

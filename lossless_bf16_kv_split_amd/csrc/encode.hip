@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const uint16_t* __re
     __syncthreads();
 
     const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
-    const uint64_t end = min(begin + (1ull << chunk_log2), n);
+    const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
     uint32_t* mine = h + (threadIdx.x % kHistCopies) * kHistPitch;
 
     // 8 words per 16-byte load; four loads in flight per thread.  The loads
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
         const uint32_t b = 2 * t + j;
         if (b < chunks) {
             const uint64_t start = (uint64_t)b << chunk_log2;
-            const uint64_t len = min(1ull << chunk_log2, n - start);
+            const uint64_t len = min_u64(uint64_t{1} << chunk_log2, n - start);
             uint64_t kept = 0;
 #pragma unroll
             for (int c = 0; c < 16; c++) kept += v[j][c];
@@ -328,7 +328,13 @@ __device__ __forceinline__ uint32_t byte_of(uint32_t lo, uint32_t hi, int k) {
 
 // Escape records of one pack tile go to their final slots: a lane holds at
 // most 8 escapes, so four ballots on the bits of its count give its
-// exclusive prefix within the wave; wave totals meet in LDS.
+// exclusive prefix within the wave; wave totals meet in LDS.  A tile with
+// few escapes writes them from the lanes that found them.  A tile with many
+// first lays them out in LDS in slot order, then stores them with
+// consecutive threads on consecutive slots, so that each store instruction
+// fills whole cache lines instead of scattering 4- and 1-byte writes.
+constexpr uint32_t kStageMin = 1024;  // escapes per tile from which records are staged
+
 struct EscapeOut {
     uint8_t* pos;        // u32 positions (mod 2^32)
     uint8_t* exp;        // u8 exponents
@@ -336,12 +342,35 @@ struct EscapeOut {
     bool pos_aligned;    // pos is 4-byte aligned
 };
 
-__device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t i0, uint32_t ex_lo,
+// 16-byte aligned so that a wave reads all wave totals with wide LDS loads
+struct alignas(16) PackLds {
+    uint32_t wave_escapes[2][kPackWaves];
+    uint8_t lut[256];                      // exponent -> code, 0x10 = escape
+    uint16_t stage_off[kPackTile];         // tile offset of each staged escape
+    uint8_t stage_exp[kPackTile];
+};
+
+__device__ __forceinline__ void put_escape(const EscapeOut& out, uint64_t slot, uint32_t pos,
+                                           uint32_t exponent) {
+    if (slot >= out.limit) return;
+    if (out.pos_aligned) {
+        *reinterpret_cast<uint32_t*>(out.pos + 4 * slot) = pos;
+    } else {
+        out.pos[4 * slot + 0] = (uint8_t)(pos & 0xFF);
+        out.pos[4 * slot + 1] = (uint8_t)((pos >> 8) & 0xFF);
+        out.pos[4 * slot + 2] = (uint8_t)((pos >> 16) & 0xFF);
+        out.pos[4 * slot + 3] = (uint8_t)(pos >> 24);
+    }
+    out.exp[slot] = (uint8_t)exponent;
+}
+
+__device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t t0, uint32_t ex_lo,
                                                   uint32_t ex_hi, uint64_t slot_base,
-                                                  uint32_t (*wave_escapes)[kPackWaves],
-                                                  int parity, const EscapeOut& out) {
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+                                                  PackLds& lds, int parity,
+                                                  const EscapeOut& out) {
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = t >> 6;
     const uint32_t cnt = __popc(mask);
     const uint64_t b0 = __ballot(cnt & 1u);
     const uint64_t b1 = __ballot(cnt & 2u);
@@ -350,33 +379,40 @@ __device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t i0, ui
     const uint32_t lane_prefix =
         lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3);
     if (lane == 0)
-        wave_escapes[parity][wave] =
+        lds.wave_escapes[parity][wave] =
             __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3);
     __syncthreads();
     uint32_t before = 0, tile_total = 0;
 #pragma unroll
     for (int v = 0; v < kPackWaves; v++) {
-        const uint32_t x = wave_escapes[parity][v];
+        const uint32_t x = lds.wave_escapes[parity][v];
         before += v < wave ? x : 0u;
         tile_total += x;
     }
-    if (mask) {
-        uint64_t slot = slot_base + before + lane_prefix;
+    const uint32_t first = before + lane_prefix;  // this lane's first rank in the tile
+    if (tile_total >= kStageMin) {
+        if (mask) {
+            uint32_t q = first;
+#pragma unroll
+            for (int k = 0; k < 8; k++) {
+                if ((mask >> k) & 1u) {
+                    lds.stage_off[q] = (uint16_t)(8 * t + k);
+                    lds.stage_exp[q] = (uint8_t)byte_of(ex_lo, ex_hi, k);
+                    q++;
+                }
+            }
+        }
+        __syncthreads();
+        for (uint32_t q = t; q < tile_total; q += kPackThreads)
+            put_escape(out, slot_base + q, (uint32_t)((t0 + lds.stage_off[q]) & 0xFFFFFFFFull),
+                       lds.stage_exp[q]);
+    } else if (mask) {
+        uint64_t slot = slot_base + first;
 #pragma unroll
         for (int k = 0; k < 8; k++) {
             if ((mask >> k) & 1u) {
-                if (slot < out.limit) {
-                    const uint32_t pos = (uint32_t)((i0 + k) & 0xFFFFFFFFull);
-                    if (out.pos_aligned) {
-                        *reinterpret_cast<uint32_t*>(out.pos + 4 * slot) = pos;
-                    } else {
-                        out.pos[4 * slot + 0] = (uint8_t)(pos & 0xFF);
-                        out.pos[4 * slot + 1] = (uint8_t)((pos >> 8) & 0xFF);
-                        out.pos[4 * slot + 2] = (uint8_t)((pos >> 16) & 0xFF);
-                        out.pos[4 * slot + 3] = (uint8_t)(pos >> 24);
-                    }
-                    out.exp[slot] = (uint8_t)byte_of(ex_lo, ex_hi, k);
-                }
+                put_escape(out, slot, (uint32_t)((t0 + 8 * t + k) & 0xFFFFFFFFull),
+                           byte_of(ex_lo, ex_hi, k));
                 slot++;
             }
         }
@@ -385,13 +421,13 @@ __device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t i0, ui
 }
 
 template <bool kAlignedSm>
-__global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restrict__ src,
+__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP void k_pack(const uint16_t* __restrict__ src,
                                                       uint64_t n, uint32_t chunk_log2,
                                                       const uint64_t* __restrict__ chunk_base,
                                                       uint8_t* __restrict__ dst,
                                                       uint64_t dst_capacity) {
-    __shared__ uint8_t lut[256];            // exponent -> code, 0x10 = escape
-    __shared__ uint32_t wave_escapes[2][kPackWaves];
+    __shared__ PackLds lds;
+    uint8_t* lut = lds.lut;
 
     const int t = threadIdx.x;
     if (t < 256) lut[t] = 0x10;
@@ -413,21 +449,16 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restric
     uint8_t* sm = nib + (n + 1) / 2;
 
     const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
-    const uint64_t end = min(begin + (1ull << chunk_log2), n);
+    const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
     uint64_t slot_base = chunk_base[blockIdx.x];
 
     int parity = 0;
     uint64_t t0 = begin;
-    // whole tiles, no per-word checks; each tile's words are loaded one tile
-    // ahead so the loads stay in flight across this tile's barrier
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (t0 + kPackTile <= end) v = *reinterpret_cast<const uint4*>(src + t0 + (uint64_t)t * 8);
+    // whole tiles, no per-word checks
     for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
         const uint64_t i0 = t0 + (uint64_t)t * 8;
-        uint4 v_next = make_uint4(0, 0, 0, 0);
-        if (t0 + 2 * kPackTile <= end) v_next = *reinterpret_cast<const uint4*>(src + i0 + kPackTile);
+        const uint4 v = *reinterpret_cast<const uint4*>(src + i0);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        v = v_next;
         uint32_t sm_lo, sm_hi, ex_lo, ex_hi;
         split8(w, sm_lo, sm_hi, ex_lo, ex_hi);
         uint32_t nibbles = 0, mask = 0;
@@ -444,7 +475,7 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restric
 #pragma unroll
             for (int k = 0; k < 8; k++) sm[i0 + k] = (uint8_t)byte_of(sm_lo, sm_hi, k);
         }
-        slot_base += write_escapes(mask, i0, ex_lo, ex_hi, slot_base, wave_escapes, parity, esc);
+        slot_base += write_escapes(mask, t0, ex_lo, ex_hi, slot_base, lds, parity, esc);
     }
     // the ragged last tile of the input (last chunk only)
     if (t0 < end) {
@@ -471,7 +502,7 @@ __global__ __launch_bounds__(kPackThreads) void k_pack(const uint16_t* __restric
         for (uint32_t j = 0; j < (valid + 1) / 2; j++)
             nib[i0 / 2 + j] = (uint8_t)((nibbles >> (8 * j)) & 0xFF);
         for (uint32_t k = 0; k < valid; k++) sm[i0 + k] = (uint8_t)byte_of(sm_lo, sm_hi, k);
-        write_escapes(mask, i0, ex_lo, ex_hi, slot_base, wave_escapes, parity, esc);
+        write_escapes(mask, t0, ex_lo, ex_hi, slot_base, lds, parity, esc);
     }
 }
 

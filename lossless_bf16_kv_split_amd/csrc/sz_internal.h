@@ -35,6 +35,20 @@ struct EncodePlan {
 
 EncodePlan plan_encode(uint64_t n);
 
+// Residency of wide workgroups on MI355X: a wave whose kernel needs more
+// than 74 scalar registers of its own (80 with the ones the hardware
+// reserves) cannot share a SIMD with seven others, so a CU then holds one
+// 16-wave workgroup instead of two -- measured, whatever occupancy the
+// compiler reports.  Kernels that rely on eight waves per SIMD cap their
+// scalar registers with this attribute (excess values move to VGPR lanes).
+#define SZ_EIGHT_WAVE_SGPR_CAP __attribute__((amdgpu_num_sgpr(80)))
+
+// Integer minimum of two 64-bit counts (HIP's overloaded min would take a
+// mixed unsigned long / unsigned long long pair through double).
+__host__ __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) {
+    return a < b ? a : b;
+}
+
 // 16-byte non-temporal load and store (global_load/store with the nt bit)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 

@@ -42,7 +42,7 @@ KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select
                 "pack": "k_pack", "fused": "k_decode_fused", "unpack": "k_unpack",
                 "scatter": "k_scatter"}
 # sz_decode runs the single pass when more than one word in this many escapes
-FUSED_DECODE_DENSITY = 128
+FUSED_DECODE_DENSITY = 2048
 
 
 def kernel_source_hash() -> str:

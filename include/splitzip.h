@@ -93,9 +93,10 @@ sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
 /* Decompress a container of src_bytes bytes into n BF16 words at d_dst,
  * bit-exactly.  SplitZip explainer section "4. Pourquoi est-ce rapide ?"
  * (code -> exponent lookup, recombination with sign and mantissa, escaped
- * slots overwritten).  With many escapes (more than one word in 128) it runs
- * as one pass that overwrites the escaped exponents before each word is
- * stored; otherwise as the two staged passes below.  Same result either way.
+ * slots overwritten).  Unless escapes are very rare (at most one word in
+ * 2048) it runs as one pass that overwrites the escaped exponents before
+ * each word is stored; otherwise as the two staged passes below.  Same
+ * result either way.
  *   src_bytes   must equal the container's total size: the host derives E
  *               from it, so no device read is needed before launching
  *   d_status    optional device i32: SZ_OK, or SZ_ERR_CORRUPT when the

@@ -222,7 +222,7 @@ hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* 
 #define SZ_FUSED_THREADS 512
 #endif
 #ifndef SZ_FUSED_BATCH_PER_THREAD
-#define SZ_FUSED_BATCH_PER_THREAD 4
+#define SZ_FUSED_BATCH_PER_THREAD 2
 #endif
 constexpr int kFusedThreads = SZ_FUSED_THREADS;
 constexpr uint32_t kFusedTile = kFusedThreads * 8;   // words per workgroup step
@@ -296,7 +296,11 @@ __device__ __forceinline__ uint32_t bits_to_bytes(uint32_t x) {
 __global__ void k_status_clear(int32_t* status) { *status = 0; }
 
 template <bool kAlignedSm>
-__global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
+// Eight waves per SIMD (four workgroups per CU) need at most 64 VGPRs and
+// the scalar-register cap; two prefetched records per thread and no
+// register prefetch of the next tile keep the kernel inside both.
+__global__ __launch_bounds__(kFusedThreads) SZ_EIGHT_WAVE_SGPR_CAP
+__attribute__((amdgpu_waves_per_eu(8))) void k_decode_fused(
     const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e,
     uint32_t range_log2, uint16_t* __restrict__ out, int32_t* status) {
     __shared__ uint32_t batch_pos[kBatch];            // offsets from the range start
@@ -386,8 +390,8 @@ __global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
     install();
     fetch(next_kb);
 
-    // A tile's codes and sign|mantissa bytes are loaded one tile ahead, so
-    // the loads stay in flight across this tile's barriers and patching.
+    // a tile's codes and sign|mantissa bytes; their loads stay in flight
+    // while the tile's escapes are marked
     auto load_tile = [&](uint64_t i0, uint32_t& codes, uint32_t& s0, uint32_t& s1) {
         if (i0 + 8 <= end) {
             codes = *reinterpret_cast<const uint32_t*>(nib + i0 / 2);
@@ -401,15 +405,13 @@ __global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
             }
         }
     };
-    uint32_t codes = 0, s0 = 0, s1 = 0;
-    load_tile(begin + (uint64_t)t * 8, codes, s0, s1);
 
     int parity = 0;
     for (uint64_t t0 = begin; t0 < end; t0 += kFusedTile, parity ^= 1) {
         const uint64_t i0 = t0 + (uint64_t)t * 8;
         const bool full = i0 + 8 <= end;
-        uint32_t next_codes = 0, next_s0 = 0, next_s1 = 0;
-        if (t0 + kFusedTile < end) load_tile(i0 + kFusedTile, next_codes, next_s0, next_s1);
+        uint32_t codes = 0, s0 = 0, s1 = 0;
+        load_tile(i0, codes, s0, s1);
         for (int q = t; q < (int)(kFusedTile / 32); q += kFusedThreads) patch_bits[parity][q] = 0;
         __syncthreads();
 
@@ -460,9 +462,6 @@ __global__ __launch_bounds__(kFusedThreads) void k_decode_fused(
                 out[i] = (uint16_t)recombine(sm[i], ex);
             }
         }
-        codes = next_codes;
-        s0 = next_s0;
-        s1 = next_s1;
     }
     __syncthreads();
     if (t == 0 && bad && status)

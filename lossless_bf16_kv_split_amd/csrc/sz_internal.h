@@ -63,9 +63,10 @@ __device__ __forceinline__ void store_streaming(uint4* p, uint4 v) {
 }
 
 // sz_decode patches escapes inside the unpack pass when more than one word
-// in kFusedDecodeDensity is an escape; below that, a separate in-place rewrite of
-// the few escaped words costs less than the fused pass's bookkeeping.
-constexpr uint64_t kFusedDecodeDensity = 128;
+// in kFusedDecodeDensity is an escape; below that, a separate in-place
+// rewrite of the few escaped words costs less than the fused pass's
+// bookkeeping (measured crossover on MI355X: about one word in 2000).
+constexpr uint64_t kFusedDecodeDensity = 2048;
 
 inline uint64_t container_bytes(uint64_t n, uint64_t e) {
     return kPrefixBytes + (n + 1) / 2 + n + 5 * e;

@@ -290,12 +290,20 @@ hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst, uint6
 
 // ---------------------------------------------------------------- pass 3
 
-// 16 waves per workgroup and 8192-word tiles: measured fastest for this
-// read 2 / write 1.5 byte stream (fewer, longer concurrent streams).
+// A tile is kPackTile consecutive words; thread t packs kPackWords
+// consecutive words of it, so each lane loads, and stores nibbles and
+// sign|mantissa bytes, in pieces of 8 or 16 bytes.  16 waves x 16 words
+// measured fastest on the 1 GiB KV workload (381 us, against 391 us for
+// 16 x 8 and 403 us for 8 x 16); a pure load/store probe of the same byte
+// stream takes about 360 us.
 constexpr int kPackThreads = 1024;
+constexpr int kPackWords = 16;
 constexpr int kPackWaves = kPackThreads / 64;
-constexpr uint32_t kPackTile = kPackThreads * 8;  // words per workgroup step
+constexpr uint32_t kPackTile = kPackThreads * kPackWords;  // words per workgroup step
+constexpr int kPackLoads = kPackWords / 8;                 // 16-byte loads per thread
+static_assert(kPackWords == 8 || kPackWords == 16, "one or two 16-byte loads per thread");
 static_assert((1u << kMinChunkLog2) % kPackTile == 0, "chunks hold whole tiles");
+static_assert(kPackTile <= 65536, "tile offsets fit in 16 bits");
 static_assert(kPackThreads >= 256, "one LUT entry per thread");
 static_assert(2 * kSelectThreads >= kMaxChunks, "two chunks per select thread");
 
@@ -310,7 +318,7 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
 // v_perm gathers the high and low bytes of 4 words; the sign is bit 7 of
 // the high byte, the mantissa bits 6..0 of the low byte, the exponent the
 // high byte's low 7 bits above the low byte's bit 7.
-__device__ __forceinline__ void split8(const uint32_t w[4], uint32_t& sm_lo, uint32_t& sm_hi,
+__device__ __forceinline__ void split8(const uint32_t* w, uint32_t& sm_lo, uint32_t& sm_hi,
                                        uint32_t& ex_lo, uint32_t& ex_hi) {
     const uint32_t hi0 = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u);
     const uint32_t lo0 = __builtin_amdgcn_perm(w[1], w[0], 0x06040200u);
@@ -322,12 +330,39 @@ __device__ __forceinline__ void split8(const uint32_t w[4], uint32_t& sm_lo, uin
     ex_hi = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
 }
 
-__device__ __forceinline__ uint32_t byte_of(uint32_t lo, uint32_t hi, int k) {
-    return ((k < 4 ? lo : hi) >> (8 * (k & 3))) & 0xFFu;
+// byte k of a little-endian run of dwords (k known at compile time after
+// unrolling, so the array stays in registers)
+__device__ __forceinline__ uint32_t byte_at(const uint32_t* v, int k) {
+    return (v[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+}
+
+// The words of one thread, split: sign|mantissa and exponent bytes, the
+// 4-bit codes (element k in bits 4(k%8).. of nib[k/8]) and the escape mask.
+struct ThreadWords {
+    uint32_t sm[kPackWords / 4];
+    uint32_t ex[kPackWords / 4];
+    uint32_t nib[kPackWords / 8];
+    uint32_t mask;
+};
+
+__device__ __forceinline__ void encode_words(const uint32_t* w, const uint8_t* lut,
+                                             ThreadWords& r) {
+#pragma unroll
+    for (int h = 0; h < kPackWords / 8; h++)
+        split8(w + 4 * h, r.sm[2 * h], r.sm[2 * h + 1], r.ex[2 * h], r.ex[2 * h + 1]);
+    r.mask = 0;
+#pragma unroll
+    for (int h = 0; h < kPackWords / 8; h++) r.nib[h] = 0;
+#pragma unroll
+    for (int k = 0; k < kPackWords; k++) {
+        const uint32_t code = lut[byte_at(r.ex, k)];
+        r.nib[k >> 3] |= (code & 0xFu) << (4 * (k & 7));
+        r.mask |= (code >> 4) << k;
+    }
 }
 
 // Escape records of one pack tile go to their final slots: a lane holds at
-// most 8 escapes, so four ballots on the bits of its count give its
+// most 16 escapes, so five ballots on the bits of its count give its
 // exclusive prefix within the wave; wave totals meet in LDS.  A tile with
 // few escapes writes them from the lanes that found them.  A tile with many
 // first lays them out in LDS in slot order, then stores them with
@@ -364,23 +399,23 @@ __device__ __forceinline__ void put_escape(const EscapeOut& out, uint64_t slot, 
     out.exp[slot] = (uint8_t)exponent;
 }
 
-__device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t t0, uint32_t ex_lo,
-                                                  uint32_t ex_hi, uint64_t slot_base,
-                                                  PackLds& lds, int parity,
+// Positions are stored modulo 2^32, so their sums are taken in 32 bits.
+__device__ __forceinline__ uint32_t write_escapes(const ThreadWords& r, uint64_t t0,
+                                                  uint64_t slot_base, PackLds& lds, int parity,
                                                   const EscapeOut& out) {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
+    const uint32_t mask = r.mask;
     const uint32_t cnt = __popc(mask);
-    const uint64_t b0 = __ballot(cnt & 1u);
-    const uint64_t b1 = __ballot(cnt & 2u);
-    const uint64_t b2 = __ballot(cnt & 4u);
-    const uint64_t b3 = __ballot(cnt & 8u);
-    const uint32_t lane_prefix =
-        lanes_below(b0) + 2 * lanes_below(b1) + 4 * lanes_below(b2) + 8 * lanes_below(b3);
-    if (lane == 0)
-        lds.wave_escapes[parity][wave] =
-            __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2) + 8 * __popcll(b3);
+    uint32_t lane_prefix = 0, wave_total = 0;
+#pragma unroll
+    for (int b = 0; b < (kPackWords == 16 ? 5 : 4); b++) {
+        const uint64_t bits = __ballot(cnt & (1u << b));
+        lane_prefix += lanes_below(bits) << b;
+        wave_total += (uint32_t)__popcll(bits) << b;
+    }
+    if (lane == 0) lds.wave_escapes[parity][wave] = wave_total;
     __syncthreads();
     uint32_t before = 0, tile_total = 0;
 #pragma unroll
@@ -394,25 +429,24 @@ __device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t t0, ui
         if (mask) {
             uint32_t q = first;
 #pragma unroll
-            for (int k = 0; k < 8; k++) {
+            for (int k = 0; k < kPackWords; k++) {
                 if ((mask >> k) & 1u) {
-                    lds.stage_off[q] = (uint16_t)(8 * t + k);
-                    lds.stage_exp[q] = (uint8_t)byte_of(ex_lo, ex_hi, k);
+                    lds.stage_off[q] = (uint16_t)(kPackWords * t + k);
+                    lds.stage_exp[q] = (uint8_t)byte_at(r.ex, k);
                     q++;
                 }
             }
         }
         __syncthreads();
         for (uint32_t q = t; q < tile_total; q += kPackThreads)
-            put_escape(out, slot_base + q, (uint32_t)((t0 + lds.stage_off[q]) & 0xFFFFFFFFull),
-                       lds.stage_exp[q]);
+            put_escape(out, slot_base + q, (uint32_t)t0 + lds.stage_off[q], lds.stage_exp[q]);
     } else if (mask) {
         uint64_t slot = slot_base + first;
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
+        for (int k = 0; k < kPackWords; k++) {
             if ((mask >> k) & 1u) {
-                put_escape(out, slot, (uint32_t)((t0 + 8 * t + k) & 0xFFFFFFFFull),
-                           byte_of(ex_lo, ex_hi, k));
+                put_escape(out, slot, (uint32_t)t0 + (uint32_t)(kPackWords * t + k),
+                           byte_at(r.ex, k));
                 slot++;
             }
         }
@@ -420,12 +454,37 @@ __device__ __forceinline__ uint32_t write_escapes(uint32_t mask, uint64_t t0, ui
     return tile_total;
 }
 
+// One whole tile: thread t packs words t0 + kPackWords*t onwards, loaded in
+// w; returns the tile's escape count.
 template <bool kAlignedSm>
-__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP void k_pack(const uint16_t* __restrict__ src,
-                                                      uint64_t n, uint32_t chunk_log2,
-                                                      const uint64_t* __restrict__ chunk_base,
-                                                      uint8_t* __restrict__ dst,
-                                                      uint64_t dst_capacity) {
+__device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0, const uint8_t* lut,
+                                              uint8_t* nib, uint8_t* sm, uint64_t slot_base,
+                                              PackLds& lds, int parity, const EscapeOut& esc) {
+    const uint64_t i0 = t0 + (uint64_t)threadIdx.x * kPackWords;
+    ThreadWords r;
+    encode_words(w, lut, r);
+    if constexpr (kPackWords == 16) {
+        *reinterpret_cast<uint2*>(nib + i0 / 2) = make_uint2(r.nib[0], r.nib[1]);
+    } else {
+        *reinterpret_cast<uint32_t*>(nib + i0 / 2) = r.nib[0];
+    }
+    if (kAlignedSm) {
+        if constexpr (kPackWords == 16)
+            *reinterpret_cast<uint4*>(sm + i0) = make_uint4(r.sm[0], r.sm[1], r.sm[2], r.sm[3]);
+        else
+            *reinterpret_cast<uint2*>(sm + i0) = make_uint2(r.sm[0], r.sm[1]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < kPackWords; k++) sm[i0 + k] = (uint8_t)byte_at(r.sm, k);
+    }
+    return write_escapes(r, t0, slot_base, lds, parity, esc);
+}
+
+template <bool kAlignedSm>
+__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
+__attribute__((amdgpu_waves_per_eu(8))) void k_pack(
+    const uint16_t* __restrict__ src, uint64_t n, uint32_t chunk_log2,
+    const uint64_t* __restrict__ chunk_base, uint8_t* __restrict__ dst, uint64_t dst_capacity) {
     __shared__ PackLds lds;
     uint8_t* lut = lds.lut;
 
@@ -456,53 +515,46 @@ __global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP void k_pack(co
     uint64_t t0 = begin;
     // whole tiles, no per-word checks
     for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
-        const uint64_t i0 = t0 + (uint64_t)t * 8;
-        const uint4 v = *reinterpret_cast<const uint4*>(src + i0);
-        const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-        uint32_t sm_lo, sm_hi, ex_lo, ex_hi;
-        split8(w, sm_lo, sm_hi, ex_lo, ex_hi);
-        uint32_t nibbles = 0, mask = 0;
+        const uint4* p = reinterpret_cast<const uint4*>(src + t0 + (uint64_t)t * kPackWords);
+        uint32_t w[kPackWords / 2];
 #pragma unroll
-        for (int k = 0; k < 8; k++) {
-            const uint32_t code = lut[byte_of(ex_lo, ex_hi, k)];
-            nibbles |= (code & 0xFu) << (4 * k);
-            mask |= (code >> 4) << k;
+        for (int h = 0; h < kPackLoads; h++) {
+            const uint4 v = p[h];
+            w[4 * h + 0] = v.x;
+            w[4 * h + 1] = v.y;
+            w[4 * h + 2] = v.z;
+            w[4 * h + 3] = v.w;
         }
-        *reinterpret_cast<uint32_t*>(nib + i0 / 2) = nibbles;
-        if (kAlignedSm) {
-            *reinterpret_cast<uint2*>(sm + i0) = make_uint2(sm_lo, sm_hi);
-        } else {
-#pragma unroll
-            for (int k = 0; k < 8; k++) sm[i0 + k] = (uint8_t)byte_of(sm_lo, sm_hi, k);
-        }
-        slot_base += write_escapes(mask, t0, ex_lo, ex_hi, slot_base, lds, parity, esc);
+        slot_base += pack_tile<kAlignedSm>(w, t0, lut, nib, sm, slot_base, lds, parity, esc);
     }
-    // the ragged last tile of the input (last chunk only)
+    // the ragged last tile of the input (last chunk only); every index below
+    // is a compile-time constant after unrolling, so nothing leaves registers
     if (t0 < end) {
-        const uint64_t i0 = t0 + (uint64_t)t * 8;
-        const uint32_t valid = i0 + 8 <= end ? 8u : (i0 < end ? (uint32_t)(end - i0) : 0u);
-        uint64_t lo4 = 0, hi4 = 0;  // words 0..3 and 4..7
-        for (uint32_t k = 0; k < valid; k++) {
-            const uint64_t word = src[i0 + k];
-            if (k < 4)
-                lo4 |= word << (16 * k);
-            else
-                hi4 |= word << (16 * (k - 4));
+        const uint64_t i0 = t0 + (uint64_t)t * kPackWords;
+        const uint32_t valid =
+            i0 + kPackWords <= end ? kPackWords : (i0 < end ? (uint32_t)(end - i0) : 0u);
+        uint32_t w[kPackWords / 2];
+#pragma unroll
+        for (int j = 0; j < kPackWords / 2; j++) {
+            const uint32_t lo = 2 * j < (int)valid ? src[i0 + 2 * j] : 0u;
+            const uint32_t hi = 2 * j + 1 < (int)valid ? src[i0 + 2 * j + 1] : 0u;
+            w[j] = lo | (hi << 16);
         }
-        const uint32_t w[4] = {(uint32_t)lo4, (uint32_t)(lo4 >> 32), (uint32_t)hi4,
-                               (uint32_t)(hi4 >> 32)};
-        uint32_t sm_lo, sm_hi, ex_lo, ex_hi;
-        split8(w, sm_lo, sm_hi, ex_lo, ex_hi);
-        uint32_t nibbles = 0, mask = 0;
-        for (uint32_t k = 0; k < valid; k++) {
-            const uint32_t code = lut[byte_of(ex_lo, ex_hi, k)];
-            nibbles |= (code & 0xFu) << (4 * k);
-            mask |= (code >> 4) << k;
-        }
-        for (uint32_t j = 0; j < (valid + 1) / 2; j++)
-            nib[i0 / 2 + j] = (uint8_t)((nibbles >> (8 * j)) & 0xFF);
-        for (uint32_t k = 0; k < valid; k++) sm[i0 + k] = (uint8_t)byte_of(sm_lo, sm_hi, k);
-        write_escapes(mask, t0, ex_lo, ex_hi, slot_base, lds, parity, esc);
+        ThreadWords r;
+        encode_words(w, lut, r);
+        // words past the end have no code (the pad nibble of an odd n is 0)
+        // and are no escapes
+        r.mask &= (1u << valid) - 1u;  // valid <= 16
+#pragma unroll
+        for (int k = 0; k < kPackWords; k++)
+            if (k >= (int)valid) r.nib[k >> 3] &= ~(0xFu << (4 * (k & 7)));
+#pragma unroll
+        for (int j = 0; j < kPackWords / 2; j++)
+            if (2 * j < (int)valid) nib[i0 / 2 + j] = (uint8_t)byte_at(r.nib, j);
+#pragma unroll
+        for (int k = 0; k < kPackWords; k++)
+            if (k < (int)valid) sm[i0 + k] = (uint8_t)byte_at(r.sm, k);
+        write_escapes(r, t0, slot_base, lds, parity, esc);
     }
 }
 

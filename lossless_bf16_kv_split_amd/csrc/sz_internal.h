@@ -19,7 +19,7 @@ constexpr uint64_t kMaxElements = 1ull << 36;
 // exact number of escapes of every chunk (and so into each chunk's first
 // escape slot), and the pack pass lets one workgroup stream one chunk.
 // A chunk holds whole pack tiles and the grid is at most kMaxChunks.
-constexpr uint32_t kMinChunkLog2 = 13;
+constexpr uint32_t kMinChunkLog2 = 14;
 constexpr uint32_t kMaxChunks = 2048;
 
 struct EncodePlan {

@@ -168,9 +168,9 @@ def test_worked_example(torch, sz):
 
 def test_many_chunks_ragged(torch, sz):
     # more than 2048 minimum-size chunks: larger chunks, a ragged last chunk
-    for n in (2048 * 4096 + 123, 2 * 2048 * 8192 + 77):
+    for n in (2048 * 16384 + 123, 2 * 2048 * 16384 + 77):
         check_case(torch, sz, make_words("kv", n, 7), "many chunks kv")
-    check_case(torch, sz, make_words("wide40", 2048 * 4096 + 5, 8), "many chunks wide40")
+    check_case(torch, sz, make_words("wide40", 2048 * 16384 + 5, 8), "many chunks wide40")
 
 
 def sha256(a: np.ndarray) -> str:

@@ -39,10 +39,12 @@ KERNEL_SOURCES = ["lossless_bf16_kv_split_amd/csrc/encode.hip",
                   "lossless_bf16_kv_split_amd/csrc/sz_internal.h"]
 ENCODE_PASSES = ["histogram", "codebook", "pack"]
 KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select",
-                "pack": "k_pack", "fused": "k_decode_fused", "unpack": "k_unpack",
-                "scatter": "k_scatter"}
-# sz_decode runs the single pass when more than one word in this many escapes
+                "pack": "k_pack", "fused": "k_decode_fused", "dense": "k_decode_dense",
+                "unpack": "k_unpack", "scatter": "k_scatter"}
+# sz_decode runs a single pass when more than one word in FUSED_DECODE_DENSITY
+# is an escape, the dense single pass above one in DENSE_DECODE_DENSITY
 FUSED_DECODE_DENSITY = 2048
+DENSE_DECODE_DENSITY = 32
 
 
 def kernel_source_hash() -> str:
@@ -62,6 +64,7 @@ def algorithmic_bytes(n: int, e: int) -> dict:
         "codebook": 0,                             # O(chunks) metadata only
         "pack": 2 * n + nib + sm + esc + pre,      # read words, write container
         "fused": pre + nib + sm + esc + 2 * n,     # read container, write words once
+        "dense": pre + nib + sm + esc + 2 * n,     # the same, other layout
         "unpack": pre + nib + sm + 2 * n,          # read codes + sm, write words
         "scatter": esc + 4 * e,                    # read records; read + rewrite each escaped word
     }
@@ -163,10 +166,14 @@ def main() -> int:
     container = dst[:total]
     e = int.from_bytes(container[16:24].cpu().numpy().tobytes(), "little")
 
-    # the decode passes sz_decode runs for this container (same rule)
-    dense = e > n // FUSED_DECODE_DENSITY
-    decode_passes = ["fused"] if dense else ["unpack", "scatter"]
-    other_passes = ["unpack", "scatter"] if dense else ["fused"]
+    # the decode passes sz_decode runs for this container (same rule), and
+    # the closest other form, timed after the timed region
+    if e > n // DENSE_DECODE_DENSITY:
+        decode_passes, other_passes, form = ["dense"], ["fused"], "single pass, exponent map"
+    elif e > n // FUSED_DECODE_DENSITY:
+        decode_passes, other_passes, form = ["fused"], ["unpack", "scatter"], "single pass"
+    else:
+        decode_passes, other_passes, form = ["unpack", "scatter"], ["fused"], "unpack + escape scatter"
     passes = ENCODE_PASSES + decode_passes
 
     def run_pass(p, dst_words):
@@ -178,6 +185,8 @@ def main() -> int:
             sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap, stream)
         elif p == "fused":
             sz.sz_decode_fused(container, total, dst_words, n, status, stream)
+        elif p == "dense":
+            sz.sz_decode_dense(container, total, dst_words, n, status, stream)
         elif p == "unpack":
             sz.sz_decode_unpack(container, total, dst_words, n, status, stream)
         elif p == "scatter":
@@ -284,7 +293,7 @@ def main() -> int:
         "decode_GBps": round(2 * n / (dec_ms * 1e-3) / 1e9, 2),
         "encode_frac_hbm": round(enc_alg / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "decode_frac_hbm": round(dec_alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "decode_form": "single pass" if dense else "unpack + escape scatter",
+        "decode_form": form,
         "other_decode_form_GBps": round(2 * n / (other_dec_ms * 1e-3) / 1e9, 2),
         "ratio": round(2 * n / total, 5),
         "escapes": e,

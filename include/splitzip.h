@@ -95,8 +95,9 @@ sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
  * (code -> exponent lookup, recombination with sign and mantissa, escaped
  * slots overwritten).  Unless escapes are very rare (at most one word in
  * 2048) it runs as one pass that overwrites the escaped exponents before
- * each word is stored; otherwise as the two staged passes below.  Same
- * result either way.
+ * each word is stored (sz_decode_fused, or sz_decode_dense above one escape
+ * in 32 words); otherwise as the two staged passes below.  Same result
+ * every way.
  *   src_bytes   must equal the container's total size: the host derives E
  *               from it, so no device read is needed before launching
  *   d_status    optional device i32: SZ_OK, or SZ_ERR_CORRUPT when the
@@ -158,8 +159,18 @@ sz_status sz_decode_scatter(const void *d_src, uint64_t src_bytes, void *d_dst,
  * positions, stages them in LDS and overwrites the escaped exponents before
  * the words are stored (explainer section "4. Pourquoi est-ce rapide ?").
  * Same arguments, result and status as sz_decode, which picks this form
- * for escape-dense containers. */
+ * when between one word in 2048 and one in 32 is an escape. */
 sz_status sz_decode_fused(const void *d_src, uint64_t src_bytes, void *d_dst,
+                          uint64_t n_elements, int32_t *d_status, hipStream_t stream);
+
+/* Decode in a single pass, laid out for many escapes: each workgroup walks
+ * its range in sub-ranges of 16384 words, reads the escape records of each
+ * sub-range straight from the escape stream into a per-word LDS map, and
+ * rebuilds the words with the mapped exponents in place of the codebook's
+ * (explainer section "4. Pourquoi est-ce rapide ?").  Same arguments,
+ * result and status as sz_decode, which picks this form when more than one
+ * word in 32 is an escape. */
+sz_status sz_decode_dense(const void *d_src, uint64_t src_bytes, void *d_dst,
                           uint64_t n_elements, int32_t *d_status, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */

@@ -25,7 +25,8 @@ import os
 __all__ = [
     "SplitZipError", "lib_path", "sz_max_compressed_size", "sz_workspace_size", "sz_encode",
     "sz_decode", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
-    "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_status_string", "encode",
+    "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
+    "sz_status_string", "encode",
     "decode",
     "PREFIX_BYTES", "MAX_ELEMENTS",
 ]
@@ -69,8 +70,10 @@ def _load() -> ctypes.CDLL:
     L.sz_decode_unpack.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_scatter.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_fused.argtypes = [p, u64, p, u64, p, p]
+    L.sz_decode_dense.argtypes = [p, u64, p, u64, p, p]
     for name in ("sz_encode", "sz_decode", "sz_encode_histogram", "sz_encode_codebook",
-                 "sz_encode_pack", "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused"):
+                 "sz_encode_pack", "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
+                 "sz_decode_dense"):
         getattr(L, name).restype = i32
     L.sz_status_string.argtypes = [i32]
     L.sz_status_string.restype = ctypes.c_char_p
@@ -161,6 +164,12 @@ def sz_decode_fused(src, src_bytes: int, dst, n_elements: int, d_status=None,
                     stream=None) -> None:
     _check(_lib.sz_decode_fused(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
                                 _stream(stream)), "sz_decode_fused")
+
+
+def sz_decode_dense(src, src_bytes: int, dst, n_elements: int, d_status=None,
+                    stream=None) -> None:
+    _check(_lib.sz_decode_dense(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
+                                _stream(stream)), "sz_decode_dense")
 
 
 # ---- conveniences (torch allocates; the library computes) -----------------

@@ -193,8 +193,12 @@ sz_status sz_decode(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
     const uint8_t* src = static_cast<const uint8_t*>(d_src);
     uint16_t* dst = static_cast<uint16_t*>(d_dst);
+    if (e > n / sz::kDenseDecodeDensity) {
+        // many escapes: one pass with a per-word LDS map of exponents
+        return hip_status(sz::launch_decode_dense(src, src_bytes, n, e, dst, d_status, stream));
+    }
     if (e > n / sz::kFusedDecodeDensity) {
-        // escape-dense: patch escaped exponents before each word is stored
+        // some escapes: patch escaped exponents before each word is stored
         return hip_status(sz::launch_decode_fused(src, src_bytes, n, e, dst, d_status, stream));
     }
     // escape-sparse: stream every word out, then rewrite the few escaped ones
@@ -211,6 +215,14 @@ sz_status sz_decode_fused(const void* d_src, uint64_t src_bytes, void* d_dst, ui
     uint64_t e = 0;
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
     return hip_status(sz::launch_decode_fused(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
+                                              static_cast<uint16_t*>(d_dst), d_status, stream));
+}
+
+sz_status sz_decode_dense(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
+                          int32_t* d_status, hipStream_t stream) {
+    uint64_t e = 0;
+    if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
+    return hip_status(sz::launch_decode_dense(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
                                               static_cast<uint16_t*>(d_dst), d_status, stream));
 }
 

@@ -240,19 +240,18 @@ struct EscapeReader {
     bool one_segment;
     bool aligned;
 
+    __device__ uint32_t low32(uint64_t k) const {
+        return aligned ? reinterpret_cast<const uint32_t*>(pos_lo)[k]
+                       : load4_unaligned(pos_lo + 4 * k);
+    }
+
     __device__ uint64_t position(uint64_t k) const {
         uint64_t seg = 0;
         if (!one_segment) {
 #pragma unroll
             for (int s = 0; s < 16; s++) seg += seg_end[s] <= k ? 1u : 0u;
         }
-        uint32_t lo;
-        if (aligned) {
-            lo = reinterpret_cast<const uint32_t*>(pos_lo)[k];
-        } else {
-            lo = load4_unaligned(pos_lo + 4 * k);
-        }
-        return (seg << 32) | lo;
+        return (seg << 32) | low32(k);
     }
 };
 
@@ -482,6 +481,224 @@ hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t 
     else
         k_decode_fused<false><<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(src, src_bytes, n,
                                                                              e, r, dst, status);
+    return hipGetLastError();
+}
+
+// ------------------------------------------------------------------------
+// Dense decode: the single pass again, for inputs with many escapes.  One
+// workgroup per power-of-two range of words, walked in
+// sub-ranges of kDecTile words.  For each sub-range the workgroup reads the
+// escape records that fall in it straight from the escape stream (thread t
+// takes records t, t + 512, ... after the last one consumed, and stops at
+// the first whose position lies beyond the sub-range), writes each record's
+// exponent into an LDS map with one entry per word, then rebuilds its words
+// with the map's entries taking the place of the codebook's exponents.
+// Thread t rebuilds the 8-word groups at t*8, t*8 + 4096, ... of the
+// sub-range, so each wave's loads and stores cover consecutive bytes (wider
+// per-thread runs measured slower on MI355X).  There are no LDS atomics and
+// no record staging: two barriers per sub-range.
+
+constexpr int kDenseThreads = 512;
+constexpr int kGroups = 4;                                 // 8-word groups per thread
+constexpr uint32_t kGroupStride = 8 * kDenseThreads;       // words between a thread's groups
+constexpr uint32_t kDenseTile = kGroups * kGroupStride;    // words per sub-range
+constexpr uint32_t kMapEscaped = 0x100u;                   // map entry: 0x100 | exponent
+constexpr uint32_t kNoBreak = 0xFFFFFFFFu;
+constexpr int kWalk = 2;                                   // records per thread and step
+static_assert((1u << 14) % kDenseTile == 0, "ranges of at least 2^14 words hold whole sub-ranges");
+
+// Eight 16-bit map entries (one uint4) to the exponent bytes that replace
+// e0 (elements 0..3) and e1 (elements 4..7) where an entry is set.
+__device__ __forceinline__ void patch8(uint4 m, uint32_t& e0, uint32_t& e1) {
+    if ((m.x | m.y | m.z | m.w) == 0) return;
+    const uint32_t x0 = perm(m.y, m.x, 0x06040200u);   // exponent bytes, elements 0..3
+    const uint32_t x1 = perm(m.w, m.z, 0x06040200u);   // elements 4..7
+    const uint32_t f0 = perm(m.y, m.x, 0x07050301u);   // 1 where escaped, else 0
+    const uint32_t f1 = perm(m.w, m.z, 0x07050301u);
+    e0 = bitselect(f0 * 0xFFu, x0, e0);
+    e1 = bitselect(f1 * 0xFFu, x1, e1);
+}
+
+// Codes (one dword) and sign|mantissa bytes (two dwords) of the 8 words
+// from word w; the sign|mantissa stream is 8-byte aligned or not.
+template <bool kAlignedSm>
+__device__ __forceinline__ void load_group(const uint8_t* nib, const uint8_t* sm, uint64_t w,
+                                           uint32_t& c, uint32_t& s0, uint32_t& s1) {
+    c = *reinterpret_cast<const uint32_t*>(nib + w / 2);
+    if (kAlignedSm) {
+        const uint2 v = *reinterpret_cast<const uint2*>(sm + w);
+        s0 = v.x;
+        s1 = v.y;
+    } else {
+        s0 = load4_unaligned(sm + w);
+        s1 = load4_unaligned(sm + w + 4);
+    }
+}
+
+// Eight waves per SIMD (four workgroups per CU) need at most 64 VGPRs and
+// the scalar-register cap.
+template <bool kAlignedSm>
+__global__ __launch_bounds__(kDenseThreads) SZ_EIGHT_WAVE_SGPR_CAP
+__attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
+    const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e,
+    uint32_t range_log2, uint16_t* __restrict__ out, int32_t* status) {
+    __shared__ uint4 map4[kDenseTile / 8];   // kDenseTile 16-bit entries
+    __shared__ uint64_t bounds[2];
+    __shared__ uint64_t seg_table[16];
+    __shared__ uint32_t next_rel[2];
+    __shared__ int bad;
+
+    const int t = threadIdx.x;
+    const int wave = t >> 6;
+    uint16_t* map = reinterpret_cast<uint16_t*>(map4);
+    if (t == 0) {
+        bad = 0;
+        next_rel[0] = kNoBreak;
+        next_rel[1] = kNoBreak;
+    }
+    if (blockIdx.x == 0 && t == 0 && !header_ok(src, src_bytes, n, e)) bad = 1;
+
+    const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
+    const uint8_t* nib = src + kPrefixBytes;
+    const uint8_t* sm = nib + (n + 1) / 2;
+    const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
+    EscapeReader rd;
+    rd.pos_lo = src + esc_off;
+    rd.exps = rd.pos_lo + 4 * e;
+    rd.aligned = (esc_off & 3) == 0;
+    rd.one_segment = n <= (1ull << 32);
+    rd.seg_end = seg_table;
+    if (t < 16) seg_table[t] = reinterpret_cast<const uint64_t*>(src + 32)[t];
+    // every map entry starts clear; each thread clears the entries it reads
+#pragma unroll
+    for (int g = 0; g < kGroups; g++) map4[g * kDenseThreads + t] = make_uint4(0, 0, 0, 0);
+    __syncthreads();
+
+    const uint64_t begin = min_u64((uint64_t)blockIdx.x << range_log2, n);
+    const uint64_t end = min_u64(begin + (uint64_t{1} << range_log2), n);
+
+    // escapes of this range: [k_lo, k_hi)
+    if (wave < 2) {
+        const uint64_t b = wave_lower_bound(rd, e, wave == 0 ? begin : end);
+        if ((t & 63) == 0) bounds[wave] = b;
+    }
+    __syncthreads();
+    const uint64_t k_lo = uniform64(bounds[0]);
+    const uint64_t k_hi = uniform64(bounds[1] > k_lo ? bounds[1] : k_lo);
+    if (t == 0 && blockIdx.x == gridDim.x - 1 && bounds[1] != e) bad = 1;  // positions >= n
+
+    uint64_t k_cur = k_lo;   // first record not yet placed
+    int parity = 0;
+    for (uint64_t sub = begin; sub < end; sub += kDenseTile, parity ^= 1) {
+        const uint64_t sub_end = min_u64(sub + kDenseTile, end);
+        // place this sub-range's records; a record at or above sub_end ends
+        // the thread's walk, and the lowest such index is where the next
+        // sub-range starts.  A sub-range lies inside one 2^32-word segment,
+        // whose records are [seg_lo, seg_hi): there a position is its stored
+        // low 32 bits above the segment base.
+        const uint32_t seg = (uint32_t)(sub >> 32);
+        const uint64_t seg_lo = seg == 0 ? 0 : seg_table[seg - 1];
+        const uint64_t seg_hi = seg_table[seg];
+        const uint32_t lo_begin = (uint32_t)sub;
+        const uint64_t lo_end = sub_end - ((uint64_t)seg << 32);  // at most 2^32
+        // kWalk records per thread and step, their loads issued together
+        uint32_t stop = kNoBreak;
+        const uint64_t k_start = k_cur + t;
+        for (uint64_t kb = k_start; kb < k_hi && stop == kNoBreak;
+             kb += (uint64_t)kWalk * kDenseThreads) {
+            uint32_t lo[kWalk], prev[kWalk], ex[kWalk];
+#pragma unroll
+            for (int u = 0; u < kWalk; u++) {
+                const uint64_t k = kb + (uint64_t)u * kDenseThreads;
+                const bool in = k < k_hi;
+                lo[u] = in ? rd.low32(k) : 0u;
+                prev[u] = in && k > 0 ? rd.low32(k - 1) : 0u;
+                ex[u] = in ? rd.exps[k] : 0u;
+            }
+#pragma unroll
+            for (int u = 0; u < kWalk; u++) {
+                const uint64_t k = kb + (uint64_t)u * kDenseThreads;
+                if (stop != kNoBreak || k >= k_hi) break;
+                if (k >= seg_hi || lo[u] >= lo_end) {  // beyond this sub-range
+                    stop = (uint32_t)min_u64(k - k_cur, kNoBreak - 1);
+                    break;
+                }
+                // not below this sub-range, and strictly above the record
+                // before (which, in an earlier segment, is below it anyway)
+                if (k < seg_lo || lo[u] < lo_begin ||
+                    (k > 0 && k - 1 >= seg_lo && !(lo[u] > prev[u]))) {
+                    bad = 1;
+                } else {
+                    map[lo[u] - lo_begin] = (uint16_t)(kMapEscaped | ex[u]);
+                }
+            }
+        }
+        // this thread's codes and sign|mantissa bytes: loaded after the walk,
+        // so that the walk does not hold them in registers; they arrive while
+        // the other waves finish walking
+        const bool whole = sub + kDenseTile <= end;   // the same for every thread
+        const uint64_t wt = sub + (uint64_t)t * 8;  // this thread's first word
+        uint32_t c[kGroups], s[2 * kGroups];
+#pragma unroll
+        for (int g = 0; g < kGroups; g++) {
+            const uint64_t w = wt + (uint64_t)g * kGroupStride;
+            c[g] = s[2 * g] = s[2 * g + 1] = 0;
+            if (whole || w + 8 <= sub_end) load_group<kAlignedSm>(nib, sm, w, c[g], s[2 * g], s[2 * g + 1]);
+        }
+
+        if (stop != kNoBreak) atomicMin(&next_rel[parity], stop);
+        __syncthreads();
+        const uint32_t rel = next_rel[parity];
+        k_cur = rel == kNoBreak ? k_hi : k_cur + rel;
+        if (t == 0) next_rel[parity ^ 1] = kNoBreak;
+
+        // rebuild this thread's words, clearing the map entries as they are read
+#pragma unroll
+        for (int g = 0; g < kGroups; g++) {
+            const uint64_t w = wt + (uint64_t)g * kGroupStride;
+            uint4& slot = map4[g * kDenseThreads + t];
+            if (whole || w + 8 <= sub_end) {
+                const uint4 m = slot;
+                slot = make_uint4(0, 0, 0, 0);
+                uint32_t e0, e1;
+                exponents8(c[g], cb, e0, e1);
+                patch8(m, e0, e1);
+                *reinterpret_cast<uint4*>(out + w) = words8(e0, e1, s[2 * g], s[2 * g + 1]);
+            } else if (w < sub_end) {  // the input's last, partial group
+                for (uint64_t i = w; i < sub_end; i++) {
+                    const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
+                    const uint32_t m = map[(uint32_t)(i - sub)];
+                    map[(uint32_t)(i - sub)] = 0;
+                    const uint32_t ex = (m & kMapEscaped) ? (m & 0xFFu) : codebook_byte(cb, code);
+                    out[i] = (uint16_t)recombine(sm[i], ex);
+                }
+            }
+        }
+        __syncthreads();
+    }
+    // every record of the range must have been placed
+    if (t == 0 && k_cur != k_hi) bad = 1;
+    __syncthreads();
+    if (t == 0 && bad && status)
+        __hip_atomic_fetch_max(status, kStatusCorrupt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
+                               uint16_t* dst, int32_t* status, hipStream_t stream) {
+    uint32_t r = 14;
+    while (r < 40 && ((n + (1ull << r) - 1) >> r) > 2048) r++;
+    uint64_t blocks = (n + (1ull << r) - 1) >> r;
+    if (blocks == 0) blocks = 1;  // the header check still runs
+    if (status) k_status_clear<<<1, 1, 0, stream>>>(status);
+    // the sign|mantissa stream starts at 176 + ceil(n/2): 8-byte aligned
+    // exactly when n is a multiple of 16
+    const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
+    if (aligned)
+        k_decode_dense<true><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
+            src, src_bytes, n, e, r, dst, status);
+    else
+        k_decode_dense<false><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
+            src, src_bytes, n, e, r, dst, status);
     return hipGetLastError();
 }
 

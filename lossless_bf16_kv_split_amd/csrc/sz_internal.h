@@ -66,7 +66,11 @@ __device__ __forceinline__ void store_streaming(uint4* p, uint4 v) {
 // in kFusedDecodeDensity is an escape; below that, a separate in-place
 // rewrite of the few escaped words costs less than the fused pass's
 // bookkeeping (measured crossover on MI355X: about one word in 2000).
+// Above one word in kDenseDecodeDensity the dense form's per-word LDS map
+// beats the fused form's staged record batches (measured: level at 1 in
+// 25, 8% faster at 1 in 12, 36% at 6 in 10; 1.5% slower on sparse KV).
 constexpr uint64_t kFusedDecodeDensity = 2048;
+constexpr uint64_t kDenseDecodeDensity = 32;
 
 inline uint64_t container_bytes(uint64_t n, uint64_t e) {
     return kPrefixBytes + (n + 1) / 2 + n + 5 * e;
@@ -84,6 +88,8 @@ hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uin
 hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* dst,
                           int32_t* status, hipStream_t stream);
 hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
+                               uint16_t* dst, int32_t* status, hipStream_t stream);
+hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                                uint16_t* dst, int32_t* status, hipStream_t stream);
 
 }  // namespace sz

@@ -60,13 +60,15 @@ GUARD = 64
 SENTINEL = 0x5A5A
 
 
-DECODE_FORMS = ("auto", "fused", "staged")
+DECODE_FORMS = ("auto", "fused", "dense", "staged")
 
 
 def gpu_decode(torch, sz, container_dev, n, form="auto"):
     """Decode into a buffer with GUARD sentinel words after element n; returns
     (words tensor of n, device status, guard intact).  form: "auto" is
-    sz_decode, "fused" the single pass, "staged" unpack then escape scatter."""
+    sz_decode, "fused" the single pass with staged record batches, "dense" the
+    single pass with a per-word exponent map, "staged" unpack then escape
+    scatter."""
     out = torch.full((n + GUARD,), SENTINEL, dtype=torch.int16, device="cuda")
     status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     if form == "staged":
@@ -74,6 +76,8 @@ def gpu_decode(torch, sz, container_dev, n, form="auto"):
         sz.sz_decode_scatter(container_dev, container_dev.numel(), out, n, status)
     elif form == "fused":
         sz.sz_decode_fused(container_dev, container_dev.numel(), out, n, status)
+    elif form == "dense":
+        sz.sz_decode_dense(container_dev, container_dev.numel(), out, n, status)
     else:
         sz.sz_decode(container_dev, container_dev.numel(), out, n, status)
     torch.cuda.synchronize()

@@ -117,9 +117,9 @@ def load_traffic(kernel: str, workload: str) -> float | None:
         return None
     with open(path) as f:
         t = json.load(f)
-    if t.get("kernel_source_hash") != kernel_source_hash() or t.get("workload") != workload:
-        return None
-    k = t.get("kernels", {}).get(kernel)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None  # counters taken on other kernels
+    k = t.get("workloads", {}).get(workload, {}).get("kernels", {}).get(kernel)
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 

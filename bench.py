@@ -123,6 +123,62 @@ def load_traffic(kernel: str, workload: str) -> float | None:
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def ship_bench(args, w, n, x, torch, np, sz) -> int:
+    """Transfer of the whole tensor between HBM and pinned host memory:
+    raw copies against the chunked, overlapped codec + copy calls.  PCIe
+    bound; reported apart from the codec's own line, never as its value."""
+    stream = torch.cuda.current_stream()
+    raw_host = torch.empty(2 * n, dtype=torch.uint8, pin_memory=True)
+    back = torch.empty(n, dtype=torch.int16, device="cuda")
+    xb = x.view(torch.uint8)
+
+    def wall(fn, reps):
+        ts = []
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            ts.append(time.perf_counter() - t0)
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    reps = max(args.steps // 4, 3)
+    t_d2h = wall(lambda: raw_host.copy_(xb, non_blocking=True), reps)
+    t_h2d = wall(lambda: back.view(torch.uint8).copy_(raw_host, non_blocking=True), reps)
+    ok = bool(torch.equal(back, x))
+    result = {"metric": "KV transfer between HBM and pinned host memory, GB/s of uncompressed words",
+              "workload": w.name, "n_elements": n, "bytes": 2 * n, "reps": reps,
+              "raw_to_host_GBps": round(2 * n / t_d2h / 1e9, 2),
+              "raw_from_host_GBps": round(2 * n / t_h2d / 1e9, 2), "chunks": {}}
+    for log2 in (22, 24, 26):
+        chunk = 1 << log2
+        if chunk > n and log2 != 22:
+            continue
+        chunks = -(-n // chunk)
+        # room for the raw size: shipping is pointless for data that expands
+        cap = 2 * n + (1 << 20)
+        host = torch.empty(cap, dtype=torch.uint8, pin_memory=True)
+        offs = np.zeros(chunks + 1, dtype=np.uint64)
+        status = torch.zeros(1, dtype=torch.int32, device="cuda")
+        t_to = wall(lambda: sz.sz_ship_to_host(x, n, chunk, host, cap, offs, stream), reps)
+        back.zero_()
+        t_from = wall(lambda: sz.sz_ship_from_host(host, offs, n, chunk, back, status, stream),
+                      reps)
+        good = bool(torch.equal(back, x)) and int(status.item()) == 0
+        ok = ok and good
+        result["chunks"][str(chunk)] = {
+            "to_host_GBps": round(2 * n / t_to / 1e9, 2),
+            "from_host_GBps": round(2 * n / t_from / 1e9, 2),
+            "shipped_bytes": int(offs[-1]), "ratio": round(2 * n / int(offs[-1]), 5),
+            "speedup_to_host": round(t_d2h / t_to, 3),
+            "speedup_from_host": round(t_h2d / t_from, 3), "round_trip_ok": good}
+        del host
+    result["round_trip_ok"] = ok
+    print(json.dumps(result), flush=True)
+    return 0 if ok else 1
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -133,6 +189,9 @@ def main() -> int:
                     help="oracle runs for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one device copy of known size (for PMC scaling)")
+    ap.add_argument("--ship", action="store_true",
+                    help="instead: time the compressed transfer to and from pinned host "
+                         "memory (sz_ship_to_host / sz_ship_from_host) against raw copies")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -151,6 +210,8 @@ def main() -> int:
     words = kvgen.generate(w.name)
     n = words.size
     x = torch.from_numpy(words.view(np.int16)).cuda()
+    if args.ship:
+        return ship_bench(args, w, n, x, torch, np, sz)
     cap = sz.sz_max_compressed_size(n)
     ws_bytes = sz.sz_workspace_size(n)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")

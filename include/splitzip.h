@@ -34,10 +34,12 @@
  *     tensor) owned by the caller; the library keeps none of them after the
  *     stream work completes.  BF16 and container pointers must be 16-byte
  *     aligned; workspaces 256-byte aligned.
- *   - Calls are asynchronous on `stream` and never synchronise the host.
- *     The return value reports errors found on the host before anything is
- *     launched (nothing is launched then), or SZ_ERR_HIP for a failed
- *     launch or allocation.  Results are valid once the stream work is done.
+ *   - Calls are asynchronous on `stream` and never synchronise the host,
+ *     except the two sz_ship_* calls, which return when their data is in
+ *     place.  The return value reports errors found on the host before
+ *     anything is launched (nothing is launched then), or SZ_ERR_HIP for a
+ *     failed launch or allocation.  Results are valid once the stream work
+ *     is done.
  *   - Calls on different streams may run concurrently if they use different
  *     buffers.
  */
@@ -172,6 +174,42 @@ sz_status sz_decode_fused(const void *d_src, uint64_t src_bytes, void *d_dst,
  * word in 32 is an escape. */
 sz_status sz_decode_dense(const void *d_src, uint64_t src_bytes, void *d_dst,
                           uint64_t n_elements, int32_t *d_status, hipStream_t stream);
+
+/* ---- compressed transfer to and from host memory ----------------------
+ * The explainers present the codec as a way to shrink the KV transfer
+ * between prefill and decode servers (introduction and "Les Resultats").
+ * These two calls wrap it around the transfer one GPU has, the PCIe copy
+ * to and from host memory: the n words are cut into chunks of chunk_elems
+ * words (the last one shorter), each chunk becomes an ordinary container
+ * with its own codebook, and the codec runs on `stream` while the previous
+ * chunk's container is copied on a second, library-created stream.  Both
+ * calls allocate two device staging buffers and a few events, block the
+ * host until the transfer is complete, and release everything before
+ * returning.  Host buffers should be pinned (hipHostMalloc, or a PyTorch
+ * tensor with pin_memory=True) for the copies to overlap.
+ *
+ * sz_ship_to_host: encode d_src[0..n) chunk by chunk into h_dst.
+ *   chunk_elems  > 0, a multiple of 8 (keeps every chunk 16-byte aligned)
+ *   h_dst        host buffer of h_capacity bytes; chunk c's container is at
+ *                h_dst + h_offsets[c], h_offsets[c+1] - h_offsets[c] bytes
+ *   h_offsets    host array of ceil(n / chunk_elems) + 1 entries, written
+ * SZ_ERR_CAPACITY when the containers do not fit in h_capacity (found only
+ * once a chunk's size is known: h_offsets is then valid up to the chunks
+ * shipped before it).  SZ_ERR_INVALID_ARGUMENT for a bad chunk size, NULL
+ * or misaligned pointers. */
+sz_status sz_ship_to_host(const void *d_src, uint64_t n_elements, uint64_t chunk_elems,
+                          void *h_dst, uint64_t h_capacity, uint64_t *h_offsets,
+                          hipStream_t stream);
+
+/* sz_ship_from_host: the reverse; h_src and h_offsets as sz_ship_to_host
+ * wrote them, the words land in d_dst[0..n).  Returns SZ_ERR_CORRUPT (and
+ * writes it to the optional device word *d_status, else SZ_OK there) when
+ * an offset is out of order or a chunk's size cannot be a container of its
+ * length (checked on the host before anything is copied), or when a chunk
+ * fails a device-side check. */
+sz_status sz_ship_from_host(const void *h_src, const uint64_t *h_offsets, uint64_t n_elements,
+                            uint64_t chunk_elems, void *d_dst, int32_t *d_status,
+                            hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char *sz_status_string(int status);

@@ -26,7 +26,7 @@ __all__ = [
     "SplitZipError", "lib_path", "sz_max_compressed_size", "sz_workspace_size", "sz_encode",
     "sz_decode", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
-    "sz_status_string", "encode",
+    "sz_ship_to_host", "sz_ship_from_host", "sz_status_string", "encode",
     "decode",
     "PREFIX_BYTES", "MAX_ELEMENTS",
 ]
@@ -71,9 +71,11 @@ def _load() -> ctypes.CDLL:
     L.sz_decode_scatter.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_fused.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_dense.argtypes = [p, u64, p, u64, p, p]
+    L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
+    L.sz_ship_from_host.argtypes = [p, p, u64, u64, p, p, p]
     for name in ("sz_encode", "sz_decode", "sz_encode_histogram", "sz_encode_codebook",
                  "sz_encode_pack", "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
-                 "sz_decode_dense"):
+                 "sz_decode_dense", "sz_ship_to_host", "sz_ship_from_host"):
         getattr(L, name).restype = i32
     L.sz_status_string.argtypes = [i32]
     L.sz_status_string.restype = ctypes.c_char_p
@@ -84,12 +86,16 @@ _lib = _load()
 
 
 def _ptr(x) -> int | None:
-    """Device pointer of a tensor, or an integer pointer as given (None = NULL)."""
+    """Address of a tensor's data (device, or host for the ship calls' host
+    buffers), of a NumPy array's data, or an integer pointer as given
+    (None = NULL)."""
     if x is None:
         return None
     if isinstance(x, int):
         return x
-    return x.data_ptr()
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    return x.ctypes.data
 
 
 def _stream(stream) -> int | None:
@@ -170,6 +176,21 @@ def sz_decode_dense(src, src_bytes: int, dst, n_elements: int, d_status=None,
                     stream=None) -> None:
     _check(_lib.sz_decode_dense(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
                                 _stream(stream)), "sz_decode_dense")
+
+
+def sz_ship_to_host(src, n_elements: int, chunk_elems: int, h_dst, h_capacity: int, h_offsets,
+                    stream=None) -> None:
+    """h_dst: pinned host buffer; h_offsets: host uint64 array of
+    ceil(n / chunk_elems) + 1 entries (a NumPy array or a CPU tensor)."""
+    _check(_lib.sz_ship_to_host(_ptr(src), n_elements, chunk_elems, _ptr(h_dst), h_capacity,
+                                _ptr(h_offsets), _stream(stream)), "sz_ship_to_host")
+
+
+def sz_ship_from_host(h_src, h_offsets, n_elements: int, chunk_elems: int, dst, d_status=None,
+                      stream=None) -> None:
+    _check(_lib.sz_ship_from_host(_ptr(h_src), _ptr(h_offsets), n_elements, chunk_elems,
+                                  _ptr(dst), _ptr(d_status), _stream(stream)),
+           "sz_ship_from_host")
 
 
 # ---- conveniences (torch allocates; the library computes) -----------------

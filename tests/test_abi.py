@@ -125,3 +125,32 @@ def test_staged_host_checks(sz):
     assert status_of(sz.sz_encode_codebook, n, W, ws - 256, D, cap, None, 0) == 1
     assert status_of(sz.sz_encode_pack, A, n, W, ws, D, cap - 1, 0) == 2
     assert status_of(sz.sz_encode_pack, A, n, None, ws, D, cap, 0) == 1
+
+
+def test_ship_host_checks(sz):
+    import numpy as np
+    n = 1000
+    offs = np.zeros(n // 8 + 2, dtype=np.uint64)
+    H = A + (1 << 34)  # stands in for a host buffer: never touched
+    to_host, from_host = sz.sz_ship_to_host, sz.sz_ship_from_host
+    assert status_of(to_host, A, (1 << 36) + 1, 64, H, 1 << 40, offs, 0) == 3
+    for bad_chunk in (0, 7, 12):
+        assert status_of(to_host, A, n, bad_chunk, H, 1 << 40, offs, 0) == 1
+        assert status_of(from_host, H, offs, n, bad_chunk, A, None, 0) == 1
+    assert status_of(to_host, A, n, 64, H, 1 << 40, None, 0) == 1
+    assert status_of(to_host, A, n, 64, None, 1 << 40, offs, 0) == 1
+    assert status_of(to_host, MIS, n, 64, H, 1 << 40, offs, 0) == 1
+    assert status_of(from_host, H, offs, n, 64, MIS, None, 0) == 1
+    # nothing to ship: the one offset is written, nothing else happens
+    offs[:] = 7
+    assert status_of(to_host, A, 0, 64, H, 0, offs, 0) == 0 and offs[0] == 0
+    assert status_of(from_host, H, offs, 0, 64, A, None, 0) == 0
+    # offsets that cannot describe containers are rejected before any copy
+    chunk = 512
+    sizes = [176 + chunk // 2 + chunk, 176 + (n - chunk + 1) // 2 + (n - chunk)]
+    good = np.array([0, sizes[0], sizes[0] + sizes[1]], dtype=np.uint64)
+    for bad in ([0, sizes[0] - 1, sizes[0] + sizes[1]],          # first too small
+                [0, sizes[0] + 3, sizes[0] + 3 + sizes[1]],      # not 176 + ... + 5E
+                [0, sizes[0] + sizes[1], sizes[0]]):             # out of order
+        assert status_of(from_host, H, np.array(bad, dtype=np.uint64), n, chunk, A, None, 0) == 4
+    assert good[-1] == sizes[0] + sizes[1]

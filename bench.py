@@ -123,6 +123,72 @@ def load_traffic(kernel: str, workload: str) -> float | None:
     return None if k is None else k.get("hbm_bytes_per_launch")
 
 
+def pages_bench(args, w, n, x, torch, np, sz) -> int:
+    """Whole sz_encode / sz_decode calls on the flat tensor against
+    sz_encode_pages / sz_decode_pages on the same words spread over pages
+    (slots of one pool handed out in a shuffled order), HIP events on the
+    launch stream, median of the timed calls."""
+    page = args.pages
+    stream = torch.cuda.current_stream()
+    used = -(-n // page)
+    pool = torch.empty(used * page, dtype=torch.int16, device="cuda")
+    order = np.random.default_rng(5).permutation(used)
+    for i, slot in enumerate(order):
+        m = min(page, n - i * page)
+        pool[int(slot) * page:int(slot) * page + m] = x[i * page:i * page + m]
+    table = torch.tensor([pool.data_ptr() + 2 * page * int(s_) for s_ in order],
+                         dtype=torch.int64, device="cuda")
+    out_pool = torch.empty_like(pool)
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty(n, dtype=torch.int16, device="cuda")
+    sz.sz_encode(x, n, dst, cap, size, stream)
+    total = int(size.item())
+    cont = dst[:total]
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return ts[len(ts) // 2]
+
+    cases = {
+        "encode_flat": lambda: sz.sz_encode(x, n, dst, cap, size, stream),
+        "encode_pages": lambda: sz.sz_encode_pages(table, used, page, n, dst, cap, size, status,
+                                                   stream),
+        "decode_flat": lambda: sz.sz_decode(cont, total, out, n, status, stream),
+        "decode_pages": lambda: sz.sz_decode_pages(cont, total, out_table, used, page, n, status,
+                                                   stream),
+    }
+    out_table = torch.tensor([out_pool.data_ptr() + 2 * page * int(s_) for s_ in order],
+                             dtype=torch.int64, device="cuda")
+    res = {k: round(2 * n / (timed(f) * 1e-3) / 1e9, 2) for k, f in cases.items()}
+    # correctness of the last calls: same container, same words
+    sz.sz_encode_pages(table, used, page, n, dst, cap, size, status, stream)
+    ok = int(size.item()) == total and int(status.item()) == 0
+    sz.sz_decode_pages(cont, total, out_table, used, page, n, status, stream)
+    back = torch.cat([out_pool[int(s_) * page:int(s_) * page + min(page, n - i * page)]
+                      for i, s_ in enumerate(order)])
+    ok = ok and int(status.item()) == 0 and bool(torch.equal(back, x))
+    line = {"metric": "encode/decode GB/s (uncompressed), paged against flat, 1 GPU",
+            "workload": w.name, "n_elements": n, "page_elems": page, "pages": used,
+            "steps": args.steps, "GBps": res,
+            "paged_over_flat": {"encode": round(res["encode_pages"] / res["encode_flat"], 4),
+                                "decode": round(res["decode_pages"] / res["decode_flat"], 4)},
+            "round_trip_ok": ok}
+    print(json.dumps(line), flush=True)
+    return 0 if ok else 1
+
+
 def ship_bench(args, w, n, x, torch, np, sz) -> int:
     """Transfer of the whole tensor between HBM and pinned host memory:
     raw copies against the chunked, overlapped codec + copy calls.  PCIe
@@ -189,6 +255,9 @@ def main() -> int:
                     help="oracle runs for the CPU baseline (0 = skip)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run one device copy of known size (for PMC scaling)")
+    ap.add_argument("--pages", type=int, default=0, metavar="PAGE_ELEMS",
+                    help="instead: time sz_encode_pages / sz_decode_pages on the workload "
+                         "spread over pages of this many words, against the flat calls")
     ap.add_argument("--ship", action="store_true",
                     help="instead: time the compressed transfer to and from pinned host "
                          "memory (sz_ship_to_host / sz_ship_from_host) against raw copies")
@@ -212,6 +281,8 @@ def main() -> int:
     x = torch.from_numpy(words.view(np.int16)).cuda()
     if args.ship:
         return ship_bench(args, w, n, x, torch, np, sz)
+    if args.pages:
+        return pages_bench(args, w, n, x, torch, np, sz)
     cap = sz.sz_max_compressed_size(n)
     ws_bytes = sz.sz_workspace_size(n)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")

@@ -175,6 +175,38 @@ sz_status sz_decode_fused(const void *d_src, uint64_t src_bytes, void *d_dst,
 sz_status sz_decode_dense(const void *d_src, uint64_t src_bytes, void *d_dst,
                           uint64_t n_elements, int32_t *d_status, hipStream_t stream);
 
+/* ---- paged tensors -----------------------------------------------------
+ * Serving stacks keep KV caches in fixed-size pages (the explainers'
+ * serving setting, section "Les Resultats").  These calls take such a
+ * tensor as it lies: n words spread over pages of page_elems words, page i
+ * at the device address d_pages[i] (d_pages is a device array of
+ * pointers), so that the tensor is the concatenation of the pages in table
+ * order (the last page may be partly used).  The container is exactly the
+ * one sz_encode gives for that concatenation, so any decode call reads it,
+ * and sz_decode_pages decodes any container into pages.  One launch per
+ * pass for the whole tensor, whatever the number of pages.
+ *   page_elems  a power of two, at least 16384
+ *   n_pages     entries in d_pages; only the first ceil(n / page_elems)
+ *               are read, each must be non-NULL and 16-byte aligned
+ * The table's addresses are checked on the device: a NULL or misaligned
+ * one makes the call touch no page and report SZ_ERR_INVALID_ARGUMENT in
+ * *d_status (the container is then not valid).  Pages must not overlap
+ * each other or the container.  The library allocates a small flag from
+ * its stream-ordered pool (and, for encode, sz_encode's workspace). */
+
+/* sz_encode_pages: sz_encode of the paged tensor; *d_status (optional
+ * device i32) receives SZ_OK or SZ_ERR_INVALID_ARGUMENT. */
+sz_status sz_encode_pages(const void *const *d_pages, uint64_t n_pages, uint64_t page_elems,
+                          uint64_t n_elements, void *d_dst, uint64_t dst_capacity,
+                          uint64_t *d_compressed_size, int32_t *d_status, hipStream_t stream);
+
+/* sz_decode_pages: sz_decode into the paged tensor (same forms, same
+ * checks and status; SZ_ERR_INVALID_ARGUMENT in *d_status for a bad
+ * page table). */
+sz_status sz_decode_pages(const void *d_src, uint64_t src_bytes, void *const *d_pages,
+                          uint64_t n_pages, uint64_t page_elems, uint64_t n_elements,
+                          int32_t *d_status, hipStream_t stream);
+
 /* ---- compressed transfer to and from host memory ----------------------
  * The explainers present the codec as a way to shrink the KV transfer
  * between prefill and decode servers (introduction and "Les Resultats").

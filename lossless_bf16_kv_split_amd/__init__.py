@@ -26,7 +26,8 @@ __all__ = [
     "SplitZipError", "lib_path", "sz_max_compressed_size", "sz_workspace_size", "sz_encode",
     "sz_decode", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
-    "sz_ship_to_host", "sz_ship_from_host", "sz_status_string", "encode",
+    "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host", "sz_ship_from_host",
+    "sz_status_string", "encode",
     "decode",
     "PREFIX_BYTES", "MAX_ELEMENTS",
 ]
@@ -71,11 +72,14 @@ def _load() -> ctypes.CDLL:
     L.sz_decode_scatter.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_fused.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_dense.argtypes = [p, u64, p, u64, p, p]
+    L.sz_encode_pages.argtypes = [p, u64, u64, u64, p, u64, p, p, p]
+    L.sz_decode_pages.argtypes = [p, u64, p, u64, u64, u64, p, p]
     L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
     L.sz_ship_from_host.argtypes = [p, p, u64, u64, p, p, p]
     for name in ("sz_encode", "sz_decode", "sz_encode_histogram", "sz_encode_codebook",
                  "sz_encode_pack", "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
-                 "sz_decode_dense", "sz_ship_to_host", "sz_ship_from_host"):
+                 "sz_decode_dense", "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host",
+                 "sz_ship_from_host"):
         getattr(L, name).restype = i32
     L.sz_status_string.argtypes = [i32]
     L.sz_status_string.restype = ctypes.c_char_p
@@ -176,6 +180,20 @@ def sz_decode_dense(src, src_bytes: int, dst, n_elements: int, d_status=None,
                     stream=None) -> None:
     _check(_lib.sz_decode_dense(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
                                 _stream(stream)), "sz_decode_dense")
+
+
+def sz_encode_pages(d_pages, n_pages: int, page_elems: int, n_elements: int, dst,
+                    dst_capacity: int, d_compressed_size=None, d_status=None, stream=None) -> None:
+    """d_pages: device array of page addresses (e.g. an int64 CUDA tensor)."""
+    _check(_lib.sz_encode_pages(_ptr(d_pages), n_pages, page_elems, n_elements, _ptr(dst),
+                                dst_capacity, _ptr(d_compressed_size), _ptr(d_status),
+                                _stream(stream)), "sz_encode_pages")
+
+
+def sz_decode_pages(src, src_bytes: int, d_pages, n_pages: int, page_elems: int,
+                    n_elements: int, d_status=None, stream=None) -> None:
+    _check(_lib.sz_decode_pages(_ptr(src), src_bytes, _ptr(d_pages), n_pages, page_elems,
+                                n_elements, _ptr(d_status), _stream(stream)), "sz_decode_pages")
 
 
 def sz_ship_to_host(src, n_elements: int, chunk_elems: int, h_dst, h_capacity: int, h_offsets,

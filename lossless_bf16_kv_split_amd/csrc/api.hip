@@ -94,6 +94,70 @@ sz_status check_decode_args(const void* src, uint64_t src_bytes, const void* dst
 
 sz_status hip_status(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; }
 
+sz::FlatWords flat(const void* p) {
+    return sz::FlatWords{const_cast<uint16_t*>(static_cast<const uint16_t*>(p))};
+}
+
+// histogram, codebook and pack with the workspace from the library pool
+template <class Words>
+sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capacity,
+                           uint64_t* d_compressed_size, int dev, hipMemPool_t pool,
+                           hipStream_t stream) {
+    const sz::EncodePlan p = sz::plan_encode(n);
+    void* ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, p.ws_bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    sz_status st = hip_status(sz::launch_histogram(src, p, w, stream));
+    if (st == SZ_OK)
+        st = hip_status(sz::launch_codebook(p, w, static_cast<uint8_t*>(d_dst), d_compressed_size,
+                                            stream));
+    if (st == SZ_OK)
+        st = hip_status(sz::launch_pack(src, p, w, static_cast<uint8_t*>(d_dst), dst_capacity,
+                                        num_cus(dev), stream));
+    if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
+    return st;
+}
+
+// the decode form sz_decode picks for this escape density
+template <class Words>
+sz_status decode_by_density(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
+                            Words dst, int32_t* d_status, hipStream_t stream) {
+    if (e > n / sz::kDenseDecodeDensity) {
+        // many escapes: one pass with a per-word LDS map of exponents
+        return hip_status(sz::launch_decode_dense(src, src_bytes, n, e, dst, d_status, stream));
+    }
+    if (e > n / sz::kFusedDecodeDensity) {
+        // some escapes: patch escaped exponents before each word is stored
+        return hip_status(sz::launch_decode_fused(src, src_bytes, n, e, dst, d_status, stream));
+    }
+    // escape-sparse: stream every word out, then rewrite the few escaped ones
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    sz_status st = hip_status(sz::launch_unpack(src, src_bytes, n, e, dst, d_status, num_cus(dev),
+                                                stream));
+    if (st != SZ_OK) return st;
+    return hip_status(sz::launch_scatter(src, n, e, dst, d_status, stream));
+}
+
+// Host checks of a page description: 2^k-word pages, k >= 14, enough of
+// them for n words, and a table pointer; the addresses themselves are on
+// the device and are checked there.  Returns the number of pages used.
+sz_status check_pages(const void* d_pages, uint64_t n_pages, uint64_t page_elems, uint64_t n,
+                      uint32_t* log2_out, uint64_t* used_out) {
+    if (n > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (page_elems == 0 || (page_elems & (page_elems - 1)) != 0 ||
+        page_elems < (uint64_t{1} << sz::kMinPageLog2) || page_elems > SZ_MAX_ELEMENTS)
+        return SZ_ERR_INVALID_ARGUMENT;
+    uint32_t lg = 0;
+    while ((uint64_t{1} << lg) < page_elems) lg++;
+    const uint64_t used = (n + page_elems - 1) >> lg;
+    if (used > n_pages) return SZ_ERR_INVALID_ARGUMENT;
+    if (used > 0 && (d_pages == nullptr || !aligned(d_pages, 8))) return SZ_ERR_INVALID_ARGUMENT;
+    *log2_out = lg;
+    *used_out = used;
+    return SZ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -114,7 +178,7 @@ sz_status sz_encode_histogram(const void* d_src, uint64_t n, void* d_workspace,
     if (n > 0 && (d_src == nullptr || !aligned(d_src, 16))) return SZ_ERR_INVALID_ARGUMENT;
     const sz::EncodePlan p = sz::plan_encode(n);
     if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
-    return hip_status(sz::launch_histogram(static_cast<const uint16_t*>(d_src), p,
+    return hip_status(sz::launch_histogram(flat(d_src), p,
                                            static_cast<uint8_t*>(d_workspace), stream));
 }
 
@@ -139,7 +203,7 @@ sz_status sz_encode_pack(const void* d_src, uint64_t n, const void* d_workspace,
     if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
     const int dev = current_device();
     if (dev < 0) return SZ_ERR_HIP;
-    return hip_status(sz::launch_pack(static_cast<const uint16_t*>(d_src), p,
+    return hip_status(sz::launch_pack(flat(d_src), p,
                                       static_cast<const uint8_t*>(d_workspace),
                                       static_cast<uint8_t*>(d_dst), dst_capacity, num_cus(dev),
                                       stream));
@@ -152,20 +216,8 @@ sz_status sz_encode(const void* d_src, uint64_t n, void* d_dst, uint64_t dst_cap
     if (dev < 0) return SZ_ERR_HIP;
     hipMemPool_t pool = pool_for(dev);
     if (pool == nullptr) return SZ_ERR_HIP;
-    const sz::EncodePlan p = sz::plan_encode(n);
-    void* ws = nullptr;
-    if (hipMallocFromPoolAsync(&ws, p.ws_bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
-    uint8_t* w = static_cast<uint8_t*>(ws);
-    sz_status st = hip_status(sz::launch_histogram(static_cast<const uint16_t*>(d_src), p, w, stream));
-    if (st == SZ_OK)
-        st = hip_status(sz::launch_codebook(p, w, static_cast<uint8_t*>(d_dst), d_compressed_size,
-                                            stream));
-    if (st == SZ_OK)
-        st = hip_status(sz::launch_pack(static_cast<const uint16_t*>(d_src), p, w,
-                                        static_cast<uint8_t*>(d_dst), dst_capacity, num_cus(dev),
-                                        stream));
-    if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
-    return st;
+    return encode_with_pool(flat(d_src), n, d_dst, dst_capacity, d_compressed_size, dev, pool,
+                            stream);
 }
 
 sz_status sz_decode_unpack(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
@@ -175,39 +227,23 @@ sz_status sz_decode_unpack(const void* d_src, uint64_t src_bytes, void* d_dst, u
     const int dev = current_device();
     if (dev < 0) return SZ_ERR_HIP;
     return hip_status(sz::launch_unpack(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
-                                        static_cast<uint16_t*>(d_dst), d_status, num_cus(dev),
-                                        stream));
+                                        flat(d_dst), d_status, num_cus(dev), stream));
 }
 
 sz_status sz_decode_scatter(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
                             int32_t* d_status, hipStream_t stream) {
     uint64_t e = 0;
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
-    return hip_status(sz::launch_scatter(static_cast<const uint8_t*>(d_src), n, e,
-                                         static_cast<uint16_t*>(d_dst), d_status, stream));
+    return hip_status(sz::launch_scatter(static_cast<const uint8_t*>(d_src), n, e, flat(d_dst),
+                                         d_status, stream));
 }
 
 sz_status sz_decode(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
                     int32_t* d_status, hipStream_t stream) {
     uint64_t e = 0;
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
-    const uint8_t* src = static_cast<const uint8_t*>(d_src);
-    uint16_t* dst = static_cast<uint16_t*>(d_dst);
-    if (e > n / sz::kDenseDecodeDensity) {
-        // many escapes: one pass with a per-word LDS map of exponents
-        return hip_status(sz::launch_decode_dense(src, src_bytes, n, e, dst, d_status, stream));
-    }
-    if (e > n / sz::kFusedDecodeDensity) {
-        // some escapes: patch escaped exponents before each word is stored
-        return hip_status(sz::launch_decode_fused(src, src_bytes, n, e, dst, d_status, stream));
-    }
-    // escape-sparse: stream every word out, then rewrite the few escaped ones
-    const int dev = current_device();
-    if (dev < 0) return SZ_ERR_HIP;
-    sz_status st = hip_status(sz::launch_unpack(src, src_bytes, n, e, dst, d_status, num_cus(dev),
-                                                stream));
-    if (st != SZ_OK) return st;
-    return hip_status(sz::launch_scatter(src, n, e, dst, d_status, stream));
+    return decode_by_density(static_cast<const uint8_t*>(d_src), src_bytes, n, e, flat(d_dst),
+                             d_status, stream);
 }
 
 sz_status sz_decode_fused(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
@@ -215,7 +251,7 @@ sz_status sz_decode_fused(const void* d_src, uint64_t src_bytes, void* d_dst, ui
     uint64_t e = 0;
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
     return hip_status(sz::launch_decode_fused(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
-                                              static_cast<uint16_t*>(d_dst), d_status, stream));
+                                              flat(d_dst), d_status, stream));
 }
 
 sz_status sz_decode_dense(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,
@@ -223,7 +259,60 @@ sz_status sz_decode_dense(const void* d_src, uint64_t src_bytes, void* d_dst, ui
     uint64_t e = 0;
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
     return hip_status(sz::launch_decode_dense(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
-                                              static_cast<uint16_t*>(d_dst), d_status, stream));
+                                              flat(d_dst), d_status, stream));
+}
+
+sz_status sz_encode_pages(const void* const* d_pages, uint64_t n_pages, uint64_t page_elems,
+                          uint64_t n, void* d_dst, uint64_t dst_capacity,
+                          uint64_t* d_compressed_size, int32_t* d_status, hipStream_t stream) {
+    uint32_t lg = 0;
+    uint64_t used = 0;
+    if (sz_status s = check_pages(d_pages, n_pages, page_elems, n, &lg, &used)) return s;
+    if (d_dst == nullptr || !aligned(d_dst, 16)) return SZ_ERR_INVALID_ARGUMENT;
+    if (dst_capacity < sz_max_compressed_size(n)) return SZ_ERR_CAPACITY;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    hipMemPool_t pool = pool_for(dev);
+    if (pool == nullptr) return SZ_ERR_HIP;
+    void* flag = nullptr;
+    if (hipMallocFromPoolAsync(&flag, 256, pool, stream) != hipSuccess) return SZ_ERR_HIP;
+    int32_t* bad = static_cast<int32_t*>(flag);
+    const sz::PagedWords src{reinterpret_cast<uint16_t* const*>(const_cast<void* const*>(d_pages)),
+                             lg, bad};
+    sz_status st = hip_status(sz::launch_check_pages(src.pages, used, bad, d_status, stream));
+    if (st == SZ_OK)
+        st = encode_with_pool(src, n, d_dst, dst_capacity, d_compressed_size, dev, pool, stream);
+    if (hipFreeAsync(flag, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
+    return st;
+}
+
+sz_status sz_decode_pages(const void* d_src, uint64_t src_bytes, void* const* d_pages,
+                          uint64_t n_pages, uint64_t page_elems, uint64_t n, int32_t* d_status,
+                          hipStream_t stream) {
+    uint32_t lg = 0;
+    uint64_t used = 0;
+    if (sz_status s = check_pages(d_pages, n_pages, page_elems, n, &lg, &used)) return s;
+    uint64_t e = 0;
+    // the output pages are checked on the device; here only the container
+    if (d_src == nullptr || !aligned(d_src, 16)) return SZ_ERR_INVALID_ARGUMENT;
+    const uint64_t fixed = sz::container_bytes(n, 0);
+    if (src_bytes < fixed || (src_bytes - fixed) % 5 != 0) return SZ_ERR_CORRUPT;
+    e = (src_bytes - fixed) / 5;
+    if (e > (15 * n) / 16) return SZ_ERR_CORRUPT;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    hipMemPool_t pool = pool_for(dev);
+    if (pool == nullptr) return SZ_ERR_HIP;
+    void* flag = nullptr;
+    if (hipMallocFromPoolAsync(&flag, 256, pool, stream) != hipSuccess) return SZ_ERR_HIP;
+    int32_t* bad = static_cast<int32_t*>(flag);
+    const sz::PagedWords dst{reinterpret_cast<uint16_t* const*>(d_pages), lg, bad};
+    sz_status st = hip_status(sz::launch_check_pages(dst.pages, used, bad, nullptr, stream));
+    if (st == SZ_OK)
+        st = decode_by_density(static_cast<const uint8_t*>(d_src), src_bytes, n, e, dst, d_status,
+                               stream);
+    if (hipFreeAsync(flag, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
+    return st;
 }
 
 const char* sz_status_string(int status) {

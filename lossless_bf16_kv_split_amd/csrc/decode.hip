@@ -17,6 +17,7 @@ namespace sz {
 
 constexpr int kUnpackThreads = 256;
 constexpr int kScatterThreads = 256;
+constexpr int32_t kStatusInvalid = 1;   // SZ_ERR_INVALID_ARGUMENT: a bad page table
 constexpr int32_t kStatusCorrupt = 4;
 
 // v_perm_b32: byte i of the result is byte sel[i] of the 8-byte value
@@ -102,14 +103,15 @@ __device__ bool header_ok(const uint8_t* src, uint64_t src_bytes, uint64_t n, ui
     return true;
 }
 
-template <bool kAlignedSm>
+template <bool kAlignedSm, class Words>
 __global__ __launch_bounds__(kUnpackThreads) void k_unpack(const uint8_t* __restrict__ src,
                                                           uint64_t src_bytes, uint64_t n,
-                                                          uint64_t e,
-                                                          uint16_t* __restrict__ out,
+                                                          uint64_t e, Words out,
                                                           int32_t* status) {
     if (blockIdx.x == 0 && threadIdx.x == 0 && status)
-        *status = header_ok(src, src_bytes, n, e) ? 0 : kStatusCorrupt;
+        *status = out.invalid() ? kStatusInvalid
+                                : (header_ok(src, src_bytes, n, e) ? 0 : kStatusCorrupt);
+    if (out.invalid()) return;
 
     const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
     const uint8_t* nib = src + kPrefixBytes;
@@ -131,20 +133,22 @@ __global__ __launch_bounds__(kUnpackThreads) void k_unpack(const uint8_t* __rest
         }
         // non-temporal: the words are not kept dirty in the caches, so later
         // kernels do not pay for writing them back
-        store_streaming(reinterpret_cast<uint4*>(out + 8 * g), decode8(codes, s0, s1, cb));
+        // a wave's 64 groups are 512 consecutive words: one page
+        store_streaming(reinterpret_cast<uint4*>(out.at_wave(8 * g)), decode8(codes, s0, s1, cb));
     }
 
     // the last n % 8 words
     if (blockIdx.x == gridDim.x - 1) {
         for (uint64_t i = groups * 8 + threadIdx.x; i < n; i += kUnpackThreads) {
             const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
-            out[i] = (uint16_t)recombine(sm[i], codebook_byte(cb, code));
+            *out.at(i) = (uint16_t)recombine(sm[i], codebook_byte(cb, code));
         }
     }
 }
 
+template <class Words>
 hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                         uint16_t* dst, int32_t* status, int num_cus, hipStream_t stream) {
+                         Words dst, int32_t* status, int num_cus, hipStream_t stream) {
     const uint64_t groups = n / 8;
     uint64_t blocks = (groups + kUnpackThreads - 1) / kUnpackThreads;
     // four workgroups per CU: measured fastest for this read 1.5 / write 2
@@ -154,11 +158,11 @@ hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uin
     if (blocks == 0) blocks = 1;  // header check and tail still run
     const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
     if (aligned)
-        k_unpack<true><<<(uint32_t)blocks, kUnpackThreads, 0, stream>>>(src, src_bytes, n, e,
-                                                                       dst, status);
+        k_unpack<true, Words><<<(uint32_t)blocks, kUnpackThreads, 0, stream>>>(
+            src, src_bytes, n, e, dst, status);
     else
-        k_unpack<false><<<(uint32_t)blocks, kUnpackThreads, 0, stream>>>(src, src_bytes, n, e,
-                                                                        dst, status);
+        k_unpack<false, Words><<<(uint32_t)blocks, kUnpackThreads, 0, stream>>>(
+            src, src_bytes, n, e, dst, status);
     return hipGetLastError();
 }
 
@@ -179,12 +183,12 @@ __device__ __forceinline__ uint64_t escape_position(const uint64_t* seg_end, uin
     return (seg << 32) | lo;
 }
 
+template <class Words>
 __global__ __launch_bounds__(kScatterThreads) void k_scatter(const uint8_t* __restrict__ src,
-                                                            uint64_t n, uint64_t e,
-                                                            uint16_t* __restrict__ out,
+                                                            uint64_t n, uint64_t e, Words out,
                                                             int32_t* status) {
     const uint64_t k = (uint64_t)blockIdx.x * kScatterThreads + threadIdx.x;
-    if (k >= e) return;
+    if (k >= e || out.invalid()) return;
     const uint64_t* seg_end = reinterpret_cast<const uint64_t*>(src + 32);
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
     const uint8_t* pos_lo = src + esc_off;
@@ -202,15 +206,17 @@ __global__ __launch_bounds__(kScatterThreads) void k_scatter(const uint8_t* __re
     }
     // the unpack pass already wrote sign and mantissa: replace the exponent
     // field in place (reading the word's own line, not the sm stream's)
-    const uint32_t w = out[p];
-    out[p] = (uint16_t)((w & 0x807Fu) | ((uint32_t)exps[k] << 7));
+    uint16_t* q = out.at(p);
+    const uint32_t w = *q;
+    *q = (uint16_t)((w & 0x807Fu) | ((uint32_t)exps[k] << 7));
 }
 
-hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* dst,
+template <class Words>
+hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, Words dst,
                           int32_t* status, hipStream_t stream) {
     if (e == 0) return hipSuccess;
     const uint64_t blocks = (e + kScatterThreads - 1) / kScatterThreads;
-    k_scatter<<<(uint32_t)blocks, kScatterThreads, 0, stream>>>(src, n, e, dst, status);
+    k_scatter<Words><<<(uint32_t)blocks, kScatterThreads, 0, stream>>>(src, n, e, dst, status);
     return hipGetLastError();
 }
 
@@ -294,14 +300,14 @@ __device__ __forceinline__ uint32_t bits_to_bytes(uint32_t x) {
 
 __global__ void k_status_clear(int32_t* status) { *status = 0; }
 
-template <bool kAlignedSm>
 // Eight waves per SIMD (four workgroups per CU) need at most 64 VGPRs and
 // the scalar-register cap; two prefetched records per thread and no
 // register prefetch of the next tile keep the kernel inside both.
+template <bool kAlignedSm, class Words>
 __global__ __launch_bounds__(kFusedThreads) SZ_EIGHT_WAVE_SGPR_CAP
 __attribute__((amdgpu_waves_per_eu(8))) void k_decode_fused(
     const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e,
-    uint32_t range_log2, uint16_t* __restrict__ out, int32_t* status) {
+    uint32_t range_log2, Words out, int32_t* status) {
     __shared__ uint32_t batch_pos[kBatch];            // offsets from the range start
     __shared__ uint8_t batch_exp[kBatch];
     __shared__ uint8_t patch_exp[2][kFusedTile];      // exponent of each escaped word
@@ -312,6 +318,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_fused(
 
     const int t = threadIdx.x;
     const int wave = t >> 6;
+    if (out.invalid()) {  // the same for every thread
+        if (blockIdx.x == 0 && t == 0 && status)
+            __hip_atomic_fetch_max(status, kStatusInvalid, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     if (t == 0) bad = 0;
     if (blockIdx.x == 0 && t == 0 && !header_ok(src, src_bytes, n, e)) bad = 1;
 
@@ -451,14 +463,15 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_fused(
                 e0 = bitselect(bits_to_bytes(present), pe.x, e0);
                 e1 = bitselect(bits_to_bytes(present >> 4), pe.y, e1);
             }
-            *reinterpret_cast<uint4*>(out + i0) = words8(e0, e1, s0, s1);
+            // a wave's words are 512 consecutive words: one page
+            *reinterpret_cast<uint4*>(out.at_wave(i0)) = words8(e0, e1, s0, s1);
         } else {
             for (uint32_t k = 0; k < 8 && i0 + k < end; k++) {
                 const uint64_t i = i0 + k;
                 const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
                 const uint32_t ex = (present >> k) & 1u ? patch_exp[parity][8 * t + k]
                                                         : codebook_byte(cb, code);
-                out[i] = (uint16_t)recombine(sm[i], ex);
+                *out.at(i) = (uint16_t)recombine(sm[i], ex);
             }
         }
     }
@@ -467,8 +480,9 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_fused(
         __hip_atomic_fetch_max(status, kStatusCorrupt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <class Words>
 hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                               uint16_t* dst, int32_t* status, hipStream_t stream) {
+                               Words dst, int32_t* status, hipStream_t stream) {
     uint32_t r = 13;
     while (r < 40 && ((n + (1ull << r) - 1) >> r) > 2048) r++;
     uint64_t blocks = (n + (1ull << r) - 1) >> r;
@@ -476,11 +490,11 @@ hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t 
     if (status) k_status_clear<<<1, 1, 0, stream>>>(status);
     const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
     if (aligned)
-        k_decode_fused<true><<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(src, src_bytes, n, e,
-                                                                            r, dst, status);
+        k_decode_fused<true, Words><<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(
+            src, src_bytes, n, e, r, dst, status);
     else
-        k_decode_fused<false><<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(src, src_bytes, n,
-                                                                             e, r, dst, status);
+        k_decode_fused<false, Words><<<(uint32_t)blocks, kFusedThreads, 0, stream>>>(
+            src, src_bytes, n, e, r, dst, status);
     return hipGetLastError();
 }
 
@@ -537,11 +551,11 @@ __device__ __forceinline__ void load_group(const uint8_t* nib, const uint8_t* sm
 
 // Eight waves per SIMD (four workgroups per CU) need at most 64 VGPRs and
 // the scalar-register cap.
-template <bool kAlignedSm>
+template <bool kAlignedSm, class Words>
 __global__ __launch_bounds__(kDenseThreads) SZ_EIGHT_WAVE_SGPR_CAP
 __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
     const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e,
-    uint32_t range_log2, uint16_t* __restrict__ out, int32_t* status) {
+    uint32_t range_log2, Words out, int32_t* status) {
     __shared__ uint4 map4[kDenseTile / 8];   // kDenseTile 16-bit entries
     __shared__ uint64_t bounds[2];
     __shared__ uint64_t seg_table[16];
@@ -551,6 +565,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
     const int t = threadIdx.x;
     const int wave = t >> 6;
     uint16_t* map = reinterpret_cast<uint16_t*>(map4);
+    if (out.invalid()) {  // the same for every thread
+        if (blockIdx.x == 0 && t == 0 && status)
+            __hip_atomic_fetch_max(status, kStatusInvalid, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        return;
+    }
     if (t == 0) {
         bad = 0;
         next_rel[0] = kNoBreak;
@@ -663,14 +683,16 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
                 uint32_t e0, e1;
                 exponents8(c[g], cb, e0, e1);
                 patch8(m, e0, e1);
-                *reinterpret_cast<uint4*>(out + w) = words8(e0, e1, s[2 * g], s[2 * g + 1]);
+                // a sub-range lies inside one page
+                *reinterpret_cast<uint4*>(out.at(sub) + (w - sub)) =
+                    words8(e0, e1, s[2 * g], s[2 * g + 1]);
             } else if (w < sub_end) {  // the input's last, partial group
                 for (uint64_t i = w; i < sub_end; i++) {
                     const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
                     const uint32_t m = map[(uint32_t)(i - sub)];
                     map[(uint32_t)(i - sub)] = 0;
                     const uint32_t ex = (m & kMapEscaped) ? (m & 0xFFu) : codebook_byte(cb, code);
-                    out[i] = (uint16_t)recombine(sm[i], ex);
+                    *out.at(i) = (uint16_t)recombine(sm[i], ex);
                 }
             }
         }
@@ -683,8 +705,9 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
         __hip_atomic_fetch_max(status, kStatusCorrupt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+template <class Words>
 hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                               uint16_t* dst, int32_t* status, hipStream_t stream) {
+                               Words dst, int32_t* status, hipStream_t stream) {
     uint32_t r = 14;
     while (r < 40 && ((n + (1ull << r) - 1) >> r) > 2048) r++;
     uint64_t blocks = (n + (1ull << r) - 1) >> r;
@@ -694,12 +717,25 @@ hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t 
     // exactly when n is a multiple of 16
     const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
     if (aligned)
-        k_decode_dense<true><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
+        k_decode_dense<true, Words><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
             src, src_bytes, n, e, r, dst, status);
     else
-        k_decode_dense<false><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
+        k_decode_dense<false, Words><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
             src, src_bytes, n, e, r, dst, status);
     return hipGetLastError();
 }
+
+#define SZ_DECODE_INSTANCES(W)                                                                  \
+    template hipError_t launch_unpack<W>(const uint8_t*, uint64_t, uint64_t, uint64_t, W,       \
+                                         int32_t*, int, hipStream_t);                           \
+    template hipError_t launch_scatter<W>(const uint8_t*, uint64_t, uint64_t, W, int32_t*,      \
+                                          hipStream_t);                                         \
+    template hipError_t launch_decode_fused<W>(const uint8_t*, uint64_t, uint64_t, uint64_t, W, \
+                                               int32_t*, hipStream_t);                          \
+    template hipError_t launch_decode_dense<W>(const uint8_t*, uint64_t, uint64_t, uint64_t, W, \
+                                               int32_t*, hipStream_t);
+SZ_DECODE_INSTANCES(FlatWords)
+SZ_DECODE_INSTANCES(PagedWords)
+#undef SZ_DECODE_INSTANCES
 
 }  // namespace sz

@@ -65,11 +65,12 @@ __device__ __forceinline__ void hist_uint4(uint32_t* h, const uint4& v) {
 
 // counts[bin * chunks + chunk]: bin-major, so that the codebook pass reads
 // every bin's counts, and each chunk's 16 codebook counts, coalesced
-__global__ __launch_bounds__(kHistThreads) void k_histogram(const uint16_t* __restrict__ src,
-                                                            uint64_t n, uint32_t chunk_log2,
-                                                            uint32_t chunks,
+template <class Words>
+__global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t n,
+                                                            uint32_t chunk_log2, uint32_t chunks,
                                                             uint32_t* __restrict__ counts) {
     __shared__ uint32_t h[kHistCopies * kHistPitch];
+    if (src.invalid()) return;  // the same for every thread
     for (int i = threadIdx.x; i < kHistCopies * kHistPitch; i += kHistThreads) h[i] = 0;
     __syncthreads();
 
@@ -77,27 +78,34 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const uint16_t* __re
     const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
     uint32_t* mine = h + (threadIdx.x % kHistCopies) * kHistPitch;
 
-    // 8 words per 16-byte load; four loads in flight per thread.  The loads
-    // are non-temporal: not allocating the input in the caches leaves the
-    // lines already there (often the dirty output of earlier kernels) alone,
-    // which measured 25% faster for this pass and 4% for the whole codec.
-    const uint4* v = reinterpret_cast<const uint4*>(src + begin);
-    const uint32_t groups = (uint32_t)((end - begin) >> 3);
-    uint32_t g = threadIdx.x;
-    for (; g + 3 * kHistThreads < groups; g += 4 * kHistThreads) {
-        const uint4 a = load_streaming(v + g);
-        const uint4 b = load_streaming(v + g + kHistThreads);
-        const uint4 c = load_streaming(v + g + 2 * kHistThreads);
-        const uint4 d = load_streaming(v + g + 3 * kHistThreads);
-        hist_uint4(mine, a);
-        hist_uint4(mine, b);
-        hist_uint4(mine, c);
-        hist_uint4(mine, d);
+    // the chunk in runs contiguous in memory (one run for a flat tensor)
+    for (uint64_t r0 = begin; r0 < end;) {
+        const uint64_t r1 = src.run_end(r0, end);
+        const uint16_t* base = src.at(r0);
+        // 8 words per 16-byte load; four loads in flight per thread.  The
+        // loads are non-temporal: not allocating the input in the caches
+        // leaves the lines already there (often the dirty output of earlier
+        // kernels) alone, which measured 25% faster for this pass and 4% for
+        // the whole codec.
+        const uint4* v = reinterpret_cast<const uint4*>(base);
+        const uint32_t groups = (uint32_t)((r1 - r0) >> 3);
+        uint32_t g = threadIdx.x;
+        for (; g + 3 * kHistThreads < groups; g += 4 * kHistThreads) {
+            const uint4 a = load_streaming(v + g);
+            const uint4 b = load_streaming(v + g + kHistThreads);
+            const uint4 c = load_streaming(v + g + 2 * kHistThreads);
+            const uint4 d = load_streaming(v + g + 3 * kHistThreads);
+            hist_uint4(mine, a);
+            hist_uint4(mine, b);
+            hist_uint4(mine, c);
+            hist_uint4(mine, d);
+        }
+        for (; g < groups; g += kHistThreads) hist_uint4(mine, load_streaming(v + g));
+        // fewer than 8 words left at the very end of the input
+        for (uint64_t i = ((uint64_t)groups << 3) + threadIdx.x; i < r1 - r0; i += kHistThreads)
+            hist_add(mine, (base[i] >> 7) & 0xFFu);
+        r0 = r1;
     }
-    for (; g < groups; g += kHistThreads) hist_uint4(mine, load_streaming(v + g));
-    // fewer than 8 words left at the very end of the input
-    for (uint64_t i = begin + ((uint64_t)groups << 3) + threadIdx.x; i < end; i += kHistThreads)
-        hist_add(mine, (src[i] >> 7) & 0xFFu);
     __syncthreads();
 
     for (int bin = threadIdx.x; bin < 256; bin += kHistThreads) {
@@ -108,11 +116,39 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(const uint16_t* __re
     }
 }
 
-hipError_t launch_histogram(const uint16_t* src, const EncodePlan& p, uint8_t* ws,
-                            hipStream_t stream) {
+template <class Words>
+hipError_t launch_histogram(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream) {
     if (p.chunks == 0) return hipSuccess;
-    k_histogram<<<p.chunks, kHistThreads, 0, stream>>>(
+    k_histogram<Words><<<p.chunks, kHistThreads, 0, stream>>>(
         src, p.n, p.chunk_log2, p.chunks, reinterpret_cast<uint32_t*>(ws + p.counts_off));
+    return hipGetLastError();
+}
+template hipError_t launch_histogram<FlatWords>(FlatWords, const EncodePlan&, uint8_t*,
+                                                hipStream_t);
+template hipError_t launch_histogram<PagedWords>(PagedWords, const EncodePlan&, uint8_t*,
+                                                 hipStream_t);
+
+// One workgroup: every page address must be non-NULL and 16-byte aligned.
+__global__ __launch_bounds__(256) void k_check_pages(const uint16_t* const* pages,
+                                                     uint64_t n_pages, int32_t* bad,
+                                                     int32_t* status) {
+    __shared__ int any;
+    if (threadIdx.x == 0) any = 0;
+    __syncthreads();
+    for (uint64_t i = threadIdx.x; i < n_pages; i += 256) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(pages[i]);
+        if (a == 0 || (a & 15) != 0) any = 1;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        *bad = any;
+        if (status) *status = any ? 1 : 0;  // SZ_ERR_INVALID_ARGUMENT or SZ_OK
+    }
+}
+
+hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, int32_t* bad,
+                              int32_t* status, hipStream_t stream) {
+    k_check_pages<<<1, 256, 0, stream>>>(pages, n_pages, bad, status);
     return hipGetLastError();
 }
 
@@ -480,13 +516,14 @@ __device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0, co
     return write_escapes(r, t0, slot_base, lds, parity, esc);
 }
 
-template <bool kAlignedSm>
+template <bool kAlignedSm, class Words>
 __global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
 __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
-    const uint16_t* __restrict__ src, uint64_t n, uint32_t chunk_log2,
-    const uint64_t* __restrict__ chunk_base, uint8_t* __restrict__ dst, uint64_t dst_capacity) {
+    Words src, uint64_t n, uint32_t chunk_log2, const uint64_t* __restrict__ chunk_base,
+    uint8_t* __restrict__ dst, uint64_t dst_capacity) {
     __shared__ PackLds lds;
     uint8_t* lut = lds.lut;
+    if (src.invalid()) return;  // the same for every thread
 
     const int t = threadIdx.x;
     if (t < 256) lut[t] = 0x10;
@@ -515,7 +552,8 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     uint64_t t0 = begin;
     // whole tiles, no per-word checks
     for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
-        const uint4* p = reinterpret_cast<const uint4*>(src + t0 + (uint64_t)t * kPackWords);
+        // a tile lies inside one page
+        const uint4* p = reinterpret_cast<const uint4*>(src.at(t0) + (uint64_t)t * kPackWords);
         uint32_t w[kPackWords / 2];
 #pragma unroll
         for (int h = 0; h < kPackLoads; h++) {
@@ -531,13 +569,14 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     // is a compile-time constant after unrolling, so nothing leaves registers
     if (t0 < end) {
         const uint64_t i0 = t0 + (uint64_t)t * kPackWords;
+        const uint16_t* mine = src.at(t0) + (uint64_t)t * kPackWords;
         const uint32_t valid =
             i0 + kPackWords <= end ? kPackWords : (i0 < end ? (uint32_t)(end - i0) : 0u);
         uint32_t w[kPackWords / 2];
 #pragma unroll
         for (int j = 0; j < kPackWords / 2; j++) {
-            const uint32_t lo = 2 * j < (int)valid ? src[i0 + 2 * j] : 0u;
-            const uint32_t hi = 2 * j + 1 < (int)valid ? src[i0 + 2 * j + 1] : 0u;
+            const uint32_t lo = 2 * j < (int)valid ? mine[2 * j] : 0u;
+            const uint32_t hi = 2 * j + 1 < (int)valid ? mine[2 * j + 1] : 0u;
             w[j] = lo | (hi << 16);
         }
         ThreadWords r;
@@ -558,21 +597,25 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     }
 }
 
-hipError_t launch_pack(const uint16_t* src, const EncodePlan& p, const uint8_t* ws,
-                       uint8_t* dst, uint64_t dst_capacity, int /*num_cus*/,
-                       hipStream_t stream) {
+template <class Words>
+hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
+                       uint64_t dst_capacity, int /*num_cus*/, hipStream_t stream) {
     if (p.chunks == 0) return hipSuccess;
     const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
     // the sign|mantissa stream starts at 176 + ceil(n/2): 16-byte aligned
     // exactly when n is a multiple of 32
     const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
     if (aligned)
-        k_pack<true><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base, dst,
-                                                            dst_capacity);
+        k_pack<true, Words><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base,
+                                                                   dst, dst_capacity);
     else
-        k_pack<false><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base, dst,
-                                                             dst_capacity);
+        k_pack<false, Words><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base,
+                                                                    dst, dst_capacity);
     return hipGetLastError();
 }
+template hipError_t launch_pack<FlatWords>(FlatWords, const EncodePlan&, const uint8_t*,
+                                           uint8_t*, uint64_t, int, hipStream_t);
+template hipError_t launch_pack<PagedWords>(PagedWords, const EncodePlan&, const uint8_t*,
+                                            uint8_t*, uint64_t, int, hipStream_t);
 
 }  // namespace sz

@@ -76,20 +76,68 @@ inline uint64_t container_bytes(uint64_t n, uint64_t e) {
     return kPrefixBytes + (n + 1) / 2 + n + 5 * e;
 }
 
-// Launchers (asynchronous on `stream`; return the launch status).
-hipError_t launch_histogram(const uint16_t* src, const EncodePlan& p, uint8_t* ws,
-                            hipStream_t stream);
+// Where the uncompressed words live.  Kernels address word i through
+// at(i) and walk a range in runs that are contiguous in memory: FlatWords
+// is one array (one run); PagedWords is 2^page_log2-word pages at the
+// addresses of a device table (runs end at page boundaries).  Pages hold at
+// least 2^14 words, so a pack tile (2^14 words), a decode tile or sub-range
+// and every 8-word group lie inside one page.
+// at_wave(i) is at(i) for callers whose active lanes all address one page
+// (a wave's 64 consecutive 8-word groups, 512-word aligned): the page is
+// then looked up once per wave, through a scalar load.
+struct FlatWords {
+    uint16_t* base;
+    __device__ __forceinline__ bool invalid() const { return false; }
+    __device__ __forceinline__ uint16_t* at(uint64_t i) const { return base + i; }
+    __device__ __forceinline__ uint16_t* at_wave(uint64_t i) const { return base + i; }
+    __device__ __forceinline__ uint64_t run_end(uint64_t, uint64_t end) const { return end; }
+};
+
+constexpr uint32_t kMinPageLog2 = 14;
+
+struct PagedWords {
+    uint16_t* const* pages;   // device table of page addresses
+    uint32_t page_log2;
+    const int32_t* bad;       // nonzero: the table failed its check, touch no page
+    __device__ __forceinline__ bool invalid() const { return *bad != 0; }
+    __device__ __forceinline__ uint16_t* at(uint64_t i) const {
+        return pages[i >> page_log2] + (i & ((uint64_t{1} << page_log2) - 1));
+    }
+    __device__ __forceinline__ uint16_t* at_wave(uint64_t i) const {
+        const uint64_t page = i >> page_log2;
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)page);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(page >> 32));
+        return pages[((uint64_t)hi << 32) | lo] + (i & ((uint64_t{1} << page_log2) - 1));
+    }
+    __device__ __forceinline__ uint64_t run_end(uint64_t i, uint64_t end) const {
+        return min_u64(end, ((i >> page_log2) + 1) << page_log2);
+    }
+};
+
+// Launchers (asynchronous on `stream`; return the launch status).  The
+// templates are instantiated for FlatWords and PagedWords.
+template <class Words>
+hipError_t launch_histogram(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream);
 hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst,
                            uint64_t* d_size, hipStream_t stream);
-hipError_t launch_pack(const uint16_t* src, const EncodePlan& p, const uint8_t* ws,
-                       uint8_t* dst, uint64_t dst_capacity, int num_cus, hipStream_t stream);
+template <class Words>
+hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
+                       uint64_t dst_capacity, int num_cus, hipStream_t stream);
+template <class Words>
 hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                         uint16_t* dst, int32_t* status, int num_cus, hipStream_t stream);
-hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, uint16_t* dst,
+                         Words dst, int32_t* status, int num_cus, hipStream_t stream);
+template <class Words>
+hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, Words dst,
                           int32_t* status, hipStream_t stream);
+template <class Words>
 hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                               uint16_t* dst, int32_t* status, hipStream_t stream);
+                               Words dst, int32_t* status, hipStream_t stream);
+template <class Words>
 hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                               uint16_t* dst, int32_t* status, hipStream_t stream);
+                               Words dst, int32_t* status, hipStream_t stream);
+// Checks a page table (every address non-NULL and 16-byte aligned) into
+// *bad, and mirrors the verdict into *status when given.
+hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, int32_t* bad,
+                              int32_t* status, hipStream_t stream);
 
 }  // namespace sz

@@ -154,3 +154,28 @@ def test_ship_host_checks(sz):
                 [0, sizes[0] + sizes[1], sizes[0]]):             # out of order
         assert status_of(from_host, H, np.array(bad, dtype=np.uint64), n, chunk, A, None, 0) == 4
     assert good[-1] == sizes[0] + sizes[1]
+
+
+def test_pages_host_checks(sz):
+    n = 100000
+    P = 1 << 14
+    used = -(-n // P)
+    T = A + (1 << 35)   # stands in for a device page table: never read on the host
+    cap = sz.sz_max_compressed_size(n)
+    D = A + (1 << 33)
+    enc, dec = sz.sz_encode_pages, sz.sz_decode_pages
+    assert status_of(enc, T, used, P, (1 << 36) + 1, D, 1 << 62, None, None, 0) == 3
+    for bad_page in (0, 1000, 1 << 13, (1 << 14) + 8, 3 << 14):
+        assert status_of(enc, T, used, bad_page, n, D, cap, None, None, 0) == 1
+        assert status_of(dec, D, 1 << 20, T, used, bad_page, n, None, 0) == 1
+    assert status_of(enc, T, used - 1, P, n, D, cap, None, None, 0) == 1      # too few pages
+    assert status_of(enc, None, used, P, n, D, cap, None, None, 0) == 1
+    assert status_of(enc, T + 4, used, P, n, D, cap, None, None, 0) == 1       # misaligned table
+    assert status_of(enc, T, used, P, n, None, cap, None, None, 0) == 1
+    assert status_of(enc, T, used, P, n, D + 8, cap, None, None, 0) == 1
+    assert status_of(enc, T, used, P, n, D, cap - 1, None, None, 0) == 2
+    fixed = 176 + (n + 1) // 2 + n
+    assert status_of(dec, D, fixed - 1, T, used, P, n, None, 0) == 4
+    assert status_of(dec, D, fixed + 3, T, used, P, n, None, 0) == 4
+    assert status_of(dec, None, fixed, T, used, P, n, None, 0) == 1
+    assert status_of(dec, D, fixed, T, used - 1, P, n, None, 0) == 1

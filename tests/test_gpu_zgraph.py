@@ -1,0 +1,85 @@
+"""The staged encode calls and the single-pass decode captured in a HIP graph
+(torch.cuda.CUDAGraph on ROCm) and replayed: every replay must give the
+oracle's container of the input as it is at that replay, and decode it
+bit-exactly.  Between replays the input is permuted in place (eager work on
+the device): a permutation keeps the exponent histogram, hence the
+container size the captured decode call was given, while changing every
+byte of the nibble, sign|mantissa and escape streams."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+from test_gpu_parity import make_words
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[gpu-graph]", *a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def torch():
+    import torch as t
+    assert t.cuda.is_available(), "GPU tests need a ROCm device"
+    t.cuda.set_device(0)
+    return t
+
+
+@pytest.fixture(scope="module")
+def sz(torch):
+    import lossless_bf16_kv_split_amd as m
+    return m
+
+
+@pytest.mark.parametrize("kind,form", [("kv", "fused"), ("wide40", "dense"), ("kv", "auto"),
+                                       ("narrow", "auto")])
+def test_graph_replays(torch, sz, kind, form):
+    n = (1 << 20) + 4096
+    words = make_words(kind, n, 51)
+    x = torch.from_numpy(words.view(np.int16)).cuda()
+    total = oracle.encode(words).size          # the same for every permutation
+    ws_bytes = sz.sz_workspace_size(n)
+    ws = torch.zeros(ws_bytes, dtype=torch.uint8, device="cuda")
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.zeros(cap, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    decode = {"fused": sz.sz_decode_fused, "dense": sz.sz_decode_dense, "auto": sz.sz_decode}[form]
+
+    def codec():
+        sz.sz_encode_histogram(x, n, ws, ws_bytes)
+        sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
+        sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap)
+        decode(dst[:total], total, out, n, status)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        codec()                                   # one eager run on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        codec()
+    rng = np.random.default_rng(52)
+    for replay in range(4):
+        perm = torch.from_numpy(rng.permutation(n)).cuda()
+        x.copy_(x[perm])                          # eager work between replays
+        out.zero_()
+        status.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        now = x.cpu().numpy().view(np.uint16)
+        want = oracle.encode(now)
+        say(kind, form, "replay", replay, "size", int(size.item()))
+        assert want.size == total
+        assert int(size.item()) == total
+        assert np.array_equal(dst[:total].cpu().numpy(), want), (kind, form, replay)
+        assert int(status.item()) == 0, (kind, form, replay)
+        assert torch.equal(out, x), (kind, form, replay)

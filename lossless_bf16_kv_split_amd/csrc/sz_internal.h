@@ -136,7 +136,7 @@ template <class Words>
 hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                                Words dst, int32_t* status, hipStream_t stream);
 // Checks a page table (every address non-NULL and 16-byte aligned) into
-// *bad, and mirrors the verdict into *status when given.
+// *bad, and mirrors the result into *status when given.
 hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, int32_t* bad,
                               int32_t* status, hipStream_t stream);
 

@@ -1,12 +1,13 @@
 """Benchmark of the SplitZip BF16 codec on one MI355X.
 
-One step = the whole hot path over one tensor already resident in HBM:
-exponent histogram -> top-16 codebook -> pack (encode), then decode (unpack
-with the escape overwrite in the same pass).  Every pass is bracketed by HIP
-events on the stream the kernels run on, so each kernel's average duration
-is measured inside the timed region.  The two-pass decode (unpack, then
-escape scatter) is timed as well, after the timed region.  Prints ONE JSON
-line.
+One step = the whole hot path over one tensor already resident in HBM, in
+the passes sz_encode and sz_decode run for it: encode as exponent histogram
+-> top-16 codebook -> pack, or, from 2^27 words on, as sample -> first pass
+(pack with the sampled codebook while counting) -> codebook -> finish; then
+decode in the form sz_decode picks for the escape density.  Every pass is
+bracketed by HIP events on the stream the kernels run on, so each kernel's
+average duration is measured inside the timed region.  The closest other
+decode form is timed as well, after the timed region.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_8b_kv_8k]
 
@@ -37,10 +38,16 @@ HBM_PEAK_GBPS = 8000.0
 KERNEL_SOURCES = ["lossless_bf16_kv_split_amd/csrc/encode.hip",
                   "lossless_bf16_kv_split_amd/csrc/decode.hip",
                   "lossless_bf16_kv_split_amd/csrc/sz_internal.h"]
-ENCODE_PASSES = ["histogram", "codebook", "pack"]
+TWO_READ_PASSES = ["histogram", "codebook", "pack"]
+SINGLE_READ_PASSES = ["sample", "first", "codebook", "finish"]
 KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select",
-                "pack": "k_pack", "fused": "k_decode_fused", "dense": "k_decode_dense",
+                "pack": "k_pack", "sample": "k_sample+k_rank_sample",
+                "first": "k_pack(first pass)", "finish": "k_pack(finish)",
+                "fused": "k_decode_fused", "dense": "k_decode_dense",
                 "unpack": "k_unpack", "scatter": "k_scatter"}
+# the sample of the single-read encode: 512 blocks of 2048 words
+SAMPLE_BLOCKS, SAMPLE_BLOCK_WORDS = 512, 2048
+MIN_CHUNK_LOG2, MAX_CHUNKS = 14, 2048
 # sz_decode runs a single pass when more than one word in FUSED_DECODE_DENSITY
 # is an escape, the dense single pass above one in DENSE_DECODE_DENSITY
 FUSED_DECODE_DENSITY = 2048
@@ -55,14 +62,23 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def algorithmic_bytes(n: int, e: int) -> dict:
+def algorithmic_bytes(n: int, e: int, case: str | None = None) -> dict:
     """Bytes each pass must move (per launch), from the container layout:
-    nibbles ceil(n/2), sign|mantissa n, escapes 5e, header+codebook 176."""
+    nibbles ceil(n/2), sign|mantissa n, escapes 5e, header+codebook 176.
+    The finish pass of the single-read encode moves the escape records from
+    scratch to their slots (copy), also rewrites the nibbles (remap), or
+    packs again (full)."""
     nib, sm, esc, pre = (n + 1) // 2, n, 5 * e, 176
+    finish = {"copy": 2 * esc, "remap": 2 * esc + 2 * nib}.get(case, 2 * n + nib + sm + esc)
     return {
         "histogram": 2 * n,                        # read every word once
         "codebook": 0,                             # O(chunks) metadata only
         "pack": 2 * n + nib + sm + esc + pre,      # read words, write container
+        "sample": 2 * SAMPLE_BLOCKS * SAMPLE_BLOCK_WORDS,
+        # read words, write streams + records; only count when the sample
+        # predicts many escapes
+        "first": 2 * n if case == "full:sample" else 2 * n + nib + sm + esc,
+        "finish": finish,
         "fused": pre + nib + sm + esc + 2 * n,     # read container, write words once
         "dense": pre + nib + sm + esc + 2 * n,     # the same, other layout
         "unpack": pre + nib + sm + 2 * n,          # read codes + sm, write words
@@ -109,6 +125,34 @@ def cpu_baseline(words, repeats: int) -> dict:
         "encode_GBps": round(2 * n / enc / 1e9, 4),
         "decode_GBps": round(2 * n / dec / 1e9, 4),
     }
+
+
+def single_read_case(words, codebook) -> str:
+    """Which branch the finish pass of the single-read encode takes: the
+    provisional codebook is ranked from the sample (count descending,
+    exponent ascending) and compared with the container's."""
+    import numpy as np
+    n = words.size
+    starts = (np.arange(SAMPLE_BLOCKS, dtype=np.int64) * (n // SAMPLE_BLOCKS)
+              ) // SAMPLE_BLOCK_WORDS * SAMPLE_BLOCK_WORDS
+    idx = (starts[:, None] + np.arange(SAMPLE_BLOCK_WORDS)[None, :]).ravel()
+    h = np.bincount((words[idx] >> 7) & 0xFF, minlength=256)
+    prov = sorted(range(256), key=lambda x: (-int(h[x]), x))[:16]
+    total, top = int(h.sum()), int(h[prov].sum())
+    if (total - top) * 32 > total:
+        return "full:sample"
+    if set(prov) != set(codebook):
+        return "full:set"
+    c = MIN_CHUNK_LOG2
+    while -(-n >> c) > MAX_CHUNKS:
+        c += 1
+    esc_lut = np.ones(256, dtype=np.uint8)
+    esc_lut[prov] = 0
+    per_chunk = np.add.reduceat(esc_lut[(words >> 7) & 0xFF].astype(np.uint32),
+                                np.arange(0, n, 1 << c))
+    if int(per_chunk.max()) > (1 << c) // 16:
+        return "full:overflow"
+    return "copy" if prov == list(codebook) else "remap"
 
 
 def load_traffic(kernel: str, workload: str) -> float | None:
@@ -297,6 +341,9 @@ def main() -> int:
     total = int(size.item())
     container = dst[:total]
     e = int.from_bytes(container[16:24].cpu().numpy().tobytes(), "little")
+    single = sz.sz_encode_single_read(n)
+    encode_passes = SINGLE_READ_PASSES if single else TWO_READ_PASSES
+    case = single_read_case(words, container[160:176].cpu().tolist()) if single else None
 
     # the decode passes sz_decode runs for this container (same rule), and
     # the closest other form, timed after the timed region
@@ -306,7 +353,7 @@ def main() -> int:
         decode_passes, other_passes, form = ["fused"], ["unpack", "scatter"], "single pass"
     else:
         decode_passes, other_passes, form = ["unpack", "scatter"], ["fused"], "unpack + escape scatter"
-    passes = ENCODE_PASSES + decode_passes
+    passes = encode_passes + decode_passes
 
     def run_pass(p, dst_words):
         if p == "histogram":
@@ -315,6 +362,12 @@ def main() -> int:
             sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size, stream)
         elif p == "pack":
             sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap, stream)
+        elif p == "sample":
+            sz.sz_encode_sample(x, n, ws, ws_bytes, stream)
+        elif p == "first":
+            sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap, stream)
+        elif p == "finish":
+            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, stream)
         elif p == "fused":
             sz.sz_decode_fused(container, total, dst_words, n, status, stream)
         elif p == "dense":
@@ -363,7 +416,7 @@ def main() -> int:
     out2 = torch.empty_like(out)
     other_ev = new_events(len(other_passes) + 1)
     for k in range(args.steps):
-        step(ENCODE_PASSES, out2)
+        step(encode_passes, out2)
         step(other_passes, out2, other_ev[k])
     torch.cuda.synchronize()
     for i, p in enumerate(other_passes):
@@ -371,7 +424,7 @@ def main() -> int:
     ok = ok and bool(torch.equal(out2, x)) and int(status.item()) == 0
     del out2
 
-    alg = algorithmic_bytes(n, e)
+    alg = algorithmic_bytes(n, e, case)
     kernels = {}
     for p in passes + other_passes:
         ms = avg_ms[p]
@@ -379,10 +432,11 @@ def main() -> int:
         kernels[p] = {"kernel": KERNEL_NAMES[p], "avg_ms": round(ms, 5),
                       "alg_bytes": alg[p], "GBps": round(gbps, 1),
                       "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
-    enc_ms = sum(avg_ms[p] for p in ENCODE_PASSES)
+    enc_ms = sum(avg_ms[p] for p in encode_passes)
     dec_ms = sum(avg_ms[p] for p in decode_passes)
     other_dec_ms = sum(avg_ms[p] for p in other_passes)
-    enc_alg = alg["histogram"] + alg["pack"]
+    # read the words (once, or twice), write the container
+    enc_alg = sum(alg[p] for p in encode_passes) if not single else alg["pack"]
     dec_alg = alg["fused"]  # container in, words out: the same for either form
     ms_per_step = total_ms / args.steps
 
@@ -425,6 +479,8 @@ def main() -> int:
         "decode_GBps": round(2 * n / (dec_ms * 1e-3) / 1e9, 2),
         "encode_frac_hbm": round(enc_alg / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "decode_frac_hbm": round(dec_alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "encode_form": ("single read (sampled codebook), finish case " + case) if single
+                       else "two reads (histogram, then pack)",
         "decode_form": form,
         "other_decode_form_GBps": round(2 * n / (other_dec_ms * 1e-3) / 1e9, 2),
         "ratio": round(2 * n / total, 5),

@@ -86,6 +86,10 @@ uint64_t sz_workspace_size(uint64_t n_elements);
  *                     the first `total bytes` of the container are written
  *   d_compressed_size optional device u64 that receives the container size
  *                     (the same value is stored at container offset 24)
+ * From 2^27 elements on (sz_encode_single_read(n) says 1) the input is read
+ * once when a sample of it predicts the codebook: the bytes of d_dst past the
+ * container, up to sz_max_compressed_size(n), then serve as scratch and are
+ * left unspecified.  The container is the same either way.
  * Allocates its workspace (sz_workspace_size(n)) from a library-owned,
  * stream-ordered device memory pool and returns it on the same stream. */
 sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
@@ -141,6 +145,45 @@ sz_status sz_encode_codebook(uint64_t n_elements, void *d_workspace,
 sz_status sz_encode_pack(const void *d_src, uint64_t n_elements,
                          const void *d_workspace, uint64_t workspace_bytes,
                          void *d_dst, uint64_t dst_capacity, hipStream_t stream);
+
+/* ---- staged form of the single-read encode (n >= 2^20) -----------------
+ * sz_encode_sample; sz_encode_first_pass; sz_encode_codebook;
+ * sz_encode_finish on one stream, one workspace, gives the container of
+ * sz_encode.  Not part of the pages'
+ * method: a way to read the input once.  A fixed sample (512 blocks of 2048
+ * words spread evenly over the input) gives a provisional codebook by the
+ * same ranking rule; the first pass packs every chunk with it while it
+ * takes the exact per-chunk counts; the finish pass keeps what the first
+ * pass wrote when the exact codebook equals the provisional one, rewrites
+ * the 4-bit codes when it holds the same 16 exponents in another order, and
+ * packs again (a second read) otherwise, or when a chunk held more than
+ * 1/16 escapes, or when the sample predicted more than one escape in 32.
+ * These calls return SZ_ERR_INVALID_ARGUMENT for n < 2^20 (besides the
+ * checks of the two-read calls); the first pass and the finish use the bytes
+ * of d_dst past the container, up to sz_max_compressed_size(n), as scratch. */
+
+/* 1 when sz_encode takes the single-read passes for n elements (n >= 2^27),
+ * else 0.  Host-only. */
+int sz_encode_single_read(uint64_t n_elements);
+
+/* The sample's exponent counts, then the provisional codebook and whether
+ * the first pass packs, into the workspace. */
+sz_status sz_encode_sample(const void *d_src, uint64_t n_elements, void *d_workspace,
+                           uint64_t workspace_bytes, hipStream_t stream);
+
+/* The first pass: the exact per-chunk exponent counts to the workspace (as
+ * sz_encode_histogram leaves them) and, when the sample predicts few
+ * escapes, the nibble and sign|mantissa streams plus each chunk's escape
+ * records (to the scratch area). */
+sz_status sz_encode_first_pass(const void *d_src, uint64_t n_elements,
+                               void *d_workspace, uint64_t workspace_bytes,
+                               void *d_dst, uint64_t dst_capacity, hipStream_t stream);
+
+/* After sz_encode_codebook: escape records to their final slots, codes
+ * rewritten, or the input packed again, as described above. */
+sz_status sz_encode_finish(const void *d_src, uint64_t n_elements,
+                           const void *d_workspace, uint64_t workspace_bytes,
+                           void *d_dst, uint64_t dst_capacity, hipStream_t stream);
 
 /* Decode pass 1: header check (sets *d_status to SZ_OK or SZ_ERR_CORRUPT)
  * and every word rebuilt from its code and its sign|mantissa byte. */

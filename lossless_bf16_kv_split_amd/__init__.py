@@ -25,6 +25,7 @@ import os
 __all__ = [
     "SplitZipError", "lib_path", "sz_max_compressed_size", "sz_workspace_size", "sz_encode",
     "sz_decode", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
+    "sz_encode_single_read", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
     "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host", "sz_ship_from_host",
     "sz_status_string", "encode",
@@ -68,6 +69,11 @@ def _load() -> ctypes.CDLL:
     L.sz_encode_histogram.argtypes = [p, u64, p, u64, p]
     L.sz_encode_codebook.argtypes = [u64, p, u64, p, u64, p, p]
     L.sz_encode_pack.argtypes = [p, u64, p, u64, p, u64, p]
+    L.sz_encode_single_read.argtypes = [u64]
+    L.sz_encode_single_read.restype = i32
+    L.sz_encode_sample.argtypes = [p, u64, p, u64, p]
+    L.sz_encode_first_pass.argtypes = [p, u64, p, u64, p, u64, p]
+    L.sz_encode_finish.argtypes = [p, u64, p, u64, p, u64, p]
     L.sz_decode_unpack.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_scatter.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_fused.argtypes = [p, u64, p, u64, p, p]
@@ -77,7 +83,8 @@ def _load() -> ctypes.CDLL:
     L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
     L.sz_ship_from_host.argtypes = [p, p, u64, u64, p, p, p]
     for name in ("sz_encode", "sz_decode", "sz_encode_histogram", "sz_encode_codebook",
-                 "sz_encode_pack", "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
+                 "sz_encode_pack", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
+                 "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
                  "sz_decode_dense", "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host",
                  "sz_ship_from_host"):
         getattr(L, name).restype = i32
@@ -156,6 +163,28 @@ def sz_encode_pack(src, n_elements: int, workspace, workspace_bytes: int, dst,
                    dst_capacity: int, stream=None) -> None:
     _check(_lib.sz_encode_pack(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
                                _ptr(dst), dst_capacity, _stream(stream)), "sz_encode_pack")
+
+
+def sz_encode_single_read(n_elements: int) -> bool:
+    return bool(_lib.sz_encode_single_read(n_elements))
+
+
+def sz_encode_sample(src, n_elements: int, workspace, workspace_bytes: int, stream=None) -> None:
+    _check(_lib.sz_encode_sample(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
+                                 _stream(stream)), "sz_encode_sample")
+
+
+def sz_encode_first_pass(src, n_elements: int, workspace, workspace_bytes: int, dst,
+                         dst_capacity: int, stream=None) -> None:
+    _check(_lib.sz_encode_first_pass(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
+                                     _ptr(dst), dst_capacity, _stream(stream)),
+           "sz_encode_first_pass")
+
+
+def sz_encode_finish(src, n_elements: int, workspace, workspace_bytes: int, dst,
+                     dst_capacity: int, stream=None) -> None:
+    _check(_lib.sz_encode_finish(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
+                                 _ptr(dst), dst_capacity, _stream(stream)), "sz_encode_finish")
 
 
 def sz_decode_unpack(src, src_bytes: int, dst, n_elements: int, d_status=None,

@@ -76,6 +76,13 @@ sz_status check_workspace(const void* ws, uint64_t ws_bytes, const sz::EncodePla
     return SZ_OK;
 }
 
+// The single-read passes need n >= 2^20; their scratch area lies inside
+// sz_max_compressed_size(n), which check_encode_args demands.
+sz_status check_single_read(const sz::EncodePlan& p, uint64_t dst_capacity) {
+    if (!p.single_read || p.scratch_end > dst_capacity) return SZ_ERR_INVALID_ARGUMENT;
+    return SZ_OK;
+}
+
 // Host-side container checks for decode; derives the escape count E from
 // the container size alone (total = 176 + ceil(n/2) + n + 5E).
 sz_status check_decode_args(const void* src, uint64_t src_bytes, const void* dst, uint64_t n,
@@ -107,13 +114,21 @@ sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capa
     void* ws = nullptr;
     if (hipMallocFromPoolAsync(&ws, p.ws_bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
     uint8_t* w = static_cast<uint8_t*>(ws);
-    sz_status st = hip_status(sz::launch_histogram(src, p, w, stream));
-    if (st == SZ_OK)
-        st = hip_status(sz::launch_codebook(p, w, static_cast<uint8_t*>(d_dst), d_compressed_size,
-                                            stream));
-    if (st == SZ_OK)
-        st = hip_status(sz::launch_pack(src, p, w, static_cast<uint8_t*>(d_dst), dst_capacity,
-                                        num_cus(dev), stream));
+    uint8_t* out = static_cast<uint8_t*>(d_dst);
+    sz_status st = SZ_OK;
+    if (p.single_read && n >= sz::kSingleReadAuto && p.scratch_end <= dst_capacity) {
+        // one read of the input when the sampled codebook holds; the finish
+        // pass reads it again only when it does not
+        st = hip_status(sz::launch_sample(src, p, w, stream));
+        if (st == SZ_OK) st = hip_status(sz::launch_first_pass(src, p, w, out, dst_capacity, stream));
+        if (st == SZ_OK) st = hip_status(sz::launch_codebook(p, w, out, d_compressed_size, stream));
+        if (st == SZ_OK) st = hip_status(sz::launch_finish(src, p, w, out, dst_capacity, stream));
+    } else {
+        st = hip_status(sz::launch_histogram(src, p, w, stream));
+        if (st == SZ_OK) st = hip_status(sz::launch_codebook(p, w, out, d_compressed_size, stream));
+        if (st == SZ_OK)
+            st = hip_status(sz::launch_pack(src, p, w, out, dst_capacity, num_cus(dev), stream));
+    }
     if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
     return st;
 }
@@ -207,6 +222,44 @@ sz_status sz_encode_pack(const void* d_src, uint64_t n, const void* d_workspace,
                                       static_cast<const uint8_t*>(d_workspace),
                                       static_cast<uint8_t*>(d_dst), dst_capacity, num_cus(dev),
                                       stream));
+}
+
+int sz_encode_single_read(uint64_t n) {
+    if (n > SZ_MAX_ELEMENTS) return 0;
+    return n >= sz::kSingleReadAuto && sz::plan_encode(n).single_read ? 1 : 0;
+}
+
+sz_status sz_encode_sample(const void* d_src, uint64_t n, void* d_workspace,
+                           uint64_t workspace_bytes, hipStream_t stream) {
+    if (n > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (d_src == nullptr || !aligned(d_src, 16)) return SZ_ERR_INVALID_ARGUMENT;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
+    if (!p.single_read) return SZ_ERR_INVALID_ARGUMENT;
+    return hip_status(sz::launch_sample(flat(d_src), p, static_cast<uint8_t*>(d_workspace),
+                                        stream));
+}
+
+sz_status sz_encode_first_pass(const void* d_src, uint64_t n, void* d_workspace,
+                               uint64_t workspace_bytes, void* d_dst, uint64_t dst_capacity,
+                               hipStream_t stream) {
+    if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
+    if (sz_status s = check_single_read(p, dst_capacity)) return s;
+    return hip_status(sz::launch_first_pass(flat(d_src), p, static_cast<uint8_t*>(d_workspace),
+                                            static_cast<uint8_t*>(d_dst), dst_capacity, stream));
+}
+
+sz_status sz_encode_finish(const void* d_src, uint64_t n, const void* d_workspace,
+                           uint64_t workspace_bytes, void* d_dst, uint64_t dst_capacity,
+                           hipStream_t stream) {
+    if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
+    if (sz_status s = check_single_read(p, dst_capacity)) return s;
+    return hip_status(sz::launch_finish(flat(d_src), p, static_cast<const uint8_t*>(d_workspace),
+                                        static_cast<uint8_t*>(d_dst), dst_capacity, stream));
 }
 
 sz_status sz_encode(const void* d_src, uint64_t n, void* d_dst, uint64_t dst_capacity,

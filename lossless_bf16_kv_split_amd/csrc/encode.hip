@@ -11,6 +11,21 @@
 //              bytes, ballot/popcount escape ranks, escapes written straight
 //              to their final slots in ascending position order
 //
+// and the single-read form of the same encode (large inputs), which reads
+// the input once when a sample predicts the codebook:
+//
+//   sample     512 blocks of 2048 words counted by 64 workgroups; one more
+//              ranks them into a provisional codebook
+//   first      the pack kernel with the provisional code table, counting
+//              the exact exponents of its chunk as it packs; escape records
+//              to per-chunk scratch slots past the container
+//   codebook   as above, from the first pass's counts
+//   finish     the pack kernel again: records moved into place (same
+//              codebook), codes rewritten (same 16 exponents, other order),
+//              or the chunk packed again from the input (anything else)
+//
+// The container is the same either way; the sample only decides how much
+// of the work the first pass can keep.
 // Method: SplitZip explainers (gist.science, arXiv 2605.01708), sections
 // "2. La decouverte secrete" (exponents repeat), "3. La strategie SplitZip"
 // (top-16 list, fixed 4-bit codes two per byte, rare exponents as
@@ -33,7 +48,18 @@ EncodePlan plan_encode(uint64_t n) {
     p.counts_off = 0;
     p.hist_off = align(p.counts_off + (uint64_t)p.chunks * 256 * 4);
     p.base_off = align(p.hist_off + 256 * 8);
-    p.ws_bytes = align(p.base_off + (uint64_t)p.chunks * 8);
+    p.sample_off = align(p.base_off + (uint64_t)p.chunks * 8);
+    p.ws_bytes = align(p.sample_off + sizeof(SampleArea));
+    // scratch for the provisional escape records: past every container
+    // whose chunks each hold at most spec_cap escapes, inside the worst-case
+    // container size the caller must provide
+    p.spec_cap = (uint64_t{1} << c) / 16;
+    const uint64_t e_max = (uint64_t)p.chunks * p.spec_cap;
+    const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
+    p.scratch_pos = (esc_off + 5 * e_max + 15) & ~uint64_t{15};
+    p.scratch_exp = p.scratch_pos + 4 * e_max;
+    p.scratch_end = p.scratch_exp + e_max;
+    p.single_read = n >= kSingleReadMin && p.scratch_end <= container_bytes(n, (15 * n) / 16);
     return p;
 }
 
@@ -63,6 +89,40 @@ __device__ __forceinline__ void hist_uint4(uint32_t* h, const uint4& v) {
     hist_dword(h, v.w);
 }
 
+// Adds the exponents of words [begin, end) into this thread's copy `mine`,
+// kThreads threads striding over each run that is contiguous in memory
+// (one run for a flat tensor).  8 words per 16-byte load; four loads in
+// flight per thread.  The loads are non-temporal: not allocating the input
+// in the caches leaves the lines already there (often the dirty output of
+// earlier kernels) alone, which measured 25% faster for this pass and 4%
+// for the whole codec.
+template <int kThreads, class Words>
+__device__ __forceinline__ void count_exponents(Words src, uint64_t begin, uint64_t end,
+                                                uint32_t* mine) {
+    for (uint64_t r0 = begin; r0 < end;) {
+        const uint64_t r1 = src.run_end(r0, end);
+        const uint16_t* base = src.at(r0);
+        const uint4* v = reinterpret_cast<const uint4*>(base);
+        const uint32_t groups = (uint32_t)((r1 - r0) >> 3);
+        uint32_t g = threadIdx.x;
+        for (; g + 3 * kThreads < groups; g += 4 * kThreads) {
+            const uint4 a = load_streaming(v + g);
+            const uint4 b = load_streaming(v + g + kThreads);
+            const uint4 c = load_streaming(v + g + 2 * kThreads);
+            const uint4 d = load_streaming(v + g + 3 * kThreads);
+            hist_uint4(mine, a);
+            hist_uint4(mine, b);
+            hist_uint4(mine, c);
+            hist_uint4(mine, d);
+        }
+        for (; g < groups; g += kThreads) hist_uint4(mine, load_streaming(v + g));
+        // fewer than 8 words left at the very end of the input
+        for (uint64_t i = ((uint64_t)groups << 3) + threadIdx.x; i < r1 - r0; i += kThreads)
+            hist_add(mine, (base[i] >> 7) & 0xFFu);
+        r0 = r1;
+    }
+}
+
 // counts[bin * chunks + chunk]: bin-major, so that the codebook pass reads
 // every bin's counts, and each chunk's 16 codebook counts, coalesced
 template <class Words>
@@ -76,36 +136,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t 
 
     const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
     const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
-    uint32_t* mine = h + (threadIdx.x % kHistCopies) * kHistPitch;
-
-    // the chunk in runs contiguous in memory (one run for a flat tensor)
-    for (uint64_t r0 = begin; r0 < end;) {
-        const uint64_t r1 = src.run_end(r0, end);
-        const uint16_t* base = src.at(r0);
-        // 8 words per 16-byte load; four loads in flight per thread.  The
-        // loads are non-temporal: not allocating the input in the caches
-        // leaves the lines already there (often the dirty output of earlier
-        // kernels) alone, which measured 25% faster for this pass and 4% for
-        // the whole codec.
-        const uint4* v = reinterpret_cast<const uint4*>(base);
-        const uint32_t groups = (uint32_t)((r1 - r0) >> 3);
-        uint32_t g = threadIdx.x;
-        for (; g + 3 * kHistThreads < groups; g += 4 * kHistThreads) {
-            const uint4 a = load_streaming(v + g);
-            const uint4 b = load_streaming(v + g + kHistThreads);
-            const uint4 c = load_streaming(v + g + 2 * kHistThreads);
-            const uint4 d = load_streaming(v + g + 3 * kHistThreads);
-            hist_uint4(mine, a);
-            hist_uint4(mine, b);
-            hist_uint4(mine, c);
-            hist_uint4(mine, d);
-        }
-        for (; g < groups; g += kHistThreads) hist_uint4(mine, load_streaming(v + g));
-        // fewer than 8 words left at the very end of the input
-        for (uint64_t i = ((uint64_t)groups << 3) + threadIdx.x; i < r1 - r0; i += kHistThreads)
-            hist_add(mine, (base[i] >> 7) & 0xFFu);
-        r0 = r1;
-    }
+    count_exponents<kHistThreads>(src, begin, end, h + (threadIdx.x % kHistCopies) * kHistPitch);
     __syncthreads();
 
     for (int bin = threadIdx.x; bin < 256; bin += kHistThreads) {
@@ -516,40 +547,182 @@ __device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0, co
     return write_escapes(r, t0, slot_base, lds, parity, esc);
 }
 
-template <bool kAlignedSm, class Words>
-__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
-__attribute__((amdgpu_waves_per_eu(8))) void k_pack(
-    Words src, uint64_t n, uint32_t chunk_log2, const uint64_t* __restrict__ chunk_base,
-    uint8_t* __restrict__ dst, uint64_t dst_capacity) {
-    __shared__ PackLds lds;
-    uint8_t* lut = lds.lut;
-    if (src.invalid()) return;  // the same for every thread
+// The pack kernel in three roles.
+//   kClassic: codes from the exact codebook in the header; escape records to
+//             their final slots (chunk_base).
+//   kFirst:   single-read encode, first pass: the exact exponent counts of
+//             the chunk (as the histogram pass gives them) and, when the
+//             sample predicts few escapes, the streams under the provisional
+//             codebook, escape records to the chunk's scratch slots.
+//   kFinish:  single-read encode, last pass: compares the provisional and
+//             exact codebooks; same codes: the chunk's records move from
+//             scratch to their final slots; same 16 exponents in another
+//             order: the chunk's nibbles are remapped too; otherwise (or
+//             when the first pass could not use the provisional codebook)
+//             the chunk is packed again as in kClassic.
+enum class PackRole { kClassic, kFirst, kFinish };
 
+constexpr int kSpecCopies = 16;    // exponent sub-histograms of the first pass
+constexpr int kSpecPitch = 257;
+
+// The first pass's streams stand: moves a chunk's escape records from its
+// scratch slots to their final ones and, when the two codebooks order the
+// same 16 exponents differently, rewrites the chunk's 4-bit codes.
+__device__ __forceinline__ void finish_in_place(
+    uint8_t* __restrict__ dst, uint64_t n, uint64_t begin, uint64_t end, uint32_t chunk,
+    uint32_t chunks, const uint64_t* __restrict__ chunk_base, uint64_t dst_capacity,
+    const SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
+    uint64_t scratch_exp, bool same_order) {
+    __shared__ uint8_t lut[256];    // exact exponent -> code
+    __shared__ uint8_t remap[256];  // provisional code pair -> exact code pair
     const int t = threadIdx.x;
-    if (t < 256) lut[t] = 0x10;
-    __syncthreads();
-    if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
-    __syncthreads();
-
-    const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
-    // never write an escape record outside the caller's buffer, whatever
-    // the workspace and header hold: slots below E, and all 5E escape bytes
-    // inside the buffer
+    uint8_t* nib = dst + kPrefixBytes;
+    const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
+    const uint64_t first = chunk_base[chunk];
+    const uint64_t last = chunk + 1 < chunks ? chunk_base[chunk + 1] : E;
+    const uint64_t cnt = min_u64(last - first, spec_cap);  // equal when the sets agree
+    const uint32_t* spos =
+        reinterpret_cast<const uint32_t*>(dst + scratch_pos) + (uint64_t)chunk * spec_cap;
+    const uint8_t* sexp = dst + scratch_exp + (uint64_t)chunk * spec_cap;
     EscapeOut esc;
     esc.pos = dst + esc_off;
     esc.exp = esc.pos + 4 * E;
     esc.limit = (dst_capacity >= esc_off && E <= (dst_capacity - esc_off) / 5) ? E : 0;
     esc.pos_aligned = (esc_off & 3) == 0;
+    for (uint64_t q = t; q < cnt; q += kPackThreads)
+        put_escape(esc, first + q, spos[q], sexp[q]);
+    if (!same_order) {
+        // codes: provisional code -> exact code, both nibbles of a
+        // byte, through the exact exponent -> code table
+        if (t < 256) lut[t] = 0x10;
+        __syncthreads();
+        if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
+        __syncthreads();
+        if (t < 256)
+            remap[t] = (uint8_t)((lut[area->cb[t & 15]] & 0xF) |
+                                 ((lut[area->cb[t >> 4]] & 0xF) << 4));
+        __syncthreads();
+        const uint64_t b0 = begin / 2, b1 = (end + 1) / 2;  // this chunk's nibble bytes
+        for (uint64_t b = b0 + (uint64_t)t * 16; b < b1; b += (uint64_t)kPackThreads * 16) {
+            if (b + 16 <= b1) {
+                uint4 v = *reinterpret_cast<const uint4*>(nib + b);
+                uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int j = 0; j < 4; j++) {
+                    const uint32_t x = w[j];
+                    w[j] = (uint32_t)remap[x & 0xFF] | ((uint32_t)remap[(x >> 8) & 0xFF] << 8) |
+                           ((uint32_t)remap[(x >> 16) & 0xFF] << 16) |
+                           ((uint32_t)remap[x >> 24] << 24);
+                }
+                *reinterpret_cast<uint4*>(nib + b) = make_uint4(w[0], w[1], w[2], w[3]);
+            } else {
+                for (uint64_t k = b; k < b1; k++) nib[k] = remap[nib[k]];
+            }
+        }
+        __syncthreads();
+        // escaped words keep code 0, and so does the pad nibble of an
+        // odd n: one thread per byte, the one of its first record
+        const uint64_t seg = begin & ~uint64_t{0xFFFFFFFF};
+        for (uint64_t q = t; q < cnt; q += kPackThreads) {
+            const uint64_t p = seg | spos[q];
+            if (q > 0 && (seg | spos[q - 1]) / 2 == p / 2) continue;
+            uint32_t clear = (p & 1) ? 0xF0u : 0x0Fu;
+            if (q + 1 < cnt && (seg | spos[q + 1]) / 2 == p / 2) clear = 0xFFu;
+            nib[p / 2] &= (uint8_t)~clear;
+        }
+        __syncthreads();
+        if (t == 0 && end == n && (n & 1)) nib[n / 2] &= 0x0F;
+    }
+}
+
+template <bool kAlignedSm, class Words, PackRole kRole>
+__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
+__attribute__((amdgpu_waves_per_eu(8))) void k_pack(
+    Words src, uint64_t n, uint32_t chunk_log2, const uint64_t* __restrict__ chunk_base,
+    uint8_t* __restrict__ dst, uint64_t dst_capacity, uint32_t* __restrict__ counts,
+    SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
+    uint64_t scratch_exp) {
+    constexpr bool kFirst = kRole == PackRole::kFirst;
+    __shared__ PackLds lds;
+    __shared__ uint32_t hist[kFirst ? kSpecCopies * kSpecPitch : 1];
+    uint8_t* lut = lds.lut;
+    if (src.invalid()) return;  // the same for every thread
+
+    const int t = threadIdx.x;
+    const uint32_t chunk = blockIdx.x;
+    const uint64_t begin = (uint64_t)chunk << chunk_log2;
+    const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
+    const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
     uint8_t* nib = dst + kPrefixBytes;
     uint8_t* sm = nib + (n + 1) / 2;
 
-    const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
-    const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
-    uint64_t slot_base = chunk_base[blockIdx.x];
+    if (kRole == PackRole::kFinish) {
+        // the decision every workgroup takes alike: same codes, same set, or neither
+        const uint4 prov = *reinterpret_cast<const uint4*>(area->cb);
+        const uint4 exact = *reinterpret_cast<const uint4*>(dst + kHeaderBytes);
+        const bool same_order =
+            prov.x == exact.x && prov.y == exact.y && prov.z == exact.z && prov.w == exact.w;
+        const bool usable = area->spec_on != 0 && area->overflow == 0;
+        // the same set: every exact codebook entry has a provisional code
+        const bool same_set =
+            __syncthreads_and(t >= 16 || area->lut[dst[kHeaderBytes + t]] < 16) != 0;
+        if (usable && same_set) {
+            finish_in_place(dst, n, begin, end, chunk, gridDim.x, chunk_base, dst_capacity, area,
+                            spec_cap, scratch_pos, scratch_exp, same_order);
+            return;
+        }
+    }
+
+    // code table: exponent -> code (0x10 = escape); the first pass takes the
+    // provisional one the sample pass left
+    bool spec_on = false;
+    if (kFirst) {
+        if (t < 256) lut[t] = area->lut[t];
+        spec_on = area->spec_on != 0;
+    } else {
+        if (t < 256) lut[t] = 0x10;
+        __syncthreads();
+        if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
+    }
+    uint32_t* hmine = hist;
+    if (kFirst) {
+        for (int i = t; i < kSpecCopies * kSpecPitch; i += kPackThreads) hist[i] = 0;
+        hmine = hist + (t % kSpecCopies) * kSpecPitch;
+    }
+    __syncthreads();
+    // the first pass writes the streams only when the sample predicts few
+    // escapes; otherwise it only counts (the finish pass then packs)
+    const bool write = !kFirst || spec_on;
+
+    EscapeOut esc;
+    uint64_t slot_base;
+    if (kFirst) {
+        // this chunk's scratch slots
+        esc.pos = dst + scratch_pos + 4 * (uint64_t)chunk * spec_cap;
+        esc.exp = dst + scratch_exp + (uint64_t)chunk * spec_cap;
+        esc.limit = spec_cap;
+        esc.pos_aligned = true;
+        slot_base = 0;
+    } else {
+        // never write an escape record outside the caller's buffer, whatever
+        // the workspace and header hold: slots below E, and all 5E escape
+        // bytes inside the buffer
+        const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
+        esc.pos = dst + esc_off;
+        esc.exp = esc.pos + 4 * E;
+        esc.limit = (dst_capacity >= esc_off && E <= (dst_capacity - esc_off) / 5) ? E : 0;
+        esc.pos_aligned = (esc_off & 3) == 0;
+        slot_base = chunk_base[chunk];
+    }
 
     int parity = 0;
     uint64_t t0 = begin;
+    if (!write) {
+        // counts only, at the speed of the histogram pass
+        count_exponents<kPackThreads>(src, begin, end, hmine);
+        t0 = end;
+    }
     // whole tiles, no per-word checks
     for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
         // a tile lies inside one page
@@ -563,7 +736,15 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
             w[4 * h + 2] = v.z;
             w[4 * h + 3] = v.w;
         }
-        slot_base += pack_tile<kAlignedSm>(w, t0, lut, nib, sm, slot_base, lds, parity, esc);
+        if (kFirst) {
+#pragma unroll
+            for (int j = 0; j < kPackWords / 2; j++) {
+                hist_add(hmine, (w[j] >> 7) & 0xFFu);
+                hist_add(hmine, (w[j] >> 23) & 0xFFu);
+            }
+        }
+        if (write)
+            slot_base += pack_tile<kAlignedSm>(w, t0, lut, nib, sm, slot_base, lds, parity, esc);
     }
     // the ragged last tile of the input (last chunk only); every index below
     // is a compile-time constant after unrolling, so nothing leaves registers
@@ -578,44 +759,196 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
             const uint32_t lo = 2 * j < (int)valid ? mine[2 * j] : 0u;
             const uint32_t hi = 2 * j + 1 < (int)valid ? mine[2 * j + 1] : 0u;
             w[j] = lo | (hi << 16);
+            if (kFirst) {
+                if (2 * j < (int)valid) hist_add(hmine, (lo >> 7) & 0xFFu);
+                if (2 * j + 1 < (int)valid) hist_add(hmine, (hi >> 7) & 0xFFu);
+            }
         }
-        ThreadWords r;
-        encode_words(w, lut, r);
-        // words past the end have no code (the pad nibble of an odd n is 0)
-        // and are no escapes
-        r.mask &= (1u << valid) - 1u;  // valid <= 16
+        if (write) {
+            ThreadWords r;
+            encode_words(w, lut, r);
+            // words past the end have no code (the pad nibble of an odd n is
+            // 0) and are no escapes
+            r.mask &= (1u << valid) - 1u;  // valid <= 16
 #pragma unroll
-        for (int k = 0; k < kPackWords; k++)
-            if (k >= (int)valid) r.nib[k >> 3] &= ~(0xFu << (4 * (k & 7)));
+            for (int k = 0; k < kPackWords; k++)
+                if (k >= (int)valid) r.nib[k >> 3] &= ~(0xFu << (4 * (k & 7)));
 #pragma unroll
-        for (int j = 0; j < kPackWords / 2; j++)
-            if (2 * j < (int)valid) nib[i0 / 2 + j] = (uint8_t)byte_at(r.nib, j);
+            for (int j = 0; j < kPackWords / 2; j++)
+                if (2 * j < (int)valid) nib[i0 / 2 + j] = (uint8_t)byte_at(r.nib, j);
 #pragma unroll
-        for (int k = 0; k < kPackWords; k++)
-            if (k < (int)valid) sm[i0 + k] = (uint8_t)byte_at(r.sm, k);
-        write_escapes(r, t0, slot_base, lds, parity, esc);
+            for (int k = 0; k < kPackWords; k++)
+                if (k < (int)valid) sm[i0 + k] = (uint8_t)byte_at(r.sm, k);
+            slot_base += write_escapes(r, t0, slot_base, lds, parity, esc);
+        }
     }
+    if (kFirst) {
+        __syncthreads();
+        // the chunk's exact counts, laid out as the histogram pass lays them
+        for (int b = t; b < 256; b += kPackThreads) {
+            uint32_t s = 0;
+#pragma unroll
+            for (int c = 0; c < kSpecCopies; c++) s += hist[c * kSpecPitch + b];
+            counts[(uint64_t)b * gridDim.x + chunk] = s;
+        }
+        // more escapes than scratch slots: the finish pass must pack again
+        if (t == 0 && write && slot_base > spec_cap) atomicOr(&area->overflow, 1u);
+    }
+}
+
+template <class Words, PackRole kRole>
+hipError_t launch_pack_role(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
+                            uint64_t dst_capacity, hipStream_t stream) {
+    if (p.chunks == 0) return hipSuccess;
+    const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
+    uint32_t* counts = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(ws) + p.counts_off);
+    SampleArea* area = reinterpret_cast<SampleArea*>(const_cast<uint8_t*>(ws) + p.sample_off);
+    // the sign|mantissa stream starts at 176 + ceil(n/2): 16-byte aligned
+    // exactly when n is a multiple of 32
+    const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
+    if (aligned)
+        k_pack<true, Words, kRole><<<p.chunks, kPackThreads, 0, stream>>>(
+            src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, area, p.spec_cap,
+            p.scratch_pos, p.scratch_exp);
+    else
+        k_pack<false, Words, kRole><<<p.chunks, kPackThreads, 0, stream>>>(
+            src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, area, p.spec_cap,
+            p.scratch_pos, p.scratch_exp);
+    return hipGetLastError();
 }
 
 template <class Words>
 hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
                        uint64_t dst_capacity, int /*num_cus*/, hipStream_t stream) {
-    if (p.chunks == 0) return hipSuccess;
-    const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
-    // the sign|mantissa stream starts at 176 + ceil(n/2): 16-byte aligned
-    // exactly when n is a multiple of 32
-    const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
-    if (aligned)
-        k_pack<true, Words><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base,
-                                                                   dst, dst_capacity);
-    else
-        k_pack<false, Words><<<p.chunks, kPackThreads, 0, stream>>>(src, p.n, p.chunk_log2, base,
-                                                                    dst, dst_capacity);
+    return launch_pack_role<Words, PackRole::kClassic>(src, p, ws, dst, dst_capacity, stream);
+}
+
+template <class Words>
+hipError_t launch_first_pass(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
+                             uint64_t dst_capacity, hipStream_t stream) {
+    return launch_pack_role<Words, PackRole::kFirst>(src, p, ws, dst, dst_capacity, stream);
+}
+
+template <class Words>
+hipError_t launch_finish(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
+                         uint64_t dst_capacity, hipStream_t stream) {
+    return launch_pack_role<Words, PackRole::kFinish>(src, p, ws, dst, dst_capacity, stream);
+}
+
+// ---------------------------------------------------------------- sample
+
+// 512 blocks of 2048 consecutive words, evenly spread over the input (block
+// j starts at the 2048-word boundary at or below j * n / 512): whole blocks,
+// so that a layout with a short period (a KV cache's heads x dims) is
+// sampled evenly.  Eight blocks per 1024-thread workgroup, each workgroup's
+// counts to its own row (no atomics, nothing to clear beforehand).
+constexpr uint32_t kSampleBlocks = 512;
+constexpr uint32_t kSampleBlockWords = 2048;
+constexpr uint32_t kSampleThreads = 1024;
+constexpr uint32_t kSampleLoads =
+    kSampleBlocks * kSampleBlockWords / 8 / kSampleThreads / kSampleGroups;  // per thread
+static_assert(kSampleBlocks % kSampleGroups == 0, "whole blocks per workgroup");
+static_assert(kSingleReadMin / kSampleBlocks >= kSampleBlockWords, "blocks do not overlap");
+
+template <class Words>
+__global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n,
+                                                           SampleArea* __restrict__ area) {
+    constexpr uint32_t kBlocksPerGroup = kSampleBlocks / kSampleGroups;
+    constexpr uint32_t kLoadsPerBlock = kSampleBlockWords / 8;
+    __shared__ uint32_t h[kSpecCopies * kSpecPitch];
+    if (src.invalid()) return;
+    const int t = threadIdx.x;
+    for (int i = t; i < kSpecCopies * kSpecPitch; i += kSampleThreads) h[i] = 0;
+    __syncthreads();
+    uint32_t* mine = h + (t % kSpecCopies) * kSpecPitch;
+    const uint64_t spacing = n / kSampleBlocks;
+#pragma unroll
+    for (uint32_t k = 0; k < kSampleLoads; k++) {
+        const uint32_t g = t + k * kSampleThreads;  // 16-byte group in this workgroup's share
+        const uint64_t block = (uint64_t)blockIdx.x * kBlocksPerGroup + g / kLoadsPerBlock;
+        const uint64_t start = block * spacing / kSampleBlockWords * kSampleBlockWords;
+        const uint64_t word = start + (uint64_t)(g % kLoadsPerBlock) * 8;
+        // a block lies inside one page
+        hist_uint4(mine, *reinterpret_cast<const uint4*>(src.at(word)));
+    }
+    __syncthreads();
+    for (int b = t; b < 256; b += kSampleThreads) {
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < kSpecCopies; c++) s += h[c * kSpecPitch + b];
+        area->partial[blockIdx.x][b] = s;
+    }
+}
+
+// One workgroup: sums the sample's counts, ranks the 256 exponents by the
+// codebook rule (count descending, exponent ascending), leaves the
+// provisional code table, decides whether the first pass packs (at most one
+// escape in 32 sampled words), and clears the first pass's overflow flag.
+__global__ __launch_bounds__(1024) void k_rank_sample(SampleArea* __restrict__ area) {
+    __shared__ uint32_t part[4][256];
+    __shared__ uint64_t key[256];
+    __shared__ uint32_t sums[2];
+    const int t = threadIdx.x;
+    const int bin = t & 255;
+    const int grp = t >> 8;  // four groups of 256 threads
+    {
+        uint32_t s = 0;
+#pragma unroll
+        for (uint32_t i = 0; i < kSampleGroups / 4; i++)
+            s += area->partial[grp * (kSampleGroups / 4) + i][bin];
+        part[grp][bin] = s;
+    }
+    if (t < 2) sums[t] = 0;
+    __syncthreads();
+    if (t < 256) {
+        const uint32_t c = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+        key[t] = ((uint64_t)c << 8) | (255u - (uint32_t)t);  // distinct keys
+    }
+    __syncthreads();
+    {
+        // rank = number of larger keys, each group counting over 64 of them
+        const uint64_t kx = key[bin];
+        uint32_t r = 0;
+#pragma unroll 16
+        for (int y = grp * 64; y < grp * 64 + 64; y++) r += key[y] > kx ? 1u : 0u;
+        part[grp][bin] = r;
+    }
+    __syncthreads();
+    if (t < 256) {
+        const uint32_t r = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+        const uint32_t c = (uint32_t)(key[t] >> 8);
+        area->lut[t] = r < 16 ? (uint8_t)r : (uint8_t)0x10;
+        if (r < 16) {
+            area->cb[r] = (uint8_t)t;
+            atomicAdd(&sums[1], c);
+        }
+        atomicAdd(&sums[0], c);
+    }
+    __syncthreads();
+    if (t == 0) {
+        area->spec_on = sums[0] > 0 && (uint64_t)(sums[0] - sums[1]) * 32 <= sums[0] ? 1u : 0u;
+        area->overflow = 0;
+    }
+}
+
+template <class Words>
+hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream) {
+    SampleArea* area = reinterpret_cast<SampleArea*>(ws + p.sample_off);
+    k_sample<Words><<<kSampleGroups, kSampleThreads, 0, stream>>>(src, p.n, area);
+    k_rank_sample<<<1, 1024, 0, stream>>>(area);
     return hipGetLastError();
 }
-template hipError_t launch_pack<FlatWords>(FlatWords, const EncodePlan&, const uint8_t*,
-                                           uint8_t*, uint64_t, int, hipStream_t);
-template hipError_t launch_pack<PagedWords>(PagedWords, const EncodePlan&, const uint8_t*,
-                                            uint8_t*, uint64_t, int, hipStream_t);
+
+#define SZ_ENCODE_INSTANCES(W)                                                                  \
+    template hipError_t launch_pack<W>(W, const EncodePlan&, const uint8_t*, uint8_t*,          \
+                                       uint64_t, int, hipStream_t);                             \
+    template hipError_t launch_first_pass<W>(W, const EncodePlan&, uint8_t*, uint8_t*,          \
+                                             uint64_t, hipStream_t);                            \
+    template hipError_t launch_finish<W>(W, const EncodePlan&, const uint8_t*, uint8_t*,        \
+                                         uint64_t, hipStream_t);                                \
+    template hipError_t launch_sample<W>(W, const EncodePlan&, uint8_t*, hipStream_t);
+SZ_ENCODE_INSTANCES(FlatWords)
+SZ_ENCODE_INSTANCES(PagedWords)
+#undef SZ_ENCODE_INSTANCES
 
 }  // namespace sz

@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace sz {
@@ -30,8 +31,41 @@ struct EncodePlan {
     uint64_t counts_off = 0;   // u32[256][G]   exponent counts, bin-major
     uint64_t hist_off = 0;     // u64[256]      exponent counts of the whole input
     uint64_t base_off = 0;     // u64[G]        first escape slot of each chunk
+    uint64_t sample_off = 0;   // SampleArea (single-read encode)
     uint64_t ws_bytes = 0;
+    // Single-read encode (large inputs): the first pass packs with a
+    // provisional codebook taken from a sample and puts each chunk's escape
+    // records, at most spec_cap of them, in a scratch area of the
+    // destination beyond the largest container such a pass can lead to.
+    bool single_read = false;
+    uint64_t spec_cap = 0;     // records per chunk: chunk size / 16
+    uint64_t scratch_pos = 0;  // dst offset of u32 positions[G * spec_cap], 16-byte aligned
+    uint64_t scratch_exp = 0;  // dst offset of u8 exponents[G * spec_cap]
+    uint64_t scratch_end = 0;  // first dst byte past the scratch area
 };
+
+// The sample of the single-read encode: kSampleGroups workgroups each count
+// their share, and one more workgroup ranks the sum.
+constexpr uint32_t kSampleGroups = 64;
+struct SampleArea {
+    uint32_t partial[kSampleGroups][256];  // exponent counts of each share of the sample
+    uint32_t overflow;      // set by the first pass: a chunk outgrew its scratch slots
+    uint32_t spec_on;       // the sample predicts few escapes: the first pass packs
+    uint32_t pad[2];
+    uint8_t lut[256];       // provisional exponent -> code, 0x10 = escape
+    uint8_t cb[16];         // provisional codebook, code -> exponent
+};
+static_assert(sizeof(SampleArea) % 16 == 0 && offsetof(SampleArea, lut) % 16 == 0 &&
+                  offsetof(SampleArea, cb) % 16 == 0,
+              "16-byte loads of the tables");
+
+// The single-read passes take inputs from kSingleReadMin words on (below,
+// the sample blocks would overlap); sz_encode uses them from
+// kSingleReadAuto words on.  Below that the two extra launches (sample
+// ranking, finish) cost more than the second read of the input saves: on
+// MI355X the two forms break even between 2^26 and 2^27 words of KV data.
+constexpr uint64_t kSingleReadMin = uint64_t{1} << 20;
+constexpr uint64_t kSingleReadAuto = uint64_t{1} << 27;
 
 EncodePlan plan_encode(uint64_t n);
 
@@ -123,6 +157,18 @@ hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst,
 template <class Words>
 hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
                        uint64_t dst_capacity, int num_cus, hipStream_t stream);
+// single-read encode: sample (clears and fills the sampled counts), the
+// first pass (exact per-chunk counts, and the streams under the provisional
+// codebook), then, after launch_codebook, the finish pass (moves the
+// escape records into place, remaps the codes, or packs again)
+template <class Words>
+hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream);
+template <class Words>
+hipError_t launch_first_pass(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
+                             uint64_t dst_capacity, hipStream_t stream);
+template <class Words>
+hipError_t launch_finish(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
+                         uint64_t dst_capacity, hipStream_t stream);
 template <class Words>
 hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                          Words dst, int32_t* status, int num_cus, hipStream_t stream);

@@ -127,6 +127,29 @@ def test_staged_host_checks(sz):
     assert status_of(sz.sz_encode_pack, A, n, None, ws, D, cap, 0) == 1
 
 
+def test_single_read_host_checks(sz):
+    assert not sz.sz_encode_single_read((1 << 27) - 1)
+    assert sz.sz_encode_single_read(1 << 27)
+    assert sz.sz_encode_single_read(1 << 36)
+    assert not sz.sz_encode_single_read((1 << 36) + 1)
+    W, D = A + (1 << 32), A + (1 << 36)
+    for fn in (sz.sz_encode_first_pass, sz.sz_encode_finish):
+        small = (1 << 20) - 8                                             # below the sample size
+        assert status_of(fn, A, small, W, sz.sz_workspace_size(small), D,
+                         sz.sz_max_compressed_size(small), 0) == 1
+        n = 1 << 20
+        ws, cap = sz.sz_workspace_size(n), sz.sz_max_compressed_size(n)
+        assert status_of(fn, A, n, W, ws - 1, D, cap, 0) == 1             # small workspace
+        assert status_of(fn, A, n, W, ws, D, cap - 1, 0) == 2             # small destination
+        assert status_of(fn, A, n, W, ws, D + 8, cap, 0) == 1             # misaligned
+        assert status_of(fn, A, (1 << 36) + 1, W, ws, D, cap, 0) == 3
+    small = (1 << 20) - 8
+    assert status_of(sz.sz_encode_sample, A, small, W, sz.sz_workspace_size(small), 0) == 1
+    n = 1 << 20
+    assert status_of(sz.sz_encode_sample, A, n, W, sz.sz_workspace_size(n) - 1, 0) == 1
+    assert status_of(sz.sz_encode_sample, MIS, n, W, sz.sz_workspace_size(n), 0) == 1
+
+
 def test_ship_host_checks(sz):
     import numpy as np
     n = 1000

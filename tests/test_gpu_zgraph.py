@@ -1,4 +1,4 @@
-"""The staged encode calls and the single-pass decode captured in a HIP graph
+"""The staged encode calls (both forms) and the single-pass decode captured in a HIP graph
 (torch.cuda.CUDAGraph on ROCm) and replayed: every replay must give the
 oracle's container of the input as it is at that replay, and decode it
 bit-exactly.  Between replays the input is permuted in place (eager work on
@@ -35,9 +35,10 @@ def sz(torch):
     return m
 
 
-@pytest.mark.parametrize("kind,form", [("kv", "fused"), ("wide40", "dense"), ("kv", "auto"),
-                                       ("narrow", "auto")])
-def test_graph_replays(torch, sz, kind, form):
+@pytest.mark.parametrize("kind,form,single", [("kv", "fused", False), ("wide40", "dense", False),
+                                              ("kv", "auto", False), ("narrow", "auto", False),
+                                              ("kv", "auto", True), ("wide40", "auto", True)])
+def test_graph_replays(torch, sz, kind, form, single):
     n = (1 << 20) + 4096
     words = make_words(kind, n, 51)
     x = torch.from_numpy(words.view(np.int16)).cuda()
@@ -52,9 +53,15 @@ def test_graph_replays(torch, sz, kind, form):
     decode = {"fused": sz.sz_decode_fused, "dense": sz.sz_decode_dense, "auto": sz.sz_decode}[form]
 
     def codec():
-        sz.sz_encode_histogram(x, n, ws, ws_bytes)
-        sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
-        sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap)
+        if single:                                # the single-read passes
+            sz.sz_encode_sample(x, n, ws, ws_bytes)
+            sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap)
+            sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
+            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap)
+        else:
+            sz.sz_encode_histogram(x, n, ws, ws_bytes)
+            sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
+            sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap)
         decode(dst[:total], total, out, n, status)
 
     side = torch.cuda.Stream()
@@ -77,7 +84,8 @@ def test_graph_replays(torch, sz, kind, form):
         torch.cuda.synchronize()
         now = x.cpu().numpy().view(np.uint16)
         want = oracle.encode(now)
-        say(kind, form, "replay", replay, "size", int(size.item()))
+        say(kind, form, "single" if single else "two-read", "replay", replay, "size",
+            int(size.item()))
         assert want.size == total
         assert int(size.item()) == total
         assert np.array_equal(dst[:total].cpu().numpy(), want), (kind, form, replay)

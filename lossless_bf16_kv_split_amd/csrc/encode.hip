@@ -547,178 +547,59 @@ __device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0, co
     return write_escapes(r, t0, slot_base, lds, parity, esc);
 }
 
-// The pack kernel in three roles.
-//   kClassic: codes from the exact codebook in the header; escape records to
+// The pack kernel serves two passes:
+//   kClassic  codes from the exact codebook in the header; escape records to
 //             their final slots (chunk_base).
-//   kFirst:   single-read encode, first pass: the exact exponent counts of
-//             the chunk (as the histogram pass gives them) and, when the
+//   kFirst    first pass of the single-read encode: the exact exponent counts
+//             of the chunk (as the histogram pass gives them) and, when the
 //             sample predicts few escapes, the streams under the provisional
 //             codebook, escape records to the chunk's scratch slots.
-//   kFinish:  single-read encode, last pass: compares the provisional and
-//             exact codebooks; same codes: the chunk's records move from
-//             scratch to their final slots; same 16 exponents in another
-//             order: the chunk's nibbles are remapped too; otherwise (or
-//             when the first pass could not use the provisional codebook)
-//             the chunk is packed again as in kClassic.
-enum class PackRole { kClassic, kFirst, kFinish };
+// k_finish (below) completes the single-read encode.
+enum class PackRole { kClassic, kFirst };
 
 constexpr int kSpecCopies = 16;    // exponent sub-histograms of the first pass
 constexpr int kSpecPitch = 257;
 
-// The first pass's streams stand: moves a chunk's escape records from its
-// scratch slots to their final ones and, when the two codebooks order the
-// same 16 exponents differently, rewrites the chunk's 4-bit codes.
-__device__ __forceinline__ void finish_in_place(
-    uint8_t* __restrict__ dst, uint64_t n, uint64_t begin, uint64_t end, uint32_t chunk,
-    uint32_t chunks, const uint64_t* __restrict__ chunk_base, uint64_t dst_capacity,
-    const SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
-    uint64_t scratch_exp, bool same_order) {
-    __shared__ uint8_t lut[256];    // exact exponent -> code
-    __shared__ uint8_t remap[256];  // provisional code pair -> exact code pair
-    const int t = threadIdx.x;
+// The container's escape stream.  Never writes a record outside the caller's
+// buffer, whatever the workspace and header hold: slots below E, and all 5E
+// escape bytes inside the buffer.
+__device__ __forceinline__ EscapeOut final_slots(uint8_t* dst, uint64_t n, uint64_t dst_capacity) {
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
-    uint8_t* nib = dst + kPrefixBytes;
     const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
-    const uint64_t first = chunk_base[chunk];
-    const uint64_t last = chunk + 1 < chunks ? chunk_base[chunk + 1] : E;
-    const uint64_t cnt = min_u64(last - first, spec_cap);  // equal when the sets agree
-    const uint32_t* spos =
-        reinterpret_cast<const uint32_t*>(dst + scratch_pos) + (uint64_t)chunk * spec_cap;
-    const uint8_t* sexp = dst + scratch_exp + (uint64_t)chunk * spec_cap;
     EscapeOut esc;
     esc.pos = dst + esc_off;
     esc.exp = esc.pos + 4 * E;
     esc.limit = (dst_capacity >= esc_off && E <= (dst_capacity - esc_off) / 5) ? E : 0;
     esc.pos_aligned = (esc_off & 3) == 0;
-    for (uint64_t q = t; q < cnt; q += kPackThreads)
-        put_escape(esc, first + q, spos[q], sexp[q]);
-    if (!same_order) {
-        // codes: provisional code -> exact code, both nibbles of a
-        // byte, through the exact exponent -> code table
-        if (t < 256) lut[t] = 0x10;
-        __syncthreads();
-        if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
-        __syncthreads();
-        if (t < 256)
-            remap[t] = (uint8_t)((lut[area->cb[t & 15]] & 0xF) |
-                                 ((lut[area->cb[t >> 4]] & 0xF) << 4));
-        __syncthreads();
-        const uint64_t b0 = begin / 2, b1 = (end + 1) / 2;  // this chunk's nibble bytes
-        for (uint64_t b = b0 + (uint64_t)t * 16; b < b1; b += (uint64_t)kPackThreads * 16) {
-            if (b + 16 <= b1) {
-                uint4 v = *reinterpret_cast<const uint4*>(nib + b);
-                uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-                for (int j = 0; j < 4; j++) {
-                    const uint32_t x = w[j];
-                    w[j] = (uint32_t)remap[x & 0xFF] | ((uint32_t)remap[(x >> 8) & 0xFF] << 8) |
-                           ((uint32_t)remap[(x >> 16) & 0xFF] << 16) |
-                           ((uint32_t)remap[x >> 24] << 24);
-                }
-                *reinterpret_cast<uint4*>(nib + b) = make_uint4(w[0], w[1], w[2], w[3]);
-            } else {
-                for (uint64_t k = b; k < b1; k++) nib[k] = remap[nib[k]];
-            }
-        }
-        __syncthreads();
-        // escaped words keep code 0, and so does the pad nibble of an
-        // odd n: one thread per byte, the one of its first record
-        const uint64_t seg = begin & ~uint64_t{0xFFFFFFFF};
-        for (uint64_t q = t; q < cnt; q += kPackThreads) {
-            const uint64_t p = seg | spos[q];
-            if (q > 0 && (seg | spos[q - 1]) / 2 == p / 2) continue;
-            uint32_t clear = (p & 1) ? 0xF0u : 0x0Fu;
-            if (q + 1 < cnt && (seg | spos[q + 1]) / 2 == p / 2) clear = 0xFFu;
-            nib[p / 2] &= (uint8_t)~clear;
-        }
-        __syncthreads();
-        if (t == 0 && end == n && (n & 1)) nib[n / 2] &= 0x0F;
-    }
+    return esc;
 }
 
-template <bool kAlignedSm, class Words, PackRole kRole>
-__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
-__attribute__((amdgpu_waves_per_eu(8))) void k_pack(
-    Words src, uint64_t n, uint32_t chunk_log2, const uint64_t* __restrict__ chunk_base,
-    uint8_t* __restrict__ dst, uint64_t dst_capacity, uint32_t* __restrict__ counts,
-    SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
-    uint64_t scratch_exp) {
-    constexpr bool kFirst = kRole == PackRole::kFirst;
-    __shared__ PackLds lds;
-    __shared__ uint32_t hist[kFirst ? kSpecCopies * kSpecPitch : 1];
-    uint8_t* lut = lds.lut;
-    if (src.invalid()) return;  // the same for every thread
-
+// Exact exponent -> code table (0x10 = escape) from the header's codebook;
+// the caller synchronises before using it.
+__device__ __forceinline__ void exact_code_table(const uint8_t* dst, uint8_t* lut) {
     const int t = threadIdx.x;
-    const uint32_t chunk = blockIdx.x;
-    const uint64_t begin = (uint64_t)chunk << chunk_log2;
-    const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
-    const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
+    if (t < 256) lut[t] = 0x10;
+    __syncthreads();
+    if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
+}
+
+// Packs words [begin, end) with the code table in lds.lut, escape records to
+// esc from slot slot_base on; with kCount, every exponent is also counted
+// into hmine, and with write false only that.  parity selects the next
+// tile's wave-total buffer and carries over from chunk to chunk when one
+// workgroup packs several.  Returns the number of escapes.
+template <bool kAlignedSm, bool kCount, class Words>
+__device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t begin,
+                                               uint64_t end, uint8_t* dst, const EscapeOut& esc,
+                                               uint64_t slot_base, bool write, uint32_t* hmine,
+                                               PackLds& lds, int& parity) {
+    const int t = threadIdx.x;
+    const uint8_t* lut = lds.lut;
     uint8_t* nib = dst + kPrefixBytes;
     uint8_t* sm = nib + (n + 1) / 2;
-
-    if (kRole == PackRole::kFinish) {
-        // the decision every workgroup takes alike: same codes, same set, or neither
-        const uint4 prov = *reinterpret_cast<const uint4*>(area->cb);
-        const uint4 exact = *reinterpret_cast<const uint4*>(dst + kHeaderBytes);
-        const bool same_order =
-            prov.x == exact.x && prov.y == exact.y && prov.z == exact.z && prov.w == exact.w;
-        const bool usable = area->spec_on != 0 && area->overflow == 0;
-        // the same set: every exact codebook entry has a provisional code
-        const bool same_set =
-            __syncthreads_and(t >= 16 || area->lut[dst[kHeaderBytes + t]] < 16) != 0;
-        if (usable && same_set) {
-            finish_in_place(dst, n, begin, end, chunk, gridDim.x, chunk_base, dst_capacity, area,
-                            spec_cap, scratch_pos, scratch_exp, same_order);
-            return;
-        }
-    }
-
-    // code table: exponent -> code (0x10 = escape); the first pass takes the
-    // provisional one the sample pass left
-    bool spec_on = false;
-    if (kFirst) {
-        if (t < 256) lut[t] = area->lut[t];
-        spec_on = area->spec_on != 0;
-    } else {
-        if (t < 256) lut[t] = 0x10;
-        __syncthreads();
-        if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
-    }
-    uint32_t* hmine = hist;
-    if (kFirst) {
-        for (int i = t; i < kSpecCopies * kSpecPitch; i += kPackThreads) hist[i] = 0;
-        hmine = hist + (t % kSpecCopies) * kSpecPitch;
-    }
-    __syncthreads();
-    // the first pass writes the streams only when the sample predicts few
-    // escapes; otherwise it only counts (the finish pass then packs)
-    const bool write = !kFirst || spec_on;
-
-    EscapeOut esc;
-    uint64_t slot_base;
-    if (kFirst) {
-        // this chunk's scratch slots
-        esc.pos = dst + scratch_pos + 4 * (uint64_t)chunk * spec_cap;
-        esc.exp = dst + scratch_exp + (uint64_t)chunk * spec_cap;
-        esc.limit = spec_cap;
-        esc.pos_aligned = true;
-        slot_base = 0;
-    } else {
-        // never write an escape record outside the caller's buffer, whatever
-        // the workspace and header hold: slots below E, and all 5E escape
-        // bytes inside the buffer
-        const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
-        esc.pos = dst + esc_off;
-        esc.exp = esc.pos + 4 * E;
-        esc.limit = (dst_capacity >= esc_off && E <= (dst_capacity - esc_off) / 5) ? E : 0;
-        esc.pos_aligned = (esc_off & 3) == 0;
-        slot_base = chunk_base[chunk];
-    }
-
-    int parity = 0;
+    const uint64_t first_slot = slot_base;
     uint64_t t0 = begin;
-    if (!write) {
+    if (kCount && !write) {
         // counts only, at the speed of the histogram pass
         count_exponents<kPackThreads>(src, begin, end, hmine);
         t0 = end;
@@ -736,14 +617,14 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
             w[4 * h + 2] = v.z;
             w[4 * h + 3] = v.w;
         }
-        if (kFirst) {
+        if (kCount) {
 #pragma unroll
             for (int j = 0; j < kPackWords / 2; j++) {
                 hist_add(hmine, (w[j] >> 7) & 0xFFu);
                 hist_add(hmine, (w[j] >> 23) & 0xFFu);
             }
         }
-        if (write)
+        if (!kCount || write)
             slot_base += pack_tile<kAlignedSm>(w, t0, lut, nib, sm, slot_base, lds, parity, esc);
     }
     // the ragged last tile of the input (last chunk only); every index below
@@ -759,12 +640,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
             const uint32_t lo = 2 * j < (int)valid ? mine[2 * j] : 0u;
             const uint32_t hi = 2 * j + 1 < (int)valid ? mine[2 * j + 1] : 0u;
             w[j] = lo | (hi << 16);
-            if (kFirst) {
+            if (kCount) {
                 if (2 * j < (int)valid) hist_add(hmine, (lo >> 7) & 0xFFu);
                 if (2 * j + 1 < (int)valid) hist_add(hmine, (hi >> 7) & 0xFFu);
             }
         }
-        if (write) {
+        if (!kCount || write) {
             ThreadWords r;
             encode_words(w, lut, r);
             // words past the end have no code (the pad nibble of an odd n is
@@ -781,7 +662,57 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
                 if (k < (int)valid) sm[i0 + k] = (uint8_t)byte_at(r.sm, k);
             slot_base += write_escapes(r, t0, slot_base, lds, parity, esc);
         }
+        parity ^= 1;
     }
+    return slot_base - first_slot;
+}
+
+// One workgroup per chunk.
+template <bool kAlignedSm, class Words, PackRole kRole>
+__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
+__attribute__((amdgpu_waves_per_eu(8))) void k_pack(
+    Words src, uint64_t n, uint32_t chunk_log2, const uint64_t* __restrict__ chunk_base,
+    uint8_t* __restrict__ dst, uint64_t dst_capacity, uint32_t* __restrict__ counts,
+    SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
+    uint64_t scratch_exp) {
+    constexpr bool kFirst = kRole == PackRole::kFirst;
+    __shared__ PackLds lds;
+    __shared__ uint32_t hist[kFirst ? kSpecCopies * kSpecPitch : 1];
+    if (src.invalid()) return;  // the same for every thread
+
+    const int t = threadIdx.x;
+    const uint32_t chunk = blockIdx.x;
+    const uint64_t begin = (uint64_t)chunk << chunk_log2;
+    const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
+
+    bool write = true;
+    uint32_t* hmine = nullptr;
+    EscapeOut esc;
+    uint64_t slot_base;
+    if (kFirst) {
+        // the provisional code table the sample pass left; the streams are
+        // written only when the sample predicts few escapes, otherwise this
+        // pass only counts and the finish pass packs
+        if (t < 256) lds.lut[t] = area->lut[t];
+        write = area->spec_on != 0;
+        for (int i = t; i < kSpecCopies * kSpecPitch; i += kPackThreads) hist[i] = 0;
+        hmine = hist + (t % kSpecCopies) * kSpecPitch;
+        // this chunk's scratch slots
+        esc.pos = dst + scratch_pos + 4 * (uint64_t)chunk * spec_cap;
+        esc.exp = dst + scratch_exp + (uint64_t)chunk * spec_cap;
+        esc.limit = spec_cap;
+        esc.pos_aligned = true;
+        slot_base = 0;
+    } else {
+        exact_code_table(dst, lds.lut);
+        esc = final_slots(dst, n, dst_capacity);
+        slot_base = chunk_base[chunk];
+    }
+    __syncthreads();
+
+    int parity = 0;
+    const uint64_t escapes = pack_range<kAlignedSm, kFirst>(src, n, begin, end, dst, esc,
+                                                            slot_base, write, hmine, lds, parity);
     if (kFirst) {
         __syncthreads();
         // the chunk's exact counts, laid out as the histogram pass lays them
@@ -792,7 +723,125 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
             counts[(uint64_t)b * gridDim.x + chunk] = s;
         }
         // more escapes than scratch slots: the finish pass must pack again
-        if (t == 0 && write && slot_base > spec_cap) atomicOr(&area->overflow, 1u);
+        if (t == 0 && write && escapes > spec_cap) atomicOr(&area->overflow, 1u);
+    }
+}
+
+// Workgroups of the finish pass: two per CU of MI355X.
+constexpr uint32_t kFinishGroups = 512;
+
+// The finish pass of the single-read encode.  Every workgroup takes the same
+// decision from the two codebooks and the first pass's flags:
+//  - same 16 exponents (and the first pass wrote the streams, no chunk
+//    overflowed): the streams stand.  Every escape record moves from its
+//    chunk's scratch slots to its final slot (grid-stride over the final
+//    slots, the chunk of a slot found by a search of chunk_base in LDS);
+//    when the order differs too, each chunk's 4-bit codes are rewritten
+//    (provisional code -> exact code, both nibbles of a byte at once) and
+//    the codes of its escaped words and of an odd n's pad nibble set back
+//    to 0;
+//  - otherwise every chunk is packed again from the input, the workgroups
+//    taking chunks blockIdx.x, blockIdx.x + gridDim.x, ...
+template <bool kAlignedSm, class Words>
+__global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
+__attribute__((amdgpu_waves_per_eu(8))) void k_finish(
+    Words src, uint64_t n, uint32_t chunk_log2, uint32_t chunks,
+    const uint64_t* __restrict__ chunk_base, uint8_t* __restrict__ dst, uint64_t dst_capacity,
+    const SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
+    uint64_t scratch_exp) {
+    __shared__ PackLds lds;
+    __shared__ uint8_t remap[256];  // provisional code pair -> exact code pair
+    if (src.invalid()) return;  // the same for every thread
+    const int t = threadIdx.x;
+
+    const uint4 prov = *reinterpret_cast<const uint4*>(area->cb);
+    const uint4 exact = *reinterpret_cast<const uint4*>(dst + kHeaderBytes);
+    const bool same_order =
+        prov.x == exact.x && prov.y == exact.y && prov.z == exact.z && prov.w == exact.w;
+    const bool usable = area->spec_on != 0 && area->overflow == 0;
+    // the same set: every exact codebook entry has a provisional code
+    const bool same_set =
+        __syncthreads_and(t >= 16 || area->lut[dst[kHeaderBytes + t]] < 16) != 0;
+    const EscapeOut esc = final_slots(dst, n, dst_capacity);
+
+    if (usable && same_set) {
+        const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
+        uint64_t* base = reinterpret_cast<uint64_t*>(lds.stage_off);  // chunks <= 2048
+        for (uint32_t c = t; c < chunks; c += kPackThreads) base[c] = chunk_base[c];
+        __syncthreads();
+        const uint32_t* spos = reinterpret_cast<const uint32_t*>(dst + scratch_pos);
+        const uint8_t* sexp = dst + scratch_exp;
+        for (uint64_t s = (uint64_t)blockIdx.x * kPackThreads + t; s < E;
+             s += (uint64_t)gridDim.x * kPackThreads) {
+            // the chunk holding slot s: the last c with base[c] <= s
+            uint32_t lo = 0, hi = chunks;
+            while (hi - lo > 1) {
+                const uint32_t mid = (lo + hi) / 2;
+                if (base[mid] <= s) lo = mid; else hi = mid;
+            }
+            const uint64_t q = s - base[lo];  // below spec_cap when the sets agree
+            if (q < spec_cap)
+                put_escape(esc, s, spos[(uint64_t)lo * spec_cap + q], sexp[(uint64_t)lo * spec_cap + q]);
+        }
+        if (same_order) return;
+
+        uint8_t* lut = lds.lut;
+        exact_code_table(dst, lut);
+        __syncthreads();
+        if (t < 256)
+            remap[t] = (uint8_t)((lut[area->cb[t & 15]] & 0xF) |
+                                 ((lut[area->cb[t >> 4]] & 0xF) << 4));
+        __syncthreads();
+        uint8_t* nib = dst + kPrefixBytes;
+        for (uint32_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+            const uint64_t begin = (uint64_t)c << chunk_log2;
+            const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
+            const uint64_t b0 = begin / 2, b1 = (end + 1) / 2;  // the chunk's nibble bytes
+            for (uint64_t b = b0 + (uint64_t)t * 16; b < b1; b += (uint64_t)kPackThreads * 16) {
+                if (b + 16 <= b1) {
+                    const uint4 v = *reinterpret_cast<const uint4*>(nib + b);
+                    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                    for (int j = 0; j < 4; j++) {
+                        const uint32_t x = w[j];
+                        w[j] = (uint32_t)remap[x & 0xFF] | ((uint32_t)remap[(x >> 8) & 0xFF] << 8) |
+                               ((uint32_t)remap[(x >> 16) & 0xFF] << 16) |
+                               ((uint32_t)remap[x >> 24] << 24);
+                    }
+                    *reinterpret_cast<uint4*>(nib + b) = make_uint4(w[0], w[1], w[2], w[3]);
+                } else {
+                    for (uint64_t k = b; k < b1; k++) nib[k] = remap[nib[k]];
+                }
+            }
+            __syncthreads();
+            // escaped words keep code 0: one thread per byte, the one of the
+            // byte's first record
+            const uint64_t first = base[c];
+            const uint64_t cnt = min_u64((c + 1 < chunks ? base[c + 1] : E) - first, spec_cap);
+            const uint32_t* cpos = spos + (uint64_t)c * spec_cap;
+            const uint64_t seg = begin & ~uint64_t{0xFFFFFFFF};  // a chunk lies in one segment
+            for (uint64_t q = t; q < cnt; q += kPackThreads) {
+                const uint64_t p = seg | cpos[q];
+                if (q > 0 && (seg | cpos[q - 1]) / 2 == p / 2) continue;
+                uint32_t clear = (p & 1) ? 0xF0u : 0x0Fu;
+                if (q + 1 < cnt && (seg | cpos[q + 1]) / 2 == p / 2) clear = 0xFFu;
+                nib[p / 2] &= (uint8_t)~clear;
+            }
+            __syncthreads();
+            // and so does the pad nibble of an odd n
+            if (t == 0 && end == n && (n & 1)) nib[n / 2] &= 0x0F;
+        }
+        return;
+    }
+
+    exact_code_table(dst, lds.lut);
+    __syncthreads();
+    int parity = 0;
+    for (uint32_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+        const uint64_t begin = (uint64_t)c << chunk_log2;
+        const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
+        pack_range<kAlignedSm, false>(src, n, begin, end, dst, esc, chunk_base[c], true, nullptr,
+                                      lds, parity);
     }
 }
 
@@ -832,7 +881,20 @@ hipError_t launch_first_pass(Words src, const EncodePlan& p, uint8_t* ws, uint8_
 template <class Words>
 hipError_t launch_finish(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
                          uint64_t dst_capacity, hipStream_t stream) {
-    return launch_pack_role<Words, PackRole::kFinish>(src, p, ws, dst, dst_capacity, stream);
+    if (p.chunks == 0) return hipSuccess;
+    const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
+    const SampleArea* area = reinterpret_cast<const SampleArea*>(ws + p.sample_off);
+    const uint32_t groups = p.chunks < kFinishGroups ? p.chunks : kFinishGroups;
+    const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
+    if (aligned)
+        k_finish<true, Words><<<groups, kPackThreads, 0, stream>>>(
+            src, p.n, p.chunk_log2, p.chunks, base, dst, dst_capacity, area, p.spec_cap,
+            p.scratch_pos, p.scratch_exp);
+    else
+        k_finish<false, Words><<<groups, kPackThreads, 0, stream>>>(
+            src, p.n, p.chunk_log2, p.chunks, base, dst, dst_capacity, area, p.spec_cap,
+            p.scratch_pos, p.scratch_exp);
+    return hipGetLastError();
 }
 
 // ---------------------------------------------------------------- sample

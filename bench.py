@@ -42,7 +42,7 @@ TWO_READ_PASSES = ["histogram", "codebook", "pack"]
 SINGLE_READ_PASSES = ["sample", "first", "codebook", "finish"]
 KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select",
                 "pack": "k_pack", "sample": "k_sample+k_rank_sample",
-                "first": "k_pack(first pass)", "finish": "k_pack(finish)",
+                "first": "k_pack(first pass)", "finish": "k_finish",
                 "fused": "k_decode_fused", "dense": "k_decode_dense",
                 "unpack": "k_unpack", "scatter": "k_scatter"}
 # the sample of the single-read encode: 512 blocks of 2048 words

@@ -435,8 +435,9 @@ def main() -> int:
     enc_ms = sum(avg_ms[p] for p in encode_passes)
     dec_ms = sum(avg_ms[p] for p in decode_passes)
     other_dec_ms = sum(avg_ms[p] for p in other_passes)
-    # read the words (once, or twice), write the container
-    enc_alg = sum(alg[p] for p in encode_passes) if not single else alg["pack"]
+    # the least any encode must move: read the words once, write the
+    # container (the two-read form reads them twice)
+    enc_alg = alg["pack"]
     dec_alg = alg["fused"]  # container in, words out: the same for either form
     ms_per_step = total_ms / args.steps
 

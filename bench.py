@@ -2,7 +2,7 @@
 
 One step = the whole hot path over one tensor already resident in HBM, in
 the passes sz_encode and sz_decode run for it: encode as exponent histogram
--> top-16 codebook -> pack, or, from 2^27 words on, as sample -> first pass
+-> top-16 codebook -> pack, or, from 2^26 words on, as sample -> first pass
 (pack with the sampled codebook while counting) -> codebook -> finish; then
 decode in the form sz_decode picks for the escape density.  Every pass is
 bracketed by HIP events on the stream the kernels run on, so each kernel's

@@ -86,7 +86,7 @@ uint64_t sz_workspace_size(uint64_t n_elements);
  *                     the first `total bytes` of the container are written
  *   d_compressed_size optional device u64 that receives the container size
  *                     (the same value is stored at container offset 24)
- * From 2^27 elements on (sz_encode_single_read(n) says 1) the input is read
+ * From 2^26 elements on (sz_encode_single_read(n) says 1) the input is read
  * once when a sample of it predicts the codebook: the bytes of d_dst past the
  * container, up to sz_max_compressed_size(n), then serve as scratch and are
  * left unspecified.  The container is the same either way.
@@ -162,7 +162,7 @@ sz_status sz_encode_pack(const void *d_src, uint64_t n_elements,
  * checks of the two-read calls); the first pass and the finish use the bytes
  * of d_dst past the container, up to sz_max_compressed_size(n), as scratch. */
 
-/* 1 when sz_encode takes the single-read passes for n elements (n >= 2^27),
+/* 1 when sz_encode takes the single-read passes for n elements (n >= 2^26),
  * else 0.  Host-only. */
 int sz_encode_single_read(uint64_t n_elements);
 

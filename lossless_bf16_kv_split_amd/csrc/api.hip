@@ -13,6 +13,12 @@ namespace {
 
 constexpr int kMaxDevices = 64;
 
+// sz_encode takes the single-read passes from this many words on.  Below,
+// their two extra launches (sample ranking, finish) cost more than the
+// second read of the input saves: on MI355X the two forms break even
+// between 2^25 and 2^26 words of KV data.
+constexpr uint64_t kSingleReadAuto = uint64_t{1} << 26;
+
 std::mutex g_mutex;
 hipMemPool_t g_pools[kMaxDevices] = {};
 int g_num_cus[kMaxDevices] = {};
@@ -116,7 +122,7 @@ sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capa
     uint8_t* w = static_cast<uint8_t*>(ws);
     uint8_t* out = static_cast<uint8_t*>(d_dst);
     sz_status st = SZ_OK;
-    if (p.single_read && n >= sz::kSingleReadAuto && p.scratch_end <= dst_capacity) {
+    if (p.single_read && n >= kSingleReadAuto && p.scratch_end <= dst_capacity) {
         // one read of the input when the sampled codebook holds; the finish
         // pass reads it again only when it does not
         st = hip_status(sz::launch_sample(src, p, w, stream));
@@ -226,7 +232,7 @@ sz_status sz_encode_pack(const void* d_src, uint64_t n, const void* d_workspace,
 
 int sz_encode_single_read(uint64_t n) {
     if (n > SZ_MAX_ELEMENTS) return 0;
-    return n >= sz::kSingleReadAuto && sz::plan_encode(n).single_read ? 1 : 0;
+    return n >= kSingleReadAuto && sz::plan_encode(n).single_read ? 1 : 0;
 }
 
 sz_status sz_encode_sample(const void* d_src, uint64_t n, void* d_workspace,

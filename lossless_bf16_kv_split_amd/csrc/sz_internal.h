@@ -60,12 +60,8 @@ static_assert(sizeof(SampleArea) % 16 == 0 && offsetof(SampleArea, lut) % 16 == 
               "16-byte loads of the tables");
 
 // The single-read passes take inputs from kSingleReadMin words on (below,
-// the sample blocks would overlap); sz_encode uses them from
-// kSingleReadAuto words on.  Below that the two extra launches (sample
-// ranking, finish) cost more than the second read of the input saves: on
-// MI355X the two forms break even between 2^26 and 2^27 words of KV data.
+// the sample blocks would overlap).
 constexpr uint64_t kSingleReadMin = uint64_t{1} << 20;
-constexpr uint64_t kSingleReadAuto = uint64_t{1} << 27;
 
 EncodePlan plan_encode(uint64_t n);
 

@@ -128,8 +128,8 @@ def test_staged_host_checks(sz):
 
 
 def test_single_read_host_checks(sz):
-    assert not sz.sz_encode_single_read((1 << 27) - 1)
-    assert sz.sz_encode_single_read(1 << 27)
+    assert not sz.sz_encode_single_read((1 << 26) - 1)
+    assert sz.sz_encode_single_read(1 << 26)
     assert sz.sz_encode_single_read(1 << 36)
     assert not sz.sz_encode_single_read((1 << 36) + 1)
     W, D = A + (1 << 32), A + (1 << 36)

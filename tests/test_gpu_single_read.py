@@ -1,7 +1,7 @@
 """The single-read encode, case by case.
 
 sz_encode_sample; sz_encode_first_pass; sz_encode_codebook;
-sz_encode_finish (what sz_encode runs from 2^27 words on) read the input
+sz_encode_finish (what sz_encode runs from 2^26 words on) read the input
 once when they can: the first pass packs every chunk with a provisional
 codebook ranked from a fixed sample of the input (512 blocks of 2048 words,
 block j at the 2048-word boundary at or below j * n / 512) while it counts
@@ -186,7 +186,7 @@ def test_single_read_staged_small_n_refused(torch, sz):
 
 @pytest.mark.timeout(300)
 def test_single_read_pages(torch, sz):
-    """sz_encode_pages reads the pages once too (2^27 words and more); a
+    """sz_encode_pages reads the pages once too (2^26 words and more); a
     remap case, so that the finish pass rewrites codes in a paged tensor."""
     n, page = (1 << 27) + 5, 1 << 16
     assert sz.sz_encode_single_read(n)

@@ -62,6 +62,7 @@ def ship_round_trip(torch, sz, words: np.ndarray, chunk: int, label: str):
     ("kv", 5000, 65536),                 # one short chunk
     ("wide40", 2 * 40000 + 8, 40000),    # escape-heavy, chunk not a power of two
     ("kv", 1 << 22, 1 << 20),            # several sizeable chunks
+    ("kv", (1 << 26) + 4104, 1 << 26),   # a chunk encoded in the single-read form
 ])
 def test_ship_round_trip(torch, sz, kind, n, chunk):
     ship_round_trip(torch, sz, make_words(kind, n, 31), chunk, f"{kind} {n}/{chunk}")

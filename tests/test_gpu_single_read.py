@@ -185,15 +185,18 @@ def test_single_read_staged_small_n_refused(torch, sz):
 
 
 @pytest.mark.timeout(300)
-def test_single_read_pages(torch, sz):
-    """sz_encode_pages reads the pages once too (2^26 words and more); a
-    remap case, so that the finish pass rewrites codes in a paged tensor."""
-    n, page = (1 << 27) + 5, 1 << 16
+@pytest.mark.parametrize("case,n,page", [("remap", (1 << 27) + 5, 1 << 16),
+                                         ("full:sample", (1 << 26) + 7, 1 << 14),
+                                         ("full:set", 1 << 26, 1 << 15)])
+def test_single_read_pages(torch, sz, case, n, page):
+    """sz_encode_pages reads the pages once too (2^26 words and more): codes
+    rewritten in a paged tensor, and chunks counted then packed again, or
+    packed twice, from pages."""
     assert sz.sz_encode_single_read(n)
-    label = f"pages remap n={n}"
+    label = f"pages {case} n={n} page={page}"
     say(label)
-    words = words_for("remap", n)
-    assert expected_case(words) == "remap", label
+    words = words_for(case, n)
+    assert expected_case(words) == case, label
     pool, table, order = paged(torch, n, page, 12)
     scatter_to_pages(torch, pool, order, words, page)
     cap = sz.sz_max_compressed_size(n)

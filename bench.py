@@ -424,6 +424,21 @@ def main() -> int:
     ok = ok and bool(torch.equal(out2, x)) and int(status.item()) == 0
     del out2
 
+    # the other encode form, after the timed region, each run followed by
+    # the step's decode; it must leave the same container
+    other_enc = TWO_READ_PASSES if single else (SINGLE_READ_PASSES if n >= 1 << 20 else [])
+    other_enc_ms = None
+    if other_enc:
+        ref = container.clone()
+        oe_ev = new_events(len(other_enc) + 1)
+        for k in range(args.steps):
+            step(other_enc, out, oe_ev[k])
+            step(decode_passes, out)
+        torch.cuda.synchronize()
+        other_enc_ms = sum(ev[0].elapsed_time(ev[-1]) for ev in oe_ev) / args.steps
+        ok = ok and bool(torch.equal(dst[:total], ref)) and bool(torch.equal(out, x))
+        del ref
+
     alg = algorithmic_bytes(n, e, case)
     kernels = {}
     for p in passes + other_passes:
@@ -435,9 +450,9 @@ def main() -> int:
     enc_ms = sum(avg_ms[p] for p in encode_passes)
     dec_ms = sum(avg_ms[p] for p in decode_passes)
     other_dec_ms = sum(avg_ms[p] for p in other_passes)
-    # the least any encode must move: read the words once, write the
-    # container (the two-read form reads them twice)
-    enc_alg = alg["pack"]
+    # the bytes the encode passes that ran move (the two-read form reads the
+    # words twice, the single-read form once plus the escape records' moves)
+    enc_alg = sum(alg[p] for p in encode_passes)
     dec_alg = alg["fused"]  # container in, words out: the same for either form
     ms_per_step = total_ms / args.steps
 
@@ -482,6 +497,10 @@ def main() -> int:
         "decode_frac_hbm": round(dec_alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
         "encode_form": ("single read (sampled codebook), finish case " + case) if single
                        else "two reads (histogram, then pack)",
+        "other_encode_form": None if not other_enc else
+                             ("two reads (histogram, then pack)" if single else "single read"),
+        "other_encode_form_GBps": None if other_enc_ms is None else
+                                  round(2 * n / (other_enc_ms * 1e-3) / 1e9, 2),
         "decode_form": form,
         "other_decode_form_GBps": round(2 * n / (other_dec_ms * 1e-3) / 1e9, 2),
         "ratio": round(2 * n / total, 5),

@@ -44,14 +44,15 @@ KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select
                 "pack": "k_pack", "sample": "k_sample+k_rank_sample",
                 "first": "k_pack(first pass)", "finish": "k_finish",
                 "fused": "k_decode_fused", "dense": "k_decode_dense",
+                "index": "k_tile_index", "tiles": "k_decode_tiles",
                 "unpack": "k_unpack", "scatter": "k_scatter"}
 # the sample of the single-read encode: 512 blocks of 2048 words
 SAMPLE_BLOCKS, SAMPLE_BLOCK_WORDS = 512, 2048
 MIN_CHUNK_LOG2, MAX_CHUNKS = 14, 2048
-# sz_decode runs a single pass when more than one word in FUSED_DECODE_DENSITY
-# is an escape, the dense single pass above one in DENSE_DECODE_DENSITY
-FUSED_DECODE_DENSITY = 2048
-DENSE_DECODE_DENSITY = 32
+# sz_decode's forms: the tile decode from TILE_DECODE_MIN words with up to one
+# escape in TILE_DECODE_DENSITY words; below TILE_DECODE_MIN words, unpack then
+# scatter up to one escape in SCATTER_DECODE_DENSITY; else the dense decode
+TILE_DECODE_DENSITY, SCATTER_DECODE_DENSITY, TILE_DECODE_MIN = 128, 256, 1 << 26
 
 
 def kernel_source_hash() -> str:
@@ -80,6 +81,8 @@ def algorithmic_bytes(n: int, e: int, case: str | None = None) -> dict:
         "first": 2 * n if case == "full:sample" else 2 * n + nib + sm + esc,
         "finish": finish,
         "fused": pre + nib + sm + esc + 2 * n,     # read container, write words once
+        "index": 4 * e,                            # read every escape position once
+        "tiles": pre + nib + sm + esc + 2 * n,     # as fused
         "dense": pre + nib + sm + esc + 2 * n,     # the same, other layout
         "unpack": pre + nib + sm + 2 * n,          # read codes + sm, write words
         "scatter": esc + 4 * e,                    # read records; read + rewrite each escaped word
@@ -334,6 +337,8 @@ def main() -> int:
     size = torch.zeros(1, dtype=torch.int64, device="cuda")
     out = torch.empty(n, dtype=torch.int16, device="cuda")
     status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dws_bytes = sz.sz_decode_workspace_size(n)
+    dws = torch.empty(dws_bytes, dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
     # container size is known after one encode; decode needs it on the host
@@ -347,12 +352,14 @@ def main() -> int:
 
     # the decode passes sz_decode runs for this container (same rule), and
     # the closest other form, timed after the timed region
-    if e > n // DENSE_DECODE_DENSITY:
-        decode_passes, other_passes, form = ["dense"], ["fused"], "single pass, exponent map"
-    elif e > n // FUSED_DECODE_DENSITY:
-        decode_passes, other_passes, form = ["fused"], ["unpack", "scatter"], "single pass"
+    if n < TILE_DECODE_MIN and e <= n // SCATTER_DECODE_DENSITY:
+        decode_passes, other_passes, form = ["unpack", "scatter"], ["index", "tiles"], \
+            "unpack + escape scatter"
+    elif e > n // TILE_DECODE_DENSITY or n < TILE_DECODE_MIN:
+        decode_passes, other_passes, form = ["dense"], ["index", "tiles"], "single pass, exponent map"
     else:
-        decode_passes, other_passes, form = ["unpack", "scatter"], ["fused"], "unpack + escape scatter"
+        decode_passes, other_passes, form = (["index", "tiles"], ["dense"],
+                                             "single pass over grid-stride tiles")
     passes = encode_passes + decode_passes
 
     def run_pass(p, dst_words):
@@ -372,6 +379,10 @@ def main() -> int:
             sz.sz_decode_fused(container, total, dst_words, n, status, stream)
         elif p == "dense":
             sz.sz_decode_dense(container, total, dst_words, n, status, stream)
+        elif p == "index":
+            sz.sz_decode_index(container, total, n, dws, dws_bytes, stream)
+        elif p == "tiles":
+            sz.sz_decode_tiles(container, total, dws, dws_bytes, dst_words, n, status, stream)
         elif p == "unpack":
             sz.sz_decode_unpack(container, total, dst_words, n, status, stream)
         elif p == "scatter":
@@ -453,7 +464,7 @@ def main() -> int:
     # the bytes the encode passes that ran move (the two-read form reads the
     # words twice, the single-read form once plus the escape records' moves)
     enc_alg = sum(alg[p] for p in encode_passes)
-    dec_alg = alg["fused"]  # container in, words out: the same for either form
+    dec_alg = sum(alg[p] for p in decode_passes)  # the bytes the decode passes move
     ms_per_step = total_ms / args.steps
 
     dominant = max([p for p in passes if p != "codebook"], key=lambda p: avg_ms[p])

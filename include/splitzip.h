@@ -99,11 +99,14 @@ sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
 /* Decompress a container of src_bytes bytes into n BF16 words at d_dst,
  * bit-exactly.  SplitZip explainer section "4. Pourquoi est-ce rapide ?"
  * (code -> exponent lookup, recombination with sign and mantissa, escaped
- * slots overwritten).  Unless escapes are very rare (at most one word in
- * 2048) it runs as one pass that overwrites the escaped exponents before
- * each word is stored (sz_decode_fused, or sz_decode_dense above one escape
- * in 32 words); otherwise as the two staged passes below.  Same result
- * every way.
+ * slots overwritten).  The form depends on the size and escape density:
+ * from 2^26 words with at most one escape in 128, one pass over grid-stride
+ * tiles (sz_decode_index, then sz_decode_tiles, with a workspace from a
+ * library-owned stream-ordered pool); below 2^26 words with at most one
+ * escape in 256, the two passes sz_decode_unpack and sz_decode_scatter;
+ * otherwise, and whenever the stream is being captured into a graph, one
+ * pass with a per-word exponent map (sz_decode_dense).  Same result every
+ * way.
  *   src_bytes   must equal the container's total size: the host derives E
  *               from it, so no device read is needed before launching
  *   d_status    optional device i32: SZ_OK, or SZ_ERR_CORRUPT when the
@@ -203,8 +206,7 @@ sz_status sz_decode_scatter(const void *d_src, uint64_t src_bytes, void *d_dst,
  * finds its range's escape records by a 64-way search over the sorted
  * positions, stages them in LDS and overwrites the escaped exponents before
  * the words are stored (explainer section "4. Pourquoi est-ce rapide ?").
- * Same arguments, result and status as sz_decode, which picks this form
- * when between one word in 2048 and one in 32 is an escape. */
+ * Same arguments, result and status as sz_decode. */
 sz_status sz_decode_fused(const void *d_src, uint64_t src_bytes, void *d_dst,
                           uint64_t n_elements, int32_t *d_status, hipStream_t stream);
 
@@ -213,10 +215,31 @@ sz_status sz_decode_fused(const void *d_src, uint64_t src_bytes, void *d_dst,
  * sub-range straight from the escape stream into a per-word LDS map, and
  * rebuilds the words with the mapped exponents in place of the codebook's
  * (explainer section "4. Pourquoi est-ce rapide ?").  Same arguments,
- * result and status as sz_decode, which picks this form when more than one
- * word in 32 is an escape. */
+ * result and status as sz_decode, which picks this form above one escape
+ * in 128 words, for small tensors above one in 256, and whenever it cannot
+ * allocate. */
 sz_status sz_decode_dense(const void *d_src, uint64_t src_bytes, void *d_dst,
                           uint64_t n_elements, int32_t *d_status, hipStream_t stream);
+
+/* Decode in a single pass with the words handed out grid-stride, in two
+ * calls over a caller workspace of sz_decode_workspace_size(n) bytes
+ * (256-byte aligned, not overlapping the container or the output).
+ * sz_decode_index records, for every 4096-word tile, the first escape
+ * record at or after the tile's start, and checks the header and that the
+ * records ascend below n; sz_decode_tiles then has a few workgroups per CU
+ * take tiles b, b + grid, ..., mark each tile's records in an LDS exponent
+ * map and rebuild its words (explainer section "4. Pourquoi est-ce
+ * rapide ?").  sz_decode_tiles writes *d_status (optional): SZ_OK, or
+ * SZ_ERR_CORRUPT when the index call found a fault (the output content is
+ * then unspecified, but no write leaves d_dst[0..n)).  Together they give
+ * the result and status of sz_decode, which takes this form, with a
+ * workspace from its pool, from 2^26 words with up to one escape in 128. */
+uint64_t sz_decode_workspace_size(uint64_t n_elements);
+sz_status sz_decode_index(const void *d_src, uint64_t src_bytes, uint64_t n_elements,
+                          void *d_workspace, uint64_t workspace_bytes, hipStream_t stream);
+sz_status sz_decode_tiles(const void *d_src, uint64_t src_bytes, const void *d_workspace,
+                          uint64_t workspace_bytes, void *d_dst, uint64_t n_elements,
+                          int32_t *d_status, hipStream_t stream);
 
 /* ---- paged tensors -----------------------------------------------------
  * Serving stacks keep KV caches in fixed-size pages (the explainers'

@@ -27,6 +27,7 @@ __all__ = [
     "sz_decode", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
     "sz_encode_single_read", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
+    "sz_decode_workspace_size", "sz_decode_index", "sz_decode_tiles",
     "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host", "sz_ship_from_host",
     "sz_status_string", "encode",
     "decode",
@@ -78,6 +79,10 @@ def _load() -> ctypes.CDLL:
     L.sz_decode_scatter.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_fused.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_dense.argtypes = [p, u64, p, u64, p, p]
+    L.sz_decode_workspace_size.argtypes = [u64]
+    L.sz_decode_workspace_size.restype = u64
+    L.sz_decode_index.argtypes = [p, u64, u64, p, u64, p]
+    L.sz_decode_tiles.argtypes = [p, u64, p, u64, p, u64, p, p]
     L.sz_encode_pages.argtypes = [p, u64, u64, u64, p, u64, p, p, p]
     L.sz_decode_pages.argtypes = [p, u64, p, u64, u64, u64, p, p]
     L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
@@ -85,7 +90,8 @@ def _load() -> ctypes.CDLL:
     for name in ("sz_encode", "sz_decode", "sz_encode_histogram", "sz_encode_codebook",
                  "sz_encode_pack", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
                  "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
-                 "sz_decode_dense", "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host",
+                 "sz_decode_dense", "sz_decode_index", "sz_decode_tiles", "sz_encode_pages",
+                 "sz_decode_pages", "sz_ship_to_host",
                  "sz_ship_from_host"):
         getattr(L, name).restype = i32
     L.sz_status_string.argtypes = [i32]
@@ -203,6 +209,23 @@ def sz_decode_fused(src, src_bytes: int, dst, n_elements: int, d_status=None,
                     stream=None) -> None:
     _check(_lib.sz_decode_fused(_ptr(src), src_bytes, _ptr(dst), n_elements, _ptr(d_status),
                                 _stream(stream)), "sz_decode_fused")
+
+
+def sz_decode_workspace_size(n_elements: int) -> int:
+    return int(_lib.sz_decode_workspace_size(n_elements))
+
+
+def sz_decode_index(src, src_bytes: int, n_elements: int, workspace, workspace_bytes: int,
+                    stream=None) -> None:
+    _check(_lib.sz_decode_index(_ptr(src), src_bytes, n_elements, _ptr(workspace),
+                                workspace_bytes, _stream(stream)), "sz_decode_index")
+
+
+def sz_decode_tiles(src, src_bytes: int, workspace, workspace_bytes: int, dst, n_elements: int,
+                    d_status=None, stream=None) -> None:
+    _check(_lib.sz_decode_tiles(_ptr(src), src_bytes, _ptr(workspace), workspace_bytes,
+                                _ptr(dst), n_elements, _ptr(d_status), _stream(stream)),
+           "sz_decode_tiles")
 
 
 def sz_decode_dense(src, src_bytes: int, dst, n_elements: int, d_status=None,

@@ -139,25 +139,50 @@ sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capa
     return st;
 }
 
+// true while `stream` is being captured into a graph (no pool allocation then)
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
+}
+
+sz_status check_decode_workspace(const void* ws, uint64_t ws_bytes, uint64_t n) {
+    if (ws == nullptr || !aligned(ws, 256) || ws_bytes < sz::tile_index_layout(n).bytes)
+        return SZ_ERR_INVALID_ARGUMENT;
+    return SZ_OK;
+}
+
 // the decode form sz_decode picks for this escape density
 template <class Words>
 sz_status decode_by_density(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                             Words dst, int32_t* d_status, hipStream_t stream) {
-    if (e > n / sz::kDenseDecodeDensity) {
-        // many escapes: one pass with a per-word LDS map of exponents
-        return hip_status(sz::launch_decode_dense(src, src_bytes, n, e, dst, d_status, stream));
-    }
-    if (e > n / sz::kFusedDecodeDensity) {
-        // some escapes: patch escaped exponents before each word is stored
-        return hip_status(sz::launch_decode_fused(src, src_bytes, n, e, dst, d_status, stream));
-    }
-    // escape-sparse: stream every word out, then rewrite the few escaped ones
     const int dev = current_device();
     if (dev < 0) return SZ_ERR_HIP;
-    sz_status st = hip_status(sz::launch_unpack(src, src_bytes, n, e, dst, d_status, num_cus(dev),
-                                                stream));
-    if (st != SZ_OK) return st;
-    return hip_status(sz::launch_scatter(src, n, e, dst, d_status, stream));
+    if (n < sz::kTileDecodeMin && e <= n / sz::kScatterDecodeDensity) {
+        // small and sparse: stream every word out, then rewrite the escaped ones
+        sz_status st = hip_status(sz::launch_unpack(src, src_bytes, n, e, dst, d_status,
+                                                    num_cus(dev), stream));
+        if (st != SZ_OK) return st;
+        return hip_status(sz::launch_scatter(src, n, e, dst, d_status, stream));
+    }
+    // few escapes in a large tensor: tiles handed out grid-stride after a
+    // tile index, in a workspace from the pool (none under graph capture)
+    hipMemPool_t pool = e > n / sz::kTileDecodeDensity || n < sz::kTileDecodeMin ||
+                                capturing(stream)
+                            ? nullptr
+                            : pool_for(dev);
+    if (pool == nullptr) {
+        // many escapes, or no workspace: one pass with a per-word LDS map
+        return hip_status(sz::launch_decode_dense(src, src_bytes, n, e, dst, d_status, stream));
+    }
+    const sz::TileIndexLayout l = sz::tile_index_layout(n);
+    void* ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, l.bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    sz_status st = hip_status(sz::launch_tile_index(src, src_bytes, n, e, w, stream));
+    if (st == SZ_OK)
+        st = hip_status(sz::launch_decode_tiles(src, n, e, w, dst, d_status, num_cus(dev), stream));
+    if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
+    return st;
 }
 
 // Host checks of a page description: 2^k-word pages, k >= 14, enough of
@@ -303,6 +328,39 @@ sz_status sz_decode(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
     return decode_by_density(static_cast<const uint8_t*>(d_src), src_bytes, n, e, flat(d_dst),
                              d_status, stream);
+}
+
+uint64_t sz_decode_workspace_size(uint64_t n) {
+    if (n > SZ_MAX_ELEMENTS) return 0;
+    return sz::tile_index_layout(n).bytes;
+}
+
+sz_status sz_decode_index(const void* d_src, uint64_t src_bytes, uint64_t n, void* d_workspace,
+                          uint64_t workspace_bytes, hipStream_t stream) {
+    if (n > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (d_src == nullptr || !aligned(d_src, 16)) return SZ_ERR_INVALID_ARGUMENT;
+    if (sz_status s = check_decode_workspace(d_workspace, workspace_bytes, n)) return s;
+    const uint64_t fixed = sz::container_bytes(n, 0);
+    if (src_bytes < fixed || (src_bytes - fixed) % 5 != 0) return SZ_ERR_CORRUPT;
+    const uint64_t e = (src_bytes - fixed) / 5;
+    if (e > (15 * n) / 16) return SZ_ERR_CORRUPT;
+    if (overlap(d_src, src_bytes, d_workspace, workspace_bytes)) return SZ_ERR_INVALID_ARGUMENT;
+    return hip_status(sz::launch_tile_index(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
+                                            static_cast<uint8_t*>(d_workspace), stream));
+}
+
+sz_status sz_decode_tiles(const void* d_src, uint64_t src_bytes, const void* d_workspace,
+                          uint64_t workspace_bytes, void* d_dst, uint64_t n, int32_t* d_status,
+                          hipStream_t stream) {
+    uint64_t e = 0;
+    if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
+    if (sz_status s = check_decode_workspace(d_workspace, workspace_bytes, n)) return s;
+    if (overlap(d_dst, 2 * n, d_workspace, workspace_bytes)) return SZ_ERR_INVALID_ARGUMENT;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    return hip_status(sz::launch_decode_tiles(static_cast<const uint8_t*>(d_src), n, e,
+                                              static_cast<const uint8_t*>(d_workspace),
+                                              flat(d_dst), d_status, num_cus(dev), stream));
 }
 
 sz_status sz_decode_fused(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,

@@ -92,15 +92,44 @@ __device__ __forceinline__ void store_streaming(uint4* p, uint4 v) {
     __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
 }
 
-// sz_decode patches escapes inside the unpack pass when more than one word
-// in kFusedDecodeDensity is an escape; below that, a separate in-place
-// rewrite of the few escaped words costs less than the fused pass's
-// bookkeeping (measured crossover on MI355X: about one word in 2000).
-// Above one word in kDenseDecodeDensity the dense form's per-word LDS map
-// beats the fused form's staged record batches (measured: level at 1 in
-// 25, 8% faster at 1 in 12, 36% at 6 in 10; 1.5% slower on sparse KV).
-constexpr uint64_t kFusedDecodeDensity = 2048;
-constexpr uint64_t kDenseDecodeDensity = 32;
+// sz_decode's choice of decode form, measured on MI355X:
+//  - above one escape in kTileDecodeDensity words, the dense decode: over
+//    2^28 KV words with escapes injected, tile 178-185 us against dense
+//    181-196 us up to one escape in 250, dense ahead from about one in 100
+//    (187 against 195 us at 1.2%, 193 against 224 us at 2.7%);
+//  - below kTileDecodeMin words, forms that need no workspace (allocating
+//    one from the pool costs more host time than such a decode takes):
+//    unpack then scatter up to one escape in kScatterDecodeDensity words
+//    (10-26 us against 11-28 us for the others from 2^21 to 2^25 words of
+//    KV data), else the dense decode;
+//  - otherwise the tile decode (the dense one under graph capture).
+constexpr uint64_t kTileDecodeDensity = 128;
+constexpr uint64_t kScatterDecodeDensity = 256;
+constexpr uint64_t kTileDecodeMin = uint64_t{1} << 26;
+
+// Tile decode (the single pass with words handed out grid-stride): its
+// workspace holds the first escape record of every 4096-word tile and one
+// flag per index workgroup (64 tiles each).
+constexpr uint32_t kTileWords = 4096;
+constexpr uint32_t kIndexTiles = 64;
+struct TileIndexLayout {
+    uint64_t tiles = 0;     // ceil(n / kTileWords)
+    uint64_t blocks = 0;    // index workgroups, at least 1
+    uint64_t idx_off = 0;   // u64[tiles + 1]: first record of each tile, then E
+    uint64_t flag_off = 0;  // u32[blocks]: 1 where an index workgroup found a fault
+    uint64_t bytes = 0;
+};
+inline TileIndexLayout tile_index_layout(uint64_t n) {
+    TileIndexLayout l;
+    l.tiles = (n + kTileWords - 1) / kTileWords;
+    l.blocks = (l.tiles + kIndexTiles - 1) / kIndexTiles;
+    if (l.blocks == 0) l.blocks = 1;
+    auto align = [](uint64_t x) { return (x + 255) & ~uint64_t{255}; };
+    l.idx_off = 0;
+    l.flag_off = align(8 * (l.tiles + 1));
+    l.bytes = align(l.flag_off + 4 * l.blocks);
+    return l;
+}
 
 inline uint64_t container_bytes(uint64_t n, uint64_t e) {
     return kPrefixBytes + (n + 1) / 2 + n + 5 * e;
@@ -177,6 +206,13 @@ hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t 
 template <class Words>
 hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                                Words dst, int32_t* status, hipStream_t stream);
+// tile decode: index the escape stream by tile (header and record-order
+// checks included), then decode every tile; the second call writes *status
+hipError_t launch_tile_index(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
+                             uint8_t* ws, hipStream_t stream);
+template <class Words>
+hipError_t launch_decode_tiles(const uint8_t* src, uint64_t n, uint64_t e, const uint8_t* ws,
+                               Words dst, int32_t* status, int num_cus, hipStream_t stream);
 // Checks a page table (every address non-NULL and 16-byte aligned) into
 // *bad, and mirrors the result into *status when given.
 hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, int32_t* bad,

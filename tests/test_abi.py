@@ -150,6 +150,29 @@ def test_single_read_host_checks(sz):
     assert status_of(sz.sz_encode_sample, MIS, n, W, sz.sz_workspace_size(n), 0) == 1
 
 
+def test_tile_decode_host_checks(sz):
+    for n in (0, 1, 4096, 4097, 1 << 29):
+        tiles = -(-n // 4096)
+        blocks = max(1, -(-tiles // 64))
+        want = -(-(-(-8 * (tiles + 1) // 256) * 256 + 4 * blocks) // 256) * 256
+        assert sz.sz_decode_workspace_size(n) == want, n
+    assert sz.sz_decode_workspace_size((1 << 36) + 1) == 0
+    n = 1000
+    fixed = 176 + (n + 1) // 2 + n
+    W, D = A + (1 << 32), A + (1 << 33)
+    ws = sz.sz_decode_workspace_size(n)
+    assert status_of(sz.sz_decode_index, A, fixed, n, W, ws - 1, 0) == 1          # small
+    assert status_of(sz.sz_decode_index, A, fixed, n, W + 16, ws, 0) == 1         # misaligned
+    assert status_of(sz.sz_decode_index, A, fixed, n, None, ws, 0) == 1
+    assert status_of(sz.sz_decode_index, MIS, fixed, n, W, ws, 0) == 1
+    assert status_of(sz.sz_decode_index, A, fixed + 3, n, W, ws, 0) == 4          # not 5E
+    assert status_of(sz.sz_decode_index, A, fixed, n, A + 256, ws, 0) == 1        # overlap
+    assert status_of(sz.sz_decode_tiles, A, fixed, W, ws - 1, D, n, None, 0) == 1
+    assert status_of(sz.sz_decode_tiles, A, fixed - 1, W, ws, D, n, None, 0) == 4
+    assert status_of(sz.sz_decode_tiles, A, fixed, W, ws, W + 256, n, None, 0) == 1  # overlap
+    assert status_of(sz.sz_decode_tiles, A, fixed, W, ws, D, (1 << 36) + 1, None, 0) == 3
+
+
 def test_ship_host_checks(sz):
     import numpy as np
     n = 1000

@@ -60,15 +60,16 @@ GUARD = 64
 SENTINEL = 0x5A5A
 
 
-DECODE_FORMS = ("auto", "fused", "dense", "staged")
+DECODE_FORMS = ("auto", "fused", "dense", "tiles", "staged")
 
 
 def gpu_decode(torch, sz, container_dev, n, form="auto"):
     """Decode into a buffer with GUARD sentinel words after element n; returns
     (words tensor of n, device status, guard intact).  form: "auto" is
     sz_decode, "fused" the single pass with staged record batches, "dense" the
-    single pass with a per-word exponent map, "staged" unpack then escape
-    scatter."""
+    single pass with a per-word exponent map, "tiles" the single pass over
+    grid-stride tiles after a tile index (caller workspace), "staged" unpack
+    then escape scatter."""
     out = torch.full((n + GUARD,), SENTINEL, dtype=torch.int16, device="cuda")
     status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
     if form == "staged":
@@ -78,6 +79,11 @@ def gpu_decode(torch, sz, container_dev, n, form="auto"):
         sz.sz_decode_fused(container_dev, container_dev.numel(), out, n, status)
     elif form == "dense":
         sz.sz_decode_dense(container_dev, container_dev.numel(), out, n, status)
+    elif form == "tiles":
+        ws_bytes = sz.sz_decode_workspace_size(n)
+        ws = torch.full((ws_bytes,), 0x5A, dtype=torch.uint8, device="cuda")  # stale content
+        sz.sz_decode_index(container_dev, container_dev.numel(), n, ws, ws_bytes)
+        sz.sz_decode_tiles(container_dev, container_dev.numel(), ws, ws_bytes, out, n, status)
     else:
         sz.sz_decode(container_dev, container_dev.numel(), out, n, status)
     torch.cuda.synchronize()

@@ -37,7 +37,8 @@ def sz(torch):
 
 @pytest.mark.parametrize("kind,form,single", [("kv", "fused", False), ("wide40", "dense", False),
                                               ("kv", "auto", False), ("narrow", "auto", False),
-                                              ("kv", "auto", True), ("wide40", "auto", True)])
+                                              ("kv", "auto", True), ("wide40", "auto", True),
+                                              ("kv", "tiles", True)])
 def test_graph_replays(torch, sz, kind, form, single):
     n = (1 << 20) + 4096
     words = make_words(kind, n, 51)
@@ -50,7 +51,15 @@ def test_graph_replays(torch, sz, kind, form, single):
     size = torch.zeros(1, dtype=torch.int64, device="cuda")
     out = torch.zeros(n, dtype=torch.int16, device="cuda")
     status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
-    decode = {"fused": sz.sz_decode_fused, "dense": sz.sz_decode_dense, "auto": sz.sz_decode}[form]
+    dws_bytes = sz.sz_decode_workspace_size(n)
+    dws = torch.zeros(dws_bytes, dtype=torch.uint8, device="cuda")
+
+    def tiles(c, total_, out_, n_, status_):
+        sz.sz_decode_index(c, total_, n_, dws, dws_bytes)
+        sz.sz_decode_tiles(c, total_, dws, dws_bytes, out_, n_, status_)
+
+    decode = {"fused": sz.sz_decode_fused, "dense": sz.sz_decode_dense, "auto": sz.sz_decode,
+              "tiles": tiles}[form]
 
     def codec():
         if single:                                # the single-read passes

@@ -380,52 +380,86 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Split 8 BF16 words (two per dword, little-endian) into 8 sign|mantissa
-// bytes and 8 exponent bytes, 4 per dword, element k in byte k % 4.
-// v_perm gathers the high and low bytes of 4 words; the sign is bit 7 of
-// the high byte, the mantissa bits 6..0 of the low byte, the exponent the
-// high byte's low 7 bits above the low byte's bit 7.
-__device__ __forceinline__ void split8(const uint32_t* w, uint32_t& sm_lo, uint32_t& sm_hi,
-                                       uint32_t& ex_lo, uint32_t& ex_hi) {
-    const uint32_t hi0 = __builtin_amdgcn_perm(w[1], w[0], 0x07050301u);
-    const uint32_t lo0 = __builtin_amdgcn_perm(w[1], w[0], 0x06040200u);
-    const uint32_t hi1 = __builtin_amdgcn_perm(w[3], w[2], 0x07050301u);
-    const uint32_t lo1 = __builtin_amdgcn_perm(w[3], w[2], 0x06040200u);
-    sm_lo = (hi0 & 0x80808080u) | (lo0 & 0x7F7F7F7Fu);
-    sm_hi = (hi1 & 0x80808080u) | (lo1 & 0x7F7F7F7Fu);
-    ex_lo = ((hi0 << 1) & 0xFEFEFEFEu) | ((lo0 >> 7) & 0x01010101u);
-    ex_hi = ((hi1 << 1) & 0xFEFEFEFEu) | ((lo1 >> 7) & 0x01010101u);
-}
-
 // byte k of a little-endian run of dwords (k known at compile time after
 // unrolling, so the array stays in registers)
 __device__ __forceinline__ uint32_t byte_at(const uint32_t* v, int k) {
     return (v[k >> 2] >> (8 * (k & 3))) & 0xFFu;
 }
 
-// The words of one thread, split: sign|mantissa and exponent bytes, the
-// 4-bit codes (element k in bits 4(k%8).. of nib[k/8]) and the escape mask.
+// The code table the pack kernels read: one u16 per exponent, the code
+// (0..15) in bits 3..0 and, for an exponent outside the codebook, code 0
+// with bit 8 set.  Four entries of words 4j..4j+3, placed at bits 0, 4, 16
+// and 20 of one dword (entry m shifted by 4(m % 2) + 16(m / 2)), give that
+// dword's bytes 0 and 2 = the two nibble bytes of the four words, and their
+// escape flags at bits 8, 12, 24 and 28 -- no per-word code arithmetic.
+constexpr uint16_t kEscapeEntry = 0x100;
+constexpr uint32_t kFlagBits = 0x11001100u;
+
+__device__ __forceinline__ uint32_t flag_shift(int m) {
+    return m == 0 ? 8u : m == 1 ? 12u : m == 2 ? 24u : 28u;
+}
+
+// Table entry at byte offset x (twice the exponent).
+__device__ __forceinline__ uint32_t code_entry(const uint16_t* table, uint32_t x) {
+    return *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(table) + x);
+}
+
+// Exponent of the thread's word k (two words per dword, little-endian).
+__device__ __forceinline__ uint32_t exponent_of(const uint32_t* w, int k) {
+    return (w[k >> 1] >> ((k & 1) ? 23 : 7)) & 0xFFu;
+}
+
+// The words of one thread, split: sign|mantissa bytes, the 4-bit codes
+// (element k in bits 4(k%8).. of nib[k/8]), per four words the combined
+// table entries (word 4j+m escapes when bit flag_shift(m) of quad[j] is
+// set; other bits are code bits) and the number of escapes.
 struct ThreadWords {
     uint32_t sm[kPackWords / 4];
-    uint32_t ex[kPackWords / 4];
     uint32_t nib[kPackWords / 8];
-    uint32_t mask;
+    uint32_t quad[kPackWords / 4];
+    uint32_t count;
 };
 
-__device__ __forceinline__ void encode_words(const uint32_t* w, const uint8_t* lut,
-                                             ThreadWords& r) {
+__device__ __forceinline__ bool escaped(const ThreadWords& r, int k) {
+    return (r.quad[k >> 2] >> flag_shift(k & 3)) & 1u;
+}
+
+// With kCount, every exponent is also counted into hmine (its u32 count at
+// byte offset 2x from hmine, x being twice the exponent).
+template <bool kCount>
+__device__ __forceinline__ void encode_words(const uint32_t* w, const uint16_t* table,
+                                             ThreadWords& r, uint32_t* hmine) {
+#pragma unroll
+    for (int h = 0; h < kPackWords / 8; h++) {
+        // sign bit of the high byte, mantissa bits of the low byte
+        const uint32_t* v = w + 4 * h;
+        const uint32_t hi0 = __builtin_amdgcn_perm(v[1], v[0], 0x07050301u);
+        const uint32_t lo0 = __builtin_amdgcn_perm(v[1], v[0], 0x06040200u);
+        const uint32_t hi1 = __builtin_amdgcn_perm(v[3], v[2], 0x07050301u);
+        const uint32_t lo1 = __builtin_amdgcn_perm(v[3], v[2], 0x06040200u);
+        r.sm[2 * h] = (hi0 & 0x80808080u) | (lo0 & 0x7F7F7F7Fu);
+        r.sm[2 * h + 1] = (hi1 & 0x80808080u) | (lo1 & 0x7F7F7F7Fu);
+    }
+    r.count = 0;
+#pragma unroll
+    for (int j = 0; j < kPackWords / 4; j++) {
+        const uint32_t d0 = w[2 * j], d1 = w[2 * j + 1];  // words 4j, 4j+1 | 4j+2, 4j+3
+        const uint32_t x0 = (d0 >> 6) & 0x1FEu, x1 = (d0 >> 22) & 0x1FEu;
+        const uint32_t x2 = (d1 >> 6) & 0x1FEu, x3 = (d1 >> 22) & 0x1FEu;
+        if (kCount) {
+            hist_add(hmine, x0 >> 1);
+            hist_add(hmine, x1 >> 1);
+            hist_add(hmine, x2 >> 1);
+            hist_add(hmine, x3 >> 1);
+        }
+        const uint32_t a = code_entry(table, x0) | (code_entry(table, x2) << 16);
+        const uint32_t b = code_entry(table, x1) | (code_entry(table, x3) << 16);
+        r.quad[j] = a | (b << 4);
+        r.count += __popc(r.quad[j] & kFlagBits);
+    }
 #pragma unroll
     for (int h = 0; h < kPackWords / 8; h++)
-        split8(w + 4 * h, r.sm[2 * h], r.sm[2 * h + 1], r.ex[2 * h], r.ex[2 * h + 1]);
-    r.mask = 0;
-#pragma unroll
-    for (int h = 0; h < kPackWords / 8; h++) r.nib[h] = 0;
-#pragma unroll
-    for (int k = 0; k < kPackWords; k++) {
-        const uint32_t code = lut[byte_at(r.ex, k)];
-        r.nib[k >> 3] |= (code & 0xFu) << (4 * (k & 7));
-        r.mask |= (code >> 4) << k;
-    }
+        r.nib[h] = __builtin_amdgcn_perm(r.quad[2 * h + 1], r.quad[2 * h], 0x06040200u);
 }
 
 // Escape records of one pack tile go to their final slots: a lane holds at
@@ -447,6 +481,7 @@ struct EscapeOut {
 // 16-byte aligned so that a wave reads all wave totals with wide LDS loads
 struct alignas(16) PackLds {
     uint32_t wave_escapes[2][kPackWaves];
+    uint16_t code[256];                    // exponent -> table entry (see encode_words)
     uint8_t lut[256];                      // exponent -> code, 0x10 = escape
     uint16_t stage_off[kPackTile];         // tile offset of each staged escape
     uint8_t stage_exp[kPackTile];
@@ -467,20 +502,27 @@ __device__ __forceinline__ void put_escape(const EscapeOut& out, uint64_t slot, 
 }
 
 // Positions are stored modulo 2^32, so their sums are taken in 32 bits.
-__device__ __forceinline__ uint32_t write_escapes(const ThreadWords& r, uint64_t t0,
-                                                  uint64_t slot_base, PackLds& lds, int parity,
-                                                  const EscapeOut& out) {
+// w: the thread's words (for the escaped exponents).
+__device__ __forceinline__ uint32_t write_escapes(const ThreadWords& r, const uint32_t* w,
+                                                  uint64_t t0, uint64_t slot_base, PackLds& lds,
+                                                  int parity, const EscapeOut& out) {
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = t >> 6;
-    const uint32_t mask = r.mask;
-    const uint32_t cnt = __popc(mask);
+    const uint32_t cnt = r.count;
     uint32_t lane_prefix = 0, wave_total = 0;
+    if (__ballot(cnt > 1) == 0) {
+        // at most one escape per lane (the usual case on KV data): one ballot
+        const uint64_t bits = __ballot(cnt != 0);
+        lane_prefix = lanes_below(bits);
+        wave_total = (uint32_t)__popcll(bits);
+    } else {
 #pragma unroll
-    for (int b = 0; b < (kPackWords == 16 ? 5 : 4); b++) {
-        const uint64_t bits = __ballot(cnt & (1u << b));
-        lane_prefix += lanes_below(bits) << b;
-        wave_total += (uint32_t)__popcll(bits) << b;
+        for (int b = 0; b < (kPackWords == 16 ? 5 : 4); b++) {
+            const uint64_t bits = __ballot(cnt & (1u << b));
+            lane_prefix += lanes_below(bits) << b;
+            wave_total += (uint32_t)__popcll(bits) << b;
+        }
     }
     if (lane == 0) lds.wave_escapes[parity][wave] = wave_total;
     __syncthreads();
@@ -493,13 +535,13 @@ __device__ __forceinline__ uint32_t write_escapes(const ThreadWords& r, uint64_t
     }
     const uint32_t first = before + lane_prefix;  // this lane's first rank in the tile
     if (tile_total >= kStageMin) {
-        if (mask) {
+        if (cnt) {
             uint32_t q = first;
 #pragma unroll
             for (int k = 0; k < kPackWords; k++) {
-                if ((mask >> k) & 1u) {
+                if (escaped(r, k)) {
                     lds.stage_off[q] = (uint16_t)(kPackWords * t + k);
-                    lds.stage_exp[q] = (uint8_t)byte_at(r.ex, k);
+                    lds.stage_exp[q] = (uint8_t)exponent_of(w, k);
                     q++;
                 }
             }
@@ -507,13 +549,13 @@ __device__ __forceinline__ uint32_t write_escapes(const ThreadWords& r, uint64_t
         __syncthreads();
         for (uint32_t q = t; q < tile_total; q += kPackThreads)
             put_escape(out, slot_base + q, (uint32_t)t0 + lds.stage_off[q], lds.stage_exp[q]);
-    } else if (mask) {
+    } else if (cnt) {
         uint64_t slot = slot_base + first;
 #pragma unroll
         for (int k = 0; k < kPackWords; k++) {
-            if ((mask >> k) & 1u) {
+            if (escaped(r, k)) {
                 put_escape(out, slot, (uint32_t)t0 + (uint32_t)(kPackWords * t + k),
-                           byte_at(r.ex, k));
+                           exponent_of(w, k));
                 slot++;
             }
         }
@@ -522,14 +564,16 @@ __device__ __forceinline__ uint32_t write_escapes(const ThreadWords& r, uint64_t
 }
 
 // One whole tile: thread t packs words t0 + kPackWords*t onwards, loaded in
-// w; returns the tile's escape count.
-template <bool kAlignedSm>
-__device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0, const uint8_t* lut,
-                                              uint8_t* nib, uint8_t* sm, uint64_t slot_base,
-                                              PackLds& lds, int parity, const EscapeOut& esc) {
+// w (with kCount also counting their exponents into hmine); returns the
+// tile's escape count.
+template <bool kAlignedSm, bool kCount>
+__device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0,
+                                              const uint16_t* table, uint8_t* nib, uint8_t* sm,
+                                              uint64_t slot_base, PackLds& lds, int parity,
+                                              const EscapeOut& esc, uint32_t* hmine) {
     const uint64_t i0 = t0 + (uint64_t)threadIdx.x * kPackWords;
     ThreadWords r;
-    encode_words(w, lut, r);
+    encode_words<kCount>(w, table, r, hmine);
     if constexpr (kPackWords == 16) {
         *reinterpret_cast<uint2*>(nib + i0 / 2) = make_uint2(r.nib[0], r.nib[1]);
     } else {
@@ -544,7 +588,7 @@ __device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0, co
 #pragma unroll
         for (int k = 0; k < kPackWords; k++) sm[i0 + k] = (uint8_t)byte_at(r.sm, k);
     }
-    return write_escapes(r, t0, slot_base, lds, parity, esc);
+    return write_escapes(r, w, t0, slot_base, lds, parity, esc);
 }
 
 // The pack kernel serves two passes:
@@ -574,16 +618,24 @@ __device__ __forceinline__ EscapeOut final_slots(uint8_t* dst, uint64_t n, uint6
     return esc;
 }
 
-// Exact exponent -> code table (0x10 = escape) from the header's codebook;
-// the caller synchronises before using it.
-__device__ __forceinline__ void exact_code_table(const uint8_t* dst, uint8_t* lut) {
+// Exact exponent -> code tables from the header's codebook: lds.lut (0x10 =
+// escape) and lds.code (encode_words' entries); the caller synchronises
+// before using them.
+__device__ __forceinline__ void exact_code_table(const uint8_t* dst, PackLds& lds) {
     const int t = threadIdx.x;
-    if (t < 256) lut[t] = 0x10;
+    if (t < 256) {
+        lds.lut[t] = 0x10;
+        lds.code[t] = kEscapeEntry;
+    }
     __syncthreads();
-    if (t < 16) lut[dst[kHeaderBytes + t]] = (uint8_t)t;
+    if (t < 16) {
+        const uint8_t e = dst[kHeaderBytes + t];
+        lds.lut[e] = (uint8_t)t;
+        lds.code[e] = (uint16_t)t;
+    }
 }
 
-// Packs words [begin, end) with the code table in lds.lut, escape records to
+// Packs words [begin, end) with the code table in lds.code, escape records to
 // esc from slot slot_base on; with kCount, every exponent is also counted
 // into hmine, and with write false only that.  parity selects the next
 // tile's wave-total buffer and carries over from chunk to chunk when one
@@ -594,7 +646,7 @@ __device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t b
                                                uint64_t slot_base, bool write, uint32_t* hmine,
                                                PackLds& lds, int& parity) {
     const int t = threadIdx.x;
-    const uint8_t* lut = lds.lut;
+    const uint16_t* table = lds.code;
     uint8_t* nib = dst + kPrefixBytes;
     uint8_t* sm = nib + (n + 1) / 2;
     const uint64_t first_slot = slot_base;
@@ -604,7 +656,8 @@ __device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t b
         count_exponents<kPackThreads>(src, begin, end, hmine);
         t0 = end;
     }
-    // whole tiles, no per-word checks
+    // whole tiles, no per-word checks (with kCount, only entered when the
+    // streams are written: the exponents are counted while packing)
     for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
         // a tile lies inside one page
         const uint4* p = reinterpret_cast<const uint4*>(src.at(t0) + (uint64_t)t * kPackWords);
@@ -617,15 +670,8 @@ __device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t b
             w[4 * h + 2] = v.z;
             w[4 * h + 3] = v.w;
         }
-        if (kCount) {
-#pragma unroll
-            for (int j = 0; j < kPackWords / 2; j++) {
-                hist_add(hmine, (w[j] >> 7) & 0xFFu);
-                hist_add(hmine, (w[j] >> 23) & 0xFFu);
-            }
-        }
-        if (!kCount || write)
-            slot_base += pack_tile<kAlignedSm>(w, t0, lut, nib, sm, slot_base, lds, parity, esc);
+        slot_base += pack_tile<kAlignedSm, kCount>(w, t0, table, nib, sm, slot_base, lds, parity,
+                                                   esc, hmine);
     }
     // the ragged last tile of the input (last chunk only); every index below
     // is a compile-time constant after unrolling, so nothing leaves registers
@@ -647,20 +693,26 @@ __device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t b
         }
         if (!kCount || write) {
             ThreadWords r;
-            encode_words(w, lut, r);
+            encode_words<false>(w, table, r, nullptr);
             // words past the end have no code (the pad nibble of an odd n is
             // 0) and are no escapes
-            r.mask &= (1u << valid) - 1u;  // valid <= 16
+            r.count = 0;
 #pragma unroll
-            for (int k = 0; k < kPackWords; k++)
-                if (k >= (int)valid) r.nib[k >> 3] &= ~(0xFu << (4 * (k & 7)));
+            for (int k = 0; k < kPackWords; k++) {
+                if (k >= (int)valid) {
+                    r.nib[k >> 3] &= ~(0xFu << (4 * (k & 7)));
+                    r.quad[k >> 2] &= ~(1u << flag_shift(k & 3));
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < kPackWords / 4; j++) r.count += __popc(r.quad[j] & kFlagBits);
 #pragma unroll
             for (int j = 0; j < kPackWords / 2; j++)
                 if (2 * j < (int)valid) nib[i0 / 2 + j] = (uint8_t)byte_at(r.nib, j);
 #pragma unroll
             for (int k = 0; k < kPackWords; k++)
                 if (k < (int)valid) sm[i0 + k] = (uint8_t)byte_at(r.sm, k);
-            slot_base += write_escapes(r, t0, slot_base, lds, parity, esc);
+            slot_base += write_escapes(r, w, t0, slot_base, lds, parity, esc);
         }
         parity ^= 1;
     }
@@ -693,7 +745,11 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
         // the provisional code table the sample pass left; the streams are
         // written only when the sample predicts few escapes, otherwise this
         // pass only counts and the finish pass packs
-        if (t < 256) lds.lut[t] = area->lut[t];
+        if (t < 256) {
+            const uint8_t c = area->lut[t];
+            lds.lut[t] = c;
+            lds.code[t] = c < 16 ? (uint16_t)c : kEscapeEntry;
+        }
         write = area->spec_on != 0;
         for (int i = t; i < kSpecCopies * kSpecPitch; i += kPackThreads) hist[i] = 0;
         hmine = hist + (t % kSpecCopies) * kSpecPitch;
@@ -704,7 +760,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
         esc.pos_aligned = true;
         slot_base = 0;
     } else {
-        exact_code_table(dst, lds.lut);
+        exact_code_table(dst, lds);
         esc = final_slots(dst, n, dst_capacity);
         slot_base = chunk_base[chunk];
     }
@@ -786,7 +842,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
         if (same_order) return;
 
         uint8_t* lut = lds.lut;
-        exact_code_table(dst, lut);
+        exact_code_table(dst, lds);
         __syncthreads();
         if (t < 256)
             remap[t] = (uint8_t)((lut[area->cb[t & 15]] & 0xF) |
@@ -834,7 +890,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
         return;
     }
 
-    exact_code_table(dst, lds.lut);
+    exact_code_table(dst, lds);
     __syncthreads();
     int parity = 0;
     for (uint32_t c = blockIdx.x; c < chunks; c += gridDim.x) {

@@ -7,7 +7,8 @@
 //              asc), write header + codebook, and turn every chunk's counts
 //              into its exact escape count and first escape slot
 //   pack       one workgroup per chunk: 16-byte loads, 256-entry exponent
-//              -> code table in LDS, 4-bit codes two per byte, sign|mantissa
+//              -> code table in LDS whose 16-bit entries combine four at a
+//              time into two nibble bytes and four escape flags, sign|mantissa
 //              bytes, ballot/popcount escape ranks, escapes written straight
 //              to their final slots in ascending position order
 //
@@ -747,7 +748,6 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
         // pass only counts and the finish pass packs
         if (t < 256) {
             const uint8_t c = area->lut[t];
-            lds.lut[t] = c;
             lds.code[t] = c < 16 ? (uint16_t)c : kEscapeEntry;
         }
         write = area->spec_on != 0;

@@ -224,7 +224,7 @@ sz_status sz_decode_dense(const void *d_src, uint64_t src_bytes, void *d_dst,
 /* Decode in a single pass with the words handed out grid-stride, in two
  * calls over a caller workspace of sz_decode_workspace_size(n) bytes
  * (256-byte aligned, not overlapping the container or the output).
- * sz_decode_index records, for every 4096-word tile, the first escape
+ * sz_decode_index records, for every 8192-word tile, the first escape
  * record at or after the tile's start, and checks the header and that the
  * records ascend below n; sz_decode_tiles then has a few workgroups per CU
  * take tiles b, b + grid, ..., mark each tile's records in an LDS exponent

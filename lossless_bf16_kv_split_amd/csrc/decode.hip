@@ -504,16 +504,16 @@ hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t 
 
 // ------------------------------------------------------------------------
 // Tile decode: the single pass with the words handed out grid-stride.  A
-// first kernel indexes the escape stream by 4096-word tile (the first record
+// first kernel indexes the escape stream by 8192-word tile (the first record
 // of every tile) and checks the header and the records' order; then a grid
-// of a few workgroups per CU walks the tiles b, b + gridDim.x, ..., so that
+// of two workgroups per CU walks the tiles b, b + gridDim.x, ..., so that
 // the resident workgroups stream one region of memory together instead of
-// one contiguous range each (on MI355X: 343 us against 375 us for the 1 GiB
-// KV tensor).
+// one contiguous range each (on MI355X: 336-346 us against 375 us for the
+// 1 GiB KV tensor).
 
 constexpr int kIndexThreads = 256;
 constexpr int kTileThreads = kTileWords / 8;    // 8 words per thread and tile
-constexpr uint32_t kTileGroupsPerCu = 4;
+constexpr uint32_t kTileGroupsPerCu = 2;  // 16-wave workgroups: 8 waves per SIMD
 
 // One workgroup per kIndexTiles consecutive tiles.  Record k is the first of
 // the tiles after its predecessor's tile up to its own; the tiles after the

@@ -108,10 +108,14 @@ constexpr uint64_t kScatterDecodeDensity = 256;
 constexpr uint64_t kTileDecodeMin = uint64_t{1} << 26;
 
 // Tile decode (the single pass with words handed out grid-stride): its
-// workspace holds the first escape record of every 4096-word tile and one
-// flag per index workgroup (64 tiles each).
-constexpr uint32_t kTileWords = 4096;
-constexpr uint32_t kIndexTiles = 64;
+// workspace holds the first escape record of every 8192-word tile and one
+// flag per index workgroup (32 tiles each).  Measured on MI355X (1 GiB KV
+// round trip, one process): 8192-word tiles with two workgroups per CU
+// decode in 336-338 us against 345 us for 4096-word tiles with four, 363 us
+// for 2048-word tiles with eight; 32 tiles per index workgroup keep the
+// index pass at 13.6 us (64: 16.5 us).
+constexpr uint32_t kTileWords = 8192;
+constexpr uint32_t kIndexTiles = 32;
 struct TileIndexLayout {
     uint64_t tiles = 0;     // ceil(n / kTileWords)
     uint64_t blocks = 0;    // index workgroups, at least 1

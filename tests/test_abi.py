@@ -151,9 +151,9 @@ def test_single_read_host_checks(sz):
 
 
 def test_tile_decode_host_checks(sz):
-    for n in (0, 1, 4096, 4097, 1 << 29):
-        tiles = -(-n // 4096)
-        blocks = max(1, -(-tiles // 64))
+    for n in (0, 1, 8192, 8193, 1 << 29):
+        tiles = -(-n // 8192)
+        blocks = max(1, -(-tiles // 32))
         want = -(-(-(-8 * (tiles + 1) // 256) * 256 + 4 * blocks) // 256) * 256
         assert sz.sz_decode_workspace_size(n) == want, n
     assert sz.sz_decode_workspace_size((1 << 36) + 1) == 0

@@ -225,15 +225,9 @@ hipError_t launch_scatter(const uint8_t* src, uint64_t n, uint64_t e, Words dst,
 // Fused decode: unpack and escape overwrite in one pass, so every word is
 // written once.  One workgroup per power-of-two range of words.
 
-#ifndef SZ_FUSED_THREADS
-#define SZ_FUSED_THREADS 512
-#endif
-#ifndef SZ_FUSED_BATCH_PER_THREAD
-#define SZ_FUSED_BATCH_PER_THREAD 2
-#endif
-constexpr int kFusedThreads = SZ_FUSED_THREADS;
+constexpr int kFusedThreads = 512;
 constexpr uint32_t kFusedTile = kFusedThreads * 8;   // words per workgroup step
-constexpr int kBatchPerThread = SZ_FUSED_BATCH_PER_THREAD;
+constexpr int kBatchPerThread = 2;
 static_assert(kBatchPerThread >= 1 && kBatchPerThread <= 4, "prefetched exponents share one register");
 constexpr uint32_t kBatch = kFusedThreads * kBatchPerThread;  // escape records in LDS
 constexpr uint32_t kNoSlot = 0xFFFFFFFFu;

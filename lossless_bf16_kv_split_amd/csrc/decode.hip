@@ -645,6 +645,11 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_tiles(
     for (uint64_t tile = blockIdx.x; tile < whole; tile += gridDim.x, parity ^= 1) {
         const uint64_t t0 = tile * kTileWords;
         const uint64_t i0 = t0 + (uint64_t)t * 8;
+        // a wave's words are 512 consecutive words: one page, whose address
+        // (a page-table load for a paged tensor) is looked up before the
+        // tile's loads so that its latency overlaps theirs
+        uint16_t* words_out = nullptr;
+        if constexpr (Words::kPaged) words_out = out.at_wave(i0);
         const uint32_t codes = *reinterpret_cast<const uint32_t*>(nib + i0 / 2);
         uint32_t s0, s1;
         if (kAlignedSm) {
@@ -663,12 +668,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_tiles(
             e0 = bitselect(bits_to_bytes(present), pe.x, e0);
             e1 = bitselect(bits_to_bytes(present >> 4), pe.y, e1);
         }
-        // A wave's words are 512 consecutive words: one page.  The tensor is
-        // larger than the caches (this form runs from 2^26 words), so its
-        // lines are written past them: none is left dirty for the next
-        // kernel to write back (on MI355X the encode that follows a 1 GiB
-        // decode ran 24 us faster, the decode itself 4 us slower).
-        store_streaming(reinterpret_cast<uint4*>(out.at_wave(i0)), words8(e0, e1, s0, s1));
+        // The tensor is larger than the caches (this form runs from 2^26
+        // words), so its lines are written past them: none is left dirty for
+        // the next kernel to write back (on MI355X the encode that follows a
+        // 1 GiB decode ran 24 us faster, the decode itself 4 us slower).
+        if constexpr (!Words::kPaged) words_out = out.at_wave(i0);
+        store_streaming(reinterpret_cast<uint4*>(words_out), words8(e0, e1, s0, s1));
     }
     // the last, partial tile, by the workgroup whose turn it is
     if (whole < tiles && blockIdx.x == whole % gridDim.x) {

@@ -149,6 +149,7 @@ inline uint64_t container_bytes(uint64_t n, uint64_t e) {
 // (a wave's 64 consecutive 8-word groups, 512-word aligned): the page is
 // then looked up once per wave, through a scalar load.
 struct FlatWords {
+    static constexpr bool kPaged = false;
     uint16_t* base;
     __device__ __forceinline__ bool invalid() const { return false; }
     __device__ __forceinline__ uint16_t* at(uint64_t i) const { return base + i; }
@@ -159,6 +160,7 @@ struct FlatWords {
 constexpr uint32_t kMinPageLog2 = 14;
 
 struct PagedWords {
+    static constexpr bool kPaged = true;  // at() and at_wave() read the page table
     uint16_t* const* pages;   // device table of page addresses
     uint32_t page_log2;
     const int32_t* bad;       // nonzero: the table failed its check, touch no page

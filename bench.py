@@ -311,8 +311,8 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: the codec runs on a single MI355X and this "
-              "build has no multi-GPU path (use --gpus 1).", file=sys.stderr)
+        print("bench.py measures one GPU: the codec runs on a single MI355X and has no "
+              "multi-GPU path (use --gpus 1).", file=sys.stderr)
         return 2
 
     import numpy as np

@@ -215,3 +215,56 @@ def test_single_read_pages(torch, sz, case, n, page):
     torch.cuda.synchronize()
     assert int(status.item()) == 0, label
     assert np.array_equal(gather_pages(out_pool, out_order, n, page), words), label
+
+
+def narrow_words(case: str, n: int) -> np.ndarray:
+    """Ten exponents and no escapes.  "copy": exponent 110 + j drawn with
+    weight 10 - j, so that the sample ranks them as the whole input does;
+    "remap": equal weights, ranked otherwise by the sample; "full:set": as
+    "remap", and exponent 200 too, but only in words the sample does not
+    read, so the sampled codebook lacks an exponent the exact one holds."""
+    if case == "copy":
+        w = pattern(n, 70, [110 + j for j in range(10) for _ in range(10 - j)], 0.0)
+    else:
+        w = pattern(n, 70, list(range(110, 120)), 0.0)
+    if case == "full:set":
+        in_sample = np.zeros(n, dtype=bool)
+        for s in sample_starts(n):
+            in_sample[s:s + SAMPLE_BLOCK_WORDS] = True
+        rng = np.random.default_rng([71, n])
+        hit = ~in_sample & (rng.random(n) < 0.001)
+        w = np.where(hit, (w & np.uint16(0x807F)) | np.uint16(200 << 7), w).astype(np.uint16)
+    return w
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("case,n", [("copy", (1 << 22) + 9), ("remap", (1 << 22) + 9),
+                                    ("full:set", (1 << 22) + 9), ("copy", (1 << 26) + 3),
+                                    ("remap", 1 << 26), ("full:set", (1 << 26) + 1)])
+def test_single_read_no_escapes(torch, sz, case, n):
+    """Fewer than 16 distinct exponents: no escape records, and a codebook
+    filled up with exponents of count 0 in ascending order.  The staged
+    single-read passes and sz_encode must give the oracle's container, and
+    the tile decode (sz_decode's choice from 2^26 words) an index of empty
+    tiles that decodes back to the input."""
+    from test_gpu_parity import gpu_decode
+    label = f"no escapes {case} n={n}"
+    say(label)
+    words = narrow_words(case, n)
+    assert expected_case(words) == case, label
+    want = oracle.encode(words)
+    assert int(want[16:24].view(np.uint64)[0]) == 0, label  # E in the header
+    x = torch.from_numpy(words.view(np.int16)).cuda()
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.full((cap,), 0x77, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    single_read_encode(torch, sz, x, n, dst, cap, size)
+    total = int(size.item())
+    assert total == want.size and np.array_equal(dst[:total].cpu().numpy(), want), label
+    got = sz.encode(x).cpu().numpy()
+    assert got.size == want.size and np.array_equal(got, want), label
+    container = torch.from_numpy(want).cuda()
+    for form in ("auto", "tiles"):
+        y, status, guard_ok = gpu_decode(torch, sz, container, n, form)
+        assert status == 0 and guard_ok, (label, form)
+        assert torch.equal(y, x), (label, form)

@@ -48,7 +48,23 @@ KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select
                 "unpack": "k_unpack", "scatter": "k_scatter"}
 # the sample of the single-read encode: 512 blocks of 2048 words
 SAMPLE_BLOCKS, SAMPLE_BLOCK_WORDS = 512, 2048
-MIN_CHUNK_LOG2, MAX_CHUNKS = 14, 2048
+MIN_CHUNK_LOG2, PLAN_CHUNKS, RESIDENT_PACK_GROUPS = 14, 2048, 512
+
+
+def chunk_log2(n: int) -> int:
+    """The encode's chunk size (log2 words): the smallest giving at most 2048
+    chunks, halved when that leaves less than 1/50 more of the pack grid's
+    last wave of resident workgroups idle."""
+    c = MIN_CHUNK_LOG2
+    while -(-n >> c) > PLAN_CHUNKS:
+        c += 1
+    if c > MIN_CHUNK_LOG2:
+        g0, g1 = -(-n >> c), -(-n >> (c - 1))
+        s0 = -(-g0 // RESIDENT_PACK_GROUPS) * RESIDENT_PACK_GROUPS
+        s1 = -(-g1 // RESIDENT_PACK_GROUPS) * RESIDENT_PACK_GROUPS
+        if 50 * (s1 - g1) * s0 + s1 * s0 < 50 * (s0 - g0) * s1:
+            c -= 1
+    return c
 # sz_decode's forms: the tile decode from TILE_DECODE_MIN words with up to one
 # escape in TILE_DECODE_DENSITY words; below TILE_DECODE_MIN words, unpack then
 # scatter up to one escape in SCATTER_DECODE_DENSITY; else the dense decode
@@ -146,9 +162,7 @@ def single_read_case(words, codebook) -> str:
         return "full:sample"
     if set(prov) != set(codebook):
         return "full:set"
-    c = MIN_CHUNK_LOG2
-    while -(-n >> c) > MAX_CHUNKS:
-        c += 1
+    c = chunk_log2(n)
     esc_lut = np.ones(256, dtype=np.uint8)
     esc_lut[prov] = 0
     per_chunk = np.add.reduceat(esc_lut[(words >> 7) & 0xFF].astype(np.uint32),

@@ -42,7 +42,18 @@ EncodePlan plan_encode(uint64_t n) {
     EncodePlan p;
     p.n = n;
     uint32_t c = kMinChunkLog2;
-    while (c < 40 && ((n + (1ull << c) - 1) >> c) > kMaxChunks) c++;
+    while (c < 40 && ((n + (1ull << c) - 1) >> c) > kPlanChunks) c++;
+    // The pack kernels give each workgroup one chunk, so a grid that ends in
+    // a partly filled wave leaves CUs idle at its end (on MI355X, 1280 chunks
+    // of 2^22 words ran the first pass 6% below the per-byte rate of 2048
+    // chunks).  Halve the chunk when the idle share of the slots
+    // (slots - G) / slots drops by more than 1/50 -- integer form of that test.
+    if (c > kMinChunkLog2) {
+        const uint64_t g0 = (n + (1ull << c) - 1) >> c, g1 = (n + (1ull << (c - 1)) - 1) >> (c - 1);
+        const uint64_t s0 = (g0 + kResidentPackGroups - 1) / kResidentPackGroups * kResidentPackGroups;
+        const uint64_t s1 = (g1 + kResidentPackGroups - 1) / kResidentPackGroups * kResidentPackGroups;
+        if (50 * (s1 - g1) * s0 + s1 * s0 < 50 * (s0 - g0) * s1) c--;
+    }
     p.chunk_log2 = c;
     p.chunks = (uint32_t)((n + (1ull << c) - 1) >> c);
     auto align = [](uint64_t x) { return (x + 255) & ~255ull; };
@@ -220,6 +231,7 @@ __global__ __launch_bounds__(kMergeThreads) void k_merge_counts(const uint32_t* 
 
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
+constexpr int kSelectChunks = kMaxChunks / kSelectThreads;  // chunks per select thread
 
 __device__ __forceinline__ uint64_t wave_inclusive_sum(uint64_t v) {
     const int lane = threadIdx.x & 63;
@@ -269,39 +281,50 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     }
     __syncthreads();
 
-    // escapes of chunks 2t and 2t+1 = chunk length - elements whose
-    // exponent is in the codebook
+    // thread t takes chunks per * t .. per * t + per - 1 (per is the same
+    // for the whole workgroup), two at a time: the escapes of a chunk =
+    // chunk length - elements whose exponent is in the codebook.  Up to
+    // 2048 chunks this is one round of loads; two rounds keep the counts of
+    // up to four chunks from spilling.  (The codebook is the same in every
+    // lane: scalar row addresses.)
     uint32_t cb[16];
 #pragma unroll
-    for (int c = 0; c < 16; c++) cb[c] = codebook[c] & 255u;
-    // chunks 2t and 2t+1: their 16 codebook counts, coalesced across threads
-    // (bin-major layout), all in flight at once
-    uint32_t v[2][16];
+    for (int c = 0; c < 16; c++) cb[c] = __builtin_amdgcn_readfirstlane(codebook[c] & 255u);
+    const uint32_t per = (chunks + kSelectThreads - 1) / kSelectThreads;  // <= kSelectChunks
+    uint64_t esc[kSelectChunks] = {};
 #pragma unroll
-    for (int c = 0; c < 16; c++) {
-        const uint32_t* row = counts + (uint64_t)cb[c] * chunks;
+    for (int r = 0; r < kSelectChunks / 2; r++) {
+        if ((uint32_t)(2 * r) >= per) break;
+        // the two chunks' 16 codebook counts, coalesced across threads
+        // (bin-major layout), all in flight at once
+        uint32_t v[2][16];
 #pragma unroll
-        for (int j = 0; j < 2; j++) {
-            const uint32_t b = 2 * t + j;
-            v[j][c] = b < chunks ? row[b] : 0u;
+        for (int c = 0; c < 16; c++) {
+            const uint32_t* row = counts + (uint64_t)cb[c] * chunks;
+#pragma unroll
+            for (int jj = 0; jj < 2; jj++) {
+                const uint32_t j = 2 * r + jj, b = per * t + j;
+                v[jj][c] = j < per && b < chunks ? row[b] : 0u;
+            }
         }
-    }
-    uint64_t esc[2] = {0, 0};
 #pragma unroll
-    for (int j = 0; j < 2; j++) {
-        const uint32_t b = 2 * t + j;
-        if (b < chunks) {
-            const uint64_t start = (uint64_t)b << chunk_log2;
-            const uint64_t len = min_u64(uint64_t{1} << chunk_log2, n - start);
-            uint64_t kept = 0;
+        for (int jj = 0; jj < 2; jj++) {
+            const uint32_t j = 2 * r + jj, b = per * t + j;
+            if (j < per && b < chunks) {
+                const uint64_t start = (uint64_t)b << chunk_log2;
+                const uint64_t len = min_u64(uint64_t{1} << chunk_log2, n - start);
+                uint64_t kept = 0;
 #pragma unroll
-            for (int c = 0; c < 16; c++) kept += v[j][c];
-            esc[j] = len - kept;
+                for (int c = 0; c < 16; c++) kept += v[jj][c];
+                esc[2 * r + jj] = len - kept;
+            }
         }
     }
 
     // exclusive scan of the per-chunk escape counts over the workgroup
-    const uint64_t mine = esc[0] + esc[1];
+    uint64_t mine = 0;
+#pragma unroll
+    for (int j = 0; j < kSelectChunks; j++) mine += esc[j];
     const uint64_t incl = wave_inclusive_sum(mine);
     const int lane = t & 63, wave = t >> 6;
     if (lane == 63) wave_sum[wave] = incl;
@@ -314,14 +337,15 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
         }
     }
     __syncthreads();
-    const uint64_t excl = wave_off[wave] + incl - mine;
-    if (2 * t < chunks) {
-        chunk_base[2 * t] = excl;
-        base_lds[2 * t] = excl;
-    }
-    if (2 * t + 1 < chunks) {
-        chunk_base[2 * t + 1] = excl + esc[0];
-        base_lds[2 * t + 1] = excl + esc[0];
+    uint64_t excl = wave_off[wave] + incl - mine;
+#pragma unroll
+    for (int j = 0; j < kSelectChunks; j++) {
+        const uint32_t b = per * t + j;
+        if ((uint32_t)j < per && b < chunks) {
+            chunk_base[b] = excl;
+            base_lds[b] = excl;
+        }
+        excl += esc[j];
     }
     const uint64_t E = wave_off[kSelectWaves - 1] + wave_sum[kSelectWaves - 1];
     __syncthreads();
@@ -373,7 +397,7 @@ static_assert(kPackWords == 8 || kPackWords == 16, "one or two 16-byte loads per
 static_assert((1u << kMinChunkLog2) % kPackTile == 0, "chunks hold whole tiles");
 static_assert(kPackTile <= 65536, "tile offsets fit in 16 bits");
 static_assert(kPackThreads >= 256, "one LUT entry per thread");
-static_assert(2 * kSelectThreads >= kMaxChunks, "two chunks per select thread");
+static_assert(kSelectChunks * kSelectThreads == kMaxChunks, "whole chunks per select thread");
 
 // Rank of this lane's bits among lower lanes: popcount of mask below lane.
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
@@ -822,7 +846,8 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
 
     if (usable && same_set) {
         const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
-        uint64_t* base = reinterpret_cast<uint64_t*>(lds.stage_off);  // chunks <= 2048
+        static_assert(sizeof(lds.stage_off) >= kMaxChunks * sizeof(uint64_t), "chunk bases fit");
+        uint64_t* base = reinterpret_cast<uint64_t*>(lds.stage_off);
         for (uint32_t c = t; c < chunks; c += kPackThreads) base[c] = chunk_base[c];
         __syncthreads();
         const uint32_t* spos = reinterpret_cast<const uint32_t*>(dst + scratch_pos);

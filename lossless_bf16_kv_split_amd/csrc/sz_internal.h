@@ -19,9 +19,16 @@ constexpr uint64_t kMaxElements = 1ull << 36;
 // counts exponents per chunk, the codebook pass turns those counts into the
 // exact number of escapes of every chunk (and so into each chunk's first
 // escape slot), and the pack pass lets one workgroup stream one chunk.
-// A chunk holds whole pack tiles and the grid is at most kMaxChunks.
+// A chunk holds whole pack tiles.  The plan takes the smallest chunk that
+// gives at most kPlanChunks chunks, or half of it (then at most kMaxChunks
+// chunks) when that leaves less of the pack grid's last wave of resident
+// workgroups idle.
 constexpr uint32_t kMinChunkLog2 = 14;
-constexpr uint32_t kMaxChunks = 2048;
+constexpr uint32_t kPlanChunks = 2048;
+constexpr uint32_t kMaxChunks = 2 * kPlanChunks;
+// pack workgroups (1024 threads, 8 waves per SIMD) resident at once on
+// MI355X: 256 CUs x 2
+constexpr uint64_t kResidentPackGroups = 512;
 
 struct EncodePlan {
     uint64_t n = 0;

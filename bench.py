@@ -53,8 +53,9 @@ MIN_CHUNK_LOG2, PLAN_CHUNKS, RESIDENT_PACK_GROUPS = 14, 2048, 512
 
 def chunk_log2(n: int) -> int:
     """The encode's chunk size (log2 words): the smallest giving at most 2048
-    chunks, halved when that leaves less than 1/50 more of the pack grid's
-    last wave of resident workgroups idle."""
+    chunks, halved when that cuts the idle share of the pack grid's last wave
+    of resident workgroups by more than 1/50, or gives more than 3072 chunks,
+    a multiple of 4."""
     c = MIN_CHUNK_LOG2
     while -(-n >> c) > PLAN_CHUNKS:
         c += 1
@@ -62,7 +63,7 @@ def chunk_log2(n: int) -> int:
         g0, g1 = -(-n >> c), -(-n >> (c - 1))
         s0 = -(-g0 // RESIDENT_PACK_GROUPS) * RESIDENT_PACK_GROUPS
         s1 = -(-g1 // RESIDENT_PACK_GROUPS) * RESIDENT_PACK_GROUPS
-        if 50 * (s1 - g1) * s0 + s1 * s0 < 50 * (s0 - g0) * s1:
+        if 50 * (s1 - g1) * s0 + s1 * s0 < 50 * (s0 - g0) * s1 or (g1 > 3072 and g1 % 4 == 0):
             c -= 1
     return c
 # sz_decode's forms: the tile decode from TILE_DECODE_MIN words with up to one

@@ -74,7 +74,7 @@ typedef enum {
 uint64_t sz_max_compressed_size(uint64_t n_elements);
 
 /* Bytes of device workspace the staged encode calls need for n elements
- * (at most about 3.8 MB).  Host-only. */
+ * (at most about 4.3 MB).  Host-only. */
 uint64_t sz_workspace_size(uint64_t n_elements);
 
 /* Compress n BF16 words at d_src into the container format above at d_dst.

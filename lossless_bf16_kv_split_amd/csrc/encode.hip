@@ -43,16 +43,23 @@ EncodePlan plan_encode(uint64_t n) {
     p.n = n;
     uint32_t c = kMinChunkLog2;
     while (c < 40 && ((n + (1ull << c) - 1) >> c) > kPlanChunks) c++;
-    // The pack kernels give each workgroup one chunk, so a grid that ends in
-    // a partly filled wave leaves CUs idle at its end (on MI355X, 1280 chunks
-    // of 2^22 words ran the first pass 6% below the per-byte rate of 2048
-    // chunks).  Halve the chunk when the idle share of the slots
-    // (slots - G) / slots drops by more than 1/50 -- integer form of that test.
+    // Halve the chunk (on MI355X):
+    //  - when that fills the pack grid's last wave better: the pack kernels
+    //    give each workgroup one chunk, so a grid ending in a partly filled
+    //    wave leaves CUs idle (1280 chunks of 2^22 words ran the first pass
+    //    6% below the per-byte rate of 2048 chunks).  Test: the idle share of
+    //    the slots, (slots - G) / slots, drops by more than 1/50;
+    //  - when the halved plan has more than 3072 chunks, a multiple of 4: the
+    //    select then reads four chunks' counts per load, as fast as it reads
+    //    2048 chunks, and the smaller chunks stream faster (1 GiB tensor:
+    //    first pass 370 -> 359 us with 4096 chunks of 2^17 words).
     if (c > kMinChunkLog2) {
         const uint64_t g0 = (n + (1ull << c) - 1) >> c, g1 = (n + (1ull << (c - 1)) - 1) >> (c - 1);
         const uint64_t s0 = (g0 + kResidentPackGroups - 1) / kResidentPackGroups * kResidentPackGroups;
         const uint64_t s1 = (g1 + kResidentPackGroups - 1) / kResidentPackGroups * kResidentPackGroups;
-        if (50 * (s1 - g1) * s0 + s1 * s0 < 50 * (s0 - g0) * s1) c--;
+        const bool fills = 50 * (s1 - g1) * s0 + s1 * s0 < 50 * (s0 - g0) * s1;
+        const bool wide_select = g1 > 3 * kMaxChunks / 4 && g1 % 4 == 0;
+        if (fills || wide_select) c--;
     }
     p.chunk_log2 = c;
     p.chunks = (uint32_t)((n + (1ull << c) - 1) >> c);
@@ -282,41 +289,70 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
     __syncthreads();
 
     // thread t takes chunks per * t .. per * t + per - 1 (per is the same
-    // for the whole workgroup), two at a time: the escapes of a chunk =
-    // chunk length - elements whose exponent is in the codebook.  Up to
-    // 2048 chunks this is one round of loads; two rounds keep the counts of
-    // up to four chunks from spilling.  (The codebook is the same in every
-    // lane: scalar row addresses.)
+    // for the whole workgroup): the escapes of a chunk = chunk length -
+    // elements whose exponent is in the codebook.  Four chunks a thread,
+    // 16-byte aligned, are read with 16-byte loads; otherwise two chunks per
+    // round of loads (one round up to 2048 chunks; two keep the counts of up
+    // to four chunks from spilling).  The codebook is the same in every lane:
+    // scalar row addresses.
     uint32_t cb[16];
 #pragma unroll
     for (int c = 0; c < 16; c++) cb[c] = __builtin_amdgcn_readfirstlane(codebook[c] & 255u);
     const uint32_t per = (chunks + kSelectThreads - 1) / kSelectThreads;  // <= kSelectChunks
     uint64_t esc[kSelectChunks] = {};
+    if (per == 4 && chunks % 4 == 0) {
+        // four contiguous chunks per thread, 16-byte aligned: one 16-byte
+        // load per codebook row, the rows in two halves of eight
+        const uint32_t b0 = 4 * t;
+        if (b0 < chunks) {
+            uint32_t kept[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int r = 0; r < kSelectChunks / 2; r++) {
-        if ((uint32_t)(2 * r) >= per) break;
-        // the two chunks' 16 codebook counts, coalesced across threads
-        // (bin-major layout), all in flight at once
-        uint32_t v[2][16];
+            for (int h = 0; h < 2; h++) {
+                uint4 v[8];
 #pragma unroll
-        for (int c = 0; c < 16; c++) {
-            const uint32_t* row = counts + (uint64_t)cb[c] * chunks;
+                for (int c = 0; c < 8; c++)
+                    v[c] = *reinterpret_cast<const uint4*>(counts + (uint64_t)cb[8 * h + c] * chunks + b0);
+#pragma unroll
+                for (int c = 0; c < 8; c++) {
+                    kept[0] += v[c].x;
+                    kept[1] += v[c].y;
+                    kept[2] += v[c].z;
+                    kept[3] += v[c].w;
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < 4; j++) {
+                const uint64_t start = (uint64_t)(b0 + j) << chunk_log2;
+                esc[j] = min_u64(uint64_t{1} << chunk_log2, n - start) - kept[j];
+            }
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < kSelectChunks / 2; r++) {
+            if ((uint32_t)(2 * r) >= per) break;
+            // the two chunks' 16 codebook counts, coalesced across threads
+            // (bin-major layout), all in flight at once
+            uint32_t v[2][16];
+#pragma unroll
+            for (int c = 0; c < 16; c++) {
+                const uint32_t* row = counts + (uint64_t)cb[c] * chunks;
+#pragma unroll
+                for (int jj = 0; jj < 2; jj++) {
+                    const uint32_t j = 2 * r + jj, b = per * t + j;
+                    v[jj][c] = j < per && b < chunks ? row[b] : 0u;
+                }
+            }
 #pragma unroll
             for (int jj = 0; jj < 2; jj++) {
                 const uint32_t j = 2 * r + jj, b = per * t + j;
-                v[jj][c] = j < per && b < chunks ? row[b] : 0u;
-            }
-        }
+                if (j < per && b < chunks) {
+                    const uint64_t start = (uint64_t)b << chunk_log2;
+                    const uint64_t len = min_u64(uint64_t{1} << chunk_log2, n - start);
+                    uint64_t kept = 0;
 #pragma unroll
-        for (int jj = 0; jj < 2; jj++) {
-            const uint32_t j = 2 * r + jj, b = per * t + j;
-            if (j < per && b < chunks) {
-                const uint64_t start = (uint64_t)b << chunk_log2;
-                const uint64_t len = min_u64(uint64_t{1} << chunk_log2, n - start);
-                uint64_t kept = 0;
-#pragma unroll
-                for (int c = 0; c < 16; c++) kept += v[jj][c];
-                esc[2 * r + jj] = len - kept;
+                    for (int c = 0; c < 16; c++) kept += v[jj][c];
+                    esc[2 * r + jj] = len - kept;
+                }
             }
         }
     }

@@ -177,9 +177,11 @@ def test_worked_example(torch, sz):
 
 
 def test_many_chunks_ragged(torch, sz):
-    # more than 2048 minimum-size chunks: larger chunks, a ragged last
-    # chunk; the largest size takes the single-read encode
-    for n in (2048 * 16384 + 123, 3 * (1 << 24) + 5, 8192 * 16384 + 77):
+    # more than 2048 minimum-size chunks: larger chunks, a ragged last chunk,
+    # plans of 2049-4096 chunks (three or four per select thread; 4096 read
+    # four per 16-byte load); from 2^26 words the single-read encode
+    for n in (2048 * 16384 + 123, 3 * (1 << 24) + 5, (1 << 26) - 5, (1 << 26) + 3 * 16384,
+              8192 * 16384 + 77):
         check_case(torch, sz, make_words("kv", n, 7), "many chunks kv")
     check_case(torch, sz, make_words("wide40", 2048 * 16384 + 5, 8), "many chunks wide40")
 

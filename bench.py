@@ -55,11 +55,11 @@ def chunk_log2(n: int) -> int:
     """The encode's chunk size (log2 words): the smallest giving at most 2048
     chunks, halved when that cuts the idle share of the pack grid's last wave
     of resident workgroups by more than 1/50, or gives more than 3072 chunks,
-    a multiple of 4."""
+    a multiple of 4 -- never into chunks below 2^17 words."""
     c = MIN_CHUNK_LOG2
     while -(-n >> c) > PLAN_CHUNKS:
         c += 1
-    if c > MIN_CHUNK_LOG2:
+    if c > 17:
         g0, g1 = -(-n >> c), -(-n >> (c - 1))
         s0 = -(-g0 // RESIDENT_PACK_GROUPS) * RESIDENT_PACK_GROUPS
         s1 = -(-g1 // RESIDENT_PACK_GROUPS) * RESIDENT_PACK_GROUPS

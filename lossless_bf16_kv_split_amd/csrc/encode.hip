@@ -52,8 +52,11 @@ EncodePlan plan_encode(uint64_t n) {
     //  - when the halved plan has more than 3072 chunks, a multiple of 4: the
     //    select then reads four chunks' counts per load, as fast as it reads
     //    2048 chunks, and the smaller chunks stream faster (1 GiB tensor:
-    //    first pass 370 -> 359 us with 4096 chunks of 2^17 words).
-    if (c > kMinChunkLog2) {
+    //    first pass 370 -> 359 us with 4096 chunks of 2^17 words);
+    // and only into chunks of at least 2^17 words: below, the per-chunk
+    // costs (count flushes, a larger merge and select) outweigh either gain
+    // (whole sz_encode calls on 2^25 to 2^27 words ran 3-22% slower).
+    if (c > kMinHalvedChunkLog2) {
         const uint64_t g0 = (n + (1ull << c) - 1) >> c, g1 = (n + (1ull << (c - 1)) - 1) >> (c - 1);
         const uint64_t s0 = (g0 + kResidentPackGroups - 1) / kResidentPackGroups * kResidentPackGroups;
         const uint64_t s1 = (g1 + kResidentPackGroups - 1) / kResidentPackGroups * kResidentPackGroups;

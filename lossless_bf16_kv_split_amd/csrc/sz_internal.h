@@ -26,6 +26,7 @@ constexpr uint64_t kMaxElements = 1ull << 36;
 constexpr uint32_t kMinChunkLog2 = 14;
 constexpr uint32_t kPlanChunks = 2048;
 constexpr uint32_t kMaxChunks = 2 * kPlanChunks;
+constexpr uint32_t kMinHalvedChunkLog2 = 17;  // a halved chunk keeps >= 2^17 words
 // pack workgroups (1024 threads, 8 waves per SIMD) resident at once on
 // MI355X: 256 CUs x 2
 constexpr uint64_t kResidentPackGroups = 512;

@@ -177,12 +177,27 @@ def test_worked_example(torch, sz):
 
 
 def test_many_chunks_ragged(torch, sz):
-    # more than 2048 minimum-size chunks: larger chunks, a ragged last chunk,
-    # plans of 2049-4096 chunks (three or four per select thread; 4096 read
-    # four per 16-byte load); from 2^26 words the single-read encode
+    # more than 2048 minimum-size chunks: larger chunks, a ragged last chunk;
+    # from 2^26 words the single-read encode
     for n in (2048 * 16384 + 123, 3 * (1 << 24) + 5, (1 << 26) - 5, (1 << 26) + 3 * 16384,
               8192 * 16384 + 77):
         check_case(torch, sz, make_words("kv", n, 7), "many chunks kv")
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("n", [1280 * (1 << 18) - 3, 1537 * (1 << 18) - 1])
+def test_halved_chunk_plans(torch, sz, n):
+    """Plans that halve 2^18-word chunks to fill the pack grid's last wave:
+    2560 and 3074 chunks of 2^17 words, both with a ragged last chunk, whose
+    counts the select reads three and four chunks per thread in two rounds
+    (the 1 GiB workloads cover 4096 chunks read four per 16-byte load)."""
+    words = make_words("kv", n, 9)
+    want = oracle.encode(words)
+    x = to_dev(torch, words)
+    got = gpu_encode(torch, sz, x, n).cpu().numpy()
+    assert got.size == want.size and np.array_equal(got, want), n
+    y, status, guard_ok = gpu_decode(torch, sz, torch.from_numpy(want).cuda(), n)
+    assert status == 0 and guard_ok and torch.equal(y, x), n
     check_case(torch, sz, make_words("wide40", 2048 * 16384 + 5, 8), "many chunks wide40")
 
 

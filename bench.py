@@ -209,6 +209,7 @@ def pages_bench(args, w, n, x, torch, np, sz) -> int:
     sz.sz_encode(x, n, dst, cap, size, stream)
     total = int(size.item())
     cont = dst[:total]
+    flat_container = cont.clone()
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -237,6 +238,7 @@ def pages_bench(args, w, n, x, torch, np, sz) -> int:
     # correctness of the last calls: same container, same words
     sz.sz_encode_pages(table, used, page, n, dst, cap, size, status, stream)
     ok = int(size.item()) == total and int(status.item()) == 0
+    ok = ok and bool(torch.equal(dst[:total], flat_container))
     sz.sz_decode_pages(cont, total, out_table, used, page, n, status, stream)
     back = torch.cat([out_pool[int(s_) * page:int(s_) * page + min(page, n - i * page)]
                       for i, s_ in enumerate(order)])

@@ -225,3 +225,20 @@ def test_pages_host_checks(sz):
     assert status_of(dec, D, fixed + 3, T, used, P, n, None, 0) == 4
     assert status_of(dec, None, fixed, T, used, P, n, None, 0) == 1
     assert status_of(dec, D, fixed, T, used - 1, P, n, None, 0) == 1
+
+
+def test_bench_chunk_plan_matches_library(sz):
+    """bench.py predicts the single-read finish case from its own copy of the
+    encode's chunk plan; the library's workspace size (per-chunk counts and
+    bases, then a fixed sample area) fixes the chunk count it planned."""
+    import bench
+    align = lambda x: (x + 255) // 256 * 256
+    def planned(g):  # counts u32[256][g], hist u64[256], bases u64[g]
+        return align(align(align(g * 1024) + 2048) + g * 8)
+    sample_area = sz.sz_workspace_size(1) - planned(1)
+    sizes = [1, 4096, 1 << 21, (1 << 25) + 123, 3 * (1 << 24) + 5, (1 << 26) - 5,
+             (1 << 27) + 77, 3 << 26, 1 << 28, 1280 * (1 << 18) - 3, 1537 * (1 << 18) - 1,
+             1 << 29, 5368709120, 1 << 36]
+    for n in sizes:
+        g = -(-n >> bench.chunk_log2(n))
+        assert sz.sz_workspace_size(n) == planned(g) + sample_area, (n, g)

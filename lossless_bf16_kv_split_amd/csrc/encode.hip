@@ -721,10 +721,17 @@ __device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t b
         t0 = end;
     }
     // whole tiles, no per-word checks (with kCount, only entered when the
-    // streams are written: the exponents are counted while packing)
+    // streams are written: the exponents are counted while packing).  A tile
+    // lies inside one page; for a paged tensor the next tile's page address
+    // is looked up while this tile is packed, after this tile's loads are
+    // issued, so that no tile waits for its page-table entry.
+    const uint16_t* tile_words = nullptr;
+    if constexpr (Words::kPaged) {
+        if (t0 + kPackTile <= end) tile_words = src.at(t0);
+    }
     for (; t0 + kPackTile <= end; t0 += kPackTile, parity ^= 1) {
-        // a tile lies inside one page
-        const uint4* p = reinterpret_cast<const uint4*>(src.at(t0) + (uint64_t)t * kPackWords);
+        if constexpr (!Words::kPaged) tile_words = src.at(t0);
+        const uint4* p = reinterpret_cast<const uint4*>(tile_words + (uint64_t)t * kPackWords);
         uint32_t w[kPackWords / 2];
 #pragma unroll
         for (int h = 0; h < kPackLoads; h++) {
@@ -733,6 +740,9 @@ __device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t b
             w[4 * h + 1] = v.y;
             w[4 * h + 2] = v.z;
             w[4 * h + 3] = v.w;
+        }
+        if constexpr (Words::kPaged) {
+            if (t0 + 2 * kPackTile <= end) tile_words = src.at(t0 + kPackTile);
         }
         slot_base += pack_tile<kAlignedSm, kCount>(w, t0, table, nib, sm, slot_base, lds, parity,
                                                    esc, hmine);

@@ -185,12 +185,13 @@ def test_many_chunks_ragged(torch, sz):
 
 
 @pytest.mark.timeout(300)
-@pytest.mark.parametrize("n", [1280 * (1 << 18) - 3, 1537 * (1 << 18) - 1])
+@pytest.mark.parametrize("n", [1280 * (1 << 18) - 3, 1537 * (1 << 18) - 1, (1 << 29) - 3])
 def test_halved_chunk_plans(torch, sz, n):
-    """Plans that halve 2^18-word chunks to fill the pack grid's last wave:
-    2560 and 3074 chunks of 2^17 words, both with a ragged last chunk, whose
-    counts the select reads three and four chunks per thread in two rounds
-    (the 1 GiB workloads cover 4096 chunks read four per 16-byte load)."""
+    """Plans that halve 2^18-word chunks: 2560 and 3074 chunks of 2^17 words
+    (a fuller last wave of pack workgroups), whose counts the select reads
+    three and four chunks per thread in two rounds, and 4096 (more than 3072,
+    a multiple of 4), read four chunks per 16-byte load; each with a ragged
+    last chunk."""
     words = make_words("kv", n, 9)
     want = oracle.encode(words)
     x = to_dev(torch, words)

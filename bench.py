@@ -1,18 +1,25 @@
 """Benchmark of the SplitZip BF16 codec on one MI355X.
 
-One step = the whole hot path over one tensor already resident in HBM, in
-the passes sz_encode and sz_decode run for it: encode as exponent histogram
--> top-16 codebook -> pack, or, from 2^26 words on, as sample -> first pass
-(pack with the sampled codebook while counting) -> codebook -> finish; then
-decode in the form sz_decode picks for the escape density.  Every pass is
-bracketed by HIP events on the stream the kernels run on, so each kernel's
-average duration is measured inside the timed region.  The closest other
-decode form is timed as well, after the timed region.  Prints ONE JSON line.
+One step = the whole hot path over one tensor already resident in HBM: one
+sz_encode call, then one sz_decode call of its container, as a user makes
+them (workspace from the library's pool included).  HIP events on the launch
+stream bracket each call, so encode and decode are timed separately inside
+the timed region; `value` is uncompressed bytes (2 per BF16 word) per step
+time.  Which passes the calls run: encode as exponent histogram -> top-16
+codebook -> pack, or, from 2^26 words on, as sample -> first pass (pack with
+the sampled codebook while counting) -> codebook -> finish; decode in the
+form sz_decode picks for the escape density.
+
+After the timed region the same passes run again through the staged calls,
+with a HIP event around each, to give every kernel's average duration; the
+closest other decode and encode forms are timed the same way; a 1 GiB
+device-to-device hipMemcpyAsync and torch's bitwise_not over 1 GiB give the
+HBM ceilings measured in the same process.  Prints ONE JSON line.
 
   python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload llama3_8b_kv_8k]
+                  [--graph]   (staged passes replayed from HIP graphs)
 
-Throughput is uncompressed bytes (2 per BF16 word) per second.  The
-roofline object describes the kernel with the longest average duration:
+The roofline object describes the kernel with the longest average duration:
 algorithmic bytes per launch / average launch time, against the MI355X's
 8 TB/s HBM peak.  ``traffic`` (HBM bytes per launch from rocprofv3 FETCH_SIZE
 and WRITE_SIZE, scaled by what the same counters read for a copy of known
@@ -309,6 +316,65 @@ def ship_bench(args, w, n, x, torch, np, sz) -> int:
     return 0 if ok else 1
 
 
+def hip_runtime():
+    """The HIP runtime library this process already has loaded (through
+    torch and libsplitzip.so), opened again by its path for ctypes."""
+    import ctypes
+    with open("/proc/self/maps") as f:
+        for line in f:
+            path = line.split()[-1]
+            if os.path.basename(path).startswith("libamdhip64.so"):
+                lib = ctypes.CDLL(path)
+                lib.hipMemcpyAsync.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t,
+                                               ctypes.c_int, ctypes.c_void_p]
+                lib.hipMemcpyAsync.restype = ctypes.c_int
+                return lib
+    raise RuntimeError("libamdhip64 is not loaded")
+
+
+def calibration(torch, stream, reps: int = 5) -> dict:
+    """HBM ceilings measured in the same process: a 1 GiB device-to-device
+    hipMemcpyAsync and torch's bitwise_not over 1 GiB (1 GiB read, 1 GiB
+    written each); median of `reps` event-timed runs, bytes moved / time."""
+    hip = hip_runtime()
+    nbytes = 1 << 30
+    a = torch.empty(nbytes // 4, dtype=torch.int32, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    torch.cuda.synchronize()
+    hip_d2d = 3  # hipMemcpyDeviceToDevice
+
+    def memcpy():
+        st = hip.hipMemcpyAsync(b.data_ptr(), a.data_ptr(), nbytes, hip_d2d, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError(f"hipMemcpyAsync failed ({st})")
+
+    def timed(fn):
+        fn()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        ts.sort()
+        return ts[len(ts) // 2]
+
+    t_copy = timed(memcpy)
+    ok = bool(torch.equal(a, b))
+    t_not = timed(lambda: torch.bitwise_not(a, out=b))
+    ok = ok and bool(torch.equal(b, ~a))
+    del a, b
+    return {"bytes_moved": 2 * nbytes, "reps": reps,
+            "d2d_hipMemcpyAsync_ms": round(t_copy, 4),
+            "d2d_hipMemcpyAsync_GBps": round(2 * nbytes / (t_copy * 1e-3) / 1e9, 1),
+            "bitwise_not_ms": round(t_not, 4),
+            "bitwise_not_GBps": round(2 * nbytes / (t_not * 1e-3) / 1e9, 1),
+            "ok": ok}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -317,8 +383,12 @@ def main() -> int:
     ap.add_argument("--workload", default="llama3_8b_kv_8k")
     ap.add_argument("--cpu-repeats", type=int, default=2,
                     help="oracle runs for the CPU baseline (0 = skip)")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="after timing, run one device copy of known size (for PMC scaling)")
+    ap.add_argument("--no-calibration", action="store_true",
+                    help="skip the device copy and bitwise_not ceilings")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the staged passes captured in HIP graphs (one for the encode "
+                         "passes, one for the decode passes) instead of the public calls: "
+                         "GPU time without host launch cadence, for small tensors")
     ap.add_argument("--pages", type=int, default=0, metavar="PAGE_ELEMS",
                     help="instead: time sz_encode_pages / sz_decode_pages on the workload "
                          "spread over pages of this many words, against the flat calls")
@@ -413,34 +483,75 @@ def main() -> int:
         if ev:
             ev[len(seq)].record(stream)
 
-    for _ in range(args.warmup):
-        step(passes, out)
-    torch.cuda.synchronize()
-
     def new_events(k):
         return [[torch.cuda.Event(enable_timing=True) for _ in range(k)] for _ in range(args.steps)]
 
-    events = new_events(len(passes) + 1)
+    # ---- the timed region: one step = encode then decode of the tensor ----
+    if args.graph:
+        # the staged passes in two graphs, replayed: no host launch cadence
+        g_enc, g_dec = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            step(encode_passes, out)   # warm the capture stream once
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g_enc):
+            step(encode_passes, out)
+        with torch.cuda.graph(g_dec):
+            step(decode_passes, out)
+        torch.cuda.synchronize()
+        do_encode, do_decode = g_enc.replay, g_dec.replay
+        step_form = "staged passes captured in two HIP graphs (encode, decode), replayed"
+    else:
+        def do_encode():
+            sz.sz_encode(x, n, dst, cap, size, stream)
+
+        def do_decode():
+            sz.sz_decode(container, total, out, n, status, stream)
+        step_form = "public calls: sz_encode, then sz_decode"
+
+    for _ in range(args.warmup):
+        do_encode()
+        do_decode()
+    torch.cuda.synchronize()
+    call_ev = new_events(3)
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record(stream)
     for k in range(args.steps):
-        step(passes, out, events[k])
+        call_ev[k][0].record(stream)
+        do_encode()
+        call_ev[k][1].record(stream)
+        do_decode()
+        call_ev[k][2].record(stream)
     stop.record(stream)
     torch.cuda.synchronize()
     t_wall = time.perf_counter() - t_wall
     total_ms = start.elapsed_time(stop)
+    enc_ms = sum(ev[0].elapsed_time(ev[1]) for ev in call_ev) / args.steps
+    dec_ms = sum(ev[1].elapsed_time(ev[2]) for ev in call_ev) / args.steps
+    # the timed work is correct: same container, exact round trip
+    ok = bool(torch.equal(out, x)) and int(status.item()) == 0 and int(size.item()) == total
+    ok = ok and int.from_bytes(dst[24:32].cpu().numpy().tobytes(), "little") == total
 
+    # ---- per-kernel durations: the same passes, staged, one event each ----
+    for _ in range(max(1, args.warmup)):
+        step(passes, out)
+    torch.cuda.synchronize()
+    events = new_events(len(passes) + 1)
+    for k in range(args.steps):
+        step(passes, out, events[k])
+    torch.cuda.synchronize()
     avg_ms = {}
     for i, p in enumerate(passes):
         avg_ms[p] = sum(ev[i].elapsed_time(ev[i + 1]) for ev in events) / args.steps
+    staged_enc_ms = sum(avg_ms[p] for p in encode_passes)
+    staged_dec_ms = sum(avg_ms[p] for p in decode_passes)
+    ok = ok and bool(torch.equal(out, x)) and int(status.item()) == 0
 
-    # the timed work is correct: same container, exact round trip
-    ok = bool(torch.equal(out, x)) and int(status.item()) == 0 and int(size.item()) == total
-
-    # the other decode form, after the timed region; each run follows an
-    # encode, as in the step
+    # the other decode form, each run after an encode, as in the step
     out2 = torch.empty_like(out)
     other_ev = new_events(len(other_passes) + 1)
     for k in range(args.steps):
@@ -452,8 +563,8 @@ def main() -> int:
     ok = ok and bool(torch.equal(out2, x)) and int(status.item()) == 0
     del out2
 
-    # the other encode form, after the timed region, each run followed by
-    # the step's decode; it must leave the same container
+    # the other encode form, each run followed by the step's decode; it must
+    # leave the same container
     other_enc = TWO_READ_PASSES if single else (SINGLE_READ_PASSES if n >= 1 << 20 else [])
     other_enc_ms = None
     if other_enc:
@@ -475,8 +586,6 @@ def main() -> int:
         kernels[p] = {"kernel": KERNEL_NAMES[p], "avg_ms": round(ms, 5),
                       "alg_bytes": alg[p], "GBps": round(gbps, 1),
                       "frac_hbm": round(gbps / HBM_PEAK_GBPS, 4)}
-    enc_ms = sum(avg_ms[p] for p in encode_passes)
-    dec_ms = sum(avg_ms[p] for p in decode_passes)
     other_dec_ms = sum(avg_ms[p] for p in other_passes)
     # the bytes the encode passes that ran move (the two-read form reads the
     # words twice, the single-read form once plus the escape records' moves)
@@ -488,22 +597,15 @@ def main() -> int:
     ach = kernels[dominant]["GBps"]
     traffic = load_traffic(KERNEL_NAMES[dominant], w.name)
 
-    copy_ms = None
-    if args.copy_calibration:
-        # a plain stream of known size (reads 1 GiB, writes 1 GiB) under a
-        # kernel name of its own, to scale the HBM byte counters
-        a = torch.empty(1 << 28, dtype=torch.int32, device="cuda")
-        b = torch.empty_like(a)
-        a.fill_(1)
-        torch.cuda.synchronize()
-        c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        c0.record(stream)
-        torch.bitwise_not(a, out=b)
-        c1.record(stream)
-        torch.cuda.synchronize()
-        copy_ms = c0.elapsed_time(c1)
-        del a, b
+    calib = None if args.no_calibration else calibration(torch, stream)
+    if calib is not None:
+        ok = ok and calib["ok"]
+        ceiling = calib["d2d_hipMemcpyAsync_GBps"]
+        for p in kernels:
+            kernels[p]["frac_of_d2d_copy"] = round(kernels[p]["GBps"] / ceiling, 4)
 
+    enc_gbps_alg = enc_alg / (enc_ms * 1e-3) / 1e9
+    dec_gbps_alg = dec_alg / (dec_ms * 1e-3) / 1e9
     line = {
         "metric": "encode/decode GB/s (uncompressed) + compression ratio; % of HBM peak, 1 GPU",
         "value": round(2 * n / (ms_per_step * 1e-3) / 1e9, 2),
@@ -519,10 +621,19 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": w.name, "description": w.description, "n_elements": n,
                    "input_bytes": 2 * n, "seed": w.seed},
+        "step": step_form,
         "encode_GBps": round(2 * n / (enc_ms * 1e-3) / 1e9, 2),
         "decode_GBps": round(2 * n / (dec_ms * 1e-3) / 1e9, 2),
-        "encode_frac_hbm": round(enc_alg / (enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-        "decode_frac_hbm": round(dec_alg / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "encode_ms": round(enc_ms, 5),
+        "decode_ms": round(dec_ms, 5),
+        "encode_frac_hbm": round(enc_gbps_alg / HBM_PEAK_GBPS, 4),
+        "decode_frac_hbm": round(dec_gbps_alg / HBM_PEAK_GBPS, 4),
+        "staged_encode_ms": round(staged_enc_ms, 5),
+        "staged_decode_ms": round(staged_dec_ms, 5),
+        "staged_encode_frac_hbm": round(enc_alg / (staged_enc_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "staged_decode_frac_hbm": round(dec_alg / (staged_dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "encode_alg_bytes": enc_alg,
+        "decode_alg_bytes": dec_alg,
         "encode_form": ("single read (sampled codebook), finish case " + case) if single
                        else "two reads (histogram, then pack)",
         "other_encode_form": None if not other_enc else
@@ -538,15 +649,18 @@ def main() -> int:
         "kernels": kernels,
         "roofline": {"bound": "hbm", "kernel": KERNEL_NAMES[dominant], "achieved": ach,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic},
+                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": traffic,
+                     "duration_source": "HIP events around each staged pass on the launch "
+                                        f"stream, average of {args.steps} steps"},
         "kernel_source_hash": kernel_source_hash(),
         "wall_s_timed": round(t_wall, 4),
         "context": {"pages_compress_GBps": 613, "pages_decompress_GBps": 2181,
                     "pages_hardware": "not stated"},
     }
-    if copy_ms is not None:
-        line["calibration_copy_1GiB_ms"] = round(copy_ms, 4)
-        line["calibration_copy_GBps_rw"] = round(2 * (1 << 30) / (copy_ms * 1e-3) / 1e9, 1)
+    if calib is not None:
+        line["calibration"] = calib
+        line["encode_frac_of_d2d_copy"] = round(enc_gbps_alg / calib["d2d_hipMemcpyAsync_GBps"], 4)
+        line["decode_frac_of_d2d_copy"] = round(dec_gbps_alg / calib["d2d_hipMemcpyAsync_GBps"], 4)
     if args.cpu_repeats > 0:
         line["cpu_baseline"] = cpu_baseline(words, args.cpu_repeats)
     print(json.dumps(line), flush=True)

@@ -68,9 +68,13 @@ typedef enum {
 } sz_status;
 
 /* Upper bound of the container size for n elements: 176 + ceil(n/2) + n +
- * 5*floor(15n/16), since the 16 most frequent of 256 exponents always cover
- * at least n/16 elements.  Returns 0 when n > SZ_MAX_ELEMENTS.  Host-only,
- * touches no device. */
+ * 5*floor(15n/16).  SplitZip explainer section "3. La strategie SplitZip":
+ * every exponent gets a fixed 4-bit code stored two per byte (ceil(n/2)
+ * bytes), every word keeps its sign and mantissa (n bytes), and an exponent
+ * outside the 16-entry list costs one (position, exponent) note (5 bytes
+ * here); the 16 most frequent of 256 exponents always cover at least n/16
+ * elements, so at most floor(15n/16) words need a note.  Returns 0 when
+ * n > SZ_MAX_ELEMENTS.  Host-only, touches no device. */
 uint64_t sz_max_compressed_size(uint64_t n_elements);
 
 /* Bytes of device workspace the staged encode calls need for n elements
@@ -82,8 +86,10 @@ uint64_t sz_workspace_size(uint64_t n_elements);
  * codebook, 4-bit codes two per byte, escape records for the rest).
  *   d_src             n little-endian BF16 words (any bit patterns)
  *   d_dst             container buffer, dst_capacity bytes; must be at least
- *                     sz_max_compressed_size(n) (else SZ_ERR_CAPACITY); only
- *                     the first `total bytes` of the container are written
+ *                     sz_max_compressed_size(n) (else SZ_ERR_CAPACITY).  The
+ *                     container is its first `total bytes`; any byte below
+ *                     sz_max_compressed_size(n) may be written (see below),
+ *                     none at or past it
  *   d_compressed_size optional device u64 that receives the container size
  *                     (the same value is stored at container offset 24)
  * From 2^26 elements on (sz_encode_single_read(n) says 1) the input is read
@@ -91,7 +97,10 @@ uint64_t sz_workspace_size(uint64_t n_elements);
  * container, up to sz_max_compressed_size(n), then serve as scratch and are
  * left unspecified.  The container is the same either way.
  * Allocates its workspace (sz_workspace_size(n)) from a library-owned,
- * stream-ordered device memory pool and returns it on the same stream. */
+ * stream-ordered device memory pool and returns it on the same stream.
+ * While `stream` is being captured into a graph, returns
+ * SZ_ERR_INVALID_ARGUMENT and launches nothing: the staged calls below, with
+ * a workspace the caller owns, are the capturable form. */
 sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
                     uint64_t dst_capacity, uint64_t *d_compressed_size,
                     hipStream_t stream);
@@ -258,7 +267,9 @@ sz_status sz_decode_tiles(const void *d_src, uint64_t src_bytes, const void *d_w
  * one makes the call touch no page and report SZ_ERR_INVALID_ARGUMENT in
  * *d_status (the container is then not valid).  Pages must not overlap
  * each other or the container.  The library allocates a small flag from
- * its stream-ordered pool (and, for encode, sz_encode's workspace). */
+ * its stream-ordered pool (and, for encode, sz_encode's workspace), so
+ * while `stream` is being captured into a graph both calls return
+ * SZ_ERR_INVALID_ARGUMENT and launch nothing. */
 
 /* sz_encode_pages: sz_encode of the paged tensor; *d_status (optional
  * device i32) receives SZ_OK or SZ_ERR_INVALID_ARGUMENT. */

@@ -107,19 +107,21 @@ sz_status check_decode_args(const void* src, uint64_t src_bytes, const void* dst
 
 sz_status hip_status(hipError_t e) { return e == hipSuccess ? SZ_OK : SZ_ERR_HIP; }
 
+// true while `stream` is being captured into a graph (no pool allocation then)
+bool capturing(hipStream_t stream) {
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    return hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
+}
+
 sz::FlatWords flat(const void* p) {
     return sz::FlatWords{const_cast<uint16_t*>(static_cast<const uint16_t*>(p))};
 }
 
-// histogram, codebook and pack with the workspace from the library pool
+// The encode passes sz_encode runs for n words, over the workspace w
 template <class Words>
-sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capacity,
-                           uint64_t* d_compressed_size, int dev, hipMemPool_t pool,
-                           hipStream_t stream) {
-    const sz::EncodePlan p = sz::plan_encode(n);
-    void* ws = nullptr;
-    if (hipMallocFromPoolAsync(&ws, p.ws_bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
-    uint8_t* w = static_cast<uint8_t*>(ws);
+sz_status encode_passes(Words src, uint64_t n, const sz::EncodePlan& p, uint8_t* w, void* d_dst,
+                        uint64_t dst_capacity, uint64_t* d_compressed_size, int dev,
+                        hipStream_t stream) {
     uint8_t* out = static_cast<uint8_t*>(d_dst);
     sz_status st = SZ_OK;
     if (p.single_read && n >= kSingleReadAuto && p.scratch_end <= dst_capacity) {
@@ -135,14 +137,21 @@ sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capa
         if (st == SZ_OK)
             st = hip_status(sz::launch_pack(src, p, w, out, dst_capacity, num_cus(dev), stream));
     }
-    if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
     return st;
 }
 
-// true while `stream` is being captured into a graph (no pool allocation then)
-bool capturing(hipStream_t stream) {
-    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
-    return hipStreamIsCapturing(stream, &st) != hipSuccess || st != hipStreamCaptureStatusNone;
+// the same passes with the workspace from the library pool
+template <class Words>
+sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capacity,
+                           uint64_t* d_compressed_size, int dev, hipMemPool_t pool,
+                           hipStream_t stream) {
+    const sz::EncodePlan p = sz::plan_encode(n);
+    void* ws = nullptr;
+    if (hipMallocFromPoolAsync(&ws, p.ws_bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
+    sz_status st = encode_passes(src, n, p, static_cast<uint8_t*>(ws), d_dst, dst_capacity,
+                                 d_compressed_size, dev, stream);
+    if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
+    return st;
 }
 
 sz_status check_decode_workspace(const void* ws, uint64_t ws_bytes, uint64_t n) {
@@ -296,6 +305,8 @@ sz_status sz_encode_finish(const void* d_src, uint64_t n, const void* d_workspac
 sz_status sz_encode(const void* d_src, uint64_t n, void* d_dst, uint64_t dst_capacity,
                     uint64_t* d_compressed_size, hipStream_t stream) {
     if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
+    // its workspace comes from the pool, which a graph cannot capture
+    if (capturing(stream)) return SZ_ERR_INVALID_ARGUMENT;
     const int dev = current_device();
     if (dev < 0) return SZ_ERR_HIP;
     hipMemPool_t pool = pool_for(dev);
@@ -387,6 +398,7 @@ sz_status sz_encode_pages(const void* const* d_pages, uint64_t n_pages, uint64_t
     if (sz_status s = check_pages(d_pages, n_pages, page_elems, n, &lg, &used)) return s;
     if (d_dst == nullptr || !aligned(d_dst, 16)) return SZ_ERR_INVALID_ARGUMENT;
     if (dst_capacity < sz_max_compressed_size(n)) return SZ_ERR_CAPACITY;
+    if (capturing(stream)) return SZ_ERR_INVALID_ARGUMENT;  // pool memory below
     const int dev = current_device();
     if (dev < 0) return SZ_ERR_HIP;
     hipMemPool_t pool = pool_for(dev);
@@ -416,6 +428,7 @@ sz_status sz_decode_pages(const void* d_src, uint64_t src_bytes, void* const* d_
     if (src_bytes < fixed || (src_bytes - fixed) % 5 != 0) return SZ_ERR_CORRUPT;
     e = (src_bytes - fixed) / 5;
     if (e > (15 * n) / 16) return SZ_ERR_CORRUPT;
+    if (capturing(stream)) return SZ_ERR_INVALID_ARGUMENT;  // pool memory below
     const int dev = current_device();
     if (dev < 0) return SZ_ERR_HIP;
     hipMemPool_t pool = pool_for(dev);

@@ -100,3 +100,53 @@ def test_graph_replays(torch, sz, kind, form, single):
         assert np.array_equal(dst[:total].cpu().numpy(), want), (kind, form, replay)
         assert int(status.item()) == 0, (kind, form, replay)
         assert torch.equal(out, x), (kind, form, replay)
+
+
+def test_pool_calls_refused_under_capture(torch, sz):
+    """sz_encode, sz_encode_pages and sz_decode_pages take memory from the
+    library pool, so under capture they return SZ_ERR_INVALID_ARGUMENT and
+    launch nothing; sz_decode captures its workspace-free dense form, which
+    replays to the oracle's words."""
+    n = (1 << 20) + 4096
+    page = 1 << 16
+    words = make_words("kv", n, 55)
+    want = oracle.encode(words)
+    x = torch.from_numpy(words.view(np.int16)).cuda()
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.full((cap,), 0x3C, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    pages = -(-n // page)
+    pool = torch.zeros(pages * page, dtype=torch.int16, device="cuda")
+    table = torch.tensor([pool.data_ptr() + 2 * page * i for i in range(pages)],
+                         dtype=torch.int64, device="cuda")
+    container = torch.from_numpy(want).cuda()
+    out = torch.zeros(n, dtype=torch.int16, device="cuda")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    refused = []
+    with torch.cuda.graph(graph):
+        for name, call in (
+                ("sz_encode", lambda: sz.sz_encode(x, n, dst, cap, size)),
+                ("sz_encode_pages", lambda: sz.sz_encode_pages(table, pages, page, n, dst, cap,
+                                                               size, status)),
+                ("sz_decode_pages", lambda: sz.sz_decode_pages(container, want.size, table,
+                                                               pages, page, n, status))):
+            try:
+                call()
+            except sz.SplitZipError as e:
+                refused.append((name, e.status))
+        sz.sz_decode(container, want.size, out, n, status)
+    say("refused under capture:", refused)
+    assert refused == [("sz_encode", 1), ("sz_encode_pages", 1), ("sz_decode_pages", 1)]
+    for replay in range(2):
+        out.zero_()
+        status.fill_(-1)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(status.item()) == 0, replay
+        assert torch.equal(out, x), replay
+        assert int(size.item()) == 0                       # no encode ran
+        assert bool((dst == 0x3C).all().item())
+        assert bool((pool == 0).all().item())              # no page written

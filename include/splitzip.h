@@ -105,6 +105,24 @@ sz_status sz_encode(const void *d_src, uint64_t n_elements, void *d_dst,
                     uint64_t dst_capacity, uint64_t *d_compressed_size,
                     hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * sz_encode with the same arguments, passes and container, but its
+ * workspace is a fixed array of SZ_NOALLOC_WORKSPACE_BYTES in the library's
+ * device memory, one per GPU, loaded with the library and held until the
+ * process ends.  The call allocates nothing (no hipMalloc, no pool, no
+ * hipFree) and may be captured into a graph.  Every call on one GPU uses
+ * that GPU's array: calls that can overlap on one GPU (other streams, or
+ * several replays of graphs in flight at once) race and give unspecified
+ * containers, so callers serialise them.  No pass needs the array to hold
+ * anything at its start (each pass writes what the next one reads).
+ * SZ_ERR_TOO_LARGE when n's workspace (sz_workspace_size(n)) exceeds the
+ * array; with this library's chunk plan no n up to SZ_MAX_ELEMENTS does. */
+#define SZ_NOALLOC_WORKSPACE_BYTES (4608ull * 1024ull)
+sz_status sz_encode_noalloc(const void *d_src, uint64_t n_elements, void *d_dst,
+                            uint64_t dst_capacity, uint64_t *d_compressed_size,
+                            hipStream_t stream);
+
 /* Decompress a container of src_bytes bytes into n BF16 words at d_dst,
  * bit-exactly.  SplitZip explainer section "4. Pourquoi est-ce rapide ?"
  * (code -> exponent lookup, recombination with sign and mantissa, escaped

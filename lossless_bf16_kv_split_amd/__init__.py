@@ -24,18 +24,19 @@ import os
 
 __all__ = [
     "SplitZipError", "lib_path", "sz_max_compressed_size", "sz_workspace_size", "sz_encode",
-    "sz_decode", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
+    "sz_decode", "sz_encode_noalloc", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
     "sz_encode_single_read", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
     "sz_decode_workspace_size", "sz_decode_index", "sz_decode_tiles",
     "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host", "sz_ship_from_host",
     "sz_status_string", "encode",
     "decode",
-    "PREFIX_BYTES", "MAX_ELEMENTS",
+    "PREFIX_BYTES", "MAX_ELEMENTS", "NOALLOC_WORKSPACE_BYTES",
 ]
 
 PREFIX_BYTES = 176
 MAX_ELEMENTS = 1 << 36
+NOALLOC_WORKSPACE_BYTES = 4608 * 1024
 
 SZ_OK = 0
 SZ_ERR_INVALID_ARGUMENT = 1
@@ -67,6 +68,7 @@ def _load() -> ctypes.CDLL:
     L.sz_workspace_size.restype = u64
     L.sz_encode.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode.argtypes = [p, u64, p, u64, p, p]
+    L.sz_encode_noalloc.argtypes = [p, u64, p, u64, p, p]
     L.sz_encode_histogram.argtypes = [p, u64, p, u64, p]
     L.sz_encode_codebook.argtypes = [u64, p, u64, p, u64, p, p]
     L.sz_encode_pack.argtypes = [p, u64, p, u64, p, u64, p]
@@ -87,7 +89,7 @@ def _load() -> ctypes.CDLL:
     L.sz_decode_pages.argtypes = [p, u64, p, u64, u64, u64, p, p]
     L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
     L.sz_ship_from_host.argtypes = [p, p, u64, u64, p, p, p]
-    for name in ("sz_encode", "sz_decode", "sz_encode_histogram", "sz_encode_codebook",
+    for name in ("sz_encode", "sz_decode", "sz_encode_noalloc", "sz_encode_histogram", "sz_encode_codebook",
                  "sz_encode_pack", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
                  "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
                  "sz_decode_dense", "sz_decode_index", "sz_decode_tiles", "sz_encode_pages",
@@ -145,6 +147,12 @@ def sz_encode(src, n_elements: int, dst, dst_capacity: int, d_compressed_size=No
               stream=None) -> None:
     _check(_lib.sz_encode(_ptr(src), n_elements, _ptr(dst), dst_capacity,
                           _ptr(d_compressed_size), _stream(stream)), "sz_encode")
+
+
+def sz_encode_noalloc(src, n_elements: int, dst, dst_capacity: int, d_compressed_size=None,
+                      stream=None) -> None:
+    _check(_lib.sz_encode_noalloc(_ptr(src), n_elements, _ptr(dst), dst_capacity,
+                                  _ptr(d_compressed_size), _stream(stream)), "sz_encode_noalloc")
 
 
 def sz_decode(src, src_bytes: int, dst, n_elements: int, d_status=None, stream=None) -> None:

@@ -154,6 +154,24 @@ sz_status encode_with_pool(Words src, uint64_t n, void* d_dst, uint64_t dst_capa
     return st;
 }
 
+// sz_encode_noalloc's workspace: one array per GPU, loaded with the library
+// and held until the process ends.  Its name is a host-side stand-in; the
+// device address comes from hipGetSymbolAddress, once per device, with that
+// device current, and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[SZ_NOALLOC_WORKSPACE_BYTES];
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+uint8_t* scratch_for(int dev) {
+    std::lock_guard<std::mutex> lock(g_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr)
+            return nullptr;
+        g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+    }
+    return g_scratch_ptr[dev];
+}
+
 sz_status check_decode_workspace(const void* ws, uint64_t ws_bytes, uint64_t n) {
     if (ws == nullptr || !aligned(ws, 256) || ws_bytes < sz::tile_index_layout(n).bytes)
         return SZ_ERR_INVALID_ARGUMENT;
@@ -313,6 +331,19 @@ sz_status sz_encode(const void* d_src, uint64_t n, void* d_dst, uint64_t dst_cap
     if (pool == nullptr) return SZ_ERR_HIP;
     return encode_with_pool(flat(d_src), n, d_dst, dst_capacity, d_compressed_size, dev, pool,
                             stream);
+}
+
+sz_status sz_encode_noalloc(const void* d_src, uint64_t n, void* d_dst, uint64_t dst_capacity,
+                            uint64_t* d_compressed_size, hipStream_t stream) {
+    if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (p.ws_bytes > SZ_NOALLOC_WORKSPACE_BYTES) return SZ_ERR_TOO_LARGE;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    uint8_t* ws = scratch_for(dev);
+    if (ws == nullptr) return SZ_ERR_HIP;
+    return encode_passes(flat(d_src), n, p, ws, d_dst, dst_capacity, d_compressed_size, dev,
+                         stream);
 }
 
 sz_status sz_decode_unpack(const void* d_src, uint64_t src_bytes, void* d_dst, uint64_t n,

@@ -96,6 +96,22 @@ def test_encode_host_checks(sz):
     assert status_of(sz.sz_encode, A, 1000, A + 1024, cap, None, 0) == 1      # overlap
 
 
+def test_noalloc_encode_host_checks(sz):
+    """The allocation-free encode makes the same host checks as sz_encode,
+    and its fixed workspace holds the workspace of every size."""
+    cap = sz.sz_max_compressed_size(1000)
+    f = sz.sz_encode_noalloc
+    assert status_of(f, A, (1 << 36) + 1, A + (1 << 40), 1 << 62, None, 0) == 3
+    assert status_of(f, A, 1000, None, cap, None, 0) == 1
+    assert status_of(f, MIS, 1000, A + (1 << 30), cap, None, 0) == 1
+    assert status_of(f, A, 1000, A + (1 << 30), cap - 1, None, 0) == 2
+    assert status_of(f, A, 1000, A + 1024, cap, None, 0) == 1                 # overlap
+    for k in range(37):
+        for n in ((1 << k) - 1, 1 << k, (1 << k) + 1, 3 << max(k - 2, 0)):
+            if n <= 1 << 36:
+                assert sz.sz_workspace_size(n) <= sz.NOALLOC_WORKSPACE_BYTES, n
+
+
 def test_decode_host_checks(sz):
     n = 1000
     fixed = 176 + (n + 1) // 2 + n

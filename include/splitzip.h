@@ -248,19 +248,26 @@ sz_status sz_decode_fused(const void *d_src, uint64_t src_bytes, void *d_dst,
 sz_status sz_decode_dense(const void *d_src, uint64_t src_bytes, void *d_dst,
                           uint64_t n_elements, int32_t *d_status, hipStream_t stream);
 
-/* Decode in a single pass with the words handed out grid-stride, in two
- * calls over a caller workspace of sz_decode_workspace_size(n) bytes
- * (256-byte aligned, not overlapping the container or the output).
- * sz_decode_index records, for every 8192-word tile, the first escape
- * record at or after the tile's start, and checks the header and that the
- * records ascend below n; sz_decode_tiles then has a few workgroups per CU
- * take tiles b, b + grid, ..., mark each tile's records in an LDS exponent
- * map and rebuild its words (explainer section "4. Pourquoi est-ce
- * rapide ?").  sz_decode_tiles writes *d_status (optional): SZ_OK, or
- * SZ_ERR_CORRUPT when the index call found a fault (the output content is
- * then unspecified, but no write leaves d_dst[0..n)).  Together they give
- * the result and status of sz_decode, which takes this form, with a
- * workspace from its pool, from 2^26 words with up to one escape in 128. */
+/* Decode in a single pass, one short-lived workgroup per 2048-word tile, in
+ * two calls over a caller workspace of sz_decode_workspace_size(n) bytes
+ * (256-byte aligned, not overlapping the container or the output; about
+ * 72 bytes per tile plus 4 bytes per 256 possible escapes, at most 4 MiB of
+ * those).  sz_decode_index
+ * records, for every tile, the first escape record at or after the tile's
+ * start (each of its workgroups takes a run of records and fills the tile
+ * entries up to its last record: no search), and checks the header and that
+ * the records ascend below n; sz_decode_tiles then rebuilds every tile's
+ * words with its records' exponents in place of the codebook's (explainer
+ * section "4. Pourquoi est-ce rapide ?").  sz_decode_tiles writes
+ * *d_status (optional): SZ_OK, or SZ_ERR_CORRUPT when the index call found
+ * a fault (the output content is then unspecified, but no write leaves
+ * d_dst[0..n)); it only reads the workspace, so it may run again on the
+ * same index.  The index call also copies each tile's records (up to 15)
+ * into a 64-byte slot of the tile, which the tile call reads together with
+ * the tile's codes; a tile with more records reads them from the escape
+ * stream.  Together they give the result and status of sz_decode, which
+ * takes this form, with a workspace from its pool, from 2^26 words with up
+ * to one escape in 128. */
 uint64_t sz_decode_workspace_size(uint64_t n_elements);
 sz_status sz_decode_index(const void *d_src, uint64_t src_bytes, uint64_t n_elements,
                           void *d_workspace, uint64_t workspace_bytes, hipStream_t stream);

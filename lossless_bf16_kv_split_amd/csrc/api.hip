@@ -397,7 +397,9 @@ sz_status sz_decode_tiles(const void* d_src, uint64_t src_bytes, const void* d_w
     uint64_t e = 0;
     if (sz_status s = check_decode_args(d_src, src_bytes, d_dst, n, &e)) return s;
     if (sz_status s = check_decode_workspace(d_workspace, workspace_bytes, n)) return s;
-    if (overlap(d_dst, 2 * n, d_workspace, workspace_bytes)) return SZ_ERR_INVALID_ARGUMENT;
+    if (overlap(d_dst, 2 * n, d_workspace, workspace_bytes) ||
+        overlap(d_src, src_bytes, d_workspace, workspace_bytes))
+        return SZ_ERR_INVALID_ARGUMENT;
     const int dev = current_device();
     if (dev < 0) return SZ_ERR_HIP;
     return hip_status(sz::launch_decode_tiles(static_cast<const uint8_t*>(d_src), n, e,

@@ -13,6 +13,8 @@
 // every escape note; linear work with no detours.
 #include "sz_internal.h"
 
+#include <type_traits>
+
 namespace sz {
 
 constexpr int kUnpackThreads = 256;
@@ -85,23 +87,32 @@ __device__ __forceinline__ uint32_t load4_unaligned(const uint8_t* q) {
            ((uint32_t)q[3] << 24);
 }
 
+// The header's fields against n, e and the container size.  All 160 bytes
+// are loaded first (ten 16-byte loads in flight together; every container
+// holds at least 176 bytes, checked on the host), then compared, so the
+// check costs one memory round trip.
 __device__ bool header_ok(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e) {
-    if (*reinterpret_cast<const uint32_t*>(src + 0) != kMagic) return false;
-    if (*reinterpret_cast<const uint16_t*>(src + 4) != kVersion) return false;
-    if (*reinterpret_cast<const uint16_t*>(src + 6) != kElementBf16) return false;
-    if (*reinterpret_cast<const uint64_t*>(src + 8) != n) return false;
-    if (*reinterpret_cast<const uint64_t*>(src + 16) != e) return false;
-    if (*reinterpret_cast<const uint64_t*>(src + 24) != src_bytes) return false;
-    const uint64_t* seg_end = reinterpret_cast<const uint64_t*>(src + 32);
+    uint64_t h[20];
+#pragma unroll
+    for (int q = 0; q < 10; q++) {
+        const uint4 v = reinterpret_cast<const uint4*>(src)[q];
+        h[2 * q] = ((uint64_t)v.y << 32) | v.x;
+        h[2 * q + 1] = ((uint64_t)v.w << 32) | v.z;
+    }
+    bool ok = (uint32_t)h[0] == kMagic && (uint16_t)(h[0] >> 32) == kVersion &&
+              (uint16_t)(h[0] >> 48) == kElementBf16 && h[1] == n && h[2] == e &&
+              h[3] == src_bytes;
+    // seg_end[s] (h[4 + s]) never decreases, and equals e from the last
+    // segment holding words on
     const uint64_t segments_used = (n + 0xFFFFFFFFull) >> 32;
     uint64_t prev = 0;
-    for (uint32_t s = 0; s < 16; s++) {
-        const uint64_t v = seg_end[s];
-        if (v < prev) return false;
-        if ((uint64_t)s + 1 >= segments_used && v != e) return false;
+#pragma unroll
+    for (uint32_t sg = 0; sg < 16; sg++) {
+        const uint64_t v = h[4 + sg];
+        ok = ok && v >= prev && ((uint64_t)sg + 1 < segments_used || v == e);
         prev = v;
     }
-    return true;
+    return ok;
 }
 
 template <bool kAlignedSm, class Words>
@@ -497,215 +508,378 @@ hipError_t launch_decode_fused(const uint8_t* src, uint64_t src_bytes, uint64_t 
 }
 
 // ------------------------------------------------------------------------
-// Tile decode: the single pass with the words handed out grid-stride.  A
-// first kernel indexes the escape stream by 8192-word tile (the first record
-// of every tile) and checks the header and the records' order; then a grid
-// of two workgroups per CU walks the tiles b, b + gridDim.x, ..., so that
-// the resident workgroups stream one region of memory together instead of
-// one contiguous range each (on MI355X: 336-346 us against 375 us for the
-// 1 GiB KV tensor).
+// Tile decode: one 256-thread workgroup per 2048-word tile, after an index
+// pass that gives every tile its first escape record (the layout and the
+// measurements are described with kTileWords).
 
-constexpr int kIndexThreads = 256;
-constexpr int kTileThreads = kTileWords / 8;    // 8 words per thread and tile
-constexpr uint32_t kTileGroupsPerCu = 2;  // 16-wave workgroups: 8 waves per SIMD
+constexpr int kTileThreads = kTileWords / 8;   // 8 words per thread
+constexpr uint32_t kAhead = 16;   // records a tile's first record looks ahead
+static_assert(kAhead > kSlotRecords && kAhead <= 64, "look-ahead past a full slot, within a wave");
+constexpr uint32_t kNoTile = 0xFFFFFFFFu;
+constexpr uint64_t kShortGap = 32;  // tile entries a lane fills alone
 
-// One workgroup per kIndexTiles consecutive tiles.  Record k is the first of
-// the tiles after its predecessor's tile up to its own; the tiles after the
-// block's last record get the block's end record.  Every record is checked
-// against its predecessor and against the block's words, exactly as in the
-// fused decode (neighbouring blocks find the same boundary record), and a
-// fault leaves this block's flag set (entries of a faulty container may stay
-// unwritten; the tile kernel clamps what it reads).
-__global__ __launch_bounds__(kIndexThreads) void k_tile_index(const uint8_t* __restrict__ src,
-                                                              uint64_t src_bytes, uint64_t n,
-                                                              uint64_t e,
-                                                              uint64_t* __restrict__ idx,
-                                                              uint32_t* __restrict__ flags) {
-    __shared__ uint64_t bounds[2];
+// An item of the index pass: record k < e, the end item k == e (position
+// n, tile `tiles`), or nothing past it (tile kNoTile).
+struct IndexItem {
+    uint64_t pos;
+    uint32_t tile;
+    uint32_t rec;  // offset in its tile | exponent << 16 (records only)
+};
+
+template <bool kOneSegment>
+__device__ __forceinline__ uint64_t item_position(const EscapeReader& rd, uint64_t k) {
+    return kOneSegment ? (uint64_t)rd.low32(k) : rd.position(k);
+}
+
+template <bool kOneSegment>
+__device__ __forceinline__ IndexItem index_item(const EscapeReader& rd, uint64_t n, uint64_t e,
+                                                uint64_t tiles, uint64_t k) {
+    IndexItem it{0, kNoTile, 0};
+    if (k < e) {
+        it.pos = item_position<kOneSegment>(rd, k);
+        it.tile = (uint32_t)min_u64(it.pos / kTileWords, tiles);
+        it.rec = (uint32_t)(it.pos - (uint64_t)it.tile * kTileWords) | ((uint32_t)rd.exps[k] << 16);
+    } else if (k == e) {
+        it.pos = n;
+        it.tile = (uint32_t)tiles;
+    }
+    return it;
+}
+
+// One wave per group of kIndexItems items, in kIndexRows rows of 64: lane
+// L holds items k0 + 64 r + L (row r) and, in lanes 0..15, the first 16
+// items after the group.  A lane whose item is the first of its tile fills
+// idx over the gap back to its predecessor's tile (a short gap alone, a
+// long one with the whole wave), sets the record count of the empty tiles
+// in it to 0, and writes its tile's slot from the 16 items after it, which
+// it reads from the lanes holding them (the next row, or the items after
+// the group, for the lanes near the end of a row).  The rows' loads go out
+// together, so a wave waits for memory once.  Faults: a position not above
+// its predecessor, or not below n; the header (wave 0).  kOneSegment:
+// n <= 2^32, every position is its stored low 32 bits.
+template <bool kOneSegment>
+__global__ __launch_bounds__(64) void k_tile_index(
+    const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e, uint64_t groups,
+    uint64_t* __restrict__ idx, uint32_t* __restrict__ flags, uint32_t* __restrict__ slots) {
     __shared__ uint64_t seg_table[16];
-    __shared__ int bad;
-    const int t = threadIdx.x;
-    const int wave = t >> 6;
-    if (t == 0) bad = 0;
-    if (blockIdx.x == 0 && t == 0 && !header_ok(src, src_bytes, n, e)) bad = 1;
+    const uint32_t lane = threadIdx.x;
+    bool bad = false;
+    if (blockIdx.x == 0 && lane == 0) bad = !header_ok(src, src_bytes, n, e);
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
     EscapeReader rd;
     rd.pos_lo = src + esc_off;
     rd.exps = rd.pos_lo + 4 * e;
     rd.aligned = (esc_off & 3) == 0;
-    rd.one_segment = n <= (1ull << 32);
+    rd.one_segment = kOneSegment;
     rd.seg_end = seg_table;
-    if (t < 16) seg_table[t] = reinterpret_cast<const uint64_t*>(src + 32)[t];
-    __syncthreads();
-
+    if (!kOneSegment) {  // the segment table is read only past 2^32 words
+        if (lane < 16) seg_table[lane] = reinterpret_cast<const uint64_t*>(src + 32)[lane];
+        __syncthreads();
+    }
     const uint64_t tiles = (n + kTileWords - 1) / kTileWords;
-    const uint64_t t_begin = min_u64((uint64_t)blockIdx.x * kIndexTiles, tiles);
-    const uint64_t t_end = min_u64(t_begin + kIndexTiles, tiles);
-    const uint64_t nt = t_end - t_begin;  // tiles of this block, <= kIndexTiles
-    const uint64_t begin = t_begin * kTileWords;
-    const uint64_t end = min_u64(t_end * kTileWords, n);
-    if (wave < 2) {
-        const uint64_t b = wave_lower_bound(rd, e, wave == 0 ? begin : end);
-        if ((t & 63) == 0) bounds[wave] = b;
-    }
-    __syncthreads();
-    const uint64_t k_lo = uniform64(bounds[0]);
-    const uint64_t k_hi = uniform64(bounds[1] > k_lo ? bounds[1] : k_lo);
-    if (t == 0 && blockIdx.x == gridDim.x - 1) {
-        if (bounds[1] != e) bad = 1;  // positions >= n
-        idx[tiles] = k_hi;
-    }
-
-    // the block-local tile of a record inside the block's words, else nt
-    auto local_tile = [&](uint64_t p) -> uint64_t {
-        return p >= begin && p < end ? (p - begin) / kTileWords : nt;
-    };
-    for (uint64_t k = k_lo + t; k <= k_hi; k += kIndexThreads) {
-        uint64_t cur = nt;  // k == k_hi: past the block's last tile
-        if (k < k_hi) {
-            const uint64_t p = rd.position(k);
-            cur = local_tile(p);
-            if (cur == nt || (k > 0 && !(p > rd.position(k - 1)))) bad = 1;
+    for (uint64_t g = blockIdx.x; g < groups; g += gridDim.x) {
+        const uint64_t k0 = g * kIndexItems;
+        // every row's items, and the items after the group, loaded together
+        IndexItem row[kIndexRows + 1];
+        uint64_t prev_pos[kIndexRows];
+#pragma unroll
+        for (uint32_t r = 0; r <= kIndexRows; r++) {
+            const uint64_t k = k0 + 64 * r + lane;
+            row[r] = r < kIndexRows || lane < kAhead ? index_item<kOneSegment>(rd, n, e, tiles, k)
+                                                     : IndexItem{0, kNoTile, 0};
+            if (r < kIndexRows)
+                prev_pos[r] = k > 0 && k <= e ? item_position<kOneSegment>(rd, k - 1) : 0;
         }
-        const uint64_t prev = k == k_lo ? 0 : local_tile(rd.position(k - 1)) + 1;
-        for (uint64_t j = prev; j <= cur && j < nt; j++) idx[t_begin + j] = k;
+#pragma unroll
+        for (uint32_t r = 0; r < kIndexRows; r++) {
+            const uint64_t k = k0 + 64 * r + lane;
+            const IndexItem& it = row[r];
+            const uint32_t prev_tile = k > 0 && k <= e
+                                           ? (uint32_t)min_u64(prev_pos[r] / kTileWords, tiles)
+                                           : kNoTile;
+            if (k < e && (it.pos >= n || (k > 0 && !(it.pos > prev_pos[r])))) bad = true;
+            const bool first = k <= e && (k == 0 || it.tile != prev_tile);
+
+            // the next 16 items' tiles and records: item k + j is lane
+            // L + j's item of this row when L + j < 64, else lane L + j - 64's
+            // item of the next row -- the same source lane S = (L + j) mod
+            // 64 either way, which offers this row's item when S >= j and the
+            // next row's when S < j
+            uint32_t run = 1;  // this tile's items from this one on, up to 17
+            bool same = true;
+            uint32_t slot[kSlotWords];
+            slot[1] = it.rec;
+#pragma unroll
+            for (uint32_t j = 1; j <= kAhead; j++) {
+                const int addr = (int)(((lane + j) & 63u) << 2);
+                const bool offer_this = lane >= j;
+                const uint32_t tl = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                    addr, (int)(offer_this ? it.tile : row[r + 1].tile));
+                same = same && k + j < e && tl == it.tile;  // a record of this tile
+                run += same ? 1u : 0u;
+                if (j < kSlotRecords) {
+                    const uint32_t rl = (uint32_t)__builtin_amdgcn_ds_bpermute(
+                        addr, (int)(offer_this ? it.rec : row[r + 1].rec));
+                    slot[1 + j] = same ? rl : 0u;
+                }
+            }
+            slot[0] = run;
+
+            // the gap: tiles (prev_tile, tile], the tiles before this one empty
+            const uint64_t lo = k == 0 ? 0 : (uint64_t)prev_tile + 1;
+            const uint64_t hi = it.tile;  // <= tiles for items up to the end item
+            const bool has_gap = first && hi >= lo;
+            if (has_gap && hi - lo < kShortGap) {
+                for (uint64_t jt = lo; jt <= hi; jt++) {
+                    idx[jt] = k;
+                    if (jt < hi && jt < tiles) slots[jt * kSlotWords] = 0;
+                }
+            }
+            uint64_t wide = __ballot(has_gap && hi - lo >= kShortGap);
+            while (wide) {  // long gaps: the whole wave fills one at a time
+                const int src_lane = __builtin_ctzll(wide);
+                wide &= wide - 1;
+                const uint64_t wlo = uniform64(__shfl(lo, src_lane, 64));
+                const uint64_t whi = uniform64(__shfl(hi, src_lane, 64));
+                const uint64_t wk = uniform64(__shfl(k, src_lane, 64));
+                for (uint64_t jt = wlo + lane; jt <= whi; jt += 64) {
+                    idx[jt] = wk;
+                    if (jt < whi && jt < tiles) slots[jt * kSlotWords] = 0;
+                }
+            }
+            if (first && k < e && it.tile < tiles) {
+                uint4* out = reinterpret_cast<uint4*>(slots + (uint64_t)it.tile * kSlotWords);
+#pragma unroll
+                for (uint32_t q = 0; q < kSlotWords; q += 4)
+                    out[q / 4] = make_uint4(slot[q], slot[q + 1], slot[q + 2], slot[q + 3]);
+            }
+        }
     }
-    __syncthreads();
-    if (t == 0) flags[blockIdx.x] = bad ? 1u : 0u;
+    bad = __ballot(bad) != 0;
+    if (lane == 0) flags[blockIdx.x] = bad ? 1u : 0u;
 }
 
 hipError_t launch_tile_index(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                              uint8_t* ws, hipStream_t stream) {
     const TileIndexLayout l = tile_index_layout(n);
-    k_tile_index<<<(uint32_t)l.blocks, kIndexThreads, 0, stream>>>(
-        src, src_bytes, n, e, reinterpret_cast<uint64_t*>(ws + l.idx_off),
-        reinterpret_cast<uint32_t*>(ws + l.flag_off));
+    const uint64_t groups = index_groups(e);
+    const uint64_t launched = min_u64(groups, l.max_flags);
+    uint64_t* idx = reinterpret_cast<uint64_t*>(ws + l.idx_off);
+    uint32_t* flags = reinterpret_cast<uint32_t*>(ws + l.flag_off);
+    uint32_t* slots = reinterpret_cast<uint32_t*>(ws + l.slot_off);
+    if (n <= (uint64_t{1} << 32))
+        k_tile_index<true><<<(uint32_t)launched, 64, 0, stream>>>(
+            src, src_bytes, n, e, groups, idx, flags, slots);
+    else
+        k_tile_index<false><<<(uint32_t)launched, 64, 0, stream>>>(
+            src, src_bytes, n, e, groups, idx, flags, slots);
     return hipGetLastError();
 }
 
-// Workgroup 0 first turns the index blocks' flags into the status word
-// (every index workgroup wrote its flag, so nothing needs clearing).  Per
-// tile: the codes and sign|mantissa bytes are loaded, the tile's records
-// (index entries clamped to [0, E]) mark an LDS exponent map and presence
-// bits, and each thread patches and rebuilds its 8 words.
-template <bool kAlignedSm, class Words>
-__global__ __launch_bounds__(kTileThreads) SZ_EIGHT_WAVE_SGPR_CAP
-__attribute__((amdgpu_waves_per_eu(8))) void k_decode_tiles(
-    const uint8_t* __restrict__ src, uint64_t n, uint64_t e, const uint64_t* __restrict__ idx,
-    const uint32_t* __restrict__ flags, uint32_t blocks, Words out, int32_t* status) {
-    __shared__ uint8_t patch_exp[2][kTileWords];
-    __shared__ uint32_t patch_bits[2][kTileWords / 32];
-    __shared__ uint64_t seg_table[16];
+// Exponent byte k (0..7) of the pair (e0: words 0..3, e1: words 4..7) set to x.
+__device__ __forceinline__ void set_exponent(uint32_t& e0, uint32_t& e1, uint32_t k, uint32_t x) {
+    const uint32_t sh = 8 * (k & 3);
+    const uint32_t m = 0xFFu << sh;
+    if (k < 4) e0 = (e0 & ~m) | (x << sh);
+    else e1 = (e1 & ~m) | (x << sh);
+}
+
+// One lane's candidate record (offset in the tile in bits 10..0, exponent
+// in bits 23..16) where `mine` (a wave ballot) has its bit set: the wave
+// walks only the records inside its own 512 words, by lane reads, and the
+// thread whose 8 words hold a record patches that exponent.  Offsets are
+// masked to the tile, so any record content patches only this tile.
+__device__ __forceinline__ void patch_wave(uint32_t v, uint64_t mine, uint32_t& e0, uint32_t& e1) {
+    const uint32_t first = 8u * (threadIdx.x % kTileThreads);
+    while (mine) {
+        const int j = __builtin_ctzll(mine);
+        mine &= mine - 1;
+        const uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)v, j);
+        const uint32_t d = (r & (kTileWords - 1)) - first;
+        if (d < 8) set_exponent(e0, e1, d, (r >> 16) & 0xFFu);
+    }
+}
+
+// The wave's 512-word quarter of the tile, as bits 10..9 of an offset.
+__device__ __forceinline__ uint32_t wave_quarter() { return (threadIdx.x % kTileThreads) >> 6; }
+
+// The records [ks, ke) of the tile starting at word t0, 64 at a time: each
+// lane loads one record, the wave keeps those inside its own words.
+// rd.pos_lo holds 4-byte aligned positions when `aligned`; only the low 32
+// bits are compared, a tile lying inside one 2^32-word segment.
+__device__ __forceinline__ void patch_records(const EscapeReader& rd, uint64_t ks, uint64_t ke,
+                                              uint64_t t0, uint32_t& e0, uint32_t& e1) {
+    const uint32_t lane = threadIdx.x & 63;
+    for (uint64_t q0 = ks; q0 < ke; q0 += 64) {
+        const uint64_t q = q0 + lane;
+        uint32_t v = 0;
+        bool in = false;
+        if (q < ke) {
+            const uint32_t d = rd.low32(q) - (uint32_t)t0;
+            in = d < kTileWords && (d >> 9) == wave_quarter();
+            v = d | ((uint32_t)rd.exps[q] << 16);
+        }
+        patch_wave(v, __ballot(in), e0, e1);
+    }
+}
+
+// A tile's records [ks, ke) marked in an LDS exponent map between two
+// barriers (every thread of the workgroup calls it), then patched into this
+// thread's 8 exponents: for tiles with many records, where a walk through
+// lane reads would take one step per record.
+struct TileMap {
+    uint8_t exp[kTileWords];
+    uint32_t bits[kTileWords / 32];
+};
+
+__device__ __forceinline__ void patch_mapped(const EscapeReader& rd, uint64_t ks, uint64_t ke,
+                                             uint64_t t0, uint32_t& e0, uint32_t& e1,
+                                             TileMap& map) {
     const int t = threadIdx.x;
-    if (blockIdx.x == 0 && status) {
+    if (t < (int)(kTileWords / 32)) map.bits[t] = 0;
+    __syncthreads();
+    for (uint64_t q = ks + t; q < ke; q += kTileThreads) {
+        const uint32_t d = rd.low32(q) - (uint32_t)t0;
+        if (d < kTileWords) {
+            map.exp[d] = rd.exps[q];
+            atomicOr(&map.bits[d >> 5], 1u << (d & 31));
+        }
+    }
+    __syncthreads();
+    const uint32_t present = (map.bits[t >> 2] >> (8 * (t & 3))) & 0xFFu;
+    if (present) {
+        const uint2 pe = *reinterpret_cast<const uint2*>(&map.exp[8 * t]);
+        e0 = bitselect(bits_to_bytes(present), pe.x, e0);
+        e1 = bitselect(bits_to_bytes(present >> 4), pe.y, e1);
+    }
+    __syncthreads();  // the map is reused by the next tile
+}
+
+// Workgroup 0 folds the index waves' fault flags into the status; workgroup
+// b > 0 decodes tile b - 1 (a launch holds at most kMaxTileGroups + 1; past
+// that each takes tiles b - 1, b - 1 + grid - 1, ...).  Per tile: the
+// slot, the codes and sign|mantissa bytes, all loaded before anything waits
+// on one; the slot's records patched in (or, for a tile with more records
+// than its slot, the index entries, clamped to [0, E] and to one tile's
+// worth of records, and the escape stream); one 16-byte non-temporal store
+// per thread.  kDense (containers averaging more records per tile than a
+// slot holds): a tile beyond its slot marks an LDS exponent map; otherwise
+// no LDS, no barrier, no atomic.
+template <bool kAlignedSm, class Words, bool kDense>
+__global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
+    const uint8_t* __restrict__ src, uint64_t n, uint64_t e, const uint64_t* __restrict__ idx,
+    const uint32_t* __restrict__ flags, uint64_t n_flags, const uint32_t* __restrict__ slots,
+    Words out, int32_t* status) {
+    struct NoMap {};
+    __shared__ typename std::conditional<kDense, TileMap, NoMap>::type map;
+    const int t = threadIdx.x;
+    const uint32_t lane = t & 63;
+    const uint64_t workers = gridDim.x - 1;  // workgroup 0 folds the flags
+    if (blockIdx.x == 0) {
         uint32_t any = 0;
-        for (uint32_t b = t; b < blocks; b += kTileThreads) any |= flags[b];
+#pragma unroll 8
+        for (uint64_t f = t; f < n_flags; f += kTileThreads) any |= flags[f];
         any = __syncthreads_or(any);
-        if (t == 0) *status = out.invalid() ? kStatusInvalid : (any ? kStatusCorrupt : 0);
+        if (t == 0 && status) *status = out.invalid() ? kStatusInvalid : (any ? kStatusCorrupt : 0);
+        return;
     }
     if (out.invalid()) return;  // the same for every thread
 
-    const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
     const uint8_t* nib = src + kPrefixBytes;
     const uint8_t* sm = nib + (n + 1) / 2;
+    const uint64_t tiles = (n + kTileWords - 1) / kTileWords;
+    const uint64_t whole = n / kTileWords;  // tiles with all kTileWords words
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
     EscapeReader rd;
     rd.pos_lo = src + esc_off;
     rd.exps = rd.pos_lo + 4 * e;
     rd.aligned = (esc_off & 3) == 0;
     rd.one_segment = n <= (1ull << 32);
-    rd.seg_end = seg_table;
-    if (t < 16) seg_table[t] = reinterpret_cast<const uint64_t*>(src + 32)[t];
-    __syncthreads();
+    rd.seg_end = nullptr;  // unused: tiles compare the low 32 bits only
 
-    const uint64_t tiles = (n + kTileWords - 1) / kTileWords;
-    const uint64_t whole = n / kTileWords;  // tiles with all kTileWords words
-    const uint32_t* pos32 = reinterpret_cast<const uint32_t*>(rd.pos_lo);
-    const bool fast_pos = rd.one_segment && rd.aligned;  // a position is its stored u32
-
-    // the tile's escape records into the LDS map: entries clamped to [0, E]
-    auto mark = [&](uint64_t tile, uint64_t t0, int parity) {
-        const uint64_t ks = min_u64(uniform64(idx[tile]), e);
-        const uint64_t ke = min_u64(uniform64(idx[tile + 1]), e);
-        if (t < (int)(kTileWords / 32)) patch_bits[parity][t] = 0;
-        __syncthreads();
-        for (uint64_t q = ks + t; q < ke; q += kTileThreads) {
-            const uint64_t d = (fast_pos ? (uint64_t)pos32[q] : rd.position(q)) - t0;
-            if (d < kTileWords) {
-                patch_exp[parity][d] = rd.exps[q];
-                atomicOr(&patch_bits[parity][d >> 5], 1u << (d & 31));
-            }
+    // the tile's records into e0/e1: from its slot, or, past the slot's
+    // capacity, from the escape stream
+    auto patch = [&](uint64_t tile, uint64_t t0, uint32_t sv, uint32_t& e0, uint32_t& e1) {
+        const uint32_t cnt = (uint32_t)__builtin_amdgcn_readfirstlane((int)sv);
+        if (cnt <= kSlotRecords) {
+            const bool in = lane >= 1 && lane <= cnt && ((sv >> 9) & 3u) == wave_quarter();
+            patch_wave(sv, __ballot(in), e0, e1);
+            return;
         }
-        __syncthreads();
-        return (patch_bits[parity][t >> 2] >> (8 * (t & 3))) & 0xFFu;  // this thread's 8 words
+        const uint64_t ks = min_u64(uniform64(idx[tile]), e);
+        uint64_t ke = min_u64(uniform64(idx[tile + 1]), e);
+        if (ke < ks) ke = ks;                              // a faulty index: flagged
+        if (ke - ks > kTileWords) ke = ks + kTileWords;
+        if constexpr (kDense) patch_mapped(rd, ks, ke, t0, e0, e1, map);
+        else patch_records(rd, ks, ke, t0, e0, e1);
     };
 
-    int parity = 0;
-    // whole tiles: no per-word checks
-    for (uint64_t tile = blockIdx.x; tile < whole; tile += gridDim.x, parity ^= 1) {
+    for (uint64_t tile = blockIdx.x - 1; tile < tiles; tile += workers) {
         const uint64_t t0 = tile * kTileWords;
         const uint64_t i0 = t0 + (uint64_t)t * 8;
-        // a wave's words are 512 consecutive words: one page, whose address
-        // (a page-table load for a paged tensor) is looked up before the
-        // tile's loads so that its latency overlaps theirs
-        uint16_t* words_out = nullptr;
-        if constexpr (Words::kPaged) words_out = out.at_wave(i0);
-        const uint32_t codes = *reinterpret_cast<const uint32_t*>(nib + i0 / 2);
-        uint32_t s0, s1;
-        if (kAlignedSm) {
-            const uint2 v = *reinterpret_cast<const uint2*>(sm + i0);
-            s0 = v.x;
-            s1 = v.y;
+        // every load of the tile goes out before anything waits on one
+        const uint32_t sv = lane < kSlotWords ? slots[tile * kSlotWords + lane] : 0u;
+        if (tile < whole) {
+            const uint32_t codes = *reinterpret_cast<const uint32_t*>(nib + i0 / 2);
+            uint32_t s0, s1;
+            if (kAlignedSm) {
+                const uint2 v = *reinterpret_cast<const uint2*>(sm + i0);
+                s0 = v.x;
+                s1 = v.y;
+            } else {
+                s0 = load4_unaligned(sm + i0);
+                s1 = load4_unaligned(sm + i0 + 4);
+            }
+            // a wave's words are 512 consecutive words: one page
+            uint16_t* words_out = nullptr;
+            if constexpr (Words::kPaged) words_out = out.at_wave(i0);
+            const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
+            uint32_t e0, e1;
+            exponents8(codes, cb, e0, e1);
+            patch(tile, t0, sv, e0, e1);
+            if constexpr (!Words::kPaged) words_out = out.at_wave(i0);
+            // written past the caches: a decode's output is larger than they
+            // are, and lines left dirty cost the next kernel their write-back
+            store_streaming(reinterpret_cast<uint4*>(words_out), words8(e0, e1, s0, s1));
         } else {
-            s0 = load4_unaligned(sm + i0);
-            s1 = load4_unaligned(sm + i0 + 4);
-        }
-        const uint32_t present = mark(tile, t0, parity);
-        uint32_t e0, e1;
-        exponents8(codes, cb, e0, e1);
-        if (present) {
-            const uint2 pe = *reinterpret_cast<const uint2*>(&patch_exp[parity][8 * t]);
-            e0 = bitselect(bits_to_bytes(present), pe.x, e0);
-            e1 = bitselect(bits_to_bytes(present >> 4), pe.y, e1);
-        }
-        // The tensor is larger than the caches (this form runs from 2^26
-        // words), so its lines are written past them: none is left dirty for
-        // the next kernel to write back (on MI355X the encode that follows a
-        // 1 GiB decode ran 24 us faster, the decode itself 4 us slower).
-        if constexpr (!Words::kPaged) words_out = out.at_wave(i0);
-        store_streaming(reinterpret_cast<uint4*>(words_out), words8(e0, e1, s0, s1));
-    }
-    // the last, partial tile, by the workgroup whose turn it is
-    if (whole < tiles && blockIdx.x == whole % gridDim.x) {
-        const uint64_t t0 = whole * kTileWords;
-        const uint32_t present = mark(whole, t0, parity);
-        const uint64_t i0 = t0 + (uint64_t)t * 8;
-        for (uint32_t k = 0; k < 8 && i0 + k < n; k++) {
-            const uint64_t i = i0 + k;
-            const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
-            const uint32_t ex = (present >> k) & 1u ? patch_exp[parity][8 * t + k]
-                                                    : codebook_byte(cb, code);
-            *out.at(i) = (uint16_t)recombine(sm[i], ex);
+            // the partial last tile: words past n are neither read nor written
+            const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
+            uint32_t ex[8];
+            for (uint32_t k = 0; k < 8; k++) {
+                const uint64_t i = i0 + k;
+                ex[k] = i < n ? codebook_byte(cb, (nib[i / 2] >> (4 * (i & 1))) & 0xFu) : 0u;
+            }
+            uint32_t e0 = ex[0] | (ex[1] << 8) | (ex[2] << 16) | (ex[3] << 24);
+            uint32_t e1 = ex[4] | (ex[5] << 8) | (ex[6] << 16) | (ex[7] << 24);
+            patch(tile, t0, sv, e0, e1);
+            for (uint32_t k = 0; k < 8 && i0 + k < n; k++) {
+                const uint32_t x = ((k < 4 ? e0 : e1) >> (8 * (k & 3))) & 0xFFu;
+                *out.at(i0 + k) = (uint16_t)recombine(sm[i0 + k], x);
+            }
         }
     }
 }
 
 template <class Words>
 hipError_t launch_decode_tiles(const uint8_t* src, uint64_t n, uint64_t e, const uint8_t* ws,
-                               Words dst, int32_t* status, int num_cus, hipStream_t stream) {
+                               Words dst, int32_t* status, int /*num_cus*/, hipStream_t stream) {
     const TileIndexLayout l = tile_index_layout(n);
-    uint64_t groups = (uint64_t)(num_cus > 0 ? num_cus : 256) * kTileGroupsPerCu;
-    if (groups > l.tiles) groups = l.tiles;
-    if (groups == 0) groups = 1;  // the status is still written
+    const uint64_t n_flags = min_u64(index_groups(e), l.max_flags);
+    // the one that writes the status, then the tiles' workgroups
+    const uint64_t groups = min_u64(l.tiles, kMaxTileGroups) + 1;
     const uint64_t* idx = reinterpret_cast<const uint64_t*>(ws + l.idx_off);
     const uint32_t* flags = reinterpret_cast<const uint32_t*>(ws + l.flag_off);
+    const uint32_t* slots = reinterpret_cast<const uint32_t*>(ws + l.slot_off);
     const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
-    if (aligned)
-        k_decode_tiles<true, Words><<<(uint32_t)groups, kTileThreads, 0, stream>>>(
-            src, n, e, idx, flags, (uint32_t)l.blocks, dst, status);
-    else
-        k_decode_tiles<false, Words><<<(uint32_t)groups, kTileThreads, 0, stream>>>(
-            src, n, e, idx, flags, (uint32_t)l.blocks, dst, status);
+    const bool dense = e > l.tiles * kSlotRecords;
+#define SZ_TILES(A, D)                                                                   \
+    k_decode_tiles<A, Words, D><<<(uint32_t)groups, kTileThreads, 0, stream>>>(          \
+        src, n, e, idx, flags, n_flags, slots, dst, status)
+    if (aligned && !dense) SZ_TILES(true, false);
+    else if (aligned) SZ_TILES(true, true);
+    else if (!dense) SZ_TILES(false, false);
+    else SZ_TILES(false, true);
+#undef SZ_TILES
     return hipGetLastError();
 }
 

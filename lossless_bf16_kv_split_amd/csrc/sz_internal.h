@@ -115,31 +115,55 @@ constexpr uint64_t kTileDecodeDensity = 128;
 constexpr uint64_t kScatterDecodeDensity = 256;
 constexpr uint64_t kTileDecodeMin = uint64_t{1} << 26;
 
-// Tile decode (the single pass with words handed out grid-stride): its
-// workspace holds the first escape record of every 8192-word tile and one
-// flag per index workgroup (32 tiles each).  Measured on MI355X (1 GiB KV
-// round trip, one process): 8192-word tiles with two workgroups per CU
-// decode in 336-338 us against 345 us for 4096-word tiles with four, 363 us
-// for 2048-word tiles with eight; 32 tiles per index workgroup keep the
-// index pass at 13.6 us (64: 16.5 us).
-constexpr uint32_t kTileWords = 8192;
-constexpr uint32_t kIndexTiles = 32;
+// Tile decode: one short-lived 256-thread workgroup per 2048-word tile (8
+// words per thread), after an index pass that gives every tile its first
+// escape record.  On MI355X many small workgroups that each move one
+// 16-byte piece per thread and byte stream beat fewer workgroups that
+// loop: for the decode's traffic (1.5 B read, 2 B
+// written per word) on 2^29 words, 298 us with one 2048-word tile per
+// 256-thread workgroup against 328 us for the best persistent grid.
+//
+// The index pass is search-free and runs one wave per 64 items, the items
+// being the E escape records and, as item E, the end of the words (position
+// n, tile `tiles`).  An item whose tile differs from its predecessor's is
+// the first of its tile: it writes idx[j] = its index for every tile j after
+// its predecessor's tile up to its own (the tiles in between have no
+// records) and its tile's 64-byte slot: dword 0 the tile's record count (up
+// to 16 records ahead are seen, so a count above 15 only says "more than
+// 15"), dwords 1..15 the first 15 records as (offset in the tile) |
+// exponent << 16.  The decode of a tile loads its slot together with its
+// codes and sign|mantissa bytes, so a tile with at most 15 records (on the
+// 1 GiB KV tensor all but 0.014% of them, 4 on average) waits for no load
+// that depends on another; a tile with more goes through idx and the
+// escape stream.  Each launched wave writes its own fault flag (a launch
+// holds at most kMaxIndexGroups waves; past that each takes several groups
+// of 64 items).
+constexpr uint32_t kTileWords = 2048;
+constexpr uint32_t kIndexRows = 1;            // rows of 64 items per index wave
+constexpr uint32_t kIndexItems = 64 * kIndexRows;  // items per index wave
+constexpr uint64_t kMaxIndexGroups = uint64_t{1} << 20;  // launched; more loop
+constexpr uint64_t kMaxTileGroups = uint64_t{1} << 22;   // launched; more loop
+constexpr uint32_t kSlotWords = 16;                      // dwords per tile slot
+constexpr uint32_t kSlotRecords = kSlotWords - 1;
 struct TileIndexLayout {
-    uint64_t tiles = 0;     // ceil(n / kTileWords)
-    uint64_t blocks = 0;    // index workgroups, at least 1
-    uint64_t idx_off = 0;   // u64[tiles + 1]: first record of each tile, then E
-    uint64_t flag_off = 0;  // u32[blocks]: 1 where an index workgroup found a fault
+    uint64_t tiles = 0;       // ceil(n / kTileWords)
+    uint64_t max_flags = 0;   // launched index waves for any E <= floor(15n/16)
+    uint64_t idx_off = 0;     // u64[tiles + 1]: first record of each tile, then E
+    uint64_t flag_off = 0;    // u32[max_flags]: 1 where an index wave found a fault
+    uint64_t slot_off = 0;    // u32[tiles][kSlotWords]: each tile's record count and records
     uint64_t bytes = 0;
 };
+inline uint64_t index_groups(uint64_t e) { return (e + 1 + kIndexItems - 1) / kIndexItems; }
 inline TileIndexLayout tile_index_layout(uint64_t n) {
     TileIndexLayout l;
     l.tiles = (n + kTileWords - 1) / kTileWords;
-    l.blocks = (l.tiles + kIndexTiles - 1) / kIndexTiles;
-    if (l.blocks == 0) l.blocks = 1;
+    const uint64_t max_groups = index_groups((15 * n) / 16);
+    l.max_flags = max_groups < kMaxIndexGroups ? max_groups : kMaxIndexGroups;
     auto align = [](uint64_t x) { return (x + 255) & ~uint64_t{255}; };
     l.idx_off = 0;
     l.flag_off = align(8 * (l.tiles + 1));
-    l.bytes = align(l.flag_off + 4 * l.blocks);
+    l.slot_off = align(l.flag_off + 4 * l.max_flags);
+    l.bytes = align(l.slot_off + 4 * kSlotWords * l.tiles);
     return l;
 }
 

@@ -167,10 +167,15 @@ def test_single_read_host_checks(sz):
 
 
 def test_tile_decode_host_checks(sz):
-    for n in (0, 1, 8192, 8193, 1 << 29):
-        tiles = -(-n // 8192)
-        blocks = max(1, -(-tiles // 32))
-        want = -(-(-(-8 * (tiles + 1) // 256) * 256 + 4 * blocks) // 256) * 256
+    def align(x):
+        return -(-x // 256) * 256
+    for n in (0, 1, 2048, 2049, 8193, 1 << 29, 5 << 30, 1 << 36):
+        # u64 first record per 2048-word tile (+ end entry); a u32 fault flag
+        # per index wave of 64 items for the largest E (at most 2^20
+        # launched); a 64-byte record slot per tile
+        tiles = -(-n // 2048)
+        flags = min(-(-((15 * n) // 16 + 1) // 64), 1 << 20)
+        want = align(align(align(8 * (tiles + 1)) + 4 * flags) + 64 * tiles)
         assert sz.sz_decode_workspace_size(n) == want, n
     assert sz.sz_decode_workspace_size((1 << 36) + 1) == 0
     n = 1000
@@ -186,6 +191,7 @@ def test_tile_decode_host_checks(sz):
     assert status_of(sz.sz_decode_tiles, A, fixed, W, ws - 1, D, n, None, 0) == 1
     assert status_of(sz.sz_decode_tiles, A, fixed - 1, W, ws, D, n, None, 0) == 4
     assert status_of(sz.sz_decode_tiles, A, fixed, W, ws, W + 256, n, None, 0) == 1  # overlap
+    assert status_of(sz.sz_decode_tiles, A, fixed, A + 256, ws, D, n, None, 0) == 1  # with src
     assert status_of(sz.sz_decode_tiles, A, fixed, W, ws, D, (1 << 36) + 1, None, 0) == 3
 
 

@@ -9,7 +9,8 @@ decode starts and where it ends, so encode and decode are timed separately
 inside the timed region; `value` is uncompressed bytes (2 per BF16 word) per
 step time.  Which passes: encode as exponent histogram -> top-16 codebook ->
 pack, or, from 2^26 words on, as sample -> first pass (pack with the sampled
-codebook while counting) -> codebook -> finish; decode in the form sz_decode
+codebook while counting) -> finish (exact codebook, then keep, remap or pack
+again); decode in the form sz_decode
 picks for the escape density.
 
 After the timed region: the public sz_encode and sz_decode calls (each
@@ -49,9 +50,9 @@ KERNEL_SOURCES = ["lossless_bf16_kv_split_amd/csrc/encode.hip",
                   "lossless_bf16_kv_split_amd/csrc/decode.hip",
                   "lossless_bf16_kv_split_amd/csrc/sz_internal.h"]
 TWO_READ_PASSES = ["histogram", "codebook", "pack"]
-SINGLE_READ_PASSES = ["sample", "first", "codebook", "finish"]
-KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_merge_counts+k_select",
-                "pack": "k_pack", "sample": "k_sample+k_rank_sample",
+SINGLE_READ_PASSES = ["sample", "first", "finish"]
+KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_codebook",
+                "pack": "k_pack", "sample": "k_sample",
                 "first": "k_pack(first pass)", "finish": "k_finish",
                 "fused": "k_decode_fused", "dense": "k_decode_dense",
                 "index": "k_tile_index", "tiles": "k_decode_tiles",
@@ -467,7 +468,7 @@ def main() -> int:
         elif p == "first":
             sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap, stream)
         elif p == "finish":
-            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, stream)
+            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, size, stream)
         elif p == "fused":
             sz.sz_decode_fused(container, total, dst_words, n, status, stream)
         elif p == "dense":

@@ -177,17 +177,19 @@ sz_status sz_encode_pack(const void *d_src, uint64_t n_elements,
                          void *d_dst, uint64_t dst_capacity, hipStream_t stream);
 
 /* ---- staged form of the single-read encode (n >= 2^20) -----------------
- * sz_encode_sample; sz_encode_first_pass; sz_encode_codebook;
- * sz_encode_finish on one stream, one workspace, gives the container of
- * sz_encode.  Not part of the pages'
+ * sz_encode_sample; sz_encode_first_pass; sz_encode_finish on one stream,
+ * one workspace, gives the container of sz_encode.  Not part of the pages'
  * method: a way to read the input once.  A fixed sample (512 blocks of 2048
  * words spread evenly over the input) gives a provisional codebook by the
  * same ranking rule; the first pass packs every chunk with it while it
- * takes the exact per-chunk counts; the finish pass keeps what the first
- * pass wrote when the exact codebook equals the provisional one, rewrites
- * the 4-bit codes when it holds the same 16 exponents in another order, and
- * packs again (a second read) otherwise, or when a chunk held more than
- * 1/16 escapes, or when the sample predicted more than one escape in 32.
+ * takes the exact counts; the finish pass ranks the exact codebook, then
+ * keeps what the first pass wrote when the exact codebook equals the
+ * provisional one, rewrites the 4-bit codes when it holds the same 16
+ * exponents in another order, and packs again (a second read) otherwise,
+ * or when a chunk held more than 1/16 escapes, or when the sample predicted
+ * more than one escape in 32.  The workspace may hold any bytes before the
+ * first call: every call gives the same container (the first call on a
+ * workspace in an unknown state may take the slower finish).
  * These calls return SZ_ERR_INVALID_ARGUMENT for n < 2^20 (besides the
  * checks of the two-read calls); the first pass and the finish use the bytes
  * of d_dst past the container, up to sz_max_compressed_size(n), as scratch. */
@@ -209,11 +211,14 @@ sz_status sz_encode_first_pass(const void *d_src, uint64_t n_elements,
                                void *d_workspace, uint64_t workspace_bytes,
                                void *d_dst, uint64_t dst_capacity, hipStream_t stream);
 
-/* After sz_encode_codebook: escape records to their final slots, codes
- * rewritten, or the input packed again, as described above. */
+/* The exact codebook (the selection of section "3. La strategie SplitZip",
+ * as sz_encode_codebook takes it), the header, and the container size to
+ * *d_compressed_size (optional); then escape records to their final slots,
+ * codes rewritten, or the input packed again, as described above. */
 sz_status sz_encode_finish(const void *d_src, uint64_t n_elements,
-                           const void *d_workspace, uint64_t workspace_bytes,
-                           void *d_dst, uint64_t dst_capacity, hipStream_t stream);
+                           void *d_workspace, uint64_t workspace_bytes,
+                           void *d_dst, uint64_t dst_capacity,
+                           uint64_t *d_compressed_size, hipStream_t stream);
 
 /* Decode pass 1: header check (sets *d_status to SZ_OK or SZ_ERR_CORRUPT)
  * and every word rebuilt from its code and its sign|mantissa byte. */

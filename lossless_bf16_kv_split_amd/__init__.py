@@ -76,7 +76,7 @@ def _load() -> ctypes.CDLL:
     L.sz_encode_single_read.restype = i32
     L.sz_encode_sample.argtypes = [p, u64, p, u64, p]
     L.sz_encode_first_pass.argtypes = [p, u64, p, u64, p, u64, p]
-    L.sz_encode_finish.argtypes = [p, u64, p, u64, p, u64, p]
+    L.sz_encode_finish.argtypes = [p, u64, p, u64, p, u64, p, p]
     L.sz_decode_unpack.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_scatter.argtypes = [p, u64, p, u64, p, p]
     L.sz_decode_fused.argtypes = [p, u64, p, u64, p, p]
@@ -196,9 +196,10 @@ def sz_encode_first_pass(src, n_elements: int, workspace, workspace_bytes: int, 
 
 
 def sz_encode_finish(src, n_elements: int, workspace, workspace_bytes: int, dst,
-                     dst_capacity: int, stream=None) -> None:
+                     dst_capacity: int, d_compressed_size=None, stream=None) -> None:
     _check(_lib.sz_encode_finish(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
-                                 _ptr(dst), dst_capacity, _stream(stream)), "sz_encode_finish")
+                                 _ptr(dst), dst_capacity, _ptr(d_compressed_size),
+                                 _stream(stream)), "sz_encode_finish")
 
 
 def sz_decode_unpack(src, src_bytes: int, dst, n_elements: int, d_status=None,

@@ -129,8 +129,8 @@ sz_status encode_passes(Words src, uint64_t n, const sz::EncodePlan& p, uint8_t*
         // pass reads it again only when it does not
         st = hip_status(sz::launch_sample(src, p, w, stream));
         if (st == SZ_OK) st = hip_status(sz::launch_first_pass(src, p, w, out, dst_capacity, stream));
-        if (st == SZ_OK) st = hip_status(sz::launch_codebook(p, w, out, d_compressed_size, stream));
-        if (st == SZ_OK) st = hip_status(sz::launch_finish(src, p, w, out, dst_capacity, stream));
+        if (st == SZ_OK)
+            st = hip_status(sz::launch_finish(src, p, w, out, dst_capacity, d_compressed_size, stream));
     } else {
         st = hip_status(sz::launch_histogram(src, p, w, stream));
         if (st == SZ_OK) st = hip_status(sz::launch_codebook(p, w, out, d_compressed_size, stream));
@@ -309,15 +309,16 @@ sz_status sz_encode_first_pass(const void* d_src, uint64_t n, void* d_workspace,
                                             static_cast<uint8_t*>(d_dst), dst_capacity, stream));
 }
 
-sz_status sz_encode_finish(const void* d_src, uint64_t n, const void* d_workspace,
+sz_status sz_encode_finish(const void* d_src, uint64_t n, void* d_workspace,
                            uint64_t workspace_bytes, void* d_dst, uint64_t dst_capacity,
-                           hipStream_t stream) {
+                           uint64_t* d_compressed_size, hipStream_t stream) {
     if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
     const sz::EncodePlan p = sz::plan_encode(n);
     if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
     if (sz_status s = check_single_read(p, dst_capacity)) return s;
-    return hip_status(sz::launch_finish(flat(d_src), p, static_cast<const uint8_t*>(d_workspace),
-                                        static_cast<uint8_t*>(d_dst), dst_capacity, stream));
+    return hip_status(sz::launch_finish(flat(d_src), p, static_cast<uint8_t*>(d_workspace),
+                                        static_cast<uint8_t*>(d_dst), dst_capacity,
+                                        d_compressed_size, stream));
 }
 
 sz_status sz_encode(const void* d_src, uint64_t n, void* d_dst, uint64_t dst_capacity,

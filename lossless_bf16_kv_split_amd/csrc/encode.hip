@@ -70,7 +70,9 @@ EncodePlan plan_encode(uint64_t n) {
     p.counts_off = 0;
     p.hist_off = align(p.counts_off + (uint64_t)p.chunks * 256 * 4);
     p.base_off = align(p.hist_off + 256 * 8);
-    p.sample_off = align(p.base_off + (uint64_t)p.chunks * 8);
+    p.totals_off = align(p.base_off + (uint64_t)p.chunks * 8);
+    p.esc_off = align(p.totals_off + kTotalCopies * 256 * 8);
+    p.sample_off = align(p.esc_off + (uint64_t)p.chunks * 4);
     p.ws_bytes = align(p.sample_off + sizeof(SampleArea));
     // scratch for the provisional escape records: past every container
     // whose chunks each hold at most spec_cap escapes, inside the worst-case
@@ -147,12 +149,20 @@ __device__ __forceinline__ void count_exponents(Words src, uint64_t begin, uint6
 
 // counts[bin * chunks + chunk]: bin-major, so that the codebook pass reads
 // every bin's counts, and each chunk's 16 codebook counts, coalesced
+// Workgroup 0 also zeroes what the codebook pass counts up: the whole
+// input's counts and the number of its workgroups done.
 template <class Words>
 __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t n,
                                                             uint32_t chunk_log2, uint32_t chunks,
-                                                            uint32_t* __restrict__ counts) {
+                                                            uint32_t* __restrict__ counts,
+                                                            uint64_t* __restrict__ hist,
+                                                            uint32_t* __restrict__ arrivals) {
     __shared__ uint32_t h[kHistCopies * kHistPitch];
-    if (src.invalid()) return;  // the same for every thread
+    if (blockIdx.x == 0) {
+        for (int b = threadIdx.x; b < 256; b += kHistThreads) hist[b] = 0;
+        if (threadIdx.x == 0) *arrivals = 0;
+    }
+    if (blockIdx.x >= chunks || src.invalid()) return;  // the same for every thread
     for (int i = threadIdx.x; i < kHistCopies * kHistPitch; i += kHistThreads) h[i] = 0;
     __syncthreads();
 
@@ -171,9 +181,11 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t 
 
 template <class Words>
 hipError_t launch_histogram(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream) {
-    if (p.chunks == 0) return hipSuccess;
-    k_histogram<Words><<<p.chunks, kHistThreads, 0, stream>>>(
-        src, p.n, p.chunk_log2, p.chunks, reinterpret_cast<uint32_t*>(ws + p.counts_off));
+    const uint32_t groups = p.chunks > 0 ? p.chunks : 1;  // the accumulators are zeroed
+    k_histogram<Words><<<groups, kHistThreads, 0, stream>>>(
+        src, p.n, p.chunk_log2, p.chunks, reinterpret_cast<uint32_t*>(ws + p.counts_off),
+        reinterpret_cast<uint64_t*>(ws + p.hist_off),
+        &reinterpret_cast<SampleArea*>(ws + p.sample_off)->arrivals);
     return hipGetLastError();
 }
 template hipError_t launch_histogram<FlatWords>(FlatWords, const EncodePlan&, uint8_t*,
@@ -207,38 +219,6 @@ hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, in
 
 // ---------------------------------------------------------------- pass 2
 
-// hist[bin] = sum over chunks of counts[bin][chunk]; one workgroup per bin,
-// every load coalesced and in flight at once.
-constexpr int kMergeThreads = 256;
-constexpr uint32_t kMergePerThread = kMaxChunks / kMergeThreads;
-
-__global__ __launch_bounds__(kMergeThreads) void k_merge_counts(const uint32_t* __restrict__ counts,
-                                                               uint32_t chunks,
-                                                               uint64_t* __restrict__ hist) {
-    __shared__ uint64_t wave_sum[kMergeThreads / 64];
-    const uint32_t bin = blockIdx.x;
-    const uint32_t t = threadIdx.x;
-    const uint32_t* row = counts + (uint64_t)bin * chunks;
-    uint32_t v[kMergePerThread];
-#pragma unroll
-    for (uint32_t j = 0; j < kMergePerThread; j++) {
-        const uint32_t c = t + j * kMergeThreads;
-        v[j] = c < chunks ? row[c] : 0u;
-    }
-    uint64_t s = 0;
-#pragma unroll
-    for (uint32_t j = 0; j < kMergePerThread; j++) s += v[j];
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) s += __shfl_down(s, d, 64);
-    if ((t & 63) == 0) wave_sum[t >> 6] = s;
-    __syncthreads();
-    if (t == 0) {
-        uint64_t total = 0;
-        for (int w = 0; w < kMergeThreads / 64; w++) total += wave_sum[w];
-        hist[bin] = total;
-    }
-}
-
 constexpr int kSelectThreads = 1024;
 constexpr int kSelectWaves = kSelectThreads / 64;
 constexpr int kSelectChunks = kMaxChunks / kSelectThreads;  // chunks per select thread
@@ -253,56 +233,39 @@ __device__ __forceinline__ uint64_t wave_inclusive_sum(uint64_t v) {
     return v;
 }
 
-// One workgroup.  chunk_base[b] receives the number of escapes in chunks
-// before b, which is where chunk b's escape records start.
-__global__ __launch_bounds__(kSelectThreads) void k_select(
-    uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
-    const uint64_t* __restrict__ hist, uint64_t* __restrict__ chunk_base,
-    uint8_t* __restrict__ dst, uint64_t* d_size) {
-    __shared__ uint64_t key[256];
-    __shared__ uint32_t rank_part[4][256];
-    __shared__ uint32_t codebook[16];
-    __shared__ uint64_t wave_sum[kSelectWaves];
-    __shared__ uint64_t wave_off[kSelectWaves];
-    __shared__ uint64_t base_lds[kMaxChunks];
-
+// Rank of each exponent among the 256 by its key in LDS (count << 8 |
+// 255 - exponent: larger key, earlier code; the keys are distinct), as the
+// number of larger keys; four groups of 256 threads each compare against
+// 64 of the keys.  The caller synchronises after writing the keys.  Returns
+// the rank of exponent t to threads t < 256.
+__device__ __forceinline__ uint32_t rank_exponents(const uint64_t* key, uint32_t (*part)[256]) {
     const int t = threadIdx.x;
-    const int bin = t & 255;
-    const int grp = t >> 8;  // 0..3
-    if (t < 16) codebook[t] = 0;
-
-    // key(x) = count << 8 | (255 - x): "more frequent, then smaller exponent"
-    // becomes one unsigned comparison (counts stay below 2^37)
-    if (t < 256) key[t] = (hist[t] << 8) | (255u - t);
-    __syncthreads();
-
-    // rank(x) = #{y : key(y) > key(x)}; group g counts over y in [64g, 64g + 64)
-    {
-        const uint64_t kx = key[bin];
-        uint32_t r = 0;
+    const int bin = t & 255, grp = t >> 8;  // 0..3
+    const uint64_t kx = key[bin];
+    uint32_t r = 0;
 #pragma unroll 16
-        for (int y = grp * 64; y < grp * 64 + 64; y++) r += key[y] > kx ? 1u : 0u;
-        rank_part[grp][bin] = r;
-    }
+    for (int y = grp * 64; y < grp * 64 + 64; y++) r += key[y] > kx ? 1u : 0u;
+    part[grp][bin] = r;
     __syncthreads();
-    if (t < 256) {
-        const uint32_t r = rank_part[0][t] + rank_part[1][t] + rank_part[2][t] + rank_part[3][t];
-        if (r < 16) codebook[r] = (uint32_t)t;
-    }
-    __syncthreads();
+    return t < 256 ? part[0][t] + part[1][t] + part[2][t] + part[3][t] : 0u;
+}
 
-    // thread t takes chunks per * t .. per * t + per - 1 (per is the same
-    // for the whole workgroup): the escapes of a chunk = chunk length -
-    // elements whose exponent is in the codebook.  Four chunks a thread,
-    // 16-byte aligned, are read with 16-byte loads; otherwise two chunks per
-    // round of loads (one round up to 2048 chunks; two keep the counts of up
-    // to four chunks from spilling).  The codebook is the same in every lane:
-    // scalar row addresses.
+// Escape counts of chunks per * t .. per * t + per - 1 (per = ceil(chunks /
+// 1024), the same for the whole workgroup) under the codebook in LDS: chunk
+// length - elements whose exponent is in the codebook, from the bin-major
+// per-chunk counts.  Four chunks a thread, 16-byte aligned, are read with
+// 16-byte loads; otherwise two chunks per round of loads (one round up to
+// 2048 chunks; two keep the counts of up to four chunks from spilling).  The
+// codebook is the same in every lane: scalar row addresses.
+__device__ __forceinline__ void exact_chunk_escapes(const uint32_t* __restrict__ counts,
+                                                    uint32_t chunks, uint32_t chunk_log2,
+                                                    uint64_t n, const uint32_t* codebook,
+                                                    uint64_t (&esc)[kSelectChunks]) {
+    const int t = threadIdx.x;
     uint32_t cb[16];
 #pragma unroll
     for (int c = 0; c < 16; c++) cb[c] = __builtin_amdgcn_readfirstlane(codebook[c] & 255u);
     const uint32_t per = (chunks + kSelectThreads - 1) / kSelectThreads;  // <= kSelectChunks
-    uint64_t esc[kSelectChunks] = {};
     if (per == 4 && chunks % 4 == 0) {
         // four contiguous chunks per thread, 16-byte aligned: one 16-byte
         // load per codebook row, the rows in two halves of eight
@@ -359,13 +322,41 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
             }
         }
     }
+}
 
-    // exclusive scan of the per-chunk escape counts over the workgroup
+// The same escape counts one chunk at a time (its 16 codebook rows in
+// flight together), for a kernel held to 64 registers a lane.
+__device__ __forceinline__ void exact_chunk_escapes_narrow(const uint32_t* __restrict__ counts,
+                                                           uint32_t chunks, uint32_t chunk_log2,
+                                                           uint64_t n, const uint32_t* codebook,
+                                                           uint64_t (&esc)[kSelectChunks]) {
+    const int t = threadIdx.x;
+    const uint32_t per = (chunks + kSelectThreads - 1) / kSelectThreads;  // <= kSelectChunks
+#pragma unroll
+    for (int j = 0; j < kSelectChunks; j++) {
+        const uint32_t b = per * t + j;
+        if ((uint32_t)j < per && b < chunks) {
+            uint64_t kept = 0;
+#pragma unroll
+            for (int c = 0; c < 16; c++) kept += counts[(uint64_t)codebook[c] * chunks + b];
+            const uint64_t start = (uint64_t)b << chunk_log2;
+            esc[j] = min_u64(uint64_t{1} << chunk_log2, n - start) - kept;
+        }
+    }
+}
+
+// Exclusive scan of the chunks' escape counts (each thread's kSelectChunks
+// in order) over the 1024-thread workgroup: returns the escapes before this
+// thread's first chunk, and the total E to every thread.
+__device__ __forceinline__ uint64_t scan_chunk_escapes(const uint64_t (&esc)[kSelectChunks],
+                                                       uint64_t* wave_sum, uint64_t* wave_off,
+                                                       uint64_t& E) {
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
     uint64_t mine = 0;
 #pragma unroll
     for (int j = 0; j < kSelectChunks; j++) mine += esc[j];
     const uint64_t incl = wave_inclusive_sum(mine);
-    const int lane = t & 63, wave = t >> 6;
     if (lane == 63) wave_sum[wave] = incl;
     __syncthreads();
     if (t == 0) {
@@ -376,7 +367,84 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
         }
     }
     __syncthreads();
-    uint64_t excl = wave_off[wave] + incl - mine;
+    E = wave_off[kSelectWaves - 1] + wave_sum[kSelectWaves - 1];
+    return wave_off[wave] + incl - mine;
+}
+
+// The codebook pass, one launch of 256 workgroups: workgroup b sums bin b's
+// counts over the chunks (every load in flight at once, bin-major layout)
+// and adds the total to hist[b], which the pass before zeroed; device-wide
+// atomics whose returned value is waited for, so the bin is in before the
+// workgroup counts itself done.  The workgroup that arrives last reads the
+// 256 totals back through atomics and ranks them; turns every chunk's counts
+// into its escape count and first escape slot (chunk_base); writes header,
+// codebook, seg_end and *d_size; and zeroes hist and the arrival count
+// again, so the pass can run twice on one workspace, and the sample pass's
+// tickets and counts, which puts a workspace that came in with other values
+// in step for the next sample pass.
+__global__ __launch_bounds__(kSelectThreads) void k_codebook(
+    uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
+    uint64_t* __restrict__ hist, SampleArea* __restrict__ sample, uint64_t* __restrict__ chunk_base,
+    uint8_t* __restrict__ dst, uint64_t* d_size) {
+    __shared__ uint64_t key[256];
+    __shared__ uint32_t rank_part[4][256];
+    __shared__ uint32_t codebook[16];
+    __shared__ uint64_t wave_sum[kSelectWaves];
+    __shared__ uint64_t wave_off[kSelectWaves];
+    __shared__ uint64_t base_lds[kMaxChunks];
+    __shared__ uint32_t last;
+
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    {
+        const uint32_t bin = blockIdx.x;
+        const uint32_t* row = counts + (uint64_t)bin * chunks;
+        uint32_t v[kSelectChunks];
+#pragma unroll
+        for (int j = 0; j < kSelectChunks; j++) {
+            const uint32_t c = t + j * kSelectThreads;
+            v[j] = c < chunks ? row[c] : 0u;
+        }
+        uint64_t s = 0;
+#pragma unroll
+        for (int j = 0; j < kSelectChunks; j++) s += v[j];
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) s += __shfl_down(s, d, 64);
+        if (lane == 0) wave_sum[wave] = s;
+        __syncthreads();
+        if (t == 0) {
+            uint64_t total = 0;
+            for (int w = 0; w < kSelectWaves; w++) total += wave_sum[w];
+            const uint64_t before = __hip_atomic_fetch_add(hist + bin, total, __ATOMIC_RELAXED,
+                                                           __HIP_MEMORY_SCOPE_AGENT);
+            // the add has returned before the arrival is counted: the empty
+            // asm reads the returned value, so the wave waits for it
+            asm volatile("" ::"v"(before));
+            const uint32_t done = __hip_atomic_fetch_add(&sample->arrivals, 1u, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_AGENT);
+            last = done == gridDim.x - 1 ? 1u : 0u;
+        }
+        __syncthreads();
+        if (!last) return;
+    }
+
+    // the last workgroup: key(x) = count << 8 | (255 - x) turns "more
+    // frequent, then smaller exponent" into one unsigned comparison (counts
+    // stay below 2^37)
+    if (t < 256)
+        key[t] = (__hip_atomic_fetch_add(hist + t, uint64_t{0}, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT) << 8) | (255u - t);
+    __syncthreads();
+    {
+        const uint32_t r = rank_exponents(key, rank_part);
+        if (t < 256 && r < 16) codebook[r] = (uint32_t)t;
+    }
+    __syncthreads();
+    uint64_t esc[kSelectChunks] = {};
+    exact_chunk_escapes(counts, chunks, chunk_log2, n, codebook, esc);
+    const uint32_t per = (chunks + kSelectThreads - 1) / kSelectThreads;
+    uint64_t E;
+    uint64_t excl = scan_chunk_escapes(esc, wave_sum, wave_off, E);
 #pragma unroll
     for (int j = 0; j < kSelectChunks; j++) {
         const uint32_t b = per * t + j;
@@ -386,7 +454,6 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
         }
         excl += esc[j];
     }
-    const uint64_t E = wave_off[kSelectWaves - 1] + wave_sum[kSelectWaves - 1];
     __syncthreads();
     const uint64_t total = kPrefixBytes + (n + 1) / 2 + n + 5 * E;
     if (t == 0) {
@@ -406,16 +473,27 @@ __global__ __launch_bounds__(kSelectThreads) void k_select(
         *reinterpret_cast<uint64_t*>(dst + 32 + 8 * t) = v;
         dst[kHeaderBytes + t] = (uint8_t)codebook[t];
     }
+    // ready for another run of this pass on the same workspace, and the
+    // sample pass's tickets and counts back in step
+    if (t < 256) {
+        hist[t] = 0;
+        sample->sample_hist[t] = 0;
+    }
+    if (t == 0) {
+        sample->arrivals = 0;
+        sample->tickets = 0;
+    }
 }
 
 hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst, uint64_t* d_size,
                            hipStream_t stream) {
     const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + p.counts_off);
     uint64_t* hist = reinterpret_cast<uint64_t*>(ws + p.hist_off);
-    k_merge_counts<<<256, kMergeThreads, 0, stream>>>(counts, p.chunks, hist);
-    k_select<<<1, kSelectThreads, 0, stream>>>(p.n, p.chunk_log2, p.chunks, counts, hist,
-                                               reinterpret_cast<uint64_t*>(ws + p.base_off),
-                                               dst, d_size);
+    SampleArea* sample = reinterpret_cast<SampleArea*>(ws + p.sample_off);
+    k_codebook<<<256, kSelectThreads, 0, stream>>>(p.n, p.chunk_log2, p.chunks, counts, hist,
+                                                   sample,
+                                                   reinterpret_cast<uint64_t*>(ws + p.base_off),
+                                                   dst, d_size);
     return hipGetLastError();
 }
 
@@ -671,9 +749,9 @@ constexpr int kSpecPitch = 257;
 // The container's escape stream.  Never writes a record outside the caller's
 // buffer, whatever the workspace and header hold: slots below E, and all 5E
 // escape bytes inside the buffer.
-__device__ __forceinline__ EscapeOut final_slots(uint8_t* dst, uint64_t n, uint64_t dst_capacity) {
+__device__ __forceinline__ EscapeOut escape_slots(uint8_t* dst, uint64_t n, uint64_t dst_capacity,
+                                                  uint64_t E) {
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
-    const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
     EscapeOut esc;
     esc.pos = dst + esc_off;
     esc.exp = esc.pos + 4 * E;
@@ -682,10 +760,16 @@ __device__ __forceinline__ EscapeOut final_slots(uint8_t* dst, uint64_t n, uint6
     return esc;
 }
 
-// Exact exponent -> code tables from the header's codebook: lds.lut (0x10 =
-// escape) and lds.code (encode_words' entries); the caller synchronises
-// before using them.
-__device__ __forceinline__ void exact_code_table(const uint8_t* dst, PackLds& lds) {
+// The same, E read from the header.
+__device__ __forceinline__ EscapeOut final_slots(uint8_t* dst, uint64_t n, uint64_t dst_capacity) {
+    return escape_slots(dst, n, dst_capacity, *reinterpret_cast<const uint64_t*>(dst + 16));
+}
+
+// Exponent -> code tables from a codebook (code -> exponent, 16 entries in
+// LDS or global memory): lds.lut (0x10 = escape) and lds.code (encode_words'
+// entries); the caller synchronises before using them.
+template <class Entry>
+__device__ __forceinline__ void code_table(const Entry* cb, PackLds& lds) {
     const int t = threadIdx.x;
     if (t < 256) {
         lds.lut[t] = 0x10;
@@ -693,10 +777,15 @@ __device__ __forceinline__ void exact_code_table(const uint8_t* dst, PackLds& ld
     }
     __syncthreads();
     if (t < 16) {
-        const uint8_t e = dst[kHeaderBytes + t];
+        const uint8_t e = (uint8_t)cb[t];
         lds.lut[e] = (uint8_t)t;
         lds.code[e] = (uint16_t)t;
     }
+}
+
+// The same from the header's codebook.
+__device__ __forceinline__ void exact_code_table(const uint8_t* dst, PackLds& lds) {
+    code_table(dst + kHeaderBytes, lds);
 }
 
 // Packs words [begin, end) with the code table in lds.code, escape records to
@@ -799,6 +888,7 @@ __global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
 __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     Words src, uint64_t n, uint32_t chunk_log2, const uint64_t* __restrict__ chunk_base,
     uint8_t* __restrict__ dst, uint64_t dst_capacity, uint32_t* __restrict__ counts,
+    uint64_t* __restrict__ totals, uint32_t* __restrict__ chunk_esc,
     SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
     uint64_t scratch_exp) {
     constexpr bool kFirst = kRole == PackRole::kFirst;
@@ -850,7 +940,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
 #pragma unroll
             for (int c = 0; c < kSpecCopies; c++) s += hist[c * kSpecPitch + b];
             counts[(uint64_t)b * gridDim.x + chunk] = s;
+            // and into the whole input's counts (nothing waits for the add:
+            // the finish pass, a later launch, reads the sums)
+            __hip_atomic_fetch_add(totals + (chunk % kTotalCopies) * 256 + b, (uint64_t)s,
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
+        if (t == 0) chunk_esc[chunk] = (uint32_t)min_u64(escapes, ~0u);
         // more escapes than scratch slots: the finish pass must pack again
         if (t == 0 && write && escapes > spec_cap) atomicOr(&area->overflow, 1u);
     }
@@ -858,65 +953,166 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
 
 // Workgroups of the finish pass: two per CU of MI355X.
 constexpr uint32_t kFinishGroups = 512;
+constexpr uint32_t kFinishChunks = kMaxChunks / kFinishGroups;  // chunks per workgroup, at most
+static_assert(kFinishChunks * kFinishGroups == kMaxChunks, "whole chunks per finish workgroup");
+static_assert(kPackThreads == kSelectThreads, "the finish pass ranks and scans as the codebook pass");
 
-// The finish pass of the single-read encode.  Every workgroup takes the same
-// decision from the two codebooks and the first pass's flags:
-//  - same 16 exponents (and the first pass wrote the streams, no chunk
-//    overflowed): the streams stand.  Every escape record moves from its
-//    chunk's scratch slots to its final slot (grid-stride over the final
-//    slots, the chunk of a slot found by a search of chunk_base in LDS);
+// The finish pass of the single-read encode; it also takes the exact
+// codebook, with no pass of its own.  Every workgroup sums the whole input's
+// counts that the first pass added up, ranks the 256 exponents by the
+// codebook rule, and scans the chunks' escape counts -- the first pass's own
+// when it wrote the streams, no chunk outgrew its scratch slots and the
+// exact codebook holds the same 16 exponents as the provisional one (the
+// same escapes then); otherwise chunk length minus the chunk's counts of the
+// 16 codebook exponents -- so that it knows the codebook, E and the first
+// escape slot of each of its chunks without waiting for another workgroup.
+// Workgroup 0 writes header, seg_end, codebook and *d_size, and puts the
+// sample pass's tickets and counts back to zero.  Then, the same decision in
+// every workgroup:
+//  - same 16 exponents, streams written, no overflow: the streams stand.
+//    The escape records of the workgroup's chunks (chunk b, b + gridDim.x,
+//    ...) move from their scratch slots to their final slots in one sweep;
 //    when the order differs too, each chunk's 4-bit codes are rewritten
 //    (provisional code -> exact code, both nibbles of a byte at once) and
 //    the codes of its escaped words and of an odd n's pad nibble set back
 //    to 0;
-//  - otherwise every chunk is packed again from the input, the workgroups
-//    taking chunks blockIdx.x, blockIdx.x + gridDim.x, ...
+//  - otherwise the workgroup packs its chunks again from the input.
 template <bool kAlignedSm, class Words>
 __global__ __launch_bounds__(kPackThreads) SZ_EIGHT_WAVE_SGPR_CAP
 __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
     Words src, uint64_t n, uint32_t chunk_log2, uint32_t chunks,
-    const uint64_t* __restrict__ chunk_base, uint8_t* __restrict__ dst, uint64_t dst_capacity,
-    const SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
-    uint64_t scratch_exp) {
+    const uint32_t* __restrict__ counts, const uint64_t* __restrict__ totals,
+    const uint32_t* __restrict__ chunk_esc, uint8_t* __restrict__ dst, uint64_t dst_capacity,
+    SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos, uint64_t scratch_exp,
+    uint64_t* d_size) {
     __shared__ PackLds lds;
     __shared__ uint8_t remap[256];  // provisional code pair -> exact code pair
+    __shared__ uint64_t key[256];
+    __shared__ uint32_t rank_part[4][256];
+    __shared__ uint32_t codebook[16];
+    __shared__ uint64_t wave_sum[kSelectWaves];
+    __shared__ uint64_t wave_off[kSelectWaves];
+    __shared__ uint64_t my_first[kFinishChunks];  // this workgroup's chunks' first slots
+    __shared__ uint32_t my_count[kFinishChunks];  // and record counts (copy case)
+    __shared__ uint32_t mismatch;
     if (src.invalid()) return;  // the same for every thread
     const int t = threadIdx.x;
 
+    // every load the decision needs, issued at once: the provisional
+    // codebook, the first pass's flags, the whole input's counts, and the
+    // first pass's escape counts of chunks per * t .. per * t + per - 1
+    // (every chunk's entry is written by the first pass, so they are read
+    // before it is known whether they count)
     const uint4 prov = *reinterpret_cast<const uint4*>(area->cb);
-    const uint4 exact = *reinterpret_cast<const uint4*>(dst + kHeaderBytes);
-    const bool same_order =
-        prov.x == exact.x && prov.y == exact.y && prov.z == exact.z && prov.w == exact.w;
-    const bool usable = area->spec_on != 0 && area->overflow == 0;
-    // the same set: every exact codebook entry has a provisional code
-    const bool same_set =
-        __syncthreads_and(t >= 16 || area->lut[dst[kHeaderBytes + t]] < 16) != 0;
-    const EscapeOut esc = final_slots(dst, n, dst_capacity);
+    const uint32_t spec_on = area->spec_on, overflow = area->overflow;
+    const uint32_t per = (chunks + kPackThreads - 1) / kPackThreads;  // <= kSelectChunks
+    uint64_t esc[kSelectChunks] = {};
+    if (per == 4 && chunks % 4 == 0) {
+        if (4 * (uint32_t)t < chunks) {
+            const uint4 v = *reinterpret_cast<const uint4*>(chunk_esc + 4 * t);
+            esc[0] = v.x;
+            esc[1] = v.y;
+            esc[2] = v.z;
+            esc[3] = v.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < kSelectChunks; j++) {
+            const uint32_t b = per * t + j;
+            if ((uint32_t)j < per && b < chunks) esc[j] = chunk_esc[b];
+        }
+    }
+    if (t < 256) {
+        uint64_t c = 0;
+#pragma unroll
+        for (int k = 0; k < (int)kTotalCopies; k++) c += totals[k * 256 + t];
+        key[t] = (c << 8) | (255u - (uint32_t)t);
+    }
+    __syncthreads();
+    if (t == 0) mismatch = 0;
+    {
+        const uint32_t r = rank_exponents(key, rank_part);
+        if (t < 256 && r < 16) codebook[r] = (uint32_t)t;
+    }
+    __syncthreads();
+    // the same set: every exact codebook entry is one of the 16 provisional
+    // ones (a byte of prov equal to it: a zero byte of prov ^ 0x01010101 * e);
+    // the same order: entry t is provisional entry t.  Misses are or-ed into
+    // mismatch: bit 0 another set, bit 1 another order.
+    if (t < 16) {
+        const uint32_t e = codebook[t];
+        const uint32_t word = t < 4 ? prov.x : t < 8 ? prov.y : t < 12 ? prov.z : prov.w;
+        const bool in_place = ((word >> (8 * (t & 3))) & 0xFFu) == e;
+        const uint32_t v[4] = {prov.x ^ (0x01010101u * e), prov.y ^ (0x01010101u * e),
+                               prov.z ^ (0x01010101u * e), prov.w ^ (0x01010101u * e)};
+        bool found = false;
+#pragma unroll
+        for (int k = 0; k < 4; k++) found |= ((v[k] - 0x01010101u) & ~v[k] & 0x80808080u) != 0;
+        const uint32_t miss = (found ? 0u : 1u) | (in_place ? 0u : 2u);
+        if (miss) atomicOr(&mismatch, miss);
+    }
+    __syncthreads();
+    const bool same_order = (mismatch & 2u) == 0;
+    const bool keep = spec_on != 0 && overflow == 0 && (mismatch & 1u) == 0;
+    if (!keep) exact_chunk_escapes_narrow(counts, chunks, chunk_log2, n, codebook, esc);
+    uint64_t E;
+    uint64_t excl = scan_chunk_escapes(esc, wave_sum, wave_off, E);
+    const uint32_t seg_shift = 32 - chunk_log2;  // chunks per 2^32 elements: 2^seg_shift
+#pragma unroll
+    for (int j = 0; j < kSelectChunks; j++) {
+        const uint32_t b = per * t + j;
+        if ((uint32_t)j < per && b < chunks) {
+            if (b % gridDim.x == blockIdx.x) {
+                my_first[b / gridDim.x] = excl;
+                my_count[b / gridDim.x] = (uint32_t)min_u64(esc[j], spec_cap);
+            }
+            // seg_end[k]: escapes below element (k + 1) * 2^32, a chunk boundary
+            const uint32_t k = (b >> seg_shift) - 1;
+            if (blockIdx.x == 0 && b != 0 && (b & ((1u << seg_shift) - 1)) == 0 && k < 16)
+                *reinterpret_cast<uint64_t*>(dst + 32 + 8 * k) = excl;
+        }
+        excl += esc[j];
+    }
+    const uint64_t total = kPrefixBytes + (n + 1) / 2 + n + 5 * E;
+    if (blockIdx.x == 0) {
+        if (t == 0) {
+            *reinterpret_cast<uint32_t*>(dst + 0) = kMagic;
+            *reinterpret_cast<uint16_t*>(dst + 4) = kVersion;
+            *reinterpret_cast<uint16_t*>(dst + 6) = kElementBf16;
+            *reinterpret_cast<uint64_t*>(dst + 8) = n;
+            *reinterpret_cast<uint64_t*>(dst + 16) = E;
+            *reinterpret_cast<uint64_t*>(dst + 24) = total;
+            if (d_size) *d_size = total;
+            area->tickets = 0;
+        }
+        if (t < 16) {
+            if (((uint64_t)(t + 1) << seg_shift) >= chunks)
+                *reinterpret_cast<uint64_t*>(dst + 32 + 8 * t) = E;
+            dst[kHeaderBytes + t] = (uint8_t)codebook[t];
+        }
+        if (t < 256) area->sample_hist[t] = 0;
+    }
+    __syncthreads();
+    const EscapeOut esc_out = escape_slots(dst, n, dst_capacity, E);
+    const uint32_t mine = (chunks - blockIdx.x + gridDim.x - 1) / gridDim.x;  // <= kFinishChunks
 
-    if (usable && same_set) {
-        const uint64_t E = *reinterpret_cast<const uint64_t*>(dst + 16);
-        static_assert(sizeof(lds.stage_off) >= kMaxChunks * sizeof(uint64_t), "chunk bases fit");
-        uint64_t* base = reinterpret_cast<uint64_t*>(lds.stage_off);
-        for (uint32_t c = t; c < chunks; c += kPackThreads) base[c] = chunk_base[c];
-        __syncthreads();
+    if (keep) {
+        // the records of this workgroup's chunks move in one sweep,
+        // consecutive threads on consecutive records of a chunk
         const uint32_t* spos = reinterpret_cast<const uint32_t*>(dst + scratch_pos);
         const uint8_t* sexp = dst + scratch_exp;
-        for (uint64_t s = (uint64_t)blockIdx.x * kPackThreads + t; s < E;
-             s += (uint64_t)gridDim.x * kPackThreads) {
-            // the chunk holding slot s: the last c with base[c] <= s
-            uint32_t lo = 0, hi = chunks;
-            while (hi - lo > 1) {
-                const uint32_t mid = (lo + hi) / 2;
-                if (base[mid] <= s) lo = mid; else hi = mid;
-            }
-            const uint64_t q = s - base[lo];  // below spec_cap when the sets agree
-            if (q < spec_cap)
-                put_escape(esc, s, spos[(uint64_t)lo * spec_cap + q], sexp[(uint64_t)lo * spec_cap + q]);
+        uint32_t count = 0;
+        for (uint32_t j = 0; j < mine; j++) count += my_count[j];
+        for (uint32_t r = t; r < count; r += kPackThreads) {
+            uint32_t j = 0, q = r;
+            while (q >= my_count[j]) q -= my_count[j++];
+            const uint64_t from = (uint64_t)(blockIdx.x + j * gridDim.x) * spec_cap + q;
+            put_escape(esc_out, my_first[j] + q, spos[from], sexp[from]);
         }
         if (same_order) return;
 
         uint8_t* lut = lds.lut;
-        exact_code_table(dst, lds);
+        code_table(codebook, lds);
         __syncthreads();
         if (t < 256)
             remap[t] = (uint8_t)((lut[area->cb[t & 15]] & 0xF) |
@@ -946,8 +1142,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
             __syncthreads();
             // escaped words keep code 0: one thread per byte, the one of the
             // byte's first record
-            const uint64_t first = base[c];
-            const uint64_t cnt = min_u64((c + 1 < chunks ? base[c + 1] : E) - first, spec_cap);
+            const uint64_t cnt = my_count[(c - blockIdx.x) / gridDim.x];
             const uint32_t* cpos = spos + (uint64_t)c * spec_cap;
             const uint64_t seg = begin & ~uint64_t{0xFFFFFFFF};  // a chunk lies in one segment
             for (uint64_t q = t; q < cnt; q += kPackThreads) {
@@ -964,13 +1159,13 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
         return;
     }
 
-    exact_code_table(dst, lds);
+    code_table(codebook, lds);
     __syncthreads();
     int parity = 0;
-    for (uint32_t c = blockIdx.x; c < chunks; c += gridDim.x) {
+    for (uint32_t c = blockIdx.x, j = 0; c < chunks; c += gridDim.x, j++) {
         const uint64_t begin = (uint64_t)c << chunk_log2;
         const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
-        pack_range<kAlignedSm, false>(src, n, begin, end, dst, esc, chunk_base[c], true, nullptr,
+        pack_range<kAlignedSm, false>(src, n, begin, end, dst, esc_out, my_first[j], true, nullptr,
                                       lds, parity);
     }
 }
@@ -982,17 +1177,19 @@ hipError_t launch_pack_role(Words src, const EncodePlan& p, const uint8_t* ws, u
     const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
     uint32_t* counts = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(ws) + p.counts_off);
     SampleArea* area = reinterpret_cast<SampleArea*>(const_cast<uint8_t*>(ws) + p.sample_off);
+    uint64_t* totals = reinterpret_cast<uint64_t*>(const_cast<uint8_t*>(ws) + p.totals_off);
+    uint32_t* chunk_esc = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(ws) + p.esc_off);
     // the sign|mantissa stream starts at 176 + ceil(n/2): 16-byte aligned
     // exactly when n is a multiple of 32
     const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
     if (aligned)
         k_pack<true, Words, kRole><<<p.chunks, kPackThreads, 0, stream>>>(
-            src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, area, p.spec_cap,
-            p.scratch_pos, p.scratch_exp);
+            src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, totals, chunk_esc, area,
+            p.spec_cap, p.scratch_pos, p.scratch_exp);
     else
         k_pack<false, Words, kRole><<<p.chunks, kPackThreads, 0, stream>>>(
-            src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, area, p.spec_cap,
-            p.scratch_pos, p.scratch_exp);
+            src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, totals, chunk_esc, area,
+            p.spec_cap, p.scratch_pos, p.scratch_exp);
     return hipGetLastError();
 }
 
@@ -1009,21 +1206,23 @@ hipError_t launch_first_pass(Words src, const EncodePlan& p, uint8_t* ws, uint8_
 }
 
 template <class Words>
-hipError_t launch_finish(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
-                         uint64_t dst_capacity, hipStream_t stream) {
+hipError_t launch_finish(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
+                         uint64_t dst_capacity, uint64_t* d_size, hipStream_t stream) {
     if (p.chunks == 0) return hipSuccess;
-    const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
-    const SampleArea* area = reinterpret_cast<const SampleArea*>(ws + p.sample_off);
+    const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + p.counts_off);
+    const uint64_t* totals = reinterpret_cast<const uint64_t*>(ws + p.totals_off);
+    const uint32_t* chunk_esc = reinterpret_cast<const uint32_t*>(ws + p.esc_off);
+    SampleArea* area = reinterpret_cast<SampleArea*>(ws + p.sample_off);
     const uint32_t groups = p.chunks < kFinishGroups ? p.chunks : kFinishGroups;
     const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
     if (aligned)
         k_finish<true, Words><<<groups, kPackThreads, 0, stream>>>(
-            src, p.n, p.chunk_log2, p.chunks, base, dst, dst_capacity, area, p.spec_cap,
-            p.scratch_pos, p.scratch_exp);
+            src, p.n, p.chunk_log2, p.chunks, counts, totals, chunk_esc, dst, dst_capacity, area,
+            p.spec_cap, p.scratch_pos, p.scratch_exp, d_size);
     else
         k_finish<false, Words><<<groups, kPackThreads, 0, stream>>>(
-            src, p.n, p.chunk_log2, p.chunks, base, dst, dst_capacity, area, p.spec_cap,
-            p.scratch_pos, p.scratch_exp);
+            src, p.n, p.chunk_log2, p.chunks, counts, totals, chunk_esc, dst, dst_capacity, area,
+            p.spec_cap, p.scratch_pos, p.scratch_exp, d_size);
     return hipGetLastError();
 }
 
@@ -1032,8 +1231,7 @@ hipError_t launch_finish(Words src, const EncodePlan& p, const uint8_t* ws, uint
 // 512 blocks of 2048 consecutive words, evenly spread over the input (block
 // j starts at the 2048-word boundary at or below j * n / 512): whole blocks,
 // so that a layout with a short period (a KV cache's heads x dims) is
-// sampled evenly.  Eight blocks per 1024-thread workgroup, each workgroup's
-// counts to its own row (no atomics, nothing to clear beforehand).
+// sampled evenly.  Eight blocks per 1024-thread workgroup.
 constexpr uint32_t kSampleBlocks = 512;
 constexpr uint32_t kSampleBlockWords = 2048;
 constexpr uint32_t kSampleThreads = 1024;
@@ -1041,13 +1239,35 @@ constexpr uint32_t kSampleLoads =
     kSampleBlocks * kSampleBlockWords / 8 / kSampleThreads / kSampleGroups;  // per thread
 static_assert(kSampleBlocks % kSampleGroups == 0, "whole blocks per workgroup");
 static_assert(kSingleReadMin / kSampleBlocks >= kSampleBlockWords, "blocks do not overlap");
+static_assert(kSampleThreads == 1024, "four groups of 256 threads rank the exponents");
+static_assert((kSampleGroups & (kSampleGroups - 1)) == 0, "tickets wrap at a multiple of a run");
 
+// The sample pass, one launch.  Each workgroup counts its blocks, adds the
+// counts into area->sample_hist (device-wide atomics whose returned values
+// a barrier waits for) and then takes a ticket.  Tickets count on from run
+// to run, kSampleGroups a run, so the workgroup whose ticket completes a
+// multiple of kSampleGroups arrives last; the codebook pass puts tickets and
+// counts back to zero, so a workspace that came in with other values is in
+// step from its second encode on (until then the provisional codebook may
+// be ranked from part of the sample: a slower finish, never another
+// container).  The last workgroup reads the totals back, zeroing them, and
+// ranks the 256 exponents by the codebook rule (count descending, exponent
+// ascending); it leaves the provisional code table, decides whether the
+// first pass packs (at most one escape in 32 sampled words), clears the
+// first pass's overflow flag, and zeroes what the codebook pass counts up
+// (the whole input's counts and its workgroups done).
 template <class Words>
 __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n,
-                                                           SampleArea* __restrict__ area) {
+                                                           SampleArea* __restrict__ area,
+                                                           uint64_t* __restrict__ hist,
+                                                           uint64_t* __restrict__ totals) {
     constexpr uint32_t kBlocksPerGroup = kSampleBlocks / kSampleGroups;
     constexpr uint32_t kLoadsPerBlock = kSampleBlockWords / 8;
     __shared__ uint32_t h[kSpecCopies * kSpecPitch];
+    __shared__ uint32_t part[4][256];
+    __shared__ uint64_t key[256];
+    __shared__ uint32_t sums[2];
+    __shared__ uint32_t last;
     if (src.invalid()) return;
     const int t = threadIdx.x;
     for (int i = t; i < kSpecCopies * kSpecPitch; i += kSampleThreads) h[i] = 0;
@@ -1064,50 +1284,35 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
         hist_uint4(mine, *reinterpret_cast<const uint4*>(src.at(word)));
     }
     __syncthreads();
-    for (int b = t; b < 256; b += kSampleThreads) {
-        uint32_t s = 0;
-#pragma unroll
-        for (int c = 0; c < kSpecCopies; c++) s += h[c * kSpecPitch + b];
-        area->partial[blockIdx.x][b] = s;
-    }
-}
-
-// One workgroup: sums the sample's counts, ranks the 256 exponents by the
-// codebook rule (count descending, exponent ascending), leaves the
-// provisional code table, decides whether the first pass packs (at most one
-// escape in 32 sampled words), and clears the first pass's overflow flag.
-__global__ __launch_bounds__(1024) void k_rank_sample(SampleArea* __restrict__ area) {
-    __shared__ uint32_t part[4][256];
-    __shared__ uint64_t key[256];
-    __shared__ uint32_t sums[2];
-    const int t = threadIdx.x;
-    const int bin = t & 255;
-    const int grp = t >> 8;  // four groups of 256 threads
-    {
-        uint32_t s = 0;
-#pragma unroll
-        for (uint32_t i = 0; i < kSampleGroups / 4; i++)
-            s += area->partial[grp * (kSampleGroups / 4) + i][bin];
-        part[grp][bin] = s;
-    }
-    if (t < 2) sums[t] = 0;
-    __syncthreads();
+    uint32_t before = 0;
     if (t < 256) {
-        const uint32_t c = part[0][t] + part[1][t] + part[2][t] + part[3][t];
+        uint32_t s = 0;
+#pragma unroll
+        for (int c = 0; c < kSpecCopies; c++) s += h[c * kSpecPitch + t];
+        before = __hip_atomic_fetch_add(area->sample_hist + t, s, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+    }
+    // every add has returned before the ticket is taken: the empty asm reads
+    // the returned value, so the wave waits for it ahead of the barrier
+    asm volatile("" ::"v"(before));
+    __syncthreads();
+    if (t == 0) {
+        const uint32_t ticket = __hip_atomic_fetch_add(&area->tickets, 1u, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT);
+        last = (ticket + 1) % kSampleGroups == 0 ? 1u : 0u;
+    }
+    __syncthreads();
+    if (!last) return;
+
+    if (t < 2) sums[t] = 0;
+    if (t < 256) {
+        const uint32_t c = __hip_atomic_exchange(area->sample_hist + t, 0u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
         key[t] = ((uint64_t)c << 8) | (255u - (uint32_t)t);  // distinct keys
     }
     __syncthreads();
-    {
-        // rank = number of larger keys, each group counting over 64 of them
-        const uint64_t kx = key[bin];
-        uint32_t r = 0;
-#pragma unroll 16
-        for (int y = grp * 64; y < grp * 64 + 64; y++) r += key[y] > kx ? 1u : 0u;
-        part[grp][bin] = r;
-    }
-    __syncthreads();
+    const uint32_t r = rank_exponents(key, part);
     if (t < 256) {
-        const uint32_t r = part[0][t] + part[1][t] + part[2][t] + part[3][t];
         const uint32_t c = (uint32_t)(key[t] >> 8);
         area->lut[t] = r < 16 ? (uint8_t)r : (uint8_t)0x10;
         if (r < 16) {
@@ -1120,14 +1325,18 @@ __global__ __launch_bounds__(1024) void k_rank_sample(SampleArea* __restrict__ a
     if (t == 0) {
         area->spec_on = sums[0] > 0 && (uint64_t)(sums[0] - sums[1]) * 32 <= sums[0] ? 1u : 0u;
         area->overflow = 0;
+        area->arrivals = 0;
     }
+    if (t < 256) hist[t] = 0;  // the codebook pass adds the whole input's counts
+    for (uint32_t i = t; i < kTotalCopies * 256; i += kSampleThreads) totals[i] = 0;  // and the first pass
 }
 
 template <class Words>
 hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream) {
     SampleArea* area = reinterpret_cast<SampleArea*>(ws + p.sample_off);
-    k_sample<Words><<<kSampleGroups, kSampleThreads, 0, stream>>>(src, p.n, area);
-    k_rank_sample<<<1, 1024, 0, stream>>>(area);
+    k_sample<Words><<<kSampleGroups, kSampleThreads, 0, stream>>>(
+        src, p.n, area, reinterpret_cast<uint64_t*>(ws + p.hist_off),
+        reinterpret_cast<uint64_t*>(ws + p.totals_off));
     return hipGetLastError();
 }
 
@@ -1136,8 +1345,8 @@ hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_
                                        uint64_t, int, hipStream_t);                             \
     template hipError_t launch_first_pass<W>(W, const EncodePlan&, uint8_t*, uint8_t*,          \
                                              uint64_t, hipStream_t);                            \
-    template hipError_t launch_finish<W>(W, const EncodePlan&, const uint8_t*, uint8_t*,        \
-                                         uint64_t, hipStream_t);                                \
+    template hipError_t launch_finish<W>(W, const EncodePlan&, uint8_t*, uint8_t*, uint64_t,     \
+                                         uint64_t*, hipStream_t);                               \
     template hipError_t launch_sample<W>(W, const EncodePlan&, uint8_t*, hipStream_t);
 SZ_ENCODE_INSTANCES(FlatWords)
 SZ_ENCODE_INSTANCES(PagedWords)

@@ -39,6 +39,8 @@ struct EncodePlan {
     uint64_t counts_off = 0;   // u32[256][G]   exponent counts, bin-major
     uint64_t hist_off = 0;     // u64[256]      exponent counts of the whole input
     uint64_t base_off = 0;     // u64[G]        first escape slot of each chunk
+    uint64_t totals_off = 0;   // u64[kTotalCopies][256] exponent counts added up by the first pass
+    uint64_t esc_off = 0;      // u32[G]        each chunk's escapes under the provisional codebook
     uint64_t sample_off = 0;   // SampleArea (single-read encode)
     uint64_t ws_bytes = 0;
     // Single-read encode (large inputs): the first pass packs with a
@@ -52,14 +54,21 @@ struct EncodePlan {
     uint64_t scratch_end = 0;  // first dst byte past the scratch area
 };
 
-// The sample of the single-read encode: kSampleGroups workgroups each count
-// their share, and one more workgroup ranks the sum.
+// The sample of the single-read encode: kSampleGroups workgroups add their
+// counts into sample_hist and take tickets; the one that arrives last ranks
+// the total.  The area also holds the codebook pass's count of workgroups
+// done (zeroed, with the whole input's counts, by the pass before it).
 constexpr uint32_t kSampleGroups = 64;
+// Copies of the whole input's exponent counts that the first pass adds
+// into, chunk c into copy c % kTotalCopies: fewer device-wide atomics on
+// one address.
+constexpr uint32_t kTotalCopies = 4;
 struct SampleArea {
-    uint32_t partial[kSampleGroups][256];  // exponent counts of each share of the sample
+    uint32_t sample_hist[256];  // the sample's exponent counts (left zero after ranking)
+    uint32_t tickets;       // sample workgroups that added their counts, kSampleGroups a run
     uint32_t overflow;      // set by the first pass: a chunk outgrew its scratch slots
     uint32_t spec_on;       // the sample predicts few escapes: the first pass packs
-    uint32_t pad[2];
+    uint32_t arrivals;      // codebook-pass workgroups done (the last one ranks)
     uint8_t lut[256];       // provisional exponent -> code, 0x10 = escape
     uint8_t cb[16];         // provisional codebook, code -> exponent
 };
@@ -220,18 +229,19 @@ hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst,
 template <class Words>
 hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
                        uint64_t dst_capacity, int num_cus, hipStream_t stream);
-// single-read encode: sample (clears and fills the sampled counts), the
-// first pass (exact per-chunk counts, and the streams under the provisional
-// codebook), then, after launch_codebook, the finish pass (moves the
-// escape records into place, remaps the codes, or packs again)
+// single-read encode: sample (ranks the provisional codebook), the first
+// pass (exact per-chunk and whole-input counts, and the streams under the
+// provisional codebook), then the finish pass (takes the exact codebook and
+// writes the header and *d_size; moves the escape records into place,
+// remaps the codes, or packs again)
 template <class Words>
 hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream);
 template <class Words>
 hipError_t launch_first_pass(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
                              uint64_t dst_capacity, hipStream_t stream);
 template <class Words>
-hipError_t launch_finish(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
-                         uint64_t dst_capacity, hipStream_t stream);
+hipError_t launch_finish(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
+                         uint64_t dst_capacity, uint64_t* d_size, hipStream_t stream);
 template <class Words>
 hipError_t launch_unpack(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                          Words dst, int32_t* status, int num_cus, hipStream_t stream);

@@ -149,16 +149,16 @@ def test_single_read_host_checks(sz):
     assert sz.sz_encode_single_read(1 << 36)
     assert not sz.sz_encode_single_read((1 << 36) + 1)
     W, D = A + (1 << 32), A + (1 << 36)
-    for fn in (sz.sz_encode_first_pass, sz.sz_encode_finish):
+    for fn, tail in ((sz.sz_encode_first_pass, (0,)), (sz.sz_encode_finish, (None, 0))):
         small = (1 << 20) - 8                                             # below the sample size
         assert status_of(fn, A, small, W, sz.sz_workspace_size(small), D,
-                         sz.sz_max_compressed_size(small), 0) == 1
+                         sz.sz_max_compressed_size(small), *tail) == 1
         n = 1 << 20
         ws, cap = sz.sz_workspace_size(n), sz.sz_max_compressed_size(n)
-        assert status_of(fn, A, n, W, ws - 1, D, cap, 0) == 1             # small workspace
-        assert status_of(fn, A, n, W, ws, D, cap - 1, 0) == 2             # small destination
-        assert status_of(fn, A, n, W, ws, D + 8, cap, 0) == 1             # misaligned
-        assert status_of(fn, A, (1 << 36) + 1, W, ws, D, cap, 0) == 3
+        assert status_of(fn, A, n, W, ws - 1, D, cap, *tail) == 1         # small workspace
+        assert status_of(fn, A, n, W, ws, D, cap - 1, *tail) == 2         # small destination
+        assert status_of(fn, A, n, W, ws, D + 8, cap, *tail) == 1         # misaligned
+        assert status_of(fn, A, (1 << 36) + 1, W, ws, D, cap, *tail) == 3
     small = (1 << 20) - 8
     assert status_of(sz.sz_encode_sample, A, small, W, sz.sz_workspace_size(small), 0) == 1
     n = 1 << 20
@@ -252,11 +252,13 @@ def test_pages_host_checks(sz):
 def test_bench_chunk_plan_matches_library(sz):
     """bench.py predicts the single-read finish case from its own copy of the
     encode's chunk plan; the library's workspace size (per-chunk counts and
-    bases, then a fixed sample area) fixes the chunk count it planned."""
+    bases, the whole input's counts, per-chunk escape counts, then a fixed
+    sample area) fixes the chunk count it planned."""
     import bench
     align = lambda x: (x + 255) // 256 * 256
-    def planned(g):  # counts u32[256][g], hist u64[256], bases u64[g]
-        return align(align(align(g * 1024) + 2048) + g * 8)
+    def planned(g):  # counts u32[256][g], hist u64[256], bases u64[g],
+        # totals u64[4][256], escapes u32[g]
+        return align(align(align(align(align(g * 1024) + 2048) + g * 8) + 8192) + g * 4)
     sample_area = sz.sz_workspace_size(1) - planned(1)
     sizes = [1, 4096, 1 << 21, (1 << 25) + 123, 3 * (1 << 24) + 5, (1 << 26) - 5,
              (1 << 27) + 77, 3 << 26, 1 << 28, 1280 * (1 << 18) - 3, 1537 * (1 << 18) - 1,

@@ -55,8 +55,7 @@ def test_random_cases(torch, sz):
             size = torch.zeros(1, dtype=torch.int64, device="cuda")
             sz.sz_encode_sample(x, n, ws, ws_bytes)
             sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap)
-            sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
-            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap)
+            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, size)
             torch.cuda.synchronize()
             assert int(size.item()) == want.size, (i, kind, n, seed)
             assert np.array_equal(dst[:want.size].cpu().numpy(), want), (i, kind, n, seed)

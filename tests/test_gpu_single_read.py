@@ -1,12 +1,11 @@
 """The single-read encode, case by case.
 
-sz_encode_sample; sz_encode_first_pass; sz_encode_codebook;
-sz_encode_finish (what sz_encode runs from 2^26 words on) read the input
-once when they can: the first pass packs every chunk with a provisional
-codebook ranked from a fixed sample of the input (512 blocks of 2048 words,
-block j at the 2048-word boundary at or below j * n / 512) while it counts
-the exact exponents; once the exact codebook is known, the finish pass
-keeps what the first one wrote (same codes), remaps the 4-bit codes (same
+sz_encode_sample; sz_encode_first_pass; sz_encode_finish (what sz_encode
+runs from 2^26 words on) read the input once when they can: the first pass
+packs every chunk with a provisional codebook ranked from a fixed sample of
+the input (512 blocks of 2048 words, block j at the 2048-word boundary at or
+below j * n / 512) while it counts the exact exponents; the finish pass
+ranks the exact codebook and keeps what the first one wrote (same codes), remaps the 4-bit codes (same
 16 exponents in another order), or packs again (another set, a chunk with
 more escapes than its scratch slots, or a sample that predicted too many
 escapes).  Whatever the case, the container must be the oracle's, byte for
@@ -140,8 +139,7 @@ def single_read_encode(torch, sz, x, n, dst, cap, size):
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
     sz.sz_encode_sample(x, n, ws, ws_bytes)
     sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap)
-    sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
-    sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap)
+    sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, size)
 
 
 @pytest.mark.parametrize("case,n", CASES)
@@ -268,3 +266,30 @@ def test_single_read_no_escapes(torch, sz, case, n):
         y, status, guard_ok = gpu_decode(torch, sz, container, n, form)
         assert status == 0 and guard_ok, (label, form)
         assert torch.equal(y, x), (label, form)
+
+
+@pytest.mark.parametrize("fill", [0xA5, 0xFF, 0x00])
+def test_single_read_any_workspace_bytes(torch, sz, fill):
+    """The staged calls take a workspace in whatever state the caller hands
+    it over: arbitrary bytes (0xA5 leaves the sample pass's ticket count out
+    of step with its workgroups; 0xFF makes the first workgroup to arrive
+    rank a sample it has barely counted), or zeros.  Every call, the first
+    included, gives the oracle's container; from the second call on the
+    workspace is in step again."""
+    n = (1 << 22) + 77
+    words = words_for("copy", n)
+    x = torch.from_numpy(words.view(np.int16)).cuda()
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.full((cap,), 0x77, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    ws_bytes = sz.sz_workspace_size(n)
+    ws = torch.full((ws_bytes,), fill, dtype=torch.uint8, device="cuda")
+    want = oracle.encode(words)
+    for rep in range(3):
+        say(f"workspace fill {fill:#x} call {rep}")
+        sz.sz_encode_sample(x, n, ws, ws_bytes)
+        sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap)
+        sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, size)
+        total = int(size.item())
+        assert total == want.size, (fill, rep)
+        assert np.array_equal(dst[:total].cpu().numpy(), want), (fill, rep)

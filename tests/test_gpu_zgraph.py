@@ -65,8 +65,7 @@ def test_graph_replays(torch, sz, kind, form, single):
         if single:                                # the single-read passes
             sz.sz_encode_sample(x, n, ws, ws_bytes)
             sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap)
-            sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
-            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap)
+            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, size)
         else:
             sz.sz_encode_histogram(x, n, ws, ws_bytes)
             sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)

@@ -215,6 +215,20 @@ def digests():
         return json.load(f)
 
 
+def two_read_encode(torch, sz, x, n):
+    """The staged two-read encode (histogram, codebook, pack) over a caller
+    workspace; returns the container on the device."""
+    ws_bytes = sz.sz_workspace_size(n)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.empty(cap, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sz.sz_encode_histogram(x, n, ws, ws_bytes)
+    sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
+    sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap)
+    return dst[:int(size.item())]
+
+
 @pytest.mark.timeout(600)
 @pytest.mark.parametrize("name", ["single_layer_kv", "llama3_8b_kv_8k", "escape_heavy",
                                   "special_values"])
@@ -230,6 +244,10 @@ def test_workload_full(torch, sz, name):
     assert got.size == want.size == d["container_bytes"]
     assert np.array_equal(got, want), f"{name}: container differs from the oracle"
     assert sha256(got) == d["container_sha256"]
+    # the two-read form too (for the 1 GiB tensor, on its 4096-chunk plan)
+    two = two_read_encode(torch, sz, x, words.size).cpu().numpy()
+    assert np.array_equal(two, want), f"{name}: two-read container differs from the oracle"
+    del two
     for form in DECODE_FORMS:
         y, st, guard = gpu_decode(torch, sz, got_dev, words.size, form)
         assert st == 0 and guard and torch.equal(y, x), (name, form)
@@ -262,6 +280,11 @@ def test_workload_70b_32k(torch, sz):
     assert h["seg_end"][0] < h["e"], "escapes on both sides of 2^32 expected"
     say("digest")
     assert sha256(got_dev.cpu().numpy()) == d["container_sha256"]
+    say("two-read encode")
+    two = two_read_encode(torch, sz, x, x.numel())
+    assert two.numel() == d["container_bytes"]
+    assert sha256(two.cpu().numpy()) == d["container_sha256"], "two-read container differs"
+    del two
     for form in DECODE_FORMS:
         say("decode", form)
         y, st, guard = gpu_decode(torch, sz, got_dev, x.numel(), form)

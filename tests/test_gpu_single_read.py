@@ -20,6 +20,8 @@ import sys
 import numpy as np
 import pytest
 
+import bench
+import kvgen
 import oracle
 from test_gpu_parity import make_words
 from test_gpu_pages import gather_pages, paged, scatter_to_pages
@@ -28,8 +30,6 @@ pytestmark = pytest.mark.gpu
 
 SAMPLE_BLOCKS = 512
 SAMPLE_BLOCK_WORDS = 2048
-MIN_CHUNK_LOG2 = 14
-MAX_CHUNKS = 2048
 
 
 def say(*a):
@@ -70,9 +70,7 @@ def expected_case(words: np.ndarray) -> str:
     top = int(sample_hist[prov.astype(np.int64)].sum())
     if (total - top) * 32 > total:
         return "full:sample"
-    c = MIN_CHUNK_LOG2
-    while -(-n >> c) > MAX_CHUNKS:
-        c += 1
+    c = bench.chunk_log2(n)                  # the library's chunk plan
     esc = ~np.isin(exponents(words), prov.astype(np.int64))
     per_chunk = np.add.reduceat(esc.astype(np.int64), np.arange(0, n, 1 << c))
     if per_chunk.max() > (1 << c) // 16:
@@ -293,3 +291,32 @@ def test_single_read_any_workspace_bytes(torch, sz, fill):
         total = int(size.item())
         assert total == want.size, (fill, rep)
         assert np.array_equal(dst[:total].cpu().numpy(), want), (fill, rep)
+
+
+@pytest.mark.timeout(600)
+def test_single_read_repack_full_size(torch, sz):
+    """The finish's repack branch on the 1 GiB tensor's 4096-chunk plan: the
+    llama3-8B-shaped KV tensor with every tenth sampled word moved to
+    exponent 200, so the sample ranks 200 into its codebook while the whole
+    tensor does not (another set: every chunk packed again)."""
+    words = kvgen.generate("llama3_8b_kv_8k")
+    n = words.size
+    idx = (sample_starts(n)[:, None] + np.arange(SAMPLE_BLOCK_WORDS)[None, :]).ravel()[::10]
+    words[idx] = (words[idx] & np.uint16(0x807F)) | np.uint16(200 << 7)
+    assert -(-n >> bench.chunk_log2(n)) == 4096
+    assert expected_case(words) == "full:set"
+    want = oracle.encode(words)
+    x = torch.from_numpy(words.view(np.int16)).cuda()
+    cap = sz.sz_max_compressed_size(n)
+    dst = torch.full((cap,), 0x77, dtype=torch.uint8, device="cuda")
+    size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    say("full:set n=2^29, 4096 chunks")
+    single_read_encode(torch, sz, x, n, dst, cap, size)
+    total = int(size.item())
+    assert total == want.size
+    assert np.array_equal(dst[:total].cpu().numpy(), want)
+    # and sz_encode takes the same path
+    size.zero_()
+    sz.sz_encode(x, n, dst, cap, size)
+    assert int(size.item()) == want.size
+    assert np.array_equal(dst[:want.size].cpu().numpy(), want)

@@ -518,6 +518,12 @@ static_assert(kAhead > kSlotRecords && kAhead <= 64, "look-ahead past a full slo
 constexpr uint32_t kNoTile = 0xFFFFFFFFu;
 constexpr uint64_t kShortGap = 32;  // tile entries a lane fills alone
 
+// Set bits of a wave mask below this lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
 // An item of the index pass: record k < e, the end item k == e (position
 // n, tile `tiles`), or nothing past it (tile kNoTile).
 struct IndexItem {
@@ -526,19 +532,29 @@ struct IndexItem {
     uint32_t rec;  // offset in its tile | exponent << 16 (records only)
 };
 
-template <bool kOneSegment>
-__device__ __forceinline__ uint64_t item_position(const EscapeReader& rd, uint64_t k) {
-    return kOneSegment ? (uint64_t)rd.low32(k) : rd.position(k);
+// Position of record k (its stored low 32 bits, with the segment number
+// above them past 2^32 words), read with no branch so that the loads of a
+// group go out together.
+template <bool kOneSegment, bool kAlignedPos>
+__device__ __forceinline__ uint64_t record_position(const EscapeReader& rd, uint64_t k) {
+    const uint32_t lo = kAlignedPos ? reinterpret_cast<const uint32_t*>(rd.pos_lo)[k]
+                                    : load4_unaligned(rd.pos_lo + 4 * k);
+    if (kOneSegment) return lo;
+    uint64_t seg = 0;
+#pragma unroll
+    for (int sg = 0; sg < 16; sg++) seg += rd.seg_end[sg] <= k ? 1u : 0u;
+    return (seg << 32) | lo;
 }
 
-template <bool kOneSegment>
-__device__ __forceinline__ IndexItem index_item(const EscapeReader& rd, uint64_t n, uint64_t e,
-                                                uint64_t tiles, uint64_t k) {
+// Item k from its loaded position p and exponent x (both unused past the
+// records).
+__device__ __forceinline__ IndexItem make_item(uint64_t n, uint64_t e, uint64_t tiles, uint64_t k,
+                                               uint64_t p, uint32_t x) {
     IndexItem it{0, kNoTile, 0};
     if (k < e) {
-        it.pos = item_position<kOneSegment>(rd, k);
-        it.tile = (uint32_t)min_u64(it.pos / kTileWords, tiles);
-        it.rec = (uint32_t)(it.pos - (uint64_t)it.tile * kTileWords) | ((uint32_t)rd.exps[k] << 16);
+        it.pos = p;
+        it.tile = (uint32_t)min_u64(p / kTileWords, tiles);
+        it.rec = (uint32_t)(p - (uint64_t)it.tile * kTileWords) | (x << 16);
     } else if (k == e) {
         it.pos = n;
         it.tile = (uint32_t)tiles;
@@ -546,22 +562,28 @@ __device__ __forceinline__ IndexItem index_item(const EscapeReader& rd, uint64_t
     return it;
 }
 
-// One wave per group of kIndexItems items, in kIndexRows rows of 64: lane
-// L holds items k0 + 64 r + L (row r) and, in lanes 0..15, the first 16
-// items after the group.  A lane whose item is the first of its tile fills
-// idx over the gap back to its predecessor's tile (a short gap alone, a
-// long one with the whole wave), sets the record count of the empty tiles
-// in it to 0, and writes its tile's slot from the 16 items after it, which
-// it reads from the lanes holding them (the next row, or the items after
-// the group, for the lanes near the end of a row).  The rows' loads go out
-// together, so a wave waits for memory once.  Faults: a position not above
+// One wave per group of 64 items: lane L holds item k0 + L, and also
+// loads item k0 + 64 + L, so that the 16 items after the group are at hand.
+// A lane whose item is the first of its tile fills idx over the gap back to
+// its predecessor's tile (a short gap alone, a long one with the whole
+// wave), sets the record count of the empty tiles in it to 0, and has its
+// tile's slot written: the run of the tile's items (from a ballot of where
+// the tile changes), then the 15 records from its own on, taken from LDS.
+// Every global load of a group is issued before any is used (indices
+// clamped to the last record), so a wave waits for memory once.  Faults: a
+// position not above
 // its predecessor, or not below n; the header (wave 0).  kOneSegment:
-// n <= 2^32, every position is its stored low 32 bits.
-template <bool kOneSegment>
+// n <= 2^32, every position is its stored low 32 bits.  kAlignedPos: the
+// positions are 4-byte aligned.
+template <bool kOneSegment, bool kAlignedPos>
 __global__ __launch_bounds__(64) void k_tile_index(
     const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e, uint64_t groups,
     uint64_t* __restrict__ idx, uint32_t* __restrict__ flags, uint32_t* __restrict__ slots) {
     __shared__ uint64_t seg_table[16];
+    __shared__ uint32_t rec_lds[64 + kAhead];  // the items' records, then the 16 after them
+    __shared__ uint32_t lead_lds[64];  // lane of each slot's first record, in tile order
+    __shared__ uint32_t run_lds[64];   // and its tile's run
+    __shared__ uint32_t tile_lds[64];  // and its tile
     const uint32_t lane = threadIdx.x;
     bool bad = false;
     if (blockIdx.x == 0 && lane == 0) bad = !header_ok(src, src_bytes, n, e);
@@ -569,7 +591,7 @@ __global__ __launch_bounds__(64) void k_tile_index(
     EscapeReader rd;
     rd.pos_lo = src + esc_off;
     rd.exps = rd.pos_lo + 4 * e;
-    rd.aligned = (esc_off & 3) == 0;
+    rd.aligned = kAlignedPos;
     rd.one_segment = kOneSegment;
     rd.seg_end = seg_table;
     if (!kOneSegment) {  // the segment table is read only past 2^32 words
@@ -577,82 +599,91 @@ __global__ __launch_bounds__(64) void k_tile_index(
         __syncthreads();
     }
     const uint64_t tiles = (n + kTileWords - 1) / kTileWords;
+    const uint64_t last = e > 0 ? e - 1 : 0;
     for (uint64_t g = blockIdx.x; g < groups; g += gridDim.x) {
-        const uint64_t k0 = g * kIndexItems;
-        // every row's items, and the items after the group, loaded together
-        IndexItem row[kIndexRows + 1];
-        uint64_t prev_pos[kIndexRows];
-#pragma unroll
-        for (uint32_t r = 0; r <= kIndexRows; r++) {
-            const uint64_t k = k0 + 64 * r + lane;
-            row[r] = r < kIndexRows || lane < kAhead ? index_item<kOneSegment>(rd, n, e, tiles, k)
-                                                     : IndexItem{0, kNoTile, 0};
-            if (r < kIndexRows)
-                prev_pos[r] = k > 0 && k <= e ? item_position<kOneSegment>(rd, k - 1) : 0;
+        const uint64_t k = g * kIndexItems + lane;
+        const uint64_t ka = k + kIndexItems;  // the item 64 on, for the look-ahead
+        uint64_t p = 0, pp = 0, pa = 0;
+        uint32_t x = 0, xa = 0;
+        if (e > 0) {  // the same for the whole grid
+            const uint64_t kc = min_u64(k, last), kac = min_u64(ka, last);
+            const uint64_t kpc = min_u64(k > 0 ? k - 1 : 0, last);
+            p = record_position<kOneSegment, kAlignedPos>(rd, kc);
+            pp = record_position<kOneSegment, kAlignedPos>(rd, kpc);
+            pa = record_position<kOneSegment, kAlignedPos>(rd, kac);
+            x = rd.exps[kc];
+            xa = rd.exps[kac];
         }
-#pragma unroll
-        for (uint32_t r = 0; r < kIndexRows; r++) {
-            const uint64_t k = k0 + 64 * r + lane;
-            const IndexItem& it = row[r];
-            const uint32_t prev_tile = k > 0 && k <= e
-                                           ? (uint32_t)min_u64(prev_pos[r] / kTileWords, tiles)
-                                           : kNoTile;
-            if (k < e && (it.pos >= n || (k > 0 && !(it.pos > prev_pos[r])))) bad = true;
-            const bool first = k <= e && (k == 0 || it.tile != prev_tile);
+        const IndexItem it = make_item(n, e, tiles, k, p, x);
+        const IndexItem ahead = make_item(n, e, tiles, ka, pa, xa);
+        const bool has_prev = k > 0 && k <= e;
+        const uint32_t prev_tile = has_prev ? (uint32_t)min_u64(pp / kTileWords, tiles) : kNoTile;
+        if (k < e && (it.pos >= n || (k > 0 && !(it.pos > pp)))) bad = true;
+        const bool first = k <= e && (k == 0 || it.tile != prev_tile);
 
-            // the next 16 items' tiles and records: item k + j is lane
-            // L + j's item of this row when L + j < 64, else lane L + j - 64's
-            // item of the next row -- the same source lane S = (L + j) mod
-            // 64 either way, which offers this row's item when S >= j and the
-            // next row's when S < j
-            uint32_t run = 1;  // this tile's items from this one on, up to 17
-            bool same = true;
-            uint32_t slot[kSlotWords];
-            slot[1] = it.rec;
-#pragma unroll
-            for (uint32_t j = 1; j <= kAhead; j++) {
-                const int addr = (int)(((lane + j) & 63u) << 2);
-                const bool offer_this = lane >= j;
-                const uint32_t tl = (uint32_t)__builtin_amdgcn_ds_bpermute(
-                    addr, (int)(offer_this ? it.tile : row[r + 1].tile));
-                same = same && k + j < e && tl == it.tile;  // a record of this tile
-                run += same ? 1u : 0u;
-                if (j < kSlotRecords) {
-                    const uint32_t rl = (uint32_t)__builtin_amdgcn_ds_bpermute(
-                        addr, (int)(offer_this ? it.rec : row[r + 1].rec));
-                    slot[1 + j] = same ? rl : 0u;
-                }
-            }
-            slot[0] = run;
+        // a tile's run: its items from the first on, up to the next item of
+        // another tile (the group's 64 items and the 16 after it); bit i of
+        // starts (i < 64) and of starts_ahead (item 64 + i) is set where an
+        // item's tile differs from its predecessor's
+        // (both shuffles run with every lane active, then one is picked)
+        const uint32_t last_tile = (uint32_t)__shfl(it.tile, 63, 64);
+        const uint32_t prev_ahead_tile = (uint32_t)__shfl_up(ahead.tile, 1, 64);
+        const uint32_t before_ahead = lane == 0 ? last_tile : prev_ahead_tile;
+        const uint64_t starts = __ballot(it.tile != (uint32_t)__shfl_up(it.tile, 1, 64));
+        const uint64_t starts_ahead = __ballot(lane < kAhead && ahead.tile != before_ahead);
+        const uint64_t later = lane < 63 ? starts >> (lane + 1) : 0;
+        const uint32_t next = later ? lane + 1 + (uint32_t)__builtin_ctzll(later)
+                                    : (starts_ahead ? 64u + (uint32_t)__builtin_ctzll(starts_ahead)
+                                                    : 64u + kAhead);
+        const uint32_t run = min(next - lane, kAhead + 1);  // above 15: "more than 15"
 
-            // the gap: tiles (prev_tile, tile], the tiles before this one empty
-            const uint64_t lo = k == 0 ? 0 : (uint64_t)prev_tile + 1;
-            const uint64_t hi = it.tile;  // <= tiles for items up to the end item
-            const bool has_gap = first && hi >= lo;
-            if (has_gap && hi - lo < kShortGap) {
-                for (uint64_t jt = lo; jt <= hi; jt++) {
-                    idx[jt] = k;
-                    if (jt < hi && jt < tiles) slots[jt * kSlotWords] = 0;
-                }
+        // the gap: tiles (prev_tile, tile], the tiles before this one empty
+        const uint64_t lo = k == 0 ? 0 : (uint64_t)prev_tile + 1;
+        const uint64_t hi = it.tile;  // <= tiles for items up to the end item
+        const bool has_gap = first && hi >= lo;
+        if (has_gap && hi - lo < kShortGap) {
+            for (uint64_t jt = lo; jt <= hi; jt++) {
+                idx[jt] = k;
+                if (jt < hi && jt < tiles) slots[jt * kSlotWords] = 0;
             }
-            uint64_t wide = __ballot(has_gap && hi - lo >= kShortGap);
-            while (wide) {  // long gaps: the whole wave fills one at a time
-                const int src_lane = __builtin_ctzll(wide);
-                wide &= wide - 1;
-                const uint64_t wlo = uniform64(__shfl(lo, src_lane, 64));
-                const uint64_t whi = uniform64(__shfl(hi, src_lane, 64));
-                const uint64_t wk = uniform64(__shfl(k, src_lane, 64));
-                for (uint64_t jt = wlo + lane; jt <= whi; jt += 64) {
-                    idx[jt] = wk;
-                    if (jt < whi && jt < tiles) slots[jt * kSlotWords] = 0;
-                }
+        }
+        uint64_t wide = __ballot(has_gap && hi - lo >= kShortGap);
+        while (wide) {  // long gaps: the whole wave fills one at a time
+            const int src_lane = __builtin_ctzll(wide);
+            wide &= wide - 1;
+            const uint64_t wlo = uniform64(__shfl(lo, src_lane, 64));
+            const uint64_t whi = uniform64(__shfl(hi, src_lane, 64));
+            const uint64_t wk = uniform64(__shfl(k, src_lane, 64));
+            for (uint64_t jt = wlo + lane; jt <= whi; jt += 64) {
+                idx[jt] = wk;
+                if (jt < whi && jt < tiles) slots[jt * kSlotWords] = 0;
             }
-            if (first && k < e && it.tile < tiles) {
-                uint4* out = reinterpret_cast<uint4*>(slots + (uint64_t)it.tile * kSlotWords);
-#pragma unroll
-                for (uint32_t q = 0; q < kSlotWords; q += 4)
-                    out[q / 4] = make_uint4(slot[q], slot[q + 1], slot[q + 2], slot[q + 3]);
-            }
+        }
+        // the slots of the group's first-of-tile records (the run, then the
+        // records from this one on; those past the run belong to later
+        // tiles and are never read), stored in tile order by consecutive
+        // lanes on consecutive 16-byte pieces, so that the tiles of a group,
+        // mostly consecutive, are written in whole lines
+        const bool writes = first && k < e && it.tile < tiles;
+        const uint64_t wmask = __ballot(writes);
+        __syncthreads();  // the previous group's pieces are stored
+        rec_lds[lane] = it.rec;
+        if (lane < kAhead) rec_lds[64 + lane] = ahead.rec;
+        if (writes) {
+            const uint32_t jw = lanes_below(wmask);
+            lead_lds[jw] = lane;
+            run_lds[jw] = run;
+            tile_lds[jw] = it.tile;
+        }
+        __syncthreads();
+        const uint32_t pieces = 4u * (uint32_t)__popcll(wmask);
+        for (uint32_t pc = lane; pc < pieces; pc += 64) {
+            const uint32_t jw = pc / 4, w0 = 4 * (pc % 4);  // slot words w0 .. w0 + 3
+            const uint32_t* recs = rec_lds + lead_lds[jw];   // word w >= 1 is recs[w - 1]
+            const uint32_t head = recs[w0 == 0 ? 0 : w0 - 1];
+            const uint4 v = make_uint4(w0 == 0 ? run_lds[jw] : head, recs[w0], recs[w0 + 1],
+                                       recs[w0 + 2]);
+            reinterpret_cast<uint4*>(slots + (uint64_t)tile_lds[jw] * kSlotWords)[pc % 4] = v;
         }
     }
     bad = __ballot(bad) != 0;
@@ -667,12 +698,16 @@ hipError_t launch_tile_index(const uint8_t* src, uint64_t src_bytes, uint64_t n,
     uint64_t* idx = reinterpret_cast<uint64_t*>(ws + l.idx_off);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws + l.flag_off);
     uint32_t* slots = reinterpret_cast<uint32_t*>(ws + l.slot_off);
-    if (n <= (uint64_t{1} << 32))
-        k_tile_index<true><<<(uint32_t)launched, 64, 0, stream>>>(
-            src, src_bytes, n, e, groups, idx, flags, slots);
-    else
-        k_tile_index<false><<<(uint32_t)launched, 64, 0, stream>>>(
-            src, src_bytes, n, e, groups, idx, flags, slots);
+    const bool one = n <= (uint64_t{1} << 32);
+    const bool aligned = ((kPrefixBytes + (n + 1) / 2 + n) & 3) == 0;
+#define SZ_INDEX(O, A)                                                          \
+    k_tile_index<O, A><<<(uint32_t)launched, 64, 0, stream>>>(src, src_bytes, n, e, groups, \
+                                                               idx, flags, slots)
+    if (one && aligned) SZ_INDEX(true, true);
+    else if (one) SZ_INDEX(true, false);
+    else if (aligned) SZ_INDEX(false, true);
+    else SZ_INDEX(false, false);
+#undef SZ_INDEX
     return hipGetLastError();
 }
 

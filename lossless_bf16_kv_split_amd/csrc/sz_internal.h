@@ -148,8 +148,7 @@ constexpr uint64_t kTileDecodeMin = uint64_t{1} << 26;
 // holds at most kMaxIndexGroups waves; past that each takes several groups
 // of 64 items).
 constexpr uint32_t kTileWords = 2048;
-constexpr uint32_t kIndexRows = 1;            // rows of 64 items per index wave
-constexpr uint32_t kIndexItems = 64 * kIndexRows;  // items per index wave
+constexpr uint32_t kIndexItems = 64;          // items per index wave
 constexpr uint64_t kMaxIndexGroups = uint64_t{1} << 20;  // launched; more loop
 constexpr uint64_t kMaxTileGroups = uint64_t{1} << 22;   // launched; more loop
 constexpr uint32_t kSlotWords = 16;                      // dwords per tile slot

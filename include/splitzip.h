@@ -256,11 +256,12 @@ sz_status sz_decode_dense(const void *d_src, uint64_t src_bytes, void *d_dst,
 /* Decode in a single pass, one short-lived workgroup per 2048-word tile, in
  * two calls over a caller workspace of sz_decode_workspace_size(n) bytes
  * (256-byte aligned, not overlapping the container or the output; about
- * 72 bytes per tile plus 4 bytes per 256 possible escapes, at most 4 MiB of
+ * 72 bytes per tile plus 4 bytes per 64 possible escapes, at most 4 MiB of
  * those).  sz_decode_index
  * records, for every tile, the first escape record at or after the tile's
- * start (each of its workgroups takes a run of records and fills the tile
- * entries up to its last record: no search), and checks the header and that
+ * start and the tile's first records (each of its waves takes a run of 64
+ * records and fills the tile entries up to its last record: no search), and
+ * checks the header and that
  * the records ascend below n; sz_decode_tiles then rebuilds every tile's
  * words with its records' exponents in place of the codebook's (explainer
  * section "4. Pourquoi est-ce rapide ?").  sz_decode_tiles writes

@@ -139,8 +139,9 @@ constexpr uint64_t kTileDecodeMin = uint64_t{1} << 26;
 // its predecessor's tile up to its own (the tiles in between have no
 // records) and its tile's 64-byte slot: dword 0 the tile's record count (up
 // to 16 records ahead are seen, so a count above 15 only says "more than
-// 15"), dwords 1..15 the first 15 records as (offset in the tile) |
-// exponent << 16.  The decode of a tile loads its slot together with its
+// 15"), dwords 1..15 the 15 records from its first on as (offset in the
+// tile) | exponent << 16 (those past the count belong to later tiles; the
+// decode reads only the first count of them).  The decode of a tile loads its slot together with its
 // codes and sign|mantissa bytes, so a tile with at most 15 records (on the
 // 1 GiB KV tensor all but 0.014% of them, 4 on average) waits for no load
 // that depends on another; a tile with more goes through idx and the

@@ -562,8 +562,9 @@ __device__ __forceinline__ IndexItem make_item(uint64_t n, uint64_t e, uint64_t 
     return it;
 }
 
-// One wave per group of 64 items: lane L holds item k0 + L, and also
-// loads item k0 + 64 + L, so that the 16 items after the group are at hand.
+// One wave per group of 64 items: lane L holds item k0 + L, and lanes
+// 0..15 also load item k0 + 64 + L, so that the 16 items after the group
+// are at hand.
 // A lane whose item is the first of its tile fills idx over the gap back to
 // its predecessor's tile (a short gap alone, a long one with the whole
 // wave), sets the record count of the empty tiles in it to 0, and has its
@@ -606,7 +607,10 @@ __global__ __launch_bounds__(64) void k_tile_index(
         uint64_t p = 0, pp = 0, pa = 0;
         uint32_t x = 0, xa = 0;
         if (e > 0) {  // the same for the whole grid
-            const uint64_t kc = min_u64(k, last), kac = min_u64(ka, last);
+            // (only lanes 0..15 need the item 64 on; the others read their
+            // own again, from lines already fetched)
+            const uint64_t kc = min_u64(k, last);
+            const uint64_t kac = lane < kAhead ? min_u64(ka, last) : kc;
             const uint64_t kpc = min_u64(k > 0 ? k - 1 : 0, last);
             p = record_position<kOneSegment, kAlignedPos>(rd, kc);
             pp = record_position<kOneSegment, kAlignedPos>(rd, kpc);

@@ -318,15 +318,24 @@ sz_status sz_decode_pages(const void *d_src, uint64_t src_bytes, void *const *d_
 /* ---- compressed transfer to and from host memory ----------------------
  * The explainers present the codec as a way to shrink the KV transfer
  * between prefill and decode servers (introduction and "Les Resultats").
- * These two calls wrap it around the transfer one GPU has, the PCIe copy
- * to and from host memory: the n words are cut into chunks of chunk_elems
- * words (the last one shorter), each chunk becomes an ordinary container
- * with its own codebook, and the codec runs on `stream` while the previous
- * chunk's container is copied on a second, library-created stream.  Both
- * calls allocate two device staging buffers and a few events, block the
- * host until the transfer is complete, and release everything before
- * returning.  Host buffers should be pinned (hipHostMalloc, or a PyTorch
- * tensor with pin_memory=True) for the copies to overlap.
+ * These calls wrap it around the transfer one GPU has, the PCIe copy to and
+ * from host memory: the n words are cut into chunks of chunk_elems words
+ * (the last one shorter), each chunk becomes an ordinary container with its
+ * own codebook, and the codec runs on `stream` while earlier chunks'
+ * containers are copied on a second stream, through three device staging
+ * buffers.  Every call blocks the host until the transfer is complete.
+ * Host buffers should be pinned (hipHostMalloc, or a PyTorch tensor with
+ * pin_memory=True) for the copies to overlap.
+ *
+ * A transfer context (sz_ship_context_create) holds the copy stream, the
+ * staging buffers and the events for one chunk size on the device current
+ * when it is made; the _ctx calls use it and allocate nothing, except that
+ * the first decode on a context enlarges its staging buffers to hold a
+ * group of chunks (at least 2^24 words' worth, at most 128 MiB a buffer;
+ * a decode moves small chunks a group at a time), and a decode with more
+ * chunks than any before it grows the per-chunk status array.  A context
+ * serves one transfer at a time.  The one-shot calls sz_ship_to_host /
+ * sz_ship_from_host make a context, use it and release it.
  *
  * sz_ship_to_host: encode d_src[0..n) chunk by chunk into h_dst.
  *   chunk_elems  > 0, a multiple of 8 (keeps every chunk 16-byte aligned)
@@ -350,6 +359,25 @@ sz_status sz_ship_to_host(const void *d_src, uint64_t n_elements, uint64_t chunk
 sz_status sz_ship_from_host(const void *h_src, const uint64_t *h_offsets, uint64_t n_elements,
                             uint64_t chunk_elems, void *d_dst, int32_t *d_status,
                             hipStream_t stream);
+
+/* A transfer context for chunks of chunk_elems words (> 0, a multiple of
+ * 8) on the current device, to *ctx.  SZ_ERR_INVALID_ARGUMENT for a bad
+ * chunk size or NULL ctx, SZ_ERR_HIP when an allocation fails (nothing is
+ * then left allocated). */
+typedef struct sz_ship_context sz_ship_context;
+sz_status sz_ship_context_create(uint64_t chunk_elems, sz_ship_context **ctx);
+
+/* Releases a context (NULL is ignored) after its copies have drained. */
+void sz_ship_context_destroy(sz_ship_context *ctx);
+
+/* sz_ship_to_host / sz_ship_from_host over a context, with its chunk size;
+ * SZ_ERR_INVALID_ARGUMENT also when the context was made on another device. */
+sz_status sz_ship_to_host_ctx(sz_ship_context *ctx, const void *d_src, uint64_t n_elements,
+                              void *h_dst, uint64_t h_capacity, uint64_t *h_offsets,
+                              hipStream_t stream);
+sz_status sz_ship_from_host_ctx(sz_ship_context *ctx, const void *h_src,
+                                const uint64_t *h_offsets, uint64_t n_elements, void *d_dst,
+                                int32_t *d_status, hipStream_t stream);
 
 /* Static English text for a status code (never NULL). */
 const char *sz_status_string(int status);

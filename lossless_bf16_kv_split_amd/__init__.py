@@ -28,7 +28,7 @@ __all__ = [
     "sz_encode_single_read", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
     "sz_decode_workspace_size", "sz_decode_index", "sz_decode_tiles",
-    "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host", "sz_ship_from_host",
+    "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host", "sz_ship_from_host", "ShipContext",
     "sz_status_string", "encode",
     "decode",
     "PREFIX_BYTES", "MAX_ELEMENTS", "NOALLOC_WORKSPACE_BYTES",
@@ -89,12 +89,18 @@ def _load() -> ctypes.CDLL:
     L.sz_decode_pages.argtypes = [p, u64, p, u64, u64, u64, p, p]
     L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
     L.sz_ship_from_host.argtypes = [p, p, u64, u64, p, p, p]
+    L.sz_ship_context_create.argtypes = [u64, ctypes.POINTER(ctypes.c_void_p)]
+    L.sz_ship_context_destroy.argtypes = [p]
+    L.sz_ship_context_destroy.restype = None
+    L.sz_ship_to_host_ctx.argtypes = [p, p, u64, p, u64, p, p]
+    L.sz_ship_from_host_ctx.argtypes = [p, p, p, u64, p, p, p]
     for name in ("sz_encode", "sz_decode", "sz_encode_noalloc", "sz_encode_histogram", "sz_encode_codebook",
                  "sz_encode_pack", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
                  "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
                  "sz_decode_dense", "sz_decode_index", "sz_decode_tiles", "sz_encode_pages",
                  "sz_decode_pages", "sz_ship_to_host",
-                 "sz_ship_from_host"):
+                 "sz_ship_from_host", "sz_ship_context_create", "sz_ship_to_host_ctx",
+                 "sz_ship_from_host_ctx"):
         getattr(L, name).restype = i32
     L.sz_status_string.argtypes = [i32]
     L.sz_status_string.restype = ctypes.c_char_p
@@ -270,6 +276,39 @@ def sz_ship_from_host(h_src, h_offsets, n_elements: int, chunk_elems: int, dst, 
     _check(_lib.sz_ship_from_host(_ptr(h_src), _ptr(h_offsets), n_elements, chunk_elems,
                                   _ptr(dst), _ptr(d_status), _stream(stream)),
            "sz_ship_from_host")
+
+
+class ShipContext:
+    """A transfer context (sz_ship_context_create) for one chunk size on the
+    current device; released by close() or when collected."""
+
+    def __init__(self, chunk_elems: int):
+        self.handle = None
+        h = ctypes.c_void_p()
+        _check(_lib.sz_ship_context_create(chunk_elems, ctypes.byref(h)),
+               "sz_ship_context_create")
+        self.handle = h.value
+        self.chunk_elems = chunk_elems
+
+    def close(self) -> None:
+        if getattr(self, "handle", None):
+            _lib.sz_ship_context_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        self.close()
+
+    def to_host(self, src, n_elements: int, h_dst, h_capacity: int, h_offsets,
+                stream=None) -> None:
+        _check(_lib.sz_ship_to_host_ctx(self.handle, _ptr(src), n_elements, _ptr(h_dst),
+                                        h_capacity, _ptr(h_offsets), _stream(stream)),
+               "sz_ship_to_host_ctx")
+
+    def from_host(self, h_src, h_offsets, n_elements: int, dst, d_status=None,
+                  stream=None) -> None:
+        _check(_lib.sz_ship_from_host_ctx(self.handle, _ptr(h_src), _ptr(h_offsets), n_elements,
+                                          _ptr(dst), _ptr(d_status), _stream(stream)),
+               "sz_ship_from_host_ctx")
 
 
 # ---- conveniences (torch allocates; the library computes) -----------------

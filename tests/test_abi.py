@@ -266,3 +266,15 @@ def test_bench_chunk_plan_matches_library(sz):
     for n in sizes:
         g = -(-n >> bench.chunk_log2(n))
         assert sz.sz_workspace_size(n) == planned(g) + sample_area, (n, g)
+
+
+def test_ship_context_host_checks(sz):
+    """A transfer context is refused for a chunk size the calls cannot take,
+    before anything touches a device."""
+    for bad in (0, 12, (1 << 36) + 8):
+        with pytest.raises(sz.SplitZipError) as e:
+            sz.ShipContext(bad)
+        assert e.value.status == 1
+    import ctypes
+    assert sz._lib.sz_ship_context_create(65536, None) == 1
+    sz._lib.sz_ship_context_destroy(None)   # NULL is ignored

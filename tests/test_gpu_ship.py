@@ -99,3 +99,45 @@ def test_ship_corrupt_chunk_flagged(torch, sz):
         sz.sz_ship_from_host(host, offs, n, chunk, out, status)
     assert e.value.status == 4
     assert int(status.item()) == 4
+
+
+def test_ship_context_reused(torch, sz):
+    """One transfer context serves several transfers of different sizes, both
+    ways, each container the oracle's; a later decode with more chunks than
+    any before it still reports a corrupt chunk."""
+    chunk = 65536
+    ctx = sz.ShipContext(chunk)
+    try:
+        for i, (kind, n) in enumerate([("kv", 3 * chunk + 1000), ("wide40", chunk - 8),
+                                       ("kv", 9 * chunk + 24)]):
+            label = f"context {kind} {n}"
+            say(label)
+            words = make_words(kind, n, 40 + i)
+            x = torch.from_numpy(words.view(np.int16)).cuda()
+            chunks = -(-n // chunk)
+            cap = sum(sz.sz_max_compressed_size(min(chunk, n - c * chunk)) for c in range(chunks))
+            host = torch.empty(cap, dtype=torch.uint8, pin_memory=True)
+            offs = np.zeros(chunks + 1, dtype=np.uint64)
+            ctx.to_host(x, n, host, cap, offs)
+            hb = host.numpy()
+            for c in range(chunks):
+                want = oracle.encode(words[c * chunk:(c + 1) * chunk])
+                assert np.array_equal(hb[int(offs[c]):int(offs[c + 1])], want), (label, c)
+            out = torch.full((n + 64,), 0x5A5A, dtype=torch.int16, device="cuda")
+            status = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+            ctx.from_host(host, offs, n, out, status)
+            torch.cuda.synchronize()
+            assert int(status.item()) == 0 and torch.equal(out[:n], x), label
+            assert bool((out[n:] == 0x5A5A).all()), label
+        # the last tensor again, its fifth chunk's escape records swapped
+        base = int(offs[4])
+        esc = base + 176 + chunk // 2 + chunk
+        e = (int(offs[5]) - esc) // 5
+        assert e >= 2
+        hb[esc:esc + 4], hb[esc + 4:esc + 8] = hb[esc + 4:esc + 8].copy(), hb[esc:esc + 4].copy()
+        status.fill_(-1)
+        with pytest.raises(sz.SplitZipError) as err:
+            ctx.from_host(host, offs, n, out, status)
+        assert err.value.status == 4 and int(status.item()) == 4
+    finally:
+        ctx.close()

@@ -470,31 +470,36 @@ def main() -> int:
                                              "single pass over grid-stride tiles")
     passes = encode_passes + decode_passes
 
+    # the stream the passes go to: the launch stream, or the capture stream
+    # while a HIP graph is being captured
+    launch = [stream]
+
     def run_pass(p, dst_words):
+        st = launch[0]
         if p == "histogram":
-            sz.sz_encode_histogram(x, n, ws, ws_bytes, stream)
+            sz.sz_encode_histogram(x, n, ws, ws_bytes, st)
         elif p == "codebook":
-            sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size, stream)
+            sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size, st)
         elif p == "pack":
-            sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap, stream)
+            sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap, st)
         elif p == "sample":
-            sz.sz_encode_sample(x, n, ws, ws_bytes, stream)
+            sz.sz_encode_sample(x, n, ws, ws_bytes, st)
         elif p == "first":
-            sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap, stream)
+            sz.sz_encode_first_pass(x, n, ws, ws_bytes, dst, cap, st)
         elif p == "finish":
-            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, size, stream)
+            sz.sz_encode_finish(x, n, ws, ws_bytes, dst, cap, size, st)
         elif p == "fused":
-            sz.sz_decode_fused(container, total, dst_words, n, status, stream)
+            sz.sz_decode_fused(container, total, dst_words, n, status, st)
         elif p == "dense":
-            sz.sz_decode_dense(container, total, dst_words, n, status, stream)
+            sz.sz_decode_dense(container, total, dst_words, n, status, st)
         elif p == "index":
-            sz.sz_decode_index(container, total, n, dws, dws_bytes, stream)
+            sz.sz_decode_index(container, total, n, dws, dws_bytes, st)
         elif p == "tiles":
-            sz.sz_decode_tiles(container, total, dws, dws_bytes, dst_words, n, status, stream)
+            sz.sz_decode_tiles(container, total, dws, dws_bytes, dst_words, n, status, st)
         elif p == "unpack":
-            sz.sz_decode_unpack(container, total, dst_words, n, status, stream)
+            sz.sz_decode_unpack(container, total, dst_words, n, status, st)
         elif p == "scatter":
-            sz.sz_decode_scatter(container, total, dst_words, n, status, stream)
+            sz.sz_decode_scatter(container, total, dst_words, n, status, st)
 
     def step(seq, dst_words, ev=None):
         for i, p in enumerate(seq):
@@ -518,13 +523,19 @@ def main() -> int:
         side = torch.cuda.Stream()
         side.wait_stream(stream)
         with torch.cuda.stream(side):
+            launch[0] = side
             step(encode_passes, out)   # warm the capture stream once
         stream.wait_stream(side)
         torch.cuda.synchronize()
+        # the library calls take the capture stream explicitly: work sent to
+        # any other stream would run once now and be missing from the graph
         with torch.cuda.graph(g_enc):
+            launch[0] = torch.cuda.current_stream()
             step(encode_passes, out)
         with torch.cuda.graph(g_dec):
+            launch[0] = torch.cuda.current_stream()
             step(decode_passes, out)
+        launch[0] = stream
         torch.cuda.synchronize()
         do_encode, do_decode = g_enc.replay, g_dec.replay
         step_form = ("staged passes captured in two HIP graphs (encode, decode), replayed; "
@@ -560,6 +571,10 @@ def main() -> int:
     for _ in range(args.warmup):
         do_encode()
         do_decode()
+    # cleared first, so that the check below proves the timed steps (or the
+    # graph replays) wrote the words
+    out.zero_()
+    size.zero_()
     total_ms, t_wall, enc_ms, dec_ms = timed_steps(do_encode, do_decode)
     # the timed work is correct: same container, exact round trip
     ok = bool(torch.equal(out, x)) and int(status.item()) == 0 and int(size.item()) == total

@@ -315,6 +315,61 @@ sz_status sz_decode_pages(const void *d_src, uint64_t src_bytes, void *const *d_
                           uint64_t n_pages, uint64_t page_elems, uint64_t n_elements,
                           int32_t *d_status, hipStream_t stream);
 
+/* ---- per-layer blocks, one container each -----------------------------
+ * A serving stack holds a model's KV cache as one block per layer (the
+ * explainers' serving setting, section "Les Resultats"), and each block may
+ * travel on its own.  These calls take n_blocks blocks of block_elems words
+ * each, block b at the device address d_blocks[b] (a device array of
+ * pointers, each non-NULL and 16-byte aligned), and give block b its own
+ * container, exactly the one sz_encode gives for that block alone, so that
+ * sz_decode reads it too.  One launch per pass for all blocks.
+ *   containers  block b's container starts at the container buffer plus
+ *               b * pitch bytes (the buffer spans n_blocks * pitch bytes)
+ *   d_sizes     device array of n_blocks u64: block b's container size
+ *   n_blocks    1 .. 65535
+ * Block addresses are checked on the device: a NULL or misaligned one
+ * makes the calls touch none of that block's memory and report
+ * SZ_ERR_INVALID_ARGUMENT as the block's status; the other blocks are
+ * unaffected.  Blocks must not overlap one another or the containers.
+ * Neither call allocates, so both may be captured into a graph.
+ *
+ * sz_blocks_workspace_size: bytes of device workspace sz_encode_blocks
+ * needs (one sz_workspace_size(block_elems) per block, 256-byte strides,
+ * then a flag word per block); 0 for block_elems > SZ_MAX_ELEMENTS or a
+ * block count outside 1 .. 65535.  Host-only. */
+uint64_t sz_blocks_workspace_size(uint64_t block_elems, uint64_t n_blocks);
+
+/* sz_encode_blocks: sz_encode of every block, with the two-read passes
+ * (counts, codebook, pack), each one launch for all blocks.
+ *   d_dst      container buffer, 16-byte aligned; dst_pitch a multiple of
+ *              16 and at least sz_max_compressed_size(block_elems), else
+ *              SZ_ERR_CAPACITY.  Bytes of a block's pitch past its
+ *              container are not written.
+ *   d_sizes    written: each block's container size (0 for a block whose
+ *              address failed the check)
+ *   d_workspace, workspace_bytes   256-byte aligned, at least
+ *              sz_blocks_workspace_size(block_elems, n_blocks); it may hold
+ *              any bytes when the call starts
+ *   d_status   optional device array of n_blocks i32: SZ_OK or
+ *              SZ_ERR_INVALID_ARGUMENT per block */
+sz_status sz_encode_blocks(const void *const *d_blocks, uint64_t n_blocks, uint64_t block_elems,
+                           void *d_dst, uint64_t dst_pitch, uint64_t *d_sizes,
+                           void *d_workspace, uint64_t workspace_bytes, int32_t *d_status,
+                           hipStream_t stream);
+
+/* sz_decode_blocks: the reverse, block b's container read from d_src +
+ * b * src_pitch, d_sizes[b] bytes, and its words written to d_blocks[b].
+ * Each container is decoded in one pass with the checks of sz_decode (a
+ * size that is no container of block_elems words, or exceeds src_pitch,
+ * counts as corrupt, and then none of that container is read).
+ *   src_pitch  a multiple of 16, at least 176 + ceil(n/2) + n for
+ *              n = block_elems
+ *   d_status   required device array of n_blocks i32: SZ_OK, SZ_ERR_CORRUPT
+ *              or SZ_ERR_INVALID_ARGUMENT per block */
+sz_status sz_decode_blocks(const void *d_src, uint64_t src_pitch, const uint64_t *d_sizes,
+                           uint64_t n_blocks, uint64_t block_elems, void *const *d_blocks,
+                           int32_t *d_status, hipStream_t stream);
+
 /* ---- compressed transfer to and from host memory ----------------------
  * The explainers present the codec as a way to shrink the KV transfer
  * between prefill and decode servers (introduction and "Les Resultats").

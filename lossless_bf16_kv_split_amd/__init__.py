@@ -28,7 +28,8 @@ __all__ = [
     "sz_encode_single_read", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
     "sz_decode_workspace_size", "sz_decode_index", "sz_decode_tiles",
-    "sz_encode_pages", "sz_decode_pages", "sz_ship_to_host", "sz_ship_from_host", "ShipContext",
+    "sz_encode_pages", "sz_decode_pages", "sz_blocks_workspace_size", "sz_encode_blocks",
+    "sz_decode_blocks", "sz_ship_to_host", "sz_ship_from_host", "ShipContext",
     "sz_status_string", "encode",
     "decode",
     "PREFIX_BYTES", "MAX_ELEMENTS", "NOALLOC_WORKSPACE_BYTES",
@@ -87,6 +88,10 @@ def _load() -> ctypes.CDLL:
     L.sz_decode_tiles.argtypes = [p, u64, p, u64, p, u64, p, p]
     L.sz_encode_pages.argtypes = [p, u64, u64, u64, p, u64, p, p, p]
     L.sz_decode_pages.argtypes = [p, u64, p, u64, u64, u64, p, p]
+    L.sz_blocks_workspace_size.argtypes = [u64, u64]
+    L.sz_blocks_workspace_size.restype = u64
+    L.sz_encode_blocks.argtypes = [p, u64, u64, p, u64, p, p, u64, p, p]
+    L.sz_decode_blocks.argtypes = [p, u64, p, u64, u64, p, p, p]
     L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
     L.sz_ship_from_host.argtypes = [p, p, u64, u64, p, p, p]
     L.sz_ship_context_create.argtypes = [u64, ctypes.POINTER(ctypes.c_void_p)]
@@ -98,7 +103,7 @@ def _load() -> ctypes.CDLL:
                  "sz_encode_pack", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
                  "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
                  "sz_decode_dense", "sz_decode_index", "sz_decode_tiles", "sz_encode_pages",
-                 "sz_decode_pages", "sz_ship_to_host",
+                 "sz_decode_pages", "sz_encode_blocks", "sz_decode_blocks", "sz_ship_to_host",
                  "sz_ship_from_host", "sz_ship_context_create", "sz_ship_to_host_ctx",
                  "sz_ship_from_host_ctx"):
         getattr(L, name).restype = i32
@@ -261,6 +266,27 @@ def sz_decode_pages(src, src_bytes: int, d_pages, n_pages: int, page_elems: int,
                     n_elements: int, d_status=None, stream=None) -> None:
     _check(_lib.sz_decode_pages(_ptr(src), src_bytes, _ptr(d_pages), n_pages, page_elems,
                                 n_elements, _ptr(d_status), _stream(stream)), "sz_decode_pages")
+
+
+def sz_blocks_workspace_size(block_elems: int, n_blocks: int) -> int:
+    return int(_lib.sz_blocks_workspace_size(block_elems, n_blocks))
+
+
+def sz_encode_blocks(d_blocks, n_blocks: int, block_elems: int, dst, dst_pitch: int, d_sizes,
+                     workspace, workspace_bytes: int, d_status=None, stream=None) -> None:
+    """d_blocks: device array of block addresses (e.g. an int64 CUDA tensor);
+    d_sizes: device uint64 array of n_blocks entries (e.g. an int64 tensor)."""
+    _check(_lib.sz_encode_blocks(_ptr(d_blocks), n_blocks, block_elems, _ptr(dst), dst_pitch,
+                                 _ptr(d_sizes), _ptr(workspace), workspace_bytes, _ptr(d_status),
+                                 _stream(stream)), "sz_encode_blocks")
+
+
+def sz_decode_blocks(src, src_pitch: int, d_sizes, n_blocks: int, block_elems: int, d_blocks,
+                     d_status, stream=None) -> None:
+    """d_status: device int32 array of n_blocks entries (required)."""
+    _check(_lib.sz_decode_blocks(_ptr(src), src_pitch, _ptr(d_sizes), n_blocks, block_elems,
+                                 _ptr(d_blocks), _ptr(d_status), _stream(stream)),
+           "sz_decode_blocks")
 
 
 def sz_ship_to_host(src, n_elements: int, chunk_elems: int, h_dst, h_capacity: int, h_offsets,

@@ -133,7 +133,10 @@ sz_status encode_passes(Words src, uint64_t n, const sz::EncodePlan& p, uint8_t*
             st = hip_status(sz::launch_finish(src, p, w, out, dst_capacity, d_compressed_size, stream));
     } else {
         st = hip_status(sz::launch_histogram(src, p, w, stream));
-        if (st == SZ_OK) st = hip_status(sz::launch_codebook(p, w, out, d_compressed_size, stream));
+        // the codebook pass reads counts only, not the words
+        if (st == SZ_OK)
+            st = hip_status(sz::launch_codebook(sz::FlatWords{nullptr}, p, w, out,
+                                                d_compressed_size, stream));
         if (st == SZ_OK)
             st = hip_status(sz::launch_pack(src, p, w, out, dst_capacity, num_cus(dev), stream));
     }
@@ -231,6 +234,51 @@ sz_status check_pages(const void* d_pages, uint64_t n_pages, uint64_t page_elems
     return SZ_OK;
 }
 
+// Per-block calls: at most one block per grid row (HIP's grid height
+// limit), a workspace of one encode workspace per block, 256-byte strides,
+// and then a flag word per block.
+constexpr uint64_t kMaxBlocks = 65535;
+
+uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t{255}; }
+
+struct BlockLayout {
+    sz::EncodePlan plan;
+    uint64_t stride;     // bytes of workspace per block
+    uint64_t flags_off;  // the per-block flags
+    uint64_t bytes;
+};
+
+BlockLayout block_layout(uint64_t block_elems, uint64_t n_blocks) {
+    BlockLayout l;
+    l.plan = sz::plan_encode(block_elems);
+    l.stride = round256(l.plan.ws_bytes);
+    l.flags_off = n_blocks * l.stride;
+    l.bytes = l.flags_off + round256(4 * n_blocks);
+    return l;
+}
+
+// Host checks shared by the block calls: the block count, the table
+// pointer, the container buffer and its pitch, and the size array.  The
+// encode needs room for the largest container of a block; the decode only
+// a pitch that can hold a container at all (each size is checked against
+// the pitch on the device).
+sz_status check_blocks(const void* table, uint64_t n_blocks, uint64_t block_elems,
+                       const void* containers, uint64_t pitch, const void* sizes, bool encode) {
+    if (block_elems > SZ_MAX_ELEMENTS) return SZ_ERR_TOO_LARGE;
+    if (n_blocks == 0 || n_blocks > kMaxBlocks) return SZ_ERR_INVALID_ARGUMENT;
+    if (table == nullptr || !aligned(table, 8)) return SZ_ERR_INVALID_ARGUMENT;
+    if (containers == nullptr || !aligned(containers, 16) || pitch % 16 != 0)
+        return SZ_ERR_INVALID_ARGUMENT;
+    if (sizes == nullptr || !aligned(sizes, 8)) return SZ_ERR_INVALID_ARGUMENT;
+    if (encode && pitch < sz_max_compressed_size(block_elems)) return SZ_ERR_CAPACITY;
+    if (!encode && pitch < sz::container_bytes(block_elems, 0)) return SZ_ERR_INVALID_ARGUMENT;
+    return SZ_OK;
+}
+
+uint16_t* const* block_table(const void* const* t) {
+    return reinterpret_cast<uint16_t* const*>(const_cast<void* const*>(t));
+}
+
 }  // namespace
 
 extern "C" {
@@ -263,7 +311,8 @@ sz_status sz_encode_codebook(uint64_t n, void* d_workspace, uint64_t workspace_b
     if (dst_capacity < sz_max_compressed_size(n)) return SZ_ERR_CAPACITY;
     const sz::EncodePlan p = sz::plan_encode(n);
     if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
-    return hip_status(sz::launch_codebook(p, static_cast<uint8_t*>(d_workspace),
+    return hip_status(sz::launch_codebook(sz::FlatWords{nullptr}, p,
+                                          static_cast<uint8_t*>(d_workspace),
                                           static_cast<uint8_t*>(d_dst), d_compressed_size,
                                           stream));
 }
@@ -476,6 +525,56 @@ sz_status sz_decode_pages(const void* d_src, uint64_t src_bytes, void* const* d_
         st = decode_by_density(static_cast<const uint8_t*>(d_src), src_bytes, n, e, dst, d_status,
                                stream);
     if (hipFreeAsync(flag, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
+    return st;
+}
+
+uint64_t sz_blocks_workspace_size(uint64_t block_elems, uint64_t n_blocks) {
+    if (block_elems > SZ_MAX_ELEMENTS || n_blocks == 0 || n_blocks > kMaxBlocks) return 0;
+    return block_layout(block_elems, n_blocks).bytes;
+}
+
+sz_status sz_encode_blocks(const void* const* d_blocks, uint64_t n_blocks, uint64_t block_elems,
+                           void* d_dst, uint64_t dst_pitch, uint64_t* d_sizes,
+                           void* d_workspace, uint64_t workspace_bytes, int32_t* d_status,
+                           hipStream_t stream) {
+    if (sz_status s =
+            check_blocks(d_blocks, n_blocks, block_elems, d_dst, dst_pitch, d_sizes, true))
+        return s;
+    const BlockLayout l = block_layout(block_elems, n_blocks);
+    if (d_workspace == nullptr || !aligned(d_workspace, 256) || workspace_bytes < l.bytes)
+        return SZ_ERR_INVALID_ARGUMENT;
+    if (d_status != nullptr && !aligned(d_status, 4)) return SZ_ERR_INVALID_ARGUMENT;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
+    uint8_t* ws = static_cast<uint8_t*>(d_workspace);
+    uint8_t* out = static_cast<uint8_t*>(d_dst);
+    int32_t* flags = reinterpret_cast<int32_t*>(ws + l.flags_off);
+    const sz::BlockWords src{block_table(d_blocks), flags, (uint32_t)n_blocks, l.stride,
+                             dst_pitch, d_sizes};
+    sz_status st = hip_status(sz::launch_check_blocks(src.blocks, n_blocks, flags, d_status, stream));
+    if (st == SZ_OK) st = hip_status(sz::launch_histogram(src, l.plan, ws, stream));
+    if (st == SZ_OK) st = hip_status(sz::launch_codebook(src, l.plan, ws, out, nullptr, stream));
+    if (st == SZ_OK)
+        st = hip_status(sz::launch_pack(src, l.plan, ws, out, dst_pitch, num_cus(dev), stream));
+    return st;
+}
+
+sz_status sz_decode_blocks(const void* d_src, uint64_t src_pitch, const uint64_t* d_sizes,
+                           uint64_t n_blocks, uint64_t block_elems, void* const* d_blocks,
+                           int32_t* d_status, hipStream_t stream) {
+    if (sz_status s =
+            check_blocks(d_blocks, n_blocks, block_elems, d_src, src_pitch, d_sizes, false))
+        return s;
+    if (d_status == nullptr || !aligned(d_status, 4)) return SZ_ERR_INVALID_ARGUMENT;
+    // the statuses start as the address check's flags, which the decode
+    // then raises to SZ_ERR_CORRUPT where a container fails its checks
+    const sz::BlockWords dst{block_table(d_blocks), d_status, (uint32_t)n_blocks, 0, src_pitch,
+                             const_cast<uint64_t*>(d_sizes)};
+    sz_status st =
+        hip_status(sz::launch_check_blocks(dst.blocks, n_blocks, d_status, nullptr, stream));
+    if (st == SZ_OK)
+        st = hip_status(sz::launch_decode_dense(static_cast<const uint8_t*>(d_src), 0, block_elems,
+                                                0, dst, d_status, stream));
     return st;
 }
 

@@ -989,11 +989,29 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
     const int t = threadIdx.x;
     const int wave = t >> 6;
     uint16_t* map = reinterpret_cast<uint16_t*>(map4);
+    if constexpr (Words::kBlocks) status += blockIdx.y;
     if (out.invalid()) {  // the same for every thread
         if (blockIdx.x == 0 && t == 0 && status)
             __hip_atomic_fetch_max(status, kStatusInvalid, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
         return;
+    }
+    if constexpr (Words::kBlocks) {
+        // this block's container and its size, which gives E as
+        // size = 176 + ceil(n/2) + n + 5E; a size that cannot be a container
+        // of n words, or that runs past the block's pitch, is corrupt, and
+        // nothing of the container is read
+        src = byte_offset(src, block_pitch(out));
+        src_bytes = out.sizes[blockIdx.y];
+        const uint64_t fixed = container_bytes(n, 0);
+        const uint64_t extra = src_bytes - fixed;
+        e = extra / 5;
+        if (src_bytes < fixed || src_bytes > out.pitch || extra % 5 != 0 || e > (15 * n) / 16) {
+            if (blockIdx.x == 0 && t == 0)
+                __hip_atomic_fetch_max(status, kStatusCorrupt, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            return;
+        }
     }
     if (t == 0) {
         bad = 0;
@@ -1139,16 +1157,18 @@ hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t 
     while (r < 40 && ((n + (1ull << r) - 1) >> r) > kMaxDecodeRanges) r++;
     uint64_t blocks = (n + (1ull << r) - 1) >> r;
     if (blocks == 0) blocks = 1;  // the header check still runs
-    if (status) k_status_clear<<<1, 1, 0, stream>>>(status);
+    // (for blocks, the address check wrote every block's starting status)
+    if (status && !Words::kBlocks) k_status_clear<<<1, 1, 0, stream>>>(status);
     // the sign|mantissa stream starts at 176 + ceil(n/2): 8-byte aligned
     // exactly when n is a multiple of 16
     const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
+    const dim3 grid((uint32_t)blocks, grid_blocks(dst));
     if (aligned)
-        k_decode_dense<true, Words><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
-            src, src_bytes, n, e, r, dst, status);
+        k_decode_dense<true, Words><<<grid, kDenseThreads, 0, stream>>>(src, src_bytes, n, e, r,
+                                                                       dst, status);
     else
-        k_decode_dense<false, Words><<<(uint32_t)blocks, kDenseThreads, 0, stream>>>(
-            src, src_bytes, n, e, r, dst, status);
+        k_decode_dense<false, Words><<<grid, kDenseThreads, 0, stream>>>(src, src_bytes, n, e, r,
+                                                                        dst, status);
     return hipGetLastError();
 }
 
@@ -1166,5 +1186,7 @@ hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t 
 SZ_DECODE_INSTANCES(FlatWords)
 SZ_DECODE_INSTANCES(PagedWords)
 #undef SZ_DECODE_INSTANCES
+template hipError_t launch_decode_dense<BlockWords>(const uint8_t*, uint64_t, uint64_t, uint64_t,
+                                                    BlockWords, int32_t*, hipStream_t);
 
 }  // namespace sz

@@ -158,6 +158,12 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t 
                                                             uint64_t* __restrict__ hist,
                                                             uint32_t* __restrict__ arrivals) {
     __shared__ uint32_t h[kHistCopies * kHistPitch];
+    if constexpr (Words::kBlocks) {
+        const uint64_t off = block_ws(src);
+        counts = byte_offset(counts, off);
+        hist = byte_offset(hist, off);
+        arrivals = byte_offset(arrivals, off);
+    }
     if (blockIdx.x == 0) {
         for (int b = threadIdx.x; b < 256; b += kHistThreads) hist[b] = 0;
         if (threadIdx.x == 0) *arrivals = 0;
@@ -182,7 +188,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t 
 template <class Words>
 hipError_t launch_histogram(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream) {
     const uint32_t groups = p.chunks > 0 ? p.chunks : 1;  // the accumulators are zeroed
-    k_histogram<Words><<<groups, kHistThreads, 0, stream>>>(
+    k_histogram<Words><<<dim3(groups, grid_blocks(src)), kHistThreads, 0, stream>>>(
         src, p.n, p.chunk_log2, p.chunks, reinterpret_cast<uint32_t*>(ws + p.counts_off),
         reinterpret_cast<uint64_t*>(ws + p.hist_off),
         &reinterpret_cast<SampleArea*>(ws + p.sample_off)->arrivals);
@@ -191,6 +197,8 @@ hipError_t launch_histogram(Words src, const EncodePlan& p, uint8_t* ws, hipStre
 template hipError_t launch_histogram<FlatWords>(FlatWords, const EncodePlan&, uint8_t*,
                                                 hipStream_t);
 template hipError_t launch_histogram<PagedWords>(PagedWords, const EncodePlan&, uint8_t*,
+                                                 hipStream_t);
+template hipError_t launch_histogram<BlockWords>(BlockWords, const EncodePlan&, uint8_t*,
                                                  hipStream_t);
 
 // One workgroup: every page address must be non-NULL and 16-byte aligned.
@@ -214,6 +222,27 @@ __global__ __launch_bounds__(256) void k_check_pages(const uint16_t* const* page
 hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, int32_t* bad,
                               int32_t* status, hipStream_t stream) {
     k_check_pages<<<1, 256, 0, stream>>>(pages, n_pages, bad, status);
+    return hipGetLastError();
+}
+
+// One thread per block address: non-NULL and 16-byte aligned, else the
+// block is flagged and its workgroups touch none of its memory.
+__global__ __launch_bounds__(256) void k_check_blocks(const uint16_t* const* blocks,
+                                                      uint64_t n_blocks, int32_t* flags,
+                                                      int32_t* status) {
+    const uint64_t b = (uint64_t)blockIdx.x * 256 + threadIdx.x;
+    if (b >= n_blocks) return;
+    const uintptr_t a = reinterpret_cast<uintptr_t>(blocks[b]);
+    const int32_t f = (a == 0 || (a & 15) != 0) ? kBlockInvalid : 0;
+    flags[b] = f;
+    if (status) status[b] = f;
+}
+
+hipError_t launch_check_blocks(const uint16_t* const* blocks, uint64_t n_blocks, int32_t* flags,
+                               int32_t* status, hipStream_t stream) {
+    if (n_blocks == 0) return hipSuccess;
+    k_check_blocks<<<(uint32_t)((n_blocks + 255) / 256), 256, 0, stream>>>(blocks, n_blocks, flags,
+                                                                          status);
     return hipGetLastError();
 }
 
@@ -381,9 +410,11 @@ __device__ __forceinline__ uint64_t scan_chunk_escapes(const uint64_t (&esc)[kSe
 // codebook, seg_end and *d_size; and zeroes hist and the arrival count
 // again, so the pass can run twice on one workspace, and the sample pass's
 // tickets and counts, which puts a workspace that came in with other values
-// in step for the next sample pass.
+// in step for the next sample pass.  For blocks, 256 workgroups per block,
+// each block on its own workspace and container.
+template <class Words>
 __global__ __launch_bounds__(kSelectThreads) void k_codebook(
-    uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
+    Words src, uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
     uint64_t* __restrict__ hist, SampleArea* __restrict__ sample, uint64_t* __restrict__ chunk_base,
     uint8_t* __restrict__ dst, uint64_t* d_size) {
     __shared__ uint64_t key[256];
@@ -396,6 +427,19 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
 
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
+    if constexpr (Words::kBlocks) {
+        const uint64_t off = block_ws(src);
+        counts = byte_offset(counts, off);
+        hist = byte_offset(hist, off);
+        sample = byte_offset(sample, off);
+        chunk_base = byte_offset(chunk_base, off);
+        dst = byte_offset(dst, block_pitch(src));
+        d_size = src.sizes + blockIdx.y;
+        if (src.invalid()) {  // the same for every thread: no counts to read
+            if (blockIdx.x == 0 && t == 0) *d_size = 0;
+            return;
+        }
+    }
     {
         const uint32_t bin = blockIdx.x;
         const uint32_t* row = counts + (uint64_t)bin * chunks;
@@ -485,17 +529,21 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
     }
 }
 
-hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst, uint64_t* d_size,
-                           hipStream_t stream) {
+template <class Words>
+hipError_t launch_codebook(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
+                           uint64_t* d_size, hipStream_t stream) {
     const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + p.counts_off);
     uint64_t* hist = reinterpret_cast<uint64_t*>(ws + p.hist_off);
     SampleArea* sample = reinterpret_cast<SampleArea*>(ws + p.sample_off);
-    k_codebook<<<256, kSelectThreads, 0, stream>>>(p.n, p.chunk_log2, p.chunks, counts, hist,
-                                                   sample,
-                                                   reinterpret_cast<uint64_t*>(ws + p.base_off),
-                                                   dst, d_size);
+    k_codebook<Words><<<dim3(256, grid_blocks(src)), kSelectThreads, 0, stream>>>(
+        src, p.n, p.chunk_log2, p.chunks, counts, hist, sample,
+        reinterpret_cast<uint64_t*>(ws + p.base_off), dst, d_size);
     return hipGetLastError();
 }
+template hipError_t launch_codebook<FlatWords>(FlatWords, const EncodePlan&, uint8_t*, uint8_t*,
+                                               uint64_t*, hipStream_t);
+template hipError_t launch_codebook<BlockWords>(BlockWords, const EncodePlan&, uint8_t*, uint8_t*,
+                                                uint64_t*, hipStream_t);
 
 // ---------------------------------------------------------------- pass 3
 
@@ -895,6 +943,11 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     __shared__ PackLds lds;
     __shared__ uint32_t hist[kFirst ? kSpecCopies * kSpecPitch : 1];
     if (src.invalid()) return;  // the same for every thread
+    if constexpr (Words::kBlocks) {
+        static_assert(!kFirst, "blocks take the two-read encode");
+        chunk_base = byte_offset(chunk_base, block_ws(src));
+        dst = byte_offset(dst, block_pitch(src));
+    }
 
     const int t = threadIdx.x;
     const uint32_t chunk = blockIdx.x;
@@ -1183,11 +1236,11 @@ hipError_t launch_pack_role(Words src, const EncodePlan& p, const uint8_t* ws, u
     // exactly when n is a multiple of 32
     const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
     if (aligned)
-        k_pack<true, Words, kRole><<<p.chunks, kPackThreads, 0, stream>>>(
+        k_pack<true, Words, kRole><<<dim3(p.chunks, grid_blocks(src)), kPackThreads, 0, stream>>>(
             src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, totals, chunk_esc, area,
             p.spec_cap, p.scratch_pos, p.scratch_exp);
     else
-        k_pack<false, Words, kRole><<<p.chunks, kPackThreads, 0, stream>>>(
+        k_pack<false, Words, kRole><<<dim3(p.chunks, grid_blocks(src)), kPackThreads, 0, stream>>>(
             src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, totals, chunk_esc, area,
             p.spec_cap, p.scratch_pos, p.scratch_exp);
     return hipGetLastError();
@@ -1351,5 +1404,7 @@ hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_
 SZ_ENCODE_INSTANCES(FlatWords)
 SZ_ENCODE_INSTANCES(PagedWords)
 #undef SZ_ENCODE_INSTANCES
+template hipError_t launch_pack<BlockWords>(BlockWords, const EncodePlan&, const uint8_t*,
+                                            uint8_t*, uint64_t, int, hipStream_t);
 
 }  // namespace sz

@@ -176,7 +176,7 @@ inline TileIndexLayout tile_index_layout(uint64_t n) {
     return l;
 }
 
-inline uint64_t container_bytes(uint64_t n, uint64_t e) {
+__host__ __device__ inline uint64_t container_bytes(uint64_t n, uint64_t e) {
     return kPrefixBytes + (n + 1) / 2 + n + 5 * e;
 }
 
@@ -191,6 +191,7 @@ inline uint64_t container_bytes(uint64_t n, uint64_t e) {
 // then looked up once per wave, through a scalar load.
 struct FlatWords {
     static constexpr bool kPaged = false;
+    static constexpr bool kBlocks = false;
     uint16_t* base;
     __device__ __forceinline__ bool invalid() const { return false; }
     __device__ __forceinline__ uint16_t* at(uint64_t i) const { return base + i; }
@@ -202,6 +203,7 @@ constexpr uint32_t kMinPageLog2 = 14;
 
 struct PagedWords {
     static constexpr bool kPaged = true;  // at() and at_wave() read the page table
+    static constexpr bool kBlocks = false;
     uint16_t* const* pages;   // device table of page addresses
     uint32_t page_log2;
     const int32_t* bad;       // nonzero: the table failed its check, touch no page
@@ -220,11 +222,64 @@ struct PagedWords {
     }
 };
 
+// Several tensors of the same length ("blocks") in one launch, one
+// container each: blockIdx.y is the block.  Its words are at blocks[y]; its
+// encode workspace lies y * ws_stride bytes after block 0's, its container
+// y * pitch bytes after block 0's, and its container size is sizes[y]
+// (written by the encode, read by the decode).  flags[y] is
+// kBlockInvalid when the block's address failed its check (the encode keeps
+// the flags in its workspace; the decode uses its per-block statuses).
+constexpr int32_t kBlockInvalid = 1;  // SZ_ERR_INVALID_ARGUMENT
+struct BlockWords {
+    static constexpr bool kPaged = false;
+    static constexpr bool kBlocks = true;
+    uint16_t* const* blocks;  // device table of block addresses
+    const int32_t* flags;
+    uint32_t count;           // blocks (the launch's grid height)
+    uint64_t ws_stride;
+    uint64_t pitch;
+    uint64_t* sizes;
+    __device__ __forceinline__ bool invalid() const {
+        // other workgroups of the block may raise its decode status meanwhile
+        return __hip_atomic_load(flags + blockIdx.y, __ATOMIC_RELAXED,
+                                 __HIP_MEMORY_SCOPE_AGENT) == kBlockInvalid;
+    }
+    __device__ __forceinline__ uint16_t* at(uint64_t i) const { return blocks[blockIdx.y] + i; }
+    __device__ __forceinline__ uint16_t* at_wave(uint64_t i) const { return blocks[blockIdx.y] + i; }
+    __device__ __forceinline__ uint64_t run_end(uint64_t, uint64_t end) const { return end; }
+};
+
+// The launch's grid height, and this workgroup's block offsets into the
+// workspace and the containers (all 0 for a single tensor).
+template <class Words>
+inline uint32_t grid_blocks(const Words& w) {
+    if constexpr (Words::kBlocks) return w.count;
+    else return 1;
+}
+template <class Words>
+__device__ __forceinline__ uint64_t block_ws(const Words& w) {
+    if constexpr (Words::kBlocks) return (uint64_t)blockIdx.y * w.ws_stride;
+    else return 0;
+}
+template <class Words>
+__device__ __forceinline__ uint64_t block_pitch(const Words& w) {
+    if constexpr (Words::kBlocks) return (uint64_t)blockIdx.y * w.pitch;
+    else return 0;
+}
+template <class T>
+__device__ __forceinline__ T* byte_offset(T* p, uint64_t bytes) {
+    return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(p) + bytes);
+}
+
 // Launchers (asynchronous on `stream`; return the launch status).  The
-// templates are instantiated for FlatWords and PagedWords.
+// templates are instantiated for FlatWords and PagedWords, and those of the
+// two-read encode and of the dense decode also for BlockWords (one launch
+// for all blocks; ws, dst and d_size are block 0's, and src's own fields
+// give the other blocks').
 template <class Words>
 hipError_t launch_histogram(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream);
-hipError_t launch_codebook(const EncodePlan& p, uint8_t* ws, uint8_t* dst,
+template <class Words>
+hipError_t launch_codebook(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
                            uint64_t* d_size, hipStream_t stream);
 template <class Words>
 hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
@@ -265,5 +320,9 @@ hipError_t launch_decode_tiles(const uint8_t* src, uint64_t n, uint64_t e, const
 // *bad, and mirrors the result into *status when given.
 hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, int32_t* bad,
                               int32_t* status, hipStream_t stream);
+// Checks every block address of a table (non-NULL, 16-byte aligned) into
+// flags[b] (0 or kBlockInvalid), and the same into status[b] when given.
+hipError_t launch_check_blocks(const uint16_t* const* blocks, uint64_t n_blocks, int32_t* flags,
+                               int32_t* status, hipStream_t stream);
 
 }  // namespace sz

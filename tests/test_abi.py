@@ -249,6 +249,45 @@ def test_pages_host_checks(sz):
     assert status_of(dec, D, fixed, T, used - 1, P, n, None, 0) == 1
 
 
+def test_blocks_host_checks(sz):
+    """The per-block calls refuse bad counts, pointers, pitches and
+    workspaces on the host, and size their workspace as one encode
+    workspace per block plus a flag word each."""
+    n, nb = 1 << 21, 32
+    r256 = lambda x: (x + 255) // 256 * 256
+    assert sz.sz_blocks_workspace_size(n, nb) == nb * r256(sz.sz_workspace_size(n)) + 256
+    assert sz.sz_blocks_workspace_size(5000, 300) == 300 * r256(sz.sz_workspace_size(5000)) + 1280
+    for bad in ((n, 0), (n, 65536), ((1 << 36) + 1, 1)):
+        assert sz.sz_blocks_workspace_size(*bad) == 0
+    T = A + (1 << 35)    # stands in for a device block table: never read on the host
+    D = A + (1 << 33)
+    S = A + (1 << 34)
+    W = A + (1 << 36)
+    cap = sz.sz_max_compressed_size(n)
+    pitch = (cap + 15) // 16 * 16
+    wb = sz.sz_blocks_workspace_size(n, nb)
+    enc, dec = sz.sz_encode_blocks, sz.sz_decode_blocks
+    assert status_of(enc, T, nb, (1 << 36) + 1, D, 1 << 60, S, W, 1 << 40, None, 0) == 3
+    for args in ((T, 0, n, D, pitch, S, W, wb), (T, 65536, n, D, pitch, S, W, wb),
+                 (None, nb, n, D, pitch, S, W, wb), (T + 4, nb, n, D, pitch, S, W, wb),
+                 (T, nb, n, None, pitch, S, W, wb), (T, nb, n, D + 8, pitch, S, W, wb),
+                 (T, nb, n, D, pitch + 8, S, W, wb), (T, nb, n, D, pitch, None, W, wb),
+                 (T, nb, n, D, pitch, S + 4, W, wb), (T, nb, n, D, pitch, S, None, wb),
+                 (T, nb, n, D, pitch, S, W + 128, wb), (T, nb, n, D, pitch, S, W, wb - 1)):
+        assert status_of(enc, *args, None, 0) == 1, args
+    assert status_of(enc, T, nb, n, D, pitch, S, W, wb, MIS, 0) == 1
+    assert status_of(enc, T, nb, n, D, pitch - 16, S, W, wb, None, 0) == 2
+    fixed = 176 + n // 2 + n
+    assert status_of(dec, D, pitch, S, nb, n, T, None, 0) == 1                 # status required
+    assert status_of(dec, D, pitch, S, nb, n, T, MIS, 0) == 1
+    assert status_of(dec, D, (fixed - 1) // 16 * 16, S, nb, n, T, A, 0) == 1    # no room
+    assert status_of(dec, D, pitch, None, nb, n, T, A, 0) == 1
+    assert status_of(dec, D, pitch, S, 0, n, T, A, 0) == 1
+    assert status_of(dec, D, pitch, S, nb, n, None, A, 0) == 1
+    assert status_of(dec, D + 8, pitch, S, nb, n, T, A, 0) == 1
+    assert status_of(dec, D, pitch, S, nb, (1 << 36) + 1, T, A, 0) == 3
+
+
 def test_bench_chunk_plan_matches_library(sz):
     """bench.py predicts the single-read finish case from its own copy of the
     encode's chunk plan; the library's workspace size (per-chunk counts and

@@ -267,6 +267,121 @@ def pages_bench(args, w, n, x, torch, np, sz) -> int:
     return 0 if ok else 1
 
 
+def blocks_bench(args, w, n, x, torch, np, sz) -> int:
+    """The workload cut into equal blocks (one per layer, say), each at its
+    own address in a shuffled pool: sz_encode_blocks / sz_decode_blocks (one
+    launch per pass for all blocks) against one sz_encode / sz_decode call
+    per block and against the flat calls on the whole tensor.  HIP events on
+    the launch stream, median of the timed calls; every block's container
+    must equal sz_encode's of that block."""
+    nb = args.blocks
+    if n % nb != 0:
+        print(f"--blocks {nb} does not divide {n} words", file=sys.stderr)
+        return 2
+    b = n // nb
+    stream = torch.cuda.current_stream()
+    order = np.random.default_rng(6).permutation(nb)
+    pool = torch.empty(n, dtype=torch.int16, device="cuda")
+    for i, slot in enumerate(order):
+        pool[int(slot) * b:(int(slot) + 1) * b] = x[i * b:(i + 1) * b]
+    table = torch.tensor([pool.data_ptr() + 2 * b * int(s_) for s_ in order], dtype=torch.int64,
+                         device="cuda")
+    out_pool = torch.empty_like(pool)
+    out_table = torch.tensor([out_pool.data_ptr() + 2 * b * int(s_) for s_ in order],
+                             dtype=torch.int64, device="cuda")
+    views = [pool[int(s_) * b:(int(s_) + 1) * b] for s_ in order]
+    out_views = [out_pool[int(s_) * b:(int(s_) + 1) * b] for s_ in order]
+    pitch = (sz.sz_max_compressed_size(b) + 15) // 16 * 16
+    dst = torch.empty(nb * pitch, dtype=torch.uint8, device="cuda")
+    sizes = torch.zeros(nb, dtype=torch.int64, device="cuda")
+    wb = sz.sz_blocks_workspace_size(b, nb)
+    ws = torch.empty(wb, dtype=torch.uint8, device="cuda")
+    bstatus = torch.zeros(nb, dtype=torch.int32, device="cuda")
+    # the loop's containers, one per block, at the same pitch
+    ldst = torch.empty(nb * pitch, dtype=torch.uint8, device="cuda")
+    lsizes = torch.zeros(nb, dtype=torch.int64, device="cuda")
+    for i in range(nb):
+        sz.sz_encode(views[i], b, ldst[i * pitch:], pitch, lsizes[i:], stream)
+    hs = lsizes.cpu().numpy()
+    fcap = sz.sz_max_compressed_size(n)
+    fdst = torch.empty(fcap, dtype=torch.uint8, device="cuda")
+    fsize = torch.zeros(1, dtype=torch.int64, device="cuda")
+    sz.sz_encode(x, n, fdst, fcap, fsize, stream)
+    ftotal = int(fsize.item())
+    fcont = fdst[:ftotal]
+    fout = torch.empty(n, dtype=torch.int16, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(args.steps)]
+        for a, b_ in ev:
+            a.record(stream)
+            fn()
+            b_.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b_) for a, b_ in ev)
+        return ts[len(ts) // 2]
+
+    def encode_loop():
+        for i in range(nb):
+            sz.sz_encode(views[i], b, ldst[i * pitch:], pitch, lsizes[i:], stream)
+
+    def decode_loop():
+        for i in range(nb):
+            sz.sz_decode(ldst[i * pitch:], int(hs[i]), out_views[i], b, status, stream)
+
+    cases = {
+        "encode_blocks": lambda: sz.sz_encode_blocks(table, nb, b, dst, pitch, sizes, ws, wb,
+                                                     bstatus, stream),
+        "encode_per_block_calls": encode_loop,
+        "encode_flat": lambda: sz.sz_encode(x, n, fdst, fcap, fsize, stream),
+        "decode_blocks": lambda: sz.sz_decode_blocks(dst, pitch, sizes, nb, b, out_table,
+                                                     bstatus, stream),
+        "decode_per_block_calls": decode_loop,
+        "decode_flat": lambda: sz.sz_decode(fcont, ftotal, fout, n, status, stream),
+    }
+    ms = {k: timed(f) for k, f in cases.items()}
+    # the last calls' results: every block's container is sz_encode's, and
+    # both decodes give the words back
+    sz.sz_encode_blocks(table, nb, b, dst, pitch, sizes, ws, wb, bstatus, stream)
+    torch.cuda.synchronize()
+    ok = bool(torch.equal(sizes, lsizes)) and int(bstatus.abs().sum().item()) == 0
+    for i in range(nb):
+        ok = ok and bool(torch.equal(dst[i * pitch:i * pitch + int(hs[i])],
+                                     ldst[i * pitch:i * pitch + int(hs[i])]))
+    out_pool.zero_()
+    sz.sz_decode_blocks(dst, pitch, sizes, nb, b, out_table, bstatus, stream)
+    torch.cuda.synchronize()
+    ok = ok and int(bstatus.abs().sum().item()) == 0 and bool(torch.equal(out_pool, pool))
+    ok = ok and bool(torch.equal(fout, x)) and int(status.item()) == 0
+    # bytes the block calls move: the two-read encode (histogram, then pack)
+    # and the dense decode, summed over the blocks
+    es = [(int(hs[i]) - (176 + (b + 1) // 2 + b)) // 5 for i in range(nb)]
+    enc_alg = sum(algorithmic_bytes(b, e_)["histogram"] + algorithmic_bytes(b, e_)["pack"]
+                  for e_ in es)
+    dec_alg = sum(algorithmic_bytes(b, e_)["dense"] for e_ in es)
+    line = {"metric": "encode/decode GB/s (uncompressed), per-block calls against one call per "
+                      "block and the flat calls, 1 GPU",
+            "workload": w.name, "n_elements": n, "blocks": nb, "block_elems": b,
+            "container_pitch": pitch, "steps": args.steps,
+            "ms": {k: round(v, 5) for k, v in ms.items()},
+            "GBps": {k: round(2 * n / (v * 1e-3) / 1e9, 2) for k, v in ms.items()},
+            "blocks_encode_frac_hbm": round(enc_alg / (ms["encode_blocks"] * 1e-3) / 1e9
+                                            / HBM_PEAK_GBPS, 4),
+            "blocks_decode_frac_hbm": round(dec_alg / (ms["decode_blocks"] * 1e-3) / 1e9
+                                            / HBM_PEAK_GBPS, 4),
+            "blocks_over_per_block_calls": {
+                "encode": round(ms["encode_per_block_calls"] / ms["encode_blocks"], 4),
+                "decode": round(ms["decode_per_block_calls"] / ms["decode_blocks"], 4)},
+            "compressed_bytes": int(hs.sum()), "ratio": round(2 * n / int(hs.sum()), 5),
+            "round_trip_ok": ok}
+    print(json.dumps(line), flush=True)
+    return 0 if ok else 1
+
+
 def ship_bench(args, w, n, x, torch, np, sz) -> int:
     """Transfer of the whole tensor between HBM and pinned host memory:
     raw copies against the chunked, overlapped codec + copy calls, over a
@@ -413,6 +528,9 @@ def main() -> int:
     ap.add_argument("--pages", type=int, default=0, metavar="PAGE_ELEMS",
                     help="instead: time sz_encode_pages / sz_decode_pages on the workload "
                          "spread over pages of this many words, against the flat calls")
+    ap.add_argument("--blocks", type=int, default=0, metavar="N",
+                    help="instead: time sz_encode_blocks / sz_decode_blocks on the workload cut "
+                         "into N equal blocks, against one call per block and the flat calls")
     ap.add_argument("--ship", action="store_true",
                     help="instead: time the compressed transfer to and from pinned host "
                          "memory (sz_ship_to_host / sz_ship_from_host) against raw copies")
@@ -438,6 +556,8 @@ def main() -> int:
         return ship_bench(args, w, n, x, torch, np, sz)
     if args.pages:
         return pages_bench(args, w, n, x, torch, np, sz)
+    if args.blocks:
+        return blocks_bench(args, w, n, x, torch, np, sz)
     cap = sz.sz_max_compressed_size(n)
     ws_bytes = sz.sz_workspace_size(n)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")

@@ -334,13 +334,16 @@ sz_status sz_decode_pages(const void *d_src, uint64_t src_bytes, void *const *d_
  * Neither call allocates, so both may be captured into a graph.
  *
  * sz_blocks_workspace_size: bytes of device workspace sz_encode_blocks
- * needs (one sz_workspace_size(block_elems) per block, 256-byte strides,
- * then a flag word per block); 0 for block_elems > SZ_MAX_ELEMENTS or a
- * block count outside 1 .. 65535.  Host-only. */
+ * needs: for each block, the per-chunk counts and escape bases of a chunk
+ * plan made for all the blocks' words together (at most about 4.3 MB a
+ * block, much less for small blocks), at 256-byte strides, then a flag
+ * word per block; 0 for block_elems > SZ_MAX_ELEMENTS or a block count
+ * outside 1 .. 65535.  Host-only. */
 uint64_t sz_blocks_workspace_size(uint64_t block_elems, uint64_t n_blocks);
 
 /* sz_encode_blocks: sz_encode of every block, with the two-read passes
- * (counts, codebook, pack), each one launch for all blocks.
+ * (address check, counts, codebook, pack), each one launch for all
+ * blocks.
  *   d_dst      container buffer, 16-byte aligned; dst_pitch a multiple of
  *              16 and at least sz_max_compressed_size(block_elems), else
  *              SZ_ERR_CAPACITY.  Bytes of a block's pitch past its

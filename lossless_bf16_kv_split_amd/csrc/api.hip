@@ -235,8 +235,9 @@ sz_status check_pages(const void* d_pages, uint64_t n_pages, uint64_t page_elems
 }
 
 // Per-block calls: at most one block per grid row (HIP's grid height
-// limit), a workspace of one encode workspace per block, 256-byte strides,
-// and then a flag word per block.
+// limit), a workspace of one encode workspace per block (for the chunk plan
+// of all the blocks together), 256-byte strides, and then a flag word per
+// block.
 constexpr uint64_t kMaxBlocks = 65535;
 
 uint64_t round256(uint64_t x) { return (x + 255) & ~uint64_t{255}; }
@@ -250,7 +251,7 @@ struct BlockLayout {
 
 BlockLayout block_layout(uint64_t block_elems, uint64_t n_blocks) {
     BlockLayout l;
-    l.plan = sz::plan_encode(block_elems);
+    l.plan = sz::plan_blocks(block_elems, n_blocks);
     l.stride = round256(l.plan.ws_bytes);
     l.flags_off = n_blocks * l.stride;
     l.bytes = l.flags_off + round256(4 * n_blocks);
@@ -551,7 +552,8 @@ sz_status sz_encode_blocks(const void* const* d_blocks, uint64_t n_blocks, uint6
     int32_t* flags = reinterpret_cast<int32_t*>(ws + l.flags_off);
     const sz::BlockWords src{block_table(d_blocks), flags, (uint32_t)n_blocks, l.stride,
                              dst_pitch, d_sizes};
-    sz_status st = hip_status(sz::launch_check_blocks(src.blocks, n_blocks, flags, d_status, stream));
+    sz_status st = hip_status(sz::launch_check_blocks(src.blocks, n_blocks, flags, d_status, ws,
+                                                      l.plan, l.stride, stream));
     if (st == SZ_OK) st = hip_status(sz::launch_histogram(src, l.plan, ws, stream));
     if (st == SZ_OK) st = hip_status(sz::launch_codebook(src, l.plan, ws, out, nullptr, stream));
     if (st == SZ_OK)
@@ -571,7 +573,8 @@ sz_status sz_decode_blocks(const void* d_src, uint64_t src_pitch, const uint64_t
     const sz::BlockWords dst{block_table(d_blocks), d_status, (uint32_t)n_blocks, 0, src_pitch,
                              const_cast<uint64_t*>(d_sizes)};
     sz_status st =
-        hip_status(sz::launch_check_blocks(dst.blocks, n_blocks, d_status, nullptr, stream));
+        hip_status(sz::launch_check_blocks(dst.blocks, n_blocks, d_status, nullptr, nullptr,
+                                           sz::EncodePlan{}, 0, stream));
     if (st == SZ_OK)
         st = hip_status(sz::launch_decode_dense(static_cast<const uint8_t*>(d_src), 0, block_elems,
                                                 0, dst, d_status, stream));

@@ -1153,8 +1153,9 @@ hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t 
     uint32_t r = 14;
     // at most kMaxDecodeRanges workgroups: enough for several waves of
     // resident workgroups (a 10.7 GB input with 2048 ranges left the last
-    // wave a quarter full: 16% slower)
-    while (r < 40 && ((n + (1ull << r) - 1) >> r) > kMaxDecodeRanges) r++;
+    // wave a quarter full: 16% slower); for blocks, over all their words
+    const uint64_t words = n * grid_blocks(dst);
+    while (r < 40 && ((words + (1ull << r) - 1) >> r) > kMaxDecodeRanges) r++;
     uint64_t blocks = (n + (1ull << r) - 1) >> r;
     if (blocks == 0) blocks = 1;  // the header check still runs
     // (for blocks, the address check wrote every block's starting status)

@@ -39,8 +39,6 @@ namespace sz {
 // ---------------------------------------------------------------- plan
 
 EncodePlan plan_encode(uint64_t n) {
-    EncodePlan p;
-    p.n = n;
     uint32_t c = kMinChunkLog2;
     while (c < 40 && ((n + (1ull << c) - 1) >> c) > kPlanChunks) c++;
     // Halve the chunk (on MI355X):
@@ -64,6 +62,12 @@ EncodePlan plan_encode(uint64_t n) {
         const bool wide_select = g1 > 3 * kMaxChunks / 4 && g1 % 4 == 0;
         if (fills || wide_select) c--;
     }
+    return plan_encode_chunks(n, c);
+}
+
+EncodePlan plan_encode_chunks(uint64_t n, uint32_t c) {
+    EncodePlan p;
+    p.n = n;
     p.chunk_log2 = c;
     p.chunks = (uint32_t)((n + (1ull << c) - 1) >> c);
     auto align = [](uint64_t x) { return (x + 255) & ~255ull; };
@@ -85,6 +89,14 @@ EncodePlan plan_encode(uint64_t n) {
     p.scratch_end = p.scratch_exp + e_max;
     p.single_read = n >= kSingleReadMin && p.scratch_end <= container_bytes(n, (15 * n) / 16);
     return p;
+}
+
+EncodePlan plan_blocks(uint64_t block_elems, uint64_t n_blocks) {
+    uint32_t c = plan_encode(block_elems * n_blocks).chunk_log2;
+    uint32_t fit = kMinChunkLog2;  // the smallest chunk that holds a whole block
+    while (fit < 32 && (uint64_t{1} << fit) < block_elems) fit++;
+    if (c > fit) c = fit;
+    return plan_encode_chunks(block_elems, c);
 }
 
 // ---------------------------------------------------------------- pass 1
@@ -150,7 +162,9 @@ __device__ __forceinline__ void count_exponents(Words src, uint64_t begin, uint6
 // counts[bin * chunks + chunk]: bin-major, so that the codebook pass reads
 // every bin's counts, and each chunk's 16 codebook counts, coalesced
 // Workgroup 0 also zeroes what the codebook pass counts up: the whole
-// input's counts and the number of its workgroups done.
+// input's counts and the number of its workgroups done.  For blocks, every
+// workgroup adds its counts to its block's whole-input counts instead,
+// which the address check zeroed.
 template <class Words>
 __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t n,
                                                             uint32_t chunk_log2, uint32_t chunks,
@@ -164,7 +178,7 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t 
         hist = byte_offset(hist, off);
         arrivals = byte_offset(arrivals, off);
     }
-    if (blockIdx.x == 0) {
+    if (blockIdx.x == 0 && !Words::kBlocks) {
         for (int b = threadIdx.x; b < 256; b += kHistThreads) hist[b] = 0;
         if (threadIdx.x == 0) *arrivals = 0;
     }
@@ -182,6 +196,9 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t 
 #pragma unroll
         for (int c = 0; c < kHistCopies; c++) s += h[c * kHistPitch + bin];
         counts[(uint64_t)bin * chunks + blockIdx.x] = s;
+        if constexpr (Words::kBlocks)
+            __hip_atomic_fetch_add(hist + bin, (uint64_t)s, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
@@ -225,24 +242,28 @@ hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, in
     return hipGetLastError();
 }
 
-// One thread per block address: non-NULL and 16-byte aligned, else the
-// block is flagged and its workgroups touch none of its memory.
+// One workgroup per block: its address must be non-NULL and 16-byte
+// aligned, else the block is flagged and its workgroups touch none of its
+// memory; with a workspace, the block's whole-input counts start at zero.
 __global__ __launch_bounds__(256) void k_check_blocks(const uint16_t* const* blocks,
-                                                      uint64_t n_blocks, int32_t* flags,
-                                                      int32_t* status) {
-    const uint64_t b = (uint64_t)blockIdx.x * 256 + threadIdx.x;
-    if (b >= n_blocks) return;
-    const uintptr_t a = reinterpret_cast<uintptr_t>(blocks[b]);
-    const int32_t f = (a == 0 || (a & 15) != 0) ? kBlockInvalid : 0;
-    flags[b] = f;
-    if (status) status[b] = f;
+                                                      int32_t* flags, int32_t* status,
+                                                      uint64_t* hist, uint64_t ws_stride) {
+    const uint32_t b = blockIdx.x;
+    if (hist) byte_offset(hist, (uint64_t)b * ws_stride)[threadIdx.x] = 0;
+    if (threadIdx.x == 0) {
+        const uintptr_t a = reinterpret_cast<uintptr_t>(blocks[b]);
+        const int32_t f = (a == 0 || (a & 15) != 0) ? kBlockInvalid : 0;
+        flags[b] = f;
+        if (status) status[b] = f;
+    }
 }
 
 hipError_t launch_check_blocks(const uint16_t* const* blocks, uint64_t n_blocks, int32_t* flags,
-                               int32_t* status, hipStream_t stream) {
+                               int32_t* status, uint8_t* ws, const EncodePlan& p,
+                               uint64_t ws_stride, hipStream_t stream) {
     if (n_blocks == 0) return hipSuccess;
-    k_check_blocks<<<(uint32_t)((n_blocks + 255) / 256), 256, 0, stream>>>(blocks, n_blocks, flags,
-                                                                          status);
+    uint64_t* hist = ws ? reinterpret_cast<uint64_t*>(ws + p.hist_off) : nullptr;
+    k_check_blocks<<<(uint32_t)n_blocks, 256, 0, stream>>>(blocks, flags, status, hist, ws_stride);
     return hipGetLastError();
 }
 
@@ -410,8 +431,10 @@ __device__ __forceinline__ uint64_t scan_chunk_escapes(const uint64_t (&esc)[kSe
 // codebook, seg_end and *d_size; and zeroes hist and the arrival count
 // again, so the pass can run twice on one workspace, and the sample pass's
 // tickets and counts, which puts a workspace that came in with other values
-// in step for the next sample pass.  For blocks, 256 workgroups per block,
-// each block on its own workspace and container.
+// in step for the next sample pass.  For blocks, one workgroup per block,
+// each on its block's workspace and container: the count pass has already
+// added up the whole block's counts, so the workgroup goes straight to the
+// ranking.
 template <class Words>
 __global__ __launch_bounds__(kSelectThreads) void k_codebook(
     Words src, uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
@@ -436,11 +459,10 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
         dst = byte_offset(dst, block_pitch(src));
         d_size = src.sizes + blockIdx.y;
         if (src.invalid()) {  // the same for every thread: no counts to read
-            if (blockIdx.x == 0 && t == 0) *d_size = 0;
+            if (t == 0) *d_size = 0;
             return;
         }
-    }
-    {
+    } else {
         const uint32_t bin = blockIdx.x;
         const uint32_t* row = counts + (uint64_t)bin * chunks;
         uint32_t v[kSelectChunks];
@@ -535,7 +557,8 @@ hipError_t launch_codebook(Words src, const EncodePlan& p, uint8_t* ws, uint8_t*
     const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + p.counts_off);
     uint64_t* hist = reinterpret_cast<uint64_t*>(ws + p.hist_off);
     SampleArea* sample = reinterpret_cast<SampleArea*>(ws + p.sample_off);
-    k_codebook<Words><<<dim3(256, grid_blocks(src)), kSelectThreads, 0, stream>>>(
+    k_codebook<Words><<<dim3(Words::kBlocks ? 1 : 256, grid_blocks(src)), kSelectThreads, 0,
+                        stream>>>(
         src, p.n, p.chunk_log2, p.chunks, counts, hist, sample,
         reinterpret_cast<uint64_t*>(ws + p.base_off), dst, d_size);
     return hipGetLastError();

@@ -81,6 +81,15 @@ static_assert(sizeof(SampleArea) % 16 == 0 && offsetof(SampleArea, lut) % 16 == 
 constexpr uint64_t kSingleReadMin = uint64_t{1} << 20;
 
 EncodePlan plan_encode(uint64_t n);
+// The workspace layout and scratch area for n words in chunks of
+// 2^chunk_log2 words (plan_encode's own choice of chunk goes through it).
+EncodePlan plan_encode_chunks(uint64_t n, uint32_t chunk_log2);
+// The plan of each of n_blocks blocks of block_elems words encoded in one
+// launch sequence: chunks sized for all the blocks' words together (so
+// that the launch holds as many workgroups as one tensor of that size
+// would), never smaller than 2^kMinChunkLog2 words, never larger than a
+// block needs.
+EncodePlan plan_blocks(uint64_t block_elems, uint64_t n_blocks);
 
 // Residency of wide workgroups on MI355X: a wave whose kernel needs more
 // than 74 scalar registers of its own (80 with the ones the hardware
@@ -321,8 +330,11 @@ hipError_t launch_decode_tiles(const uint8_t* src, uint64_t n, uint64_t e, const
 hipError_t launch_check_pages(const uint16_t* const* pages, uint64_t n_pages, int32_t* bad,
                               int32_t* status, hipStream_t stream);
 // Checks every block address of a table (non-NULL, 16-byte aligned) into
-// flags[b] (0 or kBlockInvalid), and the same into status[b] when given.
+// flags[b] (0 or kBlockInvalid), and the same into status[b] when given;
+// with a workspace (ws != nullptr), also zeroes each block's whole-input
+// counts, which the block count pass adds up.
 hipError_t launch_check_blocks(const uint16_t* const* blocks, uint64_t n_blocks, int32_t* flags,
-                               int32_t* status, hipStream_t stream);
+                               int32_t* status, uint8_t* ws, const EncodePlan& p,
+                               uint64_t ws_stride, hipStream_t stream);
 
 }  // namespace sz

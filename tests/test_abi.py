@@ -249,14 +249,38 @@ def test_pages_host_checks(sz):
     assert status_of(dec, D, fixed, T, used - 1, P, n, None, 0) == 1
 
 
+def planned_workspace(g: int) -> int:
+    """The encode workspace of g chunks before the sample area: counts
+    u32[256][g], hist u64[256], bases u64[g], totals u64[4][256], escapes
+    u32[g], each region 256-byte aligned."""
+    align = lambda x: (x + 255) // 256 * 256
+    return align(align(align(align(align(g * 1024) + 2048) + g * 8) + 8192) + g * 4)
+
+
 def test_blocks_host_checks(sz):
     """The per-block calls refuse bad counts, pointers, pitches and
     workspaces on the host, and size their workspace as one encode
     workspace per block plus a flag word each."""
+    import bench
     n, nb = 1 << 21, 32
     r256 = lambda x: (x + 255) // 256 * 256
-    assert sz.sz_blocks_workspace_size(n, nb) == nb * r256(sz.sz_workspace_size(n)) + 256
-    assert sz.sz_blocks_workspace_size(5000, 300) == 300 * r256(sz.sz_workspace_size(5000)) + 1280
+    sample_area = sz.sz_workspace_size(1) - planned_workspace(1)
+
+    def block_ws(m, count):
+        # chunks planned for all the blocks' words, clamped to [2^14, a block]
+        fit = 14
+        while fit < 32 and (1 << fit) < m:
+            fit += 1
+        c = min(bench.chunk_log2(m * count), fit)
+        g = -(-m >> c)
+        return count * r256(planned_workspace(g) + sample_area) + r256(4 * count)
+
+    for m, count in ((n, nb), (5000, 300), (1 << 24, 32), (1 << 24, 1), ((1 << 20) + 3, 7),
+                     (0, 4), (1 << 33, 2)):
+        assert sz.sz_blocks_workspace_size(m, count) == block_ws(m, count), (m, count)
+    # 32 blocks of 2^24 words are counted in chunks of 2^17 words, as one
+    # tensor of 2^29 words is
+    assert block_ws(1 << 24, 32) < 32 * sz.sz_workspace_size(1 << 24)
     for bad in ((n, 0), (n, 65536), ((1 << 36) + 1, 1)):
         assert sz.sz_blocks_workspace_size(*bad) == 0
     T = A + (1 << 35)    # stands in for a device block table: never read on the host
@@ -294,10 +318,7 @@ def test_bench_chunk_plan_matches_library(sz):
     bases, the whole input's counts, per-chunk escape counts, then a fixed
     sample area) fixes the chunk count it planned."""
     import bench
-    align = lambda x: (x + 255) // 256 * 256
-    def planned(g):  # counts u32[256][g], hist u64[256], bases u64[g],
-        # totals u64[4][256], escapes u32[g]
-        return align(align(align(align(align(g * 1024) + 2048) + g * 8) + 8192) + g * 4)
+    planned = planned_workspace
     sample_area = sz.sz_workspace_size(1) - planned(1)
     sizes = [1, 4096, 1 << 21, (1 << 25) + 123, 3 * (1 << 24) + 5, (1 << 26) - 5,
              (1 << 27) + 77, 3 << 26, 1 << 28, 1280 * (1 << 18) - 3, 1537 * (1 << 18) - 1,

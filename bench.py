@@ -57,8 +57,9 @@ KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_codebook",
                 "fused": "k_decode_fused", "dense": "k_decode_dense",
                 "index": "k_tile_index", "tiles": "k_decode_tiles",
                 "unpack": "k_unpack", "scatter": "k_scatter"}
-# the sample of the single-read encode: 512 blocks of 2048 words
-SAMPLE_BLOCKS, SAMPLE_BLOCK_WORDS = 512, 2048
+# the sample of the single-read encode: 512 blocks of 2048 words (32 for
+# each of several blocks encoded together)
+SAMPLE_BLOCKS, SAMPLE_BLOCK_WORDS, BLOCK_SAMPLE_BLOCKS = 512, 2048, 32
 MIN_CHUNK_LOG2, PLAN_CHUNKS, RESIDENT_PACK_GROUPS = 14, 2048, 512
 
 
@@ -81,6 +82,15 @@ def chunk_log2(n: int) -> int:
 # escape in TILE_DECODE_DENSITY words; below TILE_DECODE_MIN words, unpack then
 # scatter up to one escape in SCATTER_DECODE_DENSITY; else the dense decode
 TILE_DECODE_DENSITY, SCATTER_DECODE_DENSITY, TILE_DECODE_MIN = 128, 256, 1 << 26
+
+
+def blocks_chunk_log2(block_elems: int, n_blocks: int) -> int:
+    """The chunk of sz_encode_blocks: planned for all the blocks' words,
+    clamped to [2^14, the smallest power of two holding a block]."""
+    fit = MIN_CHUNK_LOG2
+    while fit < 32 and (1 << fit) < block_elems:
+        fit += 1
+    return min(chunk_log2(block_elems * n_blocks), fit)
 
 
 def kernel_source_hash() -> str:
@@ -161,13 +171,15 @@ def cpu_baseline(words, repeats: int) -> dict:
     }
 
 
-def single_read_case(words, codebook) -> str:
+def single_read_case(words, codebook, sample_blocks: int = SAMPLE_BLOCKS,
+                     c: int | None = None) -> str:
     """Which branch the finish pass of the single-read encode takes: the
     provisional codebook is ranked from the sample (count descending,
-    exponent ascending) and compared with the container's."""
+    exponent ascending) and compared with the container's.  sample_blocks
+    and the chunk log2 c default to a single tensor's."""
     import numpy as np
     n = words.size
-    starts = (np.arange(SAMPLE_BLOCKS, dtype=np.int64) * (n // SAMPLE_BLOCKS)
+    starts = (np.arange(sample_blocks, dtype=np.int64) * (n // sample_blocks)
               ) // SAMPLE_BLOCK_WORDS * SAMPLE_BLOCK_WORDS
     idx = (starts[:, None] + np.arange(SAMPLE_BLOCK_WORDS)[None, :]).ravel()
     h = np.bincount((words[idx] >> 7) & 0xFF, minlength=256)
@@ -177,7 +189,7 @@ def single_read_case(words, codebook) -> str:
         return "full:sample"
     if set(prov) != set(codebook):
         return "full:set"
-    c = chunk_log2(n)
+    c = chunk_log2(n) if c is None else c
     esc_lut = np.ones(256, dtype=np.uint8)
     esc_lut[prov] = 0
     per_chunk = np.add.reduceat(esc_lut[(words >> 7) & 0xFF].astype(np.uint32),
@@ -267,7 +279,7 @@ def pages_bench(args, w, n, x, torch, np, sz) -> int:
     return 0 if ok else 1
 
 
-def blocks_bench(args, w, n, x, torch, np, sz) -> int:
+def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
     """The workload cut into equal blocks (one per layer, say), each at its
     own address in a shuffled pool: sz_encode_blocks / sz_decode_blocks (one
     launch per pass for all blocks) against one sz_encode / sz_decode call
@@ -357,16 +369,34 @@ def blocks_bench(args, w, n, x, torch, np, sz) -> int:
     torch.cuda.synchronize()
     ok = ok and int(bstatus.abs().sum().item()) == 0 and bool(torch.equal(out_pool, pool))
     ok = ok and bool(torch.equal(fout, x)) and int(status.item()) == 0
-    # bytes the block calls move: the two-read encode (histogram, then pack)
-    # and the dense decode, summed over the blocks
+    # bytes the block calls move, summed over the blocks: the encode form the
+    # library takes (single read from 2^26 words in all with blocks of at
+    # least 2^20 words: sample, first pass and the finish case each block
+    # takes; else counts, then pack) and the dense decode
     es = [(int(hs[i]) - (176 + (b + 1) // 2 + b)) // 5 for i in range(nb)]
-    enc_alg = sum(algorithmic_bytes(b, e_)["histogram"] + algorithmic_bytes(b, e_)["pack"]
-                  for e_ in es)
+    single = b >= 1 << 20 and n >= 1 << 26
+    c = blocks_chunk_log2(b, nb)
+    cases = []
+    enc_alg = 0
+    for i, e_ in enumerate(es):
+        if single:
+            cb = dst[i * pitch + 160:i * pitch + 176].cpu().tolist()
+            case = single_read_case(words[i * b:(i + 1) * b], cb, BLOCK_SAMPLE_BLOCKS, c)
+            a = algorithmic_bytes(b, e_, case)
+            enc_alg += 2 * BLOCK_SAMPLE_BLOCKS * SAMPLE_BLOCK_WORDS + a["first"] + a["finish"]
+            cases.append(case)
+        else:
+            a = algorithmic_bytes(b, e_)
+            enc_alg += a["histogram"] + a["pack"]
     dec_alg = sum(algorithmic_bytes(b, e_)["dense"] for e_ in es)
     line = {"metric": "encode/decode GB/s (uncompressed), per-block calls against one call per "
                       "block and the flat calls, 1 GPU",
             "workload": w.name, "n_elements": n, "blocks": nb, "block_elems": b,
-            "container_pitch": pitch, "steps": args.steps,
+            "container_pitch": pitch, "chunk_elems": 1 << c, "steps": args.steps,
+            "encode_form": ("single read, finish cases " +
+                            json.dumps({k: cases.count(k) for k in sorted(set(cases))}))
+                           if single else "two reads (counts, codebook, pack)",
+            "decode_form": "single pass, exponent map",
             "ms": {k: round(v, 5) for k, v in ms.items()},
             "GBps": {k: round(2 * n / (v * 1e-3) / 1e9, 2) for k, v in ms.items()},
             "blocks_encode_frac_hbm": round(enc_alg / (ms["encode_blocks"] * 1e-3) / 1e9
@@ -557,7 +587,7 @@ def main() -> int:
     if args.pages:
         return pages_bench(args, w, n, x, torch, np, sz)
     if args.blocks:
-        return blocks_bench(args, w, n, x, torch, np, sz)
+        return blocks_bench(args, w, n, words, x, torch, np, sz)
     cap = sz.sz_max_compressed_size(n)
     ws_bytes = sz.sz_workspace_size(n)
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")

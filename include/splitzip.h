@@ -341,13 +341,17 @@ sz_status sz_decode_pages(const void *d_src, uint64_t src_bytes, void *const *d_
  * outside 1 .. 65535.  Host-only. */
 uint64_t sz_blocks_workspace_size(uint64_t block_elems, uint64_t n_blocks);
 
-/* sz_encode_blocks: sz_encode of every block, with the two-read passes
- * (address check, counts, codebook, pack), each one launch for all
- * blocks.
+/* sz_encode_blocks: sz_encode of every block, each pass one launch for
+ * all blocks, after an address check.  The passes are the ones sz_encode
+ * takes for as many words as all blocks hold: from 2^26 words in total,
+ * with blocks of at least 2^20 words, the single-read passes (sample,
+ * first pass, finish), else the two-read ones (counts, codebook, pack).
  *   d_dst      container buffer, 16-byte aligned; dst_pitch a multiple of
  *              16 and at least sz_max_compressed_size(block_elems), else
- *              SZ_ERR_CAPACITY.  Bytes of a block's pitch past its
- *              container are not written.
+ *              SZ_ERR_CAPACITY.  In the single-read form the bytes of a
+ *              block's pitch past its container, up to
+ *              sz_max_compressed_size(block_elems), serve as scratch and are
+ *              left unspecified; no byte past that is written.
  *   d_sizes    written: each block's container size (0 for a block whose
  *              address failed the check)
  *   d_workspace, workspace_bytes   256-byte aligned, at least

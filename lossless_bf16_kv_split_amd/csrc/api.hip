@@ -554,7 +554,18 @@ sz_status sz_encode_blocks(const void* const* d_blocks, uint64_t n_blocks, uint6
                              dst_pitch, d_sizes};
     sz_status st = hip_status(sz::launch_check_blocks(src.blocks, n_blocks, flags, d_status, ws,
                                                       l.plan, l.stride, stream));
-    if (st == SZ_OK) st = hip_status(sz::launch_histogram(src, l.plan, ws, stream));
+    if (st != SZ_OK) return st;
+    if (l.plan.single_read && block_elems * n_blocks >= kSingleReadAuto &&
+        l.plan.scratch_end <= dst_pitch) {
+        // as sz_encode on as many words: one read when the sample holds
+        st = hip_status(sz::launch_sample(src, l.plan, ws, stream));
+        if (st == SZ_OK)
+            st = hip_status(sz::launch_first_pass(src, l.plan, ws, out, dst_pitch, stream));
+        if (st == SZ_OK)
+            st = hip_status(sz::launch_finish(src, l.plan, ws, out, dst_pitch, nullptr, stream));
+        return st;
+    }
+    st = hip_status(sz::launch_histogram(src, l.plan, ws, stream));
     if (st == SZ_OK) st = hip_status(sz::launch_codebook(src, l.plan, ws, out, nullptr, stream));
     if (st == SZ_OK)
         st = hip_status(sz::launch_pack(src, l.plan, ws, out, dst_pitch, num_cus(dev), stream));

@@ -967,8 +967,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     __shared__ uint32_t hist[kFirst ? kSpecCopies * kSpecPitch : 1];
     if (src.invalid()) return;  // the same for every thread
     if constexpr (Words::kBlocks) {
-        static_assert(!kFirst, "blocks take the two-read encode");
-        chunk_base = byte_offset(chunk_base, block_ws(src));
+        const uint64_t off = block_ws(src);
+        chunk_base = byte_offset(chunk_base, off);
+        counts = byte_offset(counts, off);
+        totals = byte_offset(totals, off);
+        chunk_esc = byte_offset(chunk_esc, off);
+        area = byte_offset(area, off);
         dst = byte_offset(dst, block_pitch(src));
     }
 
@@ -1071,6 +1075,19 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
     __shared__ uint64_t my_first[kFinishChunks];  // this workgroup's chunks' first slots
     __shared__ uint32_t my_count[kFinishChunks];  // and record counts (copy case)
     __shared__ uint32_t mismatch;
+    if constexpr (Words::kBlocks) {
+        const uint64_t off = block_ws(src);
+        counts = byte_offset(counts, off);
+        totals = byte_offset(totals, off);
+        chunk_esc = byte_offset(chunk_esc, off);
+        area = byte_offset(area, off);
+        dst = byte_offset(dst, block_pitch(src));
+        d_size = src.sizes + blockIdx.y;
+        if (src.invalid()) {  // the same for every thread
+            if (blockIdx.x == 0 && threadIdx.x == 0) *d_size = 0;
+            return;
+        }
+    }
     if (src.invalid()) return;  // the same for every thread
     const int t = threadIdx.x;
 
@@ -1289,14 +1306,19 @@ hipError_t launch_finish(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* d
     const uint64_t* totals = reinterpret_cast<const uint64_t*>(ws + p.totals_off);
     const uint32_t* chunk_esc = reinterpret_cast<const uint32_t*>(ws + p.esc_off);
     SampleArea* area = reinterpret_cast<SampleArea*>(ws + p.sample_off);
-    const uint32_t groups = p.chunks < kFinishGroups ? p.chunks : kFinishGroups;
+    // up to kFinishGroups workgroups per tensor or block: for blocks, one per
+    // chunk of each (fewer, with several chunks each, leave a block that has
+    // to be packed again to too few workgroups: 32 blocks of 2^24 words
+    // with 16 workgroups each took 203 us for this pass, against about 120
+    // with one per chunk)
+    const dim3 grid(p.chunks < kFinishGroups ? p.chunks : kFinishGroups, grid_blocks(src));
     const bool aligned = ((kPrefixBytes + (p.n + 1) / 2) & 15) == 0;
     if (aligned)
-        k_finish<true, Words><<<groups, kPackThreads, 0, stream>>>(
+        k_finish<true, Words><<<grid, kPackThreads, 0, stream>>>(
             src, p.n, p.chunk_log2, p.chunks, counts, totals, chunk_esc, dst, dst_capacity, area,
             p.spec_cap, p.scratch_pos, p.scratch_exp, d_size);
     else
-        k_finish<false, Words><<<groups, kPackThreads, 0, stream>>>(
+        k_finish<false, Words><<<grid, kPackThreads, 0, stream>>>(
             src, p.n, p.chunk_log2, p.chunks, counts, totals, chunk_esc, dst, dst_capacity, area,
             p.spec_cap, p.scratch_pos, p.scratch_exp, d_size);
     return hipGetLastError();
@@ -1311,18 +1333,31 @@ hipError_t launch_finish(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* d
 constexpr uint32_t kSampleBlocks = 512;
 constexpr uint32_t kSampleBlockWords = 2048;
 constexpr uint32_t kSampleThreads = 1024;
-constexpr uint32_t kSampleLoads =
-    kSampleBlocks * kSampleBlockWords / 8 / kSampleThreads / kSampleGroups;  // per thread
+constexpr uint32_t kSampleBlocksPerGroup = kSampleBlocks / kSampleGroups;
+constexpr uint32_t kSampleLoads = kSampleBlocksPerGroup * kSampleBlockWords / 8 / kSampleThreads;
 static_assert(kSampleBlocks % kSampleGroups == 0, "whole blocks per workgroup");
 static_assert(kSingleReadMin / kSampleBlocks >= kSampleBlockWords, "blocks do not overlap");
 static_assert(kSampleThreads == 1024, "four groups of 256 threads rank the exponents");
 static_assert((kSampleGroups & (kSampleGroups - 1)) == 0, "tickets wrap at a multiple of a run");
+// Per-layer blocks are sampled by fewer workgroups each, so that the sample
+// stays a small share of a small block (32 blocks of 2048 words: 1/32 of a
+// 2^21-word block).
+constexpr uint32_t kBlockSampleGroups = 4;
+static_assert((kBlockSampleGroups & (kBlockSampleGroups - 1)) == 0, "tickets wrap at a multiple of a run");
+static_assert(kSingleReadMin / (kBlockSampleGroups * kSampleBlocksPerGroup) >= kSampleBlockWords,
+              "blocks do not overlap");
+
+template <class Words>
+constexpr uint32_t sample_groups() {
+    return Words::kBlocks ? kBlockSampleGroups : kSampleGroups;
+}
 
 // The sample pass, one launch.  Each workgroup counts its blocks, adds the
 // counts into area->sample_hist (device-wide atomics whose returned values
 // a barrier waits for) and then takes a ticket.  Tickets count on from run
-// to run, kSampleGroups a run, so the workgroup whose ticket completes a
-// multiple of kSampleGroups arrives last; the codebook pass puts tickets and
+// to run, kSampleGroups a run (kBlockSampleGroups for each of several
+// blocks, each on its own area), so the workgroup whose ticket completes a
+// multiple of the run arrives last; the codebook pass puts tickets and
 // counts back to zero, so a workspace that came in with other values is in
 // step from its second encode on (until then the provisional codebook may
 // be ranked from part of the sample: a slower finish, never another
@@ -1337,19 +1372,26 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
                                                            SampleArea* __restrict__ area,
                                                            uint64_t* __restrict__ hist,
                                                            uint64_t* __restrict__ totals) {
-    constexpr uint32_t kBlocksPerGroup = kSampleBlocks / kSampleGroups;
+    constexpr uint32_t kGroups = sample_groups<Words>();
+    constexpr uint32_t kBlocksPerGroup = kSampleBlocksPerGroup;
     constexpr uint32_t kLoadsPerBlock = kSampleBlockWords / 8;
     __shared__ uint32_t h[kSpecCopies * kSpecPitch];
     __shared__ uint32_t part[4][256];
     __shared__ uint64_t key[256];
     __shared__ uint32_t sums[2];
     __shared__ uint32_t last;
+    if constexpr (Words::kBlocks) {
+        const uint64_t off = block_ws(src);
+        area = byte_offset(area, off);
+        hist = byte_offset(hist, off);
+        totals = byte_offset(totals, off);
+    }
     if (src.invalid()) return;
     const int t = threadIdx.x;
     for (int i = t; i < kSpecCopies * kSpecPitch; i += kSampleThreads) h[i] = 0;
     __syncthreads();
     uint32_t* mine = h + (t % kSpecCopies) * kSpecPitch;
-    const uint64_t spacing = n / kSampleBlocks;
+    const uint64_t spacing = n / (kGroups * kBlocksPerGroup);
 #pragma unroll
     for (uint32_t k = 0; k < kSampleLoads; k++) {
         const uint32_t g = t + k * kSampleThreads;  // 16-byte group in this workgroup's share
@@ -1375,7 +1417,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
     if (t == 0) {
         const uint32_t ticket = __hip_atomic_fetch_add(&area->tickets, 1u, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT);
-        last = (ticket + 1) % kSampleGroups == 0 ? 1u : 0u;
+        last = (ticket + 1) % kGroups == 0 ? 1u : 0u;
     }
     __syncthreads();
     if (!last) return;
@@ -1410,7 +1452,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
 template <class Words>
 hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream) {
     SampleArea* area = reinterpret_cast<SampleArea*>(ws + p.sample_off);
-    k_sample<Words><<<kSampleGroups, kSampleThreads, 0, stream>>>(
+    k_sample<Words><<<dim3(sample_groups<Words>(), grid_blocks(src)), kSampleThreads, 0, stream>>>(
         src, p.n, area, reinterpret_cast<uint64_t*>(ws + p.hist_off),
         reinterpret_cast<uint64_t*>(ws + p.totals_off));
     return hipGetLastError();
@@ -1426,8 +1468,7 @@ hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_
     template hipError_t launch_sample<W>(W, const EncodePlan&, uint8_t*, hipStream_t);
 SZ_ENCODE_INSTANCES(FlatWords)
 SZ_ENCODE_INSTANCES(PagedWords)
+SZ_ENCODE_INSTANCES(BlockWords)
 #undef SZ_ENCODE_INSTANCES
-template hipError_t launch_pack<BlockWords>(BlockWords, const EncodePlan&, const uint8_t*,
-                                            uint8_t*, uint64_t, int, hipStream_t);
 
 }  // namespace sz

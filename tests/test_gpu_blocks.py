@@ -325,3 +325,45 @@ def test_blocks_graph_replay(torch, sz, n, nb):
         for b in range(nb):
             assert np.array_equal(out.read(b), words[b]), (rep, b)
         _ = (torch.arange(1 << 20, device="cuda") * 3).sum()   # eager work between replays
+
+
+def test_blocks_full_size(torch, sz):
+    """The 1 GiB Llama-3-8B-shaped KV tensor as 32 layer blocks of 2^24
+    words, in the launch configuration the bench times: two sampled blocks'
+    containers against the oracle, every block's container against
+    sz_encode's of that block, and every block back bit-exactly."""
+    import kvgen
+    words = kvgen.generate("llama3_8b_kv_8k")
+    nb = 32
+    n = words.size // nb
+    say("full size: 32 blocks of", n)
+    blocks = [words[b * n:(b + 1) * n] for b in range(nb)]
+    blk = Blocks(torch, n, nb, 21)
+    blk.fill(torch, blocks)
+    status = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    dst, pitch, sizes = encode_blocks(torch, sz, blk, status=status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    s = sizes.cpu().numpy()
+    for b in (3, 30):
+        want = oracle.encode(blocks[b])
+        assert int(s[b]) == want.size, b
+        assert np.array_equal(dst[b * pitch:b * pitch + want.size].cpu().numpy(), want), b
+    one = torch.empty(pitch, dtype=torch.uint8, device="cuda")
+    one_size = torch.zeros(1, dtype=torch.int64, device="cuda")
+    for b in range(nb):
+        x = torch.from_numpy(blocks[b].view(np.int16)).cuda()
+        sz.sz_encode(x, n, one, pitch, one_size)
+        torch.cuda.synchronize()
+        assert int(one_size.item()) == int(s[b]), b
+        assert torch.equal(one[:int(s[b])], dst[b * pitch:b * pitch + int(s[b])]), b
+    del one
+    out = Blocks(torch, n, nb, 22)
+    dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    sz.sz_decode_blocks(dst, pitch, sizes, nb, n, out.table, dstatus)
+    torch.cuda.synchronize()
+    assert (dstatus.cpu().numpy() == 0).all()
+    out.snapshot()
+    for b in range(nb):
+        assert np.array_equal(out.read(b), blocks[b]), b
+    assert out.guards_intact()

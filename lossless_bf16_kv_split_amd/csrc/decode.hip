@@ -267,13 +267,15 @@ struct EscapeReader {
     }
 };
 
-// First k in [0, e] whose position is >= target, for one wavefront: every
-// step probes 64 evenly spaced records and keeps the bracket where the
-// predicate turns true, so the interval shrinks on every step and the loop
-// ends on any input (sorted input gives the exact lower bound).
-__device__ uint64_t wave_lower_bound(const EscapeReader& r, uint64_t e, uint64_t target) {
+// First k in [first, last] whose position is >= target (last when none
+// is), for one wavefront: every step probes 64 evenly spaced records and
+// keeps the bracket where the predicate turns true, so the interval shrinks
+// on every step and the loop ends on any input (sorted input gives the
+// exact lower bound).
+__device__ uint64_t wave_lower_bound(const EscapeReader& r, uint64_t first, uint64_t last,
+                                     uint64_t target) {
     const uint64_t lane = threadIdx.x & 63;
-    uint64_t lo = 0, hi = e;
+    uint64_t lo = first, hi = last;
     while (hi - lo > 64) {
         const uint64_t step = (hi - lo + 63) / 64;
         const uint64_t k = lo + lane * step;
@@ -351,7 +353,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_fused(
 
     // escapes of this range: [k_lo, k_hi)
     if (wave < 2) {
-        const uint64_t b = wave_lower_bound(rd, e, wave == 0 ? begin : end);
+        const uint64_t b = wave_lower_bound(rd, 0, e, wave == 0 ? begin : end);
         if ((t & 63) == 0) bounds[wave] = b;
     }
     __syncthreads();
@@ -937,13 +939,18 @@ hipError_t launch_decode_tiles(const uint8_t* src, uint64_t n, uint64_t e, const
 // no record staging: two barriers per sub-range.
 
 constexpr int kDenseThreads = 512;
+constexpr int kDenseWaves = kDenseThreads / 64;
 constexpr int kGroups = 4;                                 // 8-word groups per thread
 constexpr uint32_t kGroupStride = 8 * kDenseThreads;       // words between a thread's groups
 constexpr uint32_t kDenseTile = kGroups * kGroupStride;    // words per sub-range
 constexpr uint32_t kMapEscaped = 0x100u;                   // map entry: 0x100 | exponent
-constexpr uint32_t kNoBreak = 0xFFFFFFFFu;
-constexpr int kWalk = 2;                                   // records per thread and step
+constexpr uint32_t kDenseMaxLog2 = 16;                     // ranges of at most 2^16 words
+constexpr uint32_t kDenseSubs = (1u << kDenseMaxLog2) / kDenseTile;  // sub-ranges per range
+constexpr uint32_t kWaveRecords = 256;                     // records per wave and step
+constexpr int32_t kBufferFlags = 0x00020000;               // buffer resource word 3 on gfx9 parts
 static_assert((1u << 14) % kDenseTile == 0, "ranges of at least 2^14 words hold whole sub-ranges");
+static_assert(kDenseSubs + 1 <= kDenseWaves, "one wave per sub-range bound");
+static_assert(kWaveRecords == 4 * 64, "four records per lane and step");
 
 // Eight 16-bit map entries (one uint4) to the exponent bytes that replace
 // e0 (elements 0..3) and e1 (elements 4..7) where an entry is set.
@@ -973,17 +980,115 @@ __device__ __forceinline__ void load_group(const uint8_t* nib, const uint8_t* sm
     }
 }
 
+// The records [k0, k1) into the LDS map of the sub-range whose positions
+// (in their segment) are place_lo .. place_hi - 1.  Wave w takes a
+// contiguous slice of them, four consecutive records per lane and step:
+// with kAlignedRec (the escape stream 16-byte aligned) one 16-byte load of
+// positions and one 4-byte load of exponents for a whole group, else a
+// load per record.  Every record must lie in valid_lo .. valid_hi - 1 and
+// above its predecessor (the lane before's last record through a shuffle,
+// the previous step's last lane, or for the slice's first record one more
+// load); a record that fails sets *bad, and only records of the sub-range
+// are placed.
+template <bool kAlignedRec>
+__device__ __forceinline__ void place_records(const EscapeReader& rd, uint64_t k0, uint64_t k1,
+                                              uint32_t valid_lo, uint64_t valid_hi,
+                                              uint32_t place_lo, uint64_t place_hi, uint16_t* map,
+                                              int* bad) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const uint64_t s0 = kAlignedRec ? (k0 & ~uint64_t{3}) : k0;
+    // at least one step's worth per wave: with few records, the waves
+    // without any go straight on to their codes
+    const uint64_t spread = (k1 - s0 + 4 * kDenseWaves - 1) / (4 * kDenseWaves) * 4;
+    const uint64_t per_wave = spread > kWaveRecords ? spread : kWaveRecords;
+    const uint64_t w0 = s0 + (uint64_t)wave * per_wave;
+    const uint64_t w1 = min_u64(w0 + per_wave, k1);
+    if (w0 >= w1) return;  // the same for the whole wave
+    // per-lane offsets are 32-bit, from the slice's first record (a slice
+    // holds fewer than 2^14 records): records w0 + r
+    const uint32_t count = (uint32_t)(w1 - w0);
+    const uint32_t skip = k0 > w0 ? (uint32_t)(k0 - w0) : 0u;  // alignment, first slice only
+    const bool carried = w0 > k0;  // the slice's first record has a predecessor here
+    const uint8_t* pbase = rd.pos_lo + 4 * w0;
+    const uint8_t* xbase = rd.exps + w0;
+    // with kAlignedRec, buffer loads over the slice: a 32-bit offset per
+    // lane from the slice's base in scalar registers, and reads past the
+    // slice return 0
+    const __amdgpu_buffer_rsrc_t rpos = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(pbase), (short)0, (int32_t)(4 * count), kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rexp = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t*>(xbase), (short)0, (int32_t)count, kBufferFlags);
+    const uint32_t steps = (count + kWaveRecords - 1) / kWaveRecords;
+    // the record before the slice (every slice but the first starts past k0)
+    uint32_t carry = carried ? rd.low32(w0 - 1) : 0u;
+    for (uint32_t i = 0; i < steps; i++) {
+        const uint32_t r = i * kWaveRecords + 4 * (uint32_t)lane;
+        uint32_t v[4], x;
+        if (kAlignedRec && r + 4 <= count) {
+            const auto p = __builtin_amdgcn_raw_buffer_load_b128(rpos, 4 * r, 0, 0);
+            v[0] = p[0];
+            v[1] = p[1];
+            v[2] = p[2];
+            v[3] = p[3];
+            x = __builtin_amdgcn_raw_buffer_load_b32(rexp, r, 0, 0);
+        } else if (kAlignedRec) {
+            x = 0;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                v[u] = __builtin_amdgcn_raw_buffer_load_b32(rpos, 4 * (r + u), 0, 0);
+                x |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(rexp, r + u, 0, 0) << (8 * u);
+            }
+        } else {
+            x = 0;
+#pragma unroll
+            for (int u = 0; u < 4; u++) {
+                const bool in = r + u < count;
+                v[u] = in ? rd.low32(w0 + r + u) : 0u;
+                x |= (in ? (uint32_t)xbase[r + u] : 0u) << (8 * u);
+            }
+        }
+        // every lane takes part in both shuffles, then picks
+        const uint32_t up = __shfl_up(v[3], 1, 64);
+        const uint32_t last = __shfl(v[3], 63, 64);
+        const uint32_t before = lane == 0 ? carry : up;
+        carry = last;
+#pragma unroll
+        for (int u = 0; u < 4; u++) {
+            const uint32_t k = r + u;
+            if (k < skip || k >= count) continue;
+            const uint32_t lo = v[u];
+            const uint32_t pred = u == 0 ? before : v[u - 1];
+            const bool has_pred = k > skip || carried;
+            if (lo < valid_lo || (uint64_t)lo >= valid_hi || (has_pred && !(lo > pred)))
+                *bad = 1;
+            else if (lo >= place_lo && (uint64_t)lo < place_hi)
+                map[lo - place_lo] = (uint16_t)(kMapEscaped | ((x >> (8 * u)) & 0xFFu));
+        }
+    }
+}
+
+// One workgroup per range of at most 2^16 words, decoded in sub-ranges of
+// 16384 words.  First the record interval of every sub-range, one 64-way
+// search per wave, all at once: bound[j] = the first record at or above
+// the sub-range's start.  Then per sub-range the thread's codes and
+// sign|mantissa bytes are loaded, its records placed as 0x100 | exponent
+// into a 16-bit-per-word LDS map while those loads are in flight, and,
+// after a barrier, each thread rebuilds its 8-word groups with the map's
+// exponents where set and clears the entries it read.  Neighbouring ranges
+// compute the same bound for their shared boundary, so the intervals tile
+// [0, e) when the first starts at 0, the last ends at e and none runs
+// backwards; every record inside its sub-range and above its predecessor
+// then means the whole stream is strictly ascending.
 // Eight waves per SIMD (four workgroups per CU) need at most 64 VGPRs and
 // the scalar-register cap.
-template <bool kAlignedSm, class Words>
+template <bool kAlignedSm, bool kAlignedRec, class Words>
 __global__ __launch_bounds__(kDenseThreads) SZ_EIGHT_WAVE_SGPR_CAP
 __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
     const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e,
     uint32_t range_log2, Words out, int32_t* status) {
     __shared__ uint4 map4[kDenseTile / 8];   // kDenseTile 16-bit entries
-    __shared__ uint64_t bounds[2];
+    __shared__ uint64_t bound[kDenseSubs + 1];
     __shared__ uint64_t seg_table[16];
-    __shared__ uint32_t next_rel[2];
     __shared__ int bad;
 
     const int t = threadIdx.x;
@@ -1013,11 +1118,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
             return;
         }
     }
-    if (t == 0) {
-        bad = 0;
-        next_rel[0] = kNoBreak;
-        next_rel[1] = kNoBreak;
-    }
+    if (t == 0) bad = 0;
     if (blockIdx.x == 0 && t == 0 && !header_ok(src, src_bytes, n, e)) bad = 1;
 
     const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
@@ -1034,85 +1135,93 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
     // every map entry starts clear; each thread clears the entries it reads
 #pragma unroll
     for (int g = 0; g < kGroups; g++) map4[g * kDenseThreads + t] = make_uint4(0, 0, 0, 0);
-    __syncthreads();
 
     const uint64_t begin = min_u64((uint64_t)blockIdx.x << range_log2, n);
     const uint64_t end = min_u64(begin + (uint64_t{1} << range_log2), n);
-
-    // escapes of this range: [k_lo, k_hi)
-    if (wave < 2) {
-        const uint64_t b = wave_lower_bound(rd, e, wave == 0 ? begin : end);
-        if ((t & 63) == 0) bounds[wave] = b;
+    const uint32_t subs = (uint32_t)((end - begin + kDenseTile - 1) / kDenseTile);
+    __syncthreads();  // seg_table, read by the searches
+    // the range's records over the whole stream, then the sub-range
+    // boundaries among those alone (fewer probes, on lines the placement
+    // reads next)
+    if (wave == 0 || (wave == 1 && subs > 0)) {
+        const uint64_t b = wave_lower_bound(rd, 0, e, wave == 0 ? begin : end);
+        if ((t & 63) == 0) bound[wave == 0 ? 0 : subs] = b;
     }
     __syncthreads();
-    const uint64_t k_lo = uniform64(bounds[0]);
-    const uint64_t k_hi = uniform64(bounds[1] > k_lo ? bounds[1] : k_lo);
-    if (t == 0 && blockIdx.x == gridDim.x - 1 && bounds[1] != e) bad = 1;  // positions >= n
+    // a range with few records (one step of every wave) is read whole for
+    // each of its sub-ranges, its second and later reads from the caches;
+    // otherwise the sub-range boundaries are searched among its records
+    const uint64_t k_lo = uniform64(bound[0]);
+    const uint64_t k_hi = uniform64(bound[subs]);
+    const bool few = k_hi <= k_lo + (uint64_t)kDenseWaves * kWaveRecords;
+    if (!few && wave >= 1 && (uint32_t)wave < subs) {
+        const uint64_t b = wave_lower_bound(rd, k_lo, k_hi, begin + (uint64_t)wave * kDenseTile);
+        if ((t & 63) == 0) bound[wave] = b;
+    }
+    __syncthreads();
+    if (t == 0) {
+        if (blockIdx.x == 0 && bound[0] != 0) bad = 1;
+        if (blockIdx.x == gridDim.x - 1 && bound[subs] != e) bad = 1;  // positions >= n
+        if (k_hi < k_lo) bad = 1;
+        if (!few)  // (the searches kept the inner bounds inside [k_lo, k_hi])
+            for (uint32_t j = 0; j < subs; j++)
+                if (bound[j + 1] < bound[j]) bad = 1;
+    }
 
-    uint64_t k_cur = k_lo;   // first record not yet placed
-    int parity = 0;
-    for (uint64_t sub = begin; sub < end; sub += kDenseTile, parity ^= 1) {
+    for (uint32_t j = 0; j < subs; j++) {
+        const uint64_t sub = begin + (uint64_t)j * kDenseTile;
         const uint64_t sub_end = min_u64(sub + kDenseTile, end);
-        // place this sub-range's records; a record at or above sub_end ends
-        // the thread's walk, and the lowest such index is where the next
-        // sub-range starts.  A sub-range lies inside one 2^32-word segment,
-        // whose records are [seg_lo, seg_hi): there a position is its stored
-        // low 32 bits above the segment base.
+        // the sub-range lies inside one 2^32-word segment, whose records are
+        // [seg_lo, seg_hi): there a position is its stored low 32 bits
+        // above the segment base
+        const uint64_t k0 = few ? k_lo : uniform64(bound[j]);
+        const uint64_t k1 = few ? k_hi : uniform64(bound[j + 1]);
         const uint32_t seg = (uint32_t)(sub >> 32);
         const uint64_t seg_lo = seg == 0 ? 0 : seg_table[seg - 1];
         const uint64_t seg_hi = seg_table[seg];
-        const uint32_t lo_begin = (uint32_t)sub;
-        const uint64_t lo_end = sub_end - ((uint64_t)seg << 32);  // at most 2^32
-        // kWalk records per thread and step, their loads issued together
-        uint32_t stop = kNoBreak;
-        const uint64_t k_start = k_cur + t;
-        for (uint64_t kb = k_start; kb < k_hi && stop == kNoBreak;
-             kb += (uint64_t)kWalk * kDenseThreads) {
-            uint32_t lo[kWalk], prev[kWalk], ex[kWalk];
-#pragma unroll
-            for (int u = 0; u < kWalk; u++) {
-                const uint64_t k = kb + (uint64_t)u * kDenseThreads;
-                const bool in = k < k_hi;
-                lo[u] = in ? rd.low32(k) : 0u;
-                prev[u] = in && k > 0 ? rd.low32(k - 1) : 0u;
-                ex[u] = in ? rd.exps[k] : 0u;
-            }
-#pragma unroll
-            for (int u = 0; u < kWalk; u++) {
-                const uint64_t k = kb + (uint64_t)u * kDenseThreads;
-                if (stop != kNoBreak || k >= k_hi) break;
-                if (k >= seg_hi || lo[u] >= lo_end) {  // beyond this sub-range
-                    stop = (uint32_t)min_u64(k - k_cur, kNoBreak - 1);
-                    break;
-                }
-                // not below this sub-range, and strictly above the record
-                // before (which, in an earlier segment, is below it anyway)
-                if (k < seg_lo || lo[u] < lo_begin ||
-                    (k > 0 && k - 1 >= seg_lo && !(lo[u] > prev[u]))) {
-                    bad = 1;
-                } else {
-                    map[lo[u] - lo_begin] = (uint16_t)(kMapEscaped | ex[u]);
-                }
-            }
+        const uint64_t base = (uint64_t)seg << 32;  // a range lies inside one segment
+        if (k0 < seg_lo || k1 > seg_hi) {
+            if (t == 0 && k1 > k0) bad = 1;
+        } else if (k1 > k0) {
+            place_records<kAlignedRec>(rd, k0, k1, (uint32_t)(few ? begin : sub),
+                                       (few ? end : sub_end) - base, (uint32_t)sub,
+                                       sub_end - base, map, &bad);
         }
-        // this thread's codes and sign|mantissa bytes: loaded after the walk,
-        // so that the walk does not hold them in registers; they arrive while
-        // the other waves finish walking
+        // this thread's codes and sign|mantissa bytes: loaded after the
+        // records, so that the placement does not hold them in registers;
+        // they arrive while the other waves finish placing
         const bool whole = sub + kDenseTile <= end;   // the same for every thread
         const uint64_t wt = sub + (uint64_t)t * 8;  // this thread's first word
         uint32_t c[kGroups], s[2 * kGroups];
+        if constexpr (kAlignedSm) {
+            // buffer loads over the sub-range's streams: 32-bit offsets per
+            // lane from bases in scalar registers
+            const uint32_t words = (uint32_t)(sub_end - sub);
+            const __amdgpu_buffer_rsrc_t rnib = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(nib + sub / 2), (short)0, (int32_t)((words + 1) / 2),
+                kBufferFlags);
+            const __amdgpu_buffer_rsrc_t rsm = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t*>(sm + sub), (short)0, (int32_t)words, kBufferFlags);
 #pragma unroll
-        for (int g = 0; g < kGroups; g++) {
-            const uint64_t w = wt + (uint64_t)g * kGroupStride;
-            c[g] = s[2 * g] = s[2 * g + 1] = 0;
-            if (whole || w + 8 <= sub_end) load_group<kAlignedSm>(nib, sm, w, c[g], s[2 * g], s[2 * g + 1]);
+            for (int g = 0; g < kGroups; g++) {
+                const uint32_t w = (uint32_t)t * 8 + (uint32_t)g * kGroupStride;  // from sub
+                c[g] = s[2 * g] = s[2 * g + 1] = 0;
+                if (whole || w + 8 <= words) {
+                    c[g] = __builtin_amdgcn_raw_buffer_load_b32(rnib, w / 2, 0, 0);
+                    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rsm, w, 0, 0);
+                    s[2 * g] = v[0];
+                    s[2 * g + 1] = v[1];
+                }
+            }
+        } else {
+#pragma unroll
+            for (int g = 0; g < kGroups; g++) {
+                const uint64_t w = wt + (uint64_t)g * kGroupStride;
+                c[g] = s[2 * g] = s[2 * g + 1] = 0;
+                if (whole || w + 8 <= sub_end) load_group<kAlignedSm>(nib, sm, w, c[g], s[2 * g], s[2 * g + 1]);
+            }
         }
-
-        if (stop != kNoBreak) atomicMin(&next_rel[parity], stop);
         __syncthreads();
-        const uint32_t rel = next_rel[parity];
-        k_cur = rel == kNoBreak ? k_hi : k_cur + rel;
-        if (t == 0) next_rel[parity ^ 1] = kNoBreak;
 
         // rebuild this thread's words, clearing the map entries as they are read
 #pragma unroll
@@ -1140,8 +1249,6 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
         }
         __syncthreads();
     }
-    // every record of the range must have been placed
-    if (t == 0 && k_cur != k_hi) bad = 1;
     __syncthreads();
     if (t == 0 && bad && status)
         __hip_atomic_fetch_max(status, kStatusCorrupt, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1151,25 +1258,32 @@ template <class Words>
 hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                                Words dst, int32_t* status, hipStream_t stream) {
     uint32_t r = 14;
-    // at most kMaxDecodeRanges workgroups: enough for several waves of
-    // resident workgroups (a 10.7 GB input with 2048 ranges left the last
-    // wave a quarter full: 16% slower); for blocks, over all their words
+    // up to kMaxDecodeRanges workgroups as long as ranges stay at most
+    // 2^kDenseMaxLog2 words (beyond, more workgroups): enough for several
+    // waves of resident workgroups (a 10.7 GB input with 2048 ranges left
+    // the last wave a quarter full: 16% slower); for blocks, over all their
+    // words
     const uint64_t words = n * grid_blocks(dst);
-    while (r < 40 && ((words + (1ull << r) - 1) >> r) > kMaxDecodeRanges) r++;
+    while (r < kDenseMaxLog2 && ((words + (1ull << r) - 1) >> r) > kMaxDecodeRanges) r++;
     uint64_t blocks = (n + (1ull << r) - 1) >> r;
     if (blocks == 0) blocks = 1;  // the header check still runs
     // (for blocks, the address check wrote every block's starting status)
     if (status && !Words::kBlocks) k_status_clear<<<1, 1, 0, stream>>>(status);
     // the sign|mantissa stream starts at 176 + ceil(n/2): 8-byte aligned
-    // exactly when n is a multiple of 16
-    const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
+    // exactly when n is a multiple of 16; the escape stream, at
+    // 176 + ceil(n/2) + n, 16-byte aligned when n is a multiple of 32
+    const bool aligned_sm = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
+    const bool aligned_rec = ((kPrefixBytes + (n + 1) / 2 + n) & 15) == 0;
     const dim3 grid((uint32_t)blocks, grid_blocks(dst));
-    if (aligned)
-        k_decode_dense<true, Words><<<grid, kDenseThreads, 0, stream>>>(src, src_bytes, n, e, r,
-                                                                       dst, status);
+    if (aligned_sm && aligned_rec)
+        k_decode_dense<true, true, Words><<<grid, kDenseThreads, 0, stream>>>(
+            src, src_bytes, n, e, r, dst, status);
+    else if (aligned_sm)
+        k_decode_dense<true, false, Words><<<grid, kDenseThreads, 0, stream>>>(
+            src, src_bytes, n, e, r, dst, status);
     else
-        k_decode_dense<false, Words><<<grid, kDenseThreads, 0, stream>>>(src, src_bytes, n, e, r,
-                                                                        dst, status);
+        k_decode_dense<false, false, Words><<<grid, kDenseThreads, 0, stream>>>(
+            src, src_bytes, n, e, r, dst, status);
     return hipGetLastError();
 }
 

@@ -397,6 +397,43 @@ def test_corrupt_escapes_many_ranges(torch, sz):
             assert guard and st == 4, (k, form, st)
 
 
+@pytest.mark.parametrize("kind", ["wide40", "kv"])
+def test_corrupt_escapes_dense_slices(torch, sz, kind):
+    """The dense decode with a 16-byte aligned escape stream (n a multiple of
+    32) and two sub-ranges per range: escape-dense input (sub-range bounds
+    searched, records spread over the waves' slices) and sparse KV input
+    (the range's records read whole for each sub-range).  Records swapped
+    with their successor right at a sub-range's first record, at lane,
+    step and wave-slice boundaries of its slices, and deep inside are each
+    flagged, and the intact container decodes exactly."""
+    n = (1 << 27) + (1 << 15)
+    say("dense slices", kind, n)
+    words = make_words(kind, n, 22)
+    good = oracle.encode(words)
+    r = szformat.read(good)
+    esc = 176 + n // 2 + n
+    assert esc % 16 == 0
+    pos = np.frombuffer(good[esc:esc + 4 * r.e].tobytes(), dtype=np.uint32).astype(np.int64)
+    dev = torch.from_numpy(good).cuda()
+    out, st, guard = gpu_decode(torch, sz, dev, n, "dense")
+    assert st == 0 and guard and np.array_equal(out.cpu().numpy().view(np.uint16), words)
+    # the second sub-range (16384 words) of range 100 (32768 words)
+    sub = 100 * 32768 + 16384
+    k0 = int(np.searchsorted(pos, sub))
+    k1 = int(np.searchsorted(pos, sub + 16384))
+    s0 = k0 & ~3
+    per_wave = max(256, -(-(k1 - s0) // 32) * 4)
+    picks = {k0, k0 + 1, k0 + 3, k0 + 4, s0 + 255, s0 + 256, s0 + 257, s0 + per_wave - 1,
+             s0 + per_wave, s0 + per_wave + 1, k1 - 1, r.e // 2, r.e - 1}
+    for k in sorted(x for x in picks if 1 <= x < r.e):
+        c = good.copy()
+        a, b = esc + 4 * (k - 1), esc + 4 * k
+        c[a:a + 4], c[b:b + 4] = good[b:b + 4].copy(), good[a:a + 4].copy()
+        dev.copy_(torch.from_numpy(c))
+        _, st, guard = gpu_decode(torch, sz, dev, n, "dense")
+        assert guard and st == 4, (kind, k, st)
+
+
 def test_host_errors_with_real_buffers(torch, sz):
     n = 4096
     x = torch.zeros(n, dtype=torch.int16, device="cuda")

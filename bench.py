@@ -309,6 +309,8 @@ def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
     wb = sz.sz_blocks_workspace_size(b, nb)
     ws = torch.empty(wb, dtype=torch.uint8, device="cuda")
     bstatus = torch.zeros(nb, dtype=torch.int32, device="cuda")
+    dwb = sz.sz_blocks_decode_workspace_size(b, nb)
+    dws = torch.empty(dwb, dtype=torch.uint8, device="cuda")
     # the loop's containers, one per block, at the same pitch
     ldst = torch.empty(nb * pitch, dtype=torch.uint8, device="cuda")
     lsizes = torch.zeros(nb, dtype=torch.int64, device="cuda")
@@ -351,7 +353,10 @@ def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
         "encode_per_block_calls": encode_loop,
         "encode_flat": lambda: sz.sz_encode(x, n, fdst, fcap, fsize, stream),
         "decode_blocks": lambda: sz.sz_decode_blocks(dst, pitch, sizes, nb, b, out_table,
-                                                     bstatus, stream),
+                                                     bstatus, dws, dwb, stream),
+        "decode_blocks_single_pass": lambda: sz.sz_decode_blocks(dst, pitch, sizes, nb, b,
+                                                                 out_table, bstatus,
+                                                                 stream=stream),
         "decode_per_block_calls": decode_loop,
         "decode_flat": lambda: sz.sz_decode(fcont, ftotal, fout, n, status, stream),
     }
@@ -364,15 +369,16 @@ def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
     for i in range(nb):
         ok = ok and bool(torch.equal(dst[i * pitch:i * pitch + int(hs[i])],
                                      ldst[i * pitch:i * pitch + int(hs[i])]))
-    out_pool.zero_()
-    sz.sz_decode_blocks(dst, pitch, sizes, nb, b, out_table, bstatus, stream)
-    torch.cuda.synchronize()
-    ok = ok and int(bstatus.abs().sum().item()) == 0 and bool(torch.equal(out_pool, pool))
+    for ws_args in ((dws, dwb), (None, 0)):  # both forms
+        out_pool.zero_()
+        sz.sz_decode_blocks(dst, pitch, sizes, nb, b, out_table, bstatus, *ws_args, stream=stream)
+        torch.cuda.synchronize()
+        ok = ok and int(bstatus.abs().sum().item()) == 0 and bool(torch.equal(out_pool, pool))
     ok = ok and bool(torch.equal(fout, x)) and int(status.item()) == 0
     # bytes the block calls move, summed over the blocks: the encode form the
     # library takes (single read from 2^26 words in all with blocks of at
     # least 2^20 words: sample, first pass and the finish case each block
-    # takes; else counts, then pack) and the dense decode
+    # takes; else counts, then pack) and the tile decode
     es = [(int(hs[i]) - (176 + (b + 1) // 2 + b)) // 5 for i in range(nb)]
     single = b >= 1 << 20 and n >= 1 << 26
     c = blocks_chunk_log2(b, nb)
@@ -388,7 +394,8 @@ def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
         else:
             a = algorithmic_bytes(b, e_)
             enc_alg += a["histogram"] + a["pack"]
-    dec_alg = sum(algorithmic_bytes(b, e_)["dense"] for e_ in es)
+    dec_alg = sum(algorithmic_bytes(b, e_)["index"] + algorithmic_bytes(b, e_)["tiles"]
+                  for e_ in es)
     line = {"metric": "encode/decode GB/s (uncompressed), per-block calls against one call per "
                       "block and the flat calls, 1 GPU",
             "workload": w.name, "n_elements": n, "blocks": nb, "block_elems": b,
@@ -396,7 +403,8 @@ def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
             "encode_form": ("single read, finish cases " +
                             json.dumps({k: cases.count(k) for k in sorted(set(cases))}))
                            if single else "two reads (counts, codebook, pack)",
-            "decode_form": "single pass, exponent map",
+            "decode_form": "tile index, then tiles (decode_blocks); single pass without a "
+                           "workspace (decode_blocks_single_pass)",
             "ms": {k: round(v, 5) for k, v in ms.items()},
             "GBps": {k: round(2 * n / (v * 1e-3) / 1e9, 2) for k, v in ms.items()},
             "blocks_encode_frac_hbm": round(enc_alg / (ms["encode_blocks"] * 1e-3) / 1e9

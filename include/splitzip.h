@@ -364,18 +364,33 @@ sz_status sz_encode_blocks(const void *const *d_blocks, uint64_t n_blocks, uint6
                            void *d_workspace, uint64_t workspace_bytes, int32_t *d_status,
                            hipStream_t stream);
 
+/* sz_blocks_decode_workspace_size: bytes of device workspace that give
+ * sz_decode_blocks its tile form (per block: a tile index, a fault flag
+ * per 16384 words (64 to 4096 of them) and the tiles' record slots, at
+ * 256-byte strides; about 1/30 of the block's words in bytes); 0 for bad
+ * arguments as above.  Host-only. */
+uint64_t sz_blocks_decode_workspace_size(uint64_t block_elems, uint64_t n_blocks);
+
 /* sz_decode_blocks: the reverse, block b's container read from d_src +
- * b * src_pitch, d_sizes[b] bytes, and its words written to d_blocks[b].
- * Each container is decoded in one pass with the checks of sz_decode (a
- * size that is no container of block_elems words, or exceeds src_pitch,
- * counts as corrupt, and then none of that container is read).
+ * b * src_pitch, d_sizes[b] bytes, and its words written to d_blocks[b],
+ * with the checks of sz_decode.  A size that is no container of
+ * block_elems words, or exceeds src_pitch, counts as corrupt: nothing
+ * outside the block's pitch is read, and its words are then unspecified.
+ * With d_workspace NULL, one pass per range of each block
+ * (sz_decode_dense's form, the one for escape-heavy data); with a
+ * workspace of at least sz_blocks_decode_workspace_size(block_elems,
+ * n_blocks) bytes (256-byte aligned, any content), a tile index of every
+ * block, then its tiles (sz_decode_index / sz_decode_tiles' form, the
+ * faster one for KV data, and much the slower one at many escapes per
+ * 2048 words).  Both forms are one launch per pass for all blocks.
  *   src_pitch  a multiple of 16, at least 176 + ceil(n/2) + n for
  *              n = block_elems
  *   d_status   required device array of n_blocks i32: SZ_OK, SZ_ERR_CORRUPT
  *              or SZ_ERR_INVALID_ARGUMENT per block */
 sz_status sz_decode_blocks(const void *d_src, uint64_t src_pitch, const uint64_t *d_sizes,
                            uint64_t n_blocks, uint64_t block_elems, void *const *d_blocks,
-                           int32_t *d_status, hipStream_t stream);
+                           void *d_workspace, uint64_t workspace_bytes, int32_t *d_status,
+                           hipStream_t stream);
 
 /* ---- compressed transfer to and from host memory ----------------------
  * The explainers present the codec as a way to shrink the KV transfer

@@ -29,7 +29,7 @@ __all__ = [
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
     "sz_decode_workspace_size", "sz_decode_index", "sz_decode_tiles",
     "sz_encode_pages", "sz_decode_pages", "sz_blocks_workspace_size", "sz_encode_blocks",
-    "sz_decode_blocks", "sz_ship_to_host", "sz_ship_from_host", "ShipContext",
+    "sz_decode_blocks", "sz_blocks_decode_workspace_size", "sz_ship_to_host", "sz_ship_from_host", "ShipContext",
     "sz_status_string", "encode",
     "decode",
     "PREFIX_BYTES", "MAX_ELEMENTS", "NOALLOC_WORKSPACE_BYTES",
@@ -91,7 +91,9 @@ def _load() -> ctypes.CDLL:
     L.sz_blocks_workspace_size.argtypes = [u64, u64]
     L.sz_blocks_workspace_size.restype = u64
     L.sz_encode_blocks.argtypes = [p, u64, u64, p, u64, p, p, u64, p, p]
-    L.sz_decode_blocks.argtypes = [p, u64, p, u64, u64, p, p, p]
+    L.sz_blocks_decode_workspace_size.argtypes = [u64, u64]
+    L.sz_blocks_decode_workspace_size.restype = u64
+    L.sz_decode_blocks.argtypes = [p, u64, p, u64, u64, p, p, u64, p, p]
     L.sz_ship_to_host.argtypes = [p, u64, u64, p, u64, p, p]
     L.sz_ship_from_host.argtypes = [p, p, u64, u64, p, p, p]
     L.sz_ship_context_create.argtypes = [u64, ctypes.POINTER(ctypes.c_void_p)]
@@ -281,12 +283,17 @@ def sz_encode_blocks(d_blocks, n_blocks: int, block_elems: int, dst, dst_pitch: 
                                  _stream(stream)), "sz_encode_blocks")
 
 
+def sz_blocks_decode_workspace_size(block_elems: int, n_blocks: int) -> int:
+    return int(_lib.sz_blocks_decode_workspace_size(block_elems, n_blocks))
+
+
 def sz_decode_blocks(src, src_pitch: int, d_sizes, n_blocks: int, block_elems: int, d_blocks,
-                     d_status, stream=None) -> None:
-    """d_status: device int32 array of n_blocks entries (required)."""
+                     d_status, workspace=None, workspace_bytes: int = 0, stream=None) -> None:
+    """d_status: device int32 array of n_blocks entries (required); with a
+    workspace the tile form, without it the single-pass form."""
     _check(_lib.sz_decode_blocks(_ptr(src), src_pitch, _ptr(d_sizes), n_blocks, block_elems,
-                                 _ptr(d_blocks), _ptr(d_status), _stream(stream)),
-           "sz_decode_blocks")
+                                 _ptr(d_blocks), _ptr(workspace), workspace_bytes,
+                                 _ptr(d_status), _stream(stream)), "sz_decode_blocks")
 
 
 def sz_ship_to_host(src, n_elements: int, chunk_elems: int, h_dst, h_capacity: int, h_offsets,

@@ -208,7 +208,8 @@ sz_status decode_by_density(const uint8_t* src, uint64_t src_bytes, uint64_t n, 
     void* ws = nullptr;
     if (hipMallocFromPoolAsync(&ws, l.bytes, pool, stream) != hipSuccess) return SZ_ERR_HIP;
     uint8_t* w = static_cast<uint8_t*>(ws);
-    sz_status st = hip_status(sz::launch_tile_index(src, src_bytes, n, e, w, stream));
+    sz_status st =
+        hip_status(sz::launch_tile_index(src, src_bytes, n, e, w, sz::FlatWords{nullptr}, stream));
     if (st == SZ_OK)
         st = hip_status(sz::launch_decode_tiles(src, n, e, w, dst, d_status, num_cus(dev), stream));
     if (hipFreeAsync(ws, stream) != hipSuccess && st == SZ_OK) st = SZ_ERR_HIP;
@@ -439,7 +440,7 @@ sz_status sz_decode_index(const void* d_src, uint64_t src_bytes, uint64_t n, voi
     if (e > (15 * n) / 16) return SZ_ERR_CORRUPT;
     if (overlap(d_src, src_bytes, d_workspace, workspace_bytes)) return SZ_ERR_INVALID_ARGUMENT;
     return hip_status(sz::launch_tile_index(static_cast<const uint8_t*>(d_src), src_bytes, n, e,
-                                            static_cast<uint8_t*>(d_workspace), stream));
+                                            static_cast<uint8_t*>(d_workspace), sz::FlatWords{nullptr}, stream));
 }
 
 sz_status sz_decode_tiles(const void* d_src, uint64_t src_bytes, const void* d_workspace,
@@ -572,23 +573,42 @@ sz_status sz_encode_blocks(const void* const* d_blocks, uint64_t n_blocks, uint6
     return st;
 }
 
+uint64_t sz_blocks_decode_workspace_size(uint64_t block_elems, uint64_t n_blocks) {
+    if (block_elems > SZ_MAX_ELEMENTS || n_blocks == 0 || n_blocks > kMaxBlocks) return 0;
+    return n_blocks * round256(sz::tile_index_layout(block_elems, true).bytes);
+}
+
 sz_status sz_decode_blocks(const void* d_src, uint64_t src_pitch, const uint64_t* d_sizes,
                            uint64_t n_blocks, uint64_t block_elems, void* const* d_blocks,
-                           int32_t* d_status, hipStream_t stream) {
+                           void* d_workspace, uint64_t workspace_bytes, int32_t* d_status,
+                           hipStream_t stream) {
     if (sz_status s =
             check_blocks(d_blocks, n_blocks, block_elems, d_src, src_pitch, d_sizes, false))
         return s;
     if (d_status == nullptr || !aligned(d_status, 4)) return SZ_ERR_INVALID_ARGUMENT;
+    const uint64_t ws_stride = round256(sz::tile_index_layout(block_elems, true).bytes);
+    if (d_workspace != nullptr &&
+        (!aligned(d_workspace, 256) || workspace_bytes < n_blocks * ws_stride))
+        return SZ_ERR_INVALID_ARGUMENT;
+    const int dev = current_device();
+    if (dev < 0) return SZ_ERR_HIP;
     // the statuses start as the address check's flags, which the decode
     // then raises to SZ_ERR_CORRUPT where a container fails its checks
-    const sz::BlockWords dst{block_table(d_blocks), d_status, (uint32_t)n_blocks, 0, src_pitch,
-                             const_cast<uint64_t*>(d_sizes)};
+    const sz::BlockWords dst{block_table(d_blocks), d_status, (uint32_t)n_blocks, ws_stride,
+                             src_pitch, const_cast<uint64_t*>(d_sizes)};
+    const uint8_t* src = static_cast<const uint8_t*>(d_src);
     sz_status st =
         hip_status(sz::launch_check_blocks(dst.blocks, n_blocks, d_status, nullptr, nullptr,
                                            sz::EncodePlan{}, 0, stream));
+    if (st != SZ_OK) return st;
+    if (d_workspace == nullptr)  // one pass per block range, no workspace
+        return hip_status(sz::launch_decode_dense(src, 0, block_elems, 0, dst, d_status, stream));
+    // the tile decode: index every block's escape stream, then its tiles
+    uint8_t* w = static_cast<uint8_t*>(d_workspace);
+    st = hip_status(sz::launch_tile_index(src, 0, block_elems, 0, w, dst, stream));
     if (st == SZ_OK)
-        st = hip_status(sz::launch_decode_dense(static_cast<const uint8_t*>(d_src), 0, block_elems,
-                                                0, dst, d_status, stream));
+        st = hip_status(
+            sz::launch_decode_tiles(src, block_elems, 0, w, dst, d_status, num_cus(dev), stream));
     return st;
 }
 

@@ -472,7 +472,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_fused(
                 e1 = bitselect(bits_to_bytes(present >> 4), pe.y, e1);
             }
             // a wave's words are 512 consecutive words: one page
-            *reinterpret_cast<uint4*>(out.at_wave(i0)) = words8(e0, e1, s0, s1);
+            store_global(reinterpret_cast<uint4*>(out.at_wave(i0)), words8(e0, e1, s0, s1));
         } else {
             for (uint32_t k = 0; k < 8 && i0 + k < end; k++) {
                 const uint64_t i = i0 + k;
@@ -564,6 +564,27 @@ __device__ __forceinline__ IndexItem make_item(uint64_t n, uint64_t e, uint64_t 
     return it;
 }
 
+// A block's container (at src + y * pitch) and its escape count from its
+// size, size = 176 + ceil(n/2) + n + 5E: false when the size cannot be a
+// container of n words or runs past the pitch (nothing of it may be read).
+struct BlockContainer {
+    const uint8_t* src;
+    uint64_t bytes;
+    uint64_t e;
+    bool ok;
+};
+__device__ __forceinline__ BlockContainer block_container(const BlockWords& blk, uint64_t n,
+                                                          const uint8_t* src) {
+    BlockContainer c;
+    c.src = byte_offset(src, block_pitch(blk));
+    c.bytes = blk.sizes[blockIdx.y];
+    const uint64_t fixed = container_bytes(n, 0);
+    const uint64_t extra = c.bytes - fixed;
+    c.e = extra / 5;
+    c.ok = !(c.bytes < fixed || c.bytes > blk.pitch || extra % 5 != 0 || c.e > (15 * n) / 16);
+    return c;
+}
+
 // One wave per group of 64 items: lane L holds item k0 + L, and lanes
 // 0..15 also load item k0 + 64 + L, so that the 16 items after the group
 // are at hand.
@@ -577,17 +598,32 @@ __device__ __forceinline__ IndexItem make_item(uint64_t n, uint64_t e, uint64_t 
 // position not above
 // its predecessor, or not below n; the header (wave 0).  kOneSegment:
 // n <= 2^32, every position is its stored low 32 bits.  kAlignedPos: the
-// positions are 4-byte aligned.
-template <bool kOneSegment, bool kAlignedPos>
+// positions are 4-byte aligned.  For blocks (blockIdx.y the block) the
+// container, E and the workspace are the block's, and a block whose size
+// is no container is left to the decode pass to report.
+template <bool kOneSegment, bool kAlignedPos, class Words>
 __global__ __launch_bounds__(64) void k_tile_index(
     const uint8_t* __restrict__ src, uint64_t src_bytes, uint64_t n, uint64_t e, uint64_t groups,
-    uint64_t* __restrict__ idx, uint32_t* __restrict__ flags, uint32_t* __restrict__ slots) {
+    uint64_t* __restrict__ idx, uint32_t* __restrict__ flags, uint32_t* __restrict__ slots,
+    Words blk) {
     __shared__ uint64_t seg_table[16];
     __shared__ uint32_t rec_lds[64 + kAhead];  // the items' records, then the 16 after them
     __shared__ uint32_t lead_lds[64];  // lane of each slot's first record, in tile order
     __shared__ uint32_t run_lds[64];   // and its tile's run
     __shared__ uint32_t tile_lds[64];  // and its tile
     const uint32_t lane = threadIdx.x;
+    if constexpr (Words::kBlocks) {
+        const BlockContainer c = block_container(blk, n, src);
+        if (!c.ok) return;  // the same for the wave
+        src = c.src;
+        src_bytes = c.bytes;
+        e = c.e;
+        groups = index_groups(e);
+        const uint64_t off = block_ws(blk);
+        idx = byte_offset(idx, off);
+        flags = byte_offset(flags, off);
+        slots = byte_offset(slots, off);
+    }
     bool bad = false;
     if (blockIdx.x == 0 && lane == 0) bad = !header_ok(src, src_bytes, n, e);
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
@@ -696,19 +732,21 @@ __global__ __launch_bounds__(64) void k_tile_index(
     if (lane == 0) flags[blockIdx.x] = bad ? 1u : 0u;
 }
 
+template <class Words>
 hipError_t launch_tile_index(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                             uint8_t* ws, hipStream_t stream) {
-    const TileIndexLayout l = tile_index_layout(n);
+                             uint8_t* ws, Words blk, hipStream_t stream) {
+    const TileIndexLayout l = tile_index_layout(n, Words::kBlocks);
     const uint64_t groups = index_groups(e);
-    const uint64_t launched = min_u64(groups, l.max_flags);
+    const dim3 grid((uint32_t)(Words::kBlocks ? l.max_flags : min_u64(groups, l.max_flags)),
+                    grid_blocks(blk));
     uint64_t* idx = reinterpret_cast<uint64_t*>(ws + l.idx_off);
     uint32_t* flags = reinterpret_cast<uint32_t*>(ws + l.flag_off);
     uint32_t* slots = reinterpret_cast<uint32_t*>(ws + l.slot_off);
     const bool one = n <= (uint64_t{1} << 32);
     const bool aligned = ((kPrefixBytes + (n + 1) / 2 + n) & 3) == 0;
-#define SZ_INDEX(O, A)                                                          \
-    k_tile_index<O, A><<<(uint32_t)launched, 64, 0, stream>>>(src, src_bytes, n, e, groups, \
-                                                               idx, flags, slots)
+#define SZ_INDEX(O, A)                                                                     \
+    k_tile_index<O, A, Words><<<grid, 64, 0, stream>>>(src, src_bytes, n, e, groups, idx, \
+                                                       flags, slots, blk)
     if (one && aligned) SZ_INDEX(true, true);
     else if (one) SZ_INDEX(true, false);
     else if (aligned) SZ_INDEX(false, true);
@@ -716,6 +754,10 @@ hipError_t launch_tile_index(const uint8_t* src, uint64_t src_bytes, uint64_t n,
 #undef SZ_INDEX
     return hipGetLastError();
 }
+template hipError_t launch_tile_index<FlatWords>(const uint8_t*, uint64_t, uint64_t, uint64_t,
+                                                 uint8_t*, FlatWords, hipStream_t);
+template hipError_t launch_tile_index<BlockWords>(const uint8_t*, uint64_t, uint64_t, uint64_t,
+                                                  uint8_t*, BlockWords, hipStream_t);
 
 // Exponent byte k (0..7) of the pair (e0: words 0..3, e1: words 4..7) set to x.
 __device__ __forceinline__ void set_exponent(uint32_t& e0, uint32_t& e1, uint32_t k, uint32_t x) {
@@ -816,7 +858,32 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
     const int t = threadIdx.x;
     const uint32_t lane = t & 63;
     const uint64_t workers = gridDim.x - 1;  // workgroup 0 folds the flags
+    // For blocks: this block's container, workspace and status.  A tile
+    // workgroup waits on nothing of the block's before its tile's own loads
+    // go out (a dependent load first would make every short-lived
+    // workgroup wait for memory twice): the block's words address is a
+    // scalar load first waited for at the store, which skips a NULL or
+    // misaligned one; the size, which gives E, is read only on the way to
+    // the escape stream, for a tile with more records than its slot, and a
+    // size that is no container then leaves the tile unpatched (its words
+    // are unspecified, the status says corrupt, and nothing outside the
+    // block's pitch is read).  Workgroup 0 checks the size and reports.
+    const uint8_t* const src0 = src;
+    if constexpr (Words::kBlocks) {
+        status += blockIdx.y;
+        src = byte_offset(src, block_pitch(out));
+        const uint64_t off = block_ws(out);
+        idx = byte_offset(idx, off);
+        flags = byte_offset(flags, off);
+        slots = byte_offset(slots, off);
+    }
     if (blockIdx.x == 0) {
+        if constexpr (Words::kBlocks) {
+            if (!block_container(out, n, src0).ok) {  // the same for every thread
+                if (t == 0) *status = out.invalid() ? kStatusInvalid : kStatusCorrupt;
+                return;
+            }
+        }
         uint32_t any = 0;
 #pragma unroll 8
         for (uint64_t f = t; f < n_flags; f += kTileThreads) any |= flags[f];
@@ -824,19 +891,18 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
         if (t == 0 && status) *status = out.invalid() ? kStatusInvalid : (any ? kStatusCorrupt : 0);
         return;
     }
-    if (out.invalid()) return;  // the same for every thread
+    if constexpr (!Words::kBlocks) {
+        if (out.invalid()) return;  // the same for every thread
+    }
+    // blocks: the block's address, a scalar load first waited for at the
+    // tile's store, together with the codebook's
+    const auto words = out.resolve();
 
     const uint8_t* nib = src + kPrefixBytes;
     const uint8_t* sm = nib + (n + 1) / 2;
     const uint64_t tiles = (n + kTileWords - 1) / kTileWords;
     const uint64_t whole = n / kTileWords;  // tiles with all kTileWords words
     const uint64_t esc_off = kPrefixBytes + (n + 1) / 2 + n;
-    EscapeReader rd;
-    rd.pos_lo = src + esc_off;
-    rd.exps = rd.pos_lo + 4 * e;
-    rd.aligned = (esc_off & 3) == 0;
-    rd.one_segment = n <= (1ull << 32);
-    rd.seg_end = nullptr;  // unused: tiles compare the low 32 bits only
 
     // the tile's records into e0/e1: from its slot, or, past the slot's
     // capacity, from the escape stream
@@ -847,6 +913,17 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
             patch_wave(sv, __ballot(in), e0, e1);
             return;
         }
+        if constexpr (Words::kBlocks) {
+            const BlockContainer c = block_container(out, n, src0);
+            if (!c.ok) return;  // the same for every thread: reported by workgroup 0
+            e = c.e;
+        }
+        EscapeReader rd;
+        rd.pos_lo = src + esc_off;
+        rd.exps = rd.pos_lo + 4 * e;
+        rd.aligned = (esc_off & 3) == 0;
+        rd.one_segment = n <= (1ull << 32);
+        rd.seg_end = nullptr;  // unused: tiles compare the low 32 bits only
         const uint64_t ks = min_u64(uniform64(idx[tile]), e);
         uint64_t ke = min_u64(uniform64(idx[tile + 1]), e);
         if (ke < ks) ke = ks;                              // a faulty index: flagged
@@ -860,6 +937,7 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
         const uint64_t i0 = t0 + (uint64_t)t * 8;
         // every load of the tile goes out before anything waits on one
         const uint32_t sv = lane < kSlotWords ? slots[tile * kSlotWords + lane] : 0u;
+
         if (tile < whole) {
             const uint32_t codes = *reinterpret_cast<const uint32_t*>(nib + i0 / 2);
             uint32_t s0, s1;
@@ -878,12 +956,24 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
             uint32_t e0, e1;
             exponents8(codes, cb, e0, e1);
             patch(tile, t0, sv, e0, e1);
-            if constexpr (!Words::kPaged) words_out = out.at_wave(i0);
+            bool write = true;
+            if constexpr (Words::kBlocks) {
+                // a NULL or misaligned block address: nothing written
+                const uintptr_t a = reinterpret_cast<uintptr_t>(words.base);
+                write = a != 0 && (a & 15) == 0;
+                words_out = words.at(i0);
+            } else if constexpr (!Words::kPaged) {
+                words_out = out.at_wave(i0);
+            }
             // written past the caches: a decode's output is larger than they
             // are, and lines left dirty cost the next kernel their write-back
-            store_streaming(reinterpret_cast<uint4*>(words_out), words8(e0, e1, s0, s1));
+            if (write) store_streaming(reinterpret_cast<uint4*>(words_out), words8(e0, e1, s0, s1));
         } else {
             // the partial last tile: words past n are neither read nor written
+            if constexpr (Words::kBlocks) {
+                const uintptr_t a = reinterpret_cast<uintptr_t>(words.base);
+                if (a == 0 || (a & 15) != 0) return;
+            }
             const uint4 cb = *reinterpret_cast<const uint4*>(src + kHeaderBytes);
             uint32_t ex[8];
             for (uint32_t k = 0; k < 8; k++) {
@@ -895,7 +985,7 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
             patch(tile, t0, sv, e0, e1);
             for (uint32_t k = 0; k < 8 && i0 + k < n; k++) {
                 const uint32_t x = ((k < 4 ? e0 : e1) >> (8 * (k & 3))) & 0xFFu;
-                *out.at(i0 + k) = (uint16_t)recombine(sm[i0 + k], x);
+                *words.at(i0 + k) = (uint16_t)recombine(sm[i0 + k], x);
             }
         }
     }
@@ -904,17 +994,20 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
 template <class Words>
 hipError_t launch_decode_tiles(const uint8_t* src, uint64_t n, uint64_t e, const uint8_t* ws,
                                Words dst, int32_t* status, int /*num_cus*/, hipStream_t stream) {
-    const TileIndexLayout l = tile_index_layout(n);
-    const uint64_t n_flags = min_u64(index_groups(e), l.max_flags);
+    const TileIndexLayout l = tile_index_layout(n, Words::kBlocks);
+    // (each block's index waves all write their flag)
+    const uint64_t n_flags = Words::kBlocks ? l.max_flags : min_u64(index_groups(e), l.max_flags);
     // the one that writes the status, then the tiles' workgroups
-    const uint64_t groups = min_u64(l.tiles, kMaxTileGroups) + 1;
+    const dim3 grid((uint32_t)(min_u64(l.tiles, kMaxTileGroups) + 1), grid_blocks(dst));
     const uint64_t* idx = reinterpret_cast<const uint64_t*>(ws + l.idx_off);
     const uint32_t* flags = reinterpret_cast<const uint32_t*>(ws + l.flag_off);
     const uint32_t* slots = reinterpret_cast<const uint32_t*>(ws + l.slot_off);
     const bool aligned = ((kPrefixBytes + (n + 1) / 2) & 7) == 0;
+    // (blocks pass e = 0 and take the variant for few records per tile: 2%
+    // faster on KV blocks; escape-heavy blocks are the single-pass form's)
     const bool dense = e > l.tiles * kSlotRecords;
 #define SZ_TILES(A, D)                                                                   \
-    k_decode_tiles<A, Words, D><<<(uint32_t)groups, kTileThreads, 0, stream>>>(          \
+    k_decode_tiles<A, Words, D><<<grid, kTileThreads, 0, stream>>>(                      \
         src, n, e, idx, flags, n_flags, slots, dst, status)
     if (aligned && !dense) SZ_TILES(true, false);
     else if (aligned) SZ_TILES(true, true);
@@ -947,7 +1040,6 @@ constexpr uint32_t kMapEscaped = 0x100u;                   // map entry: 0x100 |
 constexpr uint32_t kDenseMaxLog2 = 16;                     // ranges of at most 2^16 words
 constexpr uint32_t kDenseSubs = (1u << kDenseMaxLog2) / kDenseTile;  // sub-ranges per range
 constexpr uint32_t kWaveRecords = 256;                     // records per wave and step
-constexpr int32_t kBufferFlags = 0x00020000;               // buffer resource word 3 on gfx9 parts
 static_assert((1u << 14) % kDenseTile == 0, "ranges of at least 2^14 words hold whole sub-ranges");
 static_assert(kDenseSubs + 1 <= kDenseWaves, "one wave per sub-range bound");
 static_assert(kWaveRecords == 4 * 64, "four records per lane and step");
@@ -1118,6 +1210,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
             return;
         }
     }
+    const auto words = out.resolve();  // (after the address check)
     if (t == 0) bad = 0;
     if (blockIdx.x == 0 && t == 0 && !header_ok(src, src_bytes, n, e)) bad = 1;
 
@@ -1235,15 +1328,15 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_decode_dense(
                 exponents8(c[g], cb, e0, e1);
                 patch8(m, e0, e1);
                 // a sub-range lies inside one page
-                *reinterpret_cast<uint4*>(out.at(sub) + (w - sub)) =
-                    words8(e0, e1, s[2 * g], s[2 * g + 1]);
+                store_global(reinterpret_cast<uint4*>(words.at(sub) + (w - sub)),
+                             words8(e0, e1, s[2 * g], s[2 * g + 1]));
             } else if (w < sub_end) {  // the input's last, partial group
                 for (uint64_t i = w; i < sub_end; i++) {
                     const uint32_t code = (nib[i / 2] >> (4 * (i & 1))) & 0xFu;
                     const uint32_t m = map[(uint32_t)(i - sub)];
                     map[(uint32_t)(i - sub)] = 0;
                     const uint32_t ex = (m & kMapEscaped) ? (m & 0xFFu) : codebook_byte(cb, code);
-                    *out.at(i) = (uint16_t)recombine(sm[i], ex);
+                    *words.at(i) = (uint16_t)recombine(sm[i], ex);
                 }
             }
         }
@@ -1303,5 +1396,8 @@ SZ_DECODE_INSTANCES(PagedWords)
 #undef SZ_DECODE_INSTANCES
 template hipError_t launch_decode_dense<BlockWords>(const uint8_t*, uint64_t, uint64_t, uint64_t,
                                                     BlockWords, int32_t*, hipStream_t);
+template hipError_t launch_decode_tiles<BlockWords>(const uint8_t*, uint64_t, uint64_t,
+                                                    const uint8_t*, BlockWords, int32_t*, int,
+                                                    hipStream_t);
 
 }  // namespace sz

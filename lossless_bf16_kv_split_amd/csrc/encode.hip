@@ -188,7 +188,8 @@ __global__ __launch_bounds__(kHistThreads) void k_histogram(Words src, uint64_t 
 
     const uint64_t begin = (uint64_t)blockIdx.x << chunk_log2;
     const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
-    count_exponents<kHistThreads>(src, begin, end, h + (threadIdx.x % kHistCopies) * kHistPitch);
+    count_exponents<kHistThreads>(src.resolve(), begin, end,
+                                  h + (threadIdx.x % kHistCopies) * kHistPitch);
     __syncthreads();
 
     for (int bin = threadIdx.x; bin < 256; bin += kHistThreads) {
@@ -895,7 +896,7 @@ __device__ __forceinline__ uint64_t pack_range(Words src, uint64_t n, uint64_t b
         uint32_t w[kPackWords / 2];
 #pragma unroll
         for (int h = 0; h < kPackLoads; h++) {
-            const uint4 v = p[h];
+            const uint4 v = load_global(p + h);
             w[4 * h + 0] = v.x;
             w[4 * h + 1] = v.y;
             w[4 * h + 2] = v.z;
@@ -1010,7 +1011,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     __syncthreads();
 
     int parity = 0;
-    const uint64_t escapes = pack_range<kAlignedSm, kFirst>(src, n, begin, end, dst, esc,
+    const uint64_t escapes = pack_range<kAlignedSm, kFirst>(src.resolve(), n, begin, end, dst, esc,
                                                             slot_base, write, hmine, lds, parity);
     if (kFirst) {
         __syncthreads();
@@ -1254,11 +1255,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
 
     code_table(codebook, lds);
     __syncthreads();
+    const auto words = src.resolve();
     int parity = 0;
     for (uint32_t c = blockIdx.x, j = 0; c < chunks; c += gridDim.x, j++) {
         const uint64_t begin = (uint64_t)c << chunk_log2;
         const uint64_t end = min_u64(begin + (uint64_t{1} << chunk_log2), n);
-        pack_range<kAlignedSm, false>(src, n, begin, end, dst, esc_out, my_first[j], true, nullptr,
+        pack_range<kAlignedSm, false>(words, n, begin, end, dst, esc_out, my_first[j], true, nullptr,
                                       lds, parity);
     }
 }
@@ -1392,6 +1394,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
     __syncthreads();
     uint32_t* mine = h + (t % kSpecCopies) * kSpecPitch;
     const uint64_t spacing = n / (kGroups * kBlocksPerGroup);
+    const auto words = src.resolve();
 #pragma unroll
     for (uint32_t k = 0; k < kSampleLoads; k++) {
         const uint32_t g = t + k * kSampleThreads;  // 16-byte group in this workgroup's share
@@ -1399,7 +1402,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
         const uint64_t start = block * spacing / kSampleBlockWords * kSampleBlockWords;
         const uint64_t word = start + (uint64_t)(g % kLoadsPerBlock) * 8;
         // a block lies inside one page
-        hist_uint4(mine, *reinterpret_cast<const uint4*>(src.at(word)));
+        hist_uint4(mine, load_global(reinterpret_cast<const uint4*>(words.at(word))));
     }
     __syncthreads();
     uint32_t before = 0;

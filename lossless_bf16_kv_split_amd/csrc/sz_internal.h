@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -105,17 +106,40 @@ __host__ __device__ __forceinline__ uint64_t min_u64(uint64_t a, uint64_t b) {
     return a < b ? a : b;
 }
 
+// Word 3 of a buffer resource (raw buffer, 32-bit data) on gfx9-family
+// parts, gfx950 included: buffer loads take a 32-bit offset per lane from a
+// base in scalar registers and read 0 past num_records bytes.
+constexpr int32_t kBufferFlags = 0x00020000;
+
 // 16-byte non-temporal load and store (global_load/store with the nt bit)
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Loads and stores through the global address space.  A device address
+// read from a table (a page or a block) is a generic pointer to the
+// compiler, and accesses through it would be flat instructions; the tables
+// hold device memory only, so the accesses to tensor words go through
+// these (for a plain tensor argument they are what the compiler emits
+// anyway).
+// (16 bytes at a time, through the vector type: a uint4 copy would bind a
+// generic reference and lose the address space again)
+#define SZ_GLOBAL __attribute__((address_space(1)))
+__device__ __forceinline__ uint4 load_global(const uint4* p) {
+    const u32x4 v = *(const SZ_GLOBAL u32x4*)p;
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_global(uint4* p, uint4 v) {
+    const u32x4 w = {v.x, v.y, v.z, v.w};
+    *(SZ_GLOBAL u32x4*)p = w;
+}
+
 __device__ __forceinline__ uint4 load_streaming(const uint4* p) {
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const u32x4 v = __builtin_nontemporal_load((const SZ_GLOBAL u32x4*)p);
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 __device__ __forceinline__ void store_streaming(uint4* p, uint4 v) {
     const u32x4 w = {v.x, v.y, v.z, v.w};
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(p));
+    __builtin_nontemporal_store(w, (SZ_GLOBAL u32x4*)p);
 }
 
 // sz_decode's choice of decode form, measured on MI355X:
@@ -171,12 +195,24 @@ struct TileIndexLayout {
     uint64_t slot_off = 0;    // u32[tiles][kSlotWords]: each tile's record count and records
     uint64_t bytes = 0;
 };
-inline uint64_t index_groups(uint64_t e) { return (e + 1 + kIndexItems - 1) / kIndexItems; }
-inline TileIndexLayout tile_index_layout(uint64_t n) {
+__host__ __device__ inline uint64_t index_groups(uint64_t e) {
+    return (e + 1 + kIndexItems - 1) / kIndexItems;
+}
+// For several blocks in one launch the escape count of each is known only
+// on the device, so the index pass runs a number of waves per block fixed
+// by the block length -- one per 16384 words (one group of 64 records at
+// the KV data's 0.4% escapes), 64 to 4096 of them -- each taking every
+// so-many-th group of 64 items.
+inline uint64_t block_index_waves(uint64_t n) {
+    const uint64_t w = n / 16384;
+    return w < 64 ? 64 : (w > 4096 ? 4096 : w);
+}
+inline TileIndexLayout tile_index_layout(uint64_t n, bool blocks = false) {
     TileIndexLayout l;
     l.tiles = (n + kTileWords - 1) / kTileWords;
     const uint64_t max_groups = index_groups((15 * n) / 16);
     l.max_flags = max_groups < kMaxIndexGroups ? max_groups : kMaxIndexGroups;
+    if (blocks) l.max_flags = block_index_waves(n);
     auto align = [](uint64_t x) { return (x + 255) & ~uint64_t{255}; };
     l.idx_off = 0;
     l.flag_off = align(8 * (l.tiles + 1));
@@ -205,6 +241,7 @@ struct FlatWords {
     __device__ __forceinline__ bool invalid() const { return false; }
     __device__ __forceinline__ uint16_t* at(uint64_t i) const { return base + i; }
     __device__ __forceinline__ uint16_t* at_wave(uint64_t i) const { return base + i; }
+    __device__ __forceinline__ FlatWords resolve() const { return *this; }
     __device__ __forceinline__ uint64_t run_end(uint64_t, uint64_t end) const { return end; }
 };
 
@@ -229,6 +266,7 @@ struct PagedWords {
     __device__ __forceinline__ uint64_t run_end(uint64_t i, uint64_t end) const {
         return min_u64(end, ((i >> page_log2) + 1) << page_log2);
     }
+    __device__ __forceinline__ PagedWords resolve() const { return *this; }
 };
 
 // Several tensors of the same length ("blocks") in one launch, one
@@ -256,6 +294,10 @@ struct BlockWords {
     __device__ __forceinline__ uint16_t* at(uint64_t i) const { return blocks[blockIdx.y] + i; }
     __device__ __forceinline__ uint16_t* at_wave(uint64_t i) const { return blocks[blockIdx.y] + i; }
     __device__ __forceinline__ uint64_t run_end(uint64_t, uint64_t end) const { return end; }
+    // the block's words as one flat tensor, its address read once (the
+    // workgroup's loops would otherwise read the table entry again for
+    // every tile, stores in between keeping it from being hoisted)
+    __device__ __forceinline__ FlatWords resolve() const { return FlatWords{blocks[blockIdx.y]}; }
 };
 
 // The launch's grid height, and this workgroup's block offsets into the
@@ -275,9 +317,12 @@ __device__ __forceinline__ uint64_t block_pitch(const Words& w) {
     if constexpr (Words::kBlocks) return (uint64_t)blockIdx.y * w.pitch;
     else return 0;
 }
+// p advanced by a byte count, through a char pointer (an integer round
+// trip would lose the global address space and turn loads into flat ones)
 template <class T>
 __device__ __forceinline__ T* byte_offset(T* p, uint64_t bytes) {
-    return reinterpret_cast<T*>(reinterpret_cast<uintptr_t>(p) + bytes);
+    using Byte = typename std::conditional<std::is_const<T>::value, const char, char>::type;
+    return reinterpret_cast<T*>(reinterpret_cast<Byte*>(p) + bytes);
 }
 
 // Launchers (asynchronous on `stream`; return the launch status).  The
@@ -319,9 +364,14 @@ template <class Words>
 hipError_t launch_decode_dense(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
                                Words dst, int32_t* status, hipStream_t stream);
 // tile decode: index the escape stream by tile (header and record-order
-// checks included), then decode every tile; the second call writes *status
+// checks included), then decode every tile; the second call writes *status.
+// For BlockWords (one launch each for all blocks) src, ws and status are
+// block 0's, e is taken from each block's size, and ws_stride in the
+// accessor is the per-block workspace (tile_index_layout(n, true).bytes,
+// rounded up to 256).
+template <class Words>
 hipError_t launch_tile_index(const uint8_t* src, uint64_t src_bytes, uint64_t n, uint64_t e,
-                             uint8_t* ws, hipStream_t stream);
+                             uint8_t* ws, Words blocks, hipStream_t stream);
 template <class Words>
 hipError_t launch_decode_tiles(const uint8_t* src, uint64_t n, uint64_t e, const uint8_t* ws,
                                Words dst, int32_t* status, int num_cus, hipStream_t stream);

@@ -302,14 +302,27 @@ def test_blocks_host_checks(sz):
     assert status_of(enc, T, nb, n, D, pitch, S, W, wb, MIS, 0) == 1
     assert status_of(enc, T, nb, n, D, pitch - 16, S, W, wb, None, 0) == 2
     fixed = 176 + n // 2 + n
-    assert status_of(dec, D, pitch, S, nb, n, T, None, 0) == 1                 # status required
-    assert status_of(dec, D, pitch, S, nb, n, T, MIS, 0) == 1
-    assert status_of(dec, D, (fixed - 1) // 16 * 16, S, nb, n, T, A, 0) == 1    # no room
-    assert status_of(dec, D, pitch, None, nb, n, T, A, 0) == 1
-    assert status_of(dec, D, pitch, S, 0, n, T, A, 0) == 1
-    assert status_of(dec, D, pitch, S, nb, n, None, A, 0) == 1
-    assert status_of(dec, D + 8, pitch, S, nb, n, T, A, 0) == 1
-    assert status_of(dec, D, pitch, S, nb, (1 << 36) + 1, T, A, 0) == 3
+    assert status_of(dec, D, pitch, S, nb, n, T, None, None, 0, 0) == 1                 # status required
+    assert status_of(dec, D, pitch, S, nb, n, T, MIS, None, 0, 0) == 1
+    assert status_of(dec, D, (fixed - 1) // 16 * 16, S, nb, n, T, A, None, 0, 0) == 1    # no room
+    assert status_of(dec, D, pitch, None, nb, n, T, A, None, 0, 0) == 1
+    assert status_of(dec, D, pitch, S, 0, n, T, A, None, 0, 0) == 1
+    assert status_of(dec, D, pitch, S, nb, n, None, A, None, 0, 0) == 1
+    assert status_of(dec, D + 8, pitch, S, nb, n, T, A, None, 0, 0) == 1
+    assert status_of(dec, D, pitch, S, nb, (1 << 36) + 1, T, A, None, 0, 0) == 3
+    # the tile form's workspace: a tile index, a fault flag per 16384 words
+    # (64 to 4096) and the record slots per block, at 256-byte strides
+    def dws(m, count):
+        tiles = -(-m // 2048)
+        waves = min(max(m // 16384, 64), 4096)
+        return count * r256(r256(r256(8 * (tiles + 1)) + 4 * waves) + 64 * tiles)
+    for m, count in ((n, nb), (5000, 3), (1 << 24, 32), (1 << 30, 2)):
+        assert sz.sz_blocks_decode_workspace_size(m, count) == dws(m, count), (m, count)
+    dwb = sz.sz_blocks_decode_workspace_size(n, nb)
+    for bad in ((n, 0), (n, 65536), ((1 << 36) + 1, 1)):
+        assert sz.sz_blocks_decode_workspace_size(*bad) == 0
+    assert status_of(dec, D, pitch, S, nb, n, T, A, W + 128, dwb, 0) == 1    # misaligned
+    assert status_of(dec, D, pitch, S, nb, n, T, A, W, dwb - 1, 0) == 1      # too small
 
 
 def test_bench_chunk_plan_matches_library(sz):

@@ -92,6 +92,21 @@ def single_read(n: int, nb: int) -> bool:
     return n >= 1 << 20 and n * nb >= 1 << 26
 
 
+FORMS = ("dense", "tiles")
+
+
+def decode_blocks(torch, sz, src, pitch, sizes, nb, n, table, status, form, stream=None):
+    """sz_decode_blocks in one of its forms: "dense" without a workspace,
+    "tiles" with one (holding stale bytes)."""
+    if form == "tiles":
+        wb = sz.sz_blocks_decode_workspace_size(n, nb)
+        ws = torch.full((wb,), 0x5A, dtype=torch.uint8, device="cuda")
+        sz.sz_decode_blocks(src, pitch, sizes, nb, n, table, status, ws, wb, stream=stream)
+        return ws
+    sz.sz_decode_blocks(src, pitch, sizes, nb, n, table, status, stream=stream)
+    return None
+
+
 def check_containers(dst, pitch, sizes, blocks, skip=()):
     host = dst.cpu().numpy()
     sz_host = sizes.cpu().numpy().astype(np.uint64)
@@ -139,16 +154,17 @@ def test_blocks_round_trip(torch, sz, kind, n, nb):
     for b in range(nb):
         assert np.array_equal(blk.read(b), words[b]), (label, b)
 
-    # decode into a fresh pool in another order
-    out = Blocks(torch, n, nb, 10)
-    dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
-    sz.sz_decode_blocks(dst, pitch, sizes, nb, n, out.table, dstatus)
-    torch.cuda.synchronize()
-    assert (dstatus.cpu().numpy() == 0).all(), label
-    out.snapshot()
-    for b in range(nb):
-        assert np.array_equal(out.read(b), words[b]), (label, b)
-    assert out.guards_intact(), label
+    # decode into a fresh pool in another order, in both forms
+    for form in FORMS:
+        out = Blocks(torch, n, nb, 10)
+        dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+        decode_blocks(torch, sz, dst, pitch, sizes, nb, n, out.table, dstatus, form)
+        torch.cuda.synchronize()
+        assert (dstatus.cpu().numpy() == 0).all(), (label, form)
+        out.snapshot()
+        for b in range(nb):
+            assert np.array_equal(out.read(b), words[b]), (label, form, b)
+        assert out.guards_intact(), (label, form)
 
 
 @pytest.mark.parametrize("fill", [0x00, 0xA5, 0xFF])
@@ -192,14 +208,15 @@ def test_blocks_decode_by_single_tensor_call(torch, sz):
     for b in range(nb):
         x = torch.from_numpy(words[b].view(np.int16)).cuda()
         sz.sz_encode(x, n, flat[b * pitch:], pitch, fsizes[b:])
-    out = Blocks(torch, n, nb, 13)
-    st = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
-    sz.sz_decode_blocks(flat, pitch, fsizes, nb, n, out.table, st)
-    torch.cuda.synchronize()
-    assert (st.cpu().numpy() == 0).all()
-    out.snapshot()
-    for b in range(nb):
-        assert np.array_equal(out.read(b), words[b]), b
+    for form in FORMS:
+        out = Blocks(torch, n, nb, 13)
+        st = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+        decode_blocks(torch, sz, flat, pitch, fsizes, nb, n, out.table, st, form)
+        torch.cuda.synchronize()
+        assert (st.cpu().numpy() == 0).all(), form
+        out.snapshot()
+        for b in range(nb):
+            assert np.array_equal(out.read(b), words[b]), (form, b)
 
 
 @pytest.mark.parametrize("n,nb", [(65536 + 40, 5), ((1 << 20) + 8, 70)])
@@ -236,18 +253,20 @@ def test_blocks_bad_address(torch, sz, n, nb):
     for b in bad:
         x = torch.from_numpy(words[b].view(np.int16)).cuda()
         sz.sz_encode(x, n, dst2[b * pitch:], pitch, dsizes[b:])
-    dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
-    sz.sz_decode_blocks(dst2, pitch, dsizes, nb, n, out.table, dstatus)
-    torch.cuda.synchronize()
-    assert list(dstatus.cpu().numpy()) == want_st
-    out.snapshot()
-    for b in range(nb):
-        if b in bad:
-            s0 = int(out.slot[b]) * out.stride
-            assert (out.host[s0:s0 + out.stride] == SENTINEL).all(), b
-        else:
-            assert np.array_equal(out.read(b), words[b]), b
-    assert out.guards_intact()
+    for form in FORMS:
+        out.pool.fill_(SENTINEL)
+        dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+        decode_blocks(torch, sz, dst2, pitch, dsizes, nb, n, out.table, dstatus, form)
+        torch.cuda.synchronize()
+        assert list(dstatus.cpu().numpy()) == want_st, form
+        out.snapshot()
+        for b in range(nb):
+            if b in bad:
+                s0 = int(out.slot[b]) * out.stride
+                assert (out.host[s0:s0 + out.stride] == SENTINEL).all(), (form, b)
+            else:
+                assert np.array_equal(out.read(b), words[b]), (form, b)
+        assert out.guards_intact(), form
 
 
 def test_blocks_corrupt_flagged(torch, sz):
@@ -278,23 +297,25 @@ def test_blocks_corrupt_flagged(torch, sz):
                                                     packed[esc:esc + 4].copy())
     dst2 = torch.from_numpy(packed).cuda()
     sizes2 = torch.from_numpy(s).cuda()
-    out = Blocks(torch, n, nb, 17)
-    dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
-    sz.sz_decode_blocks(dst2, tight, sizes2, nb, n, out.table, dstatus)
-    torch.cuda.synchronize()
-    assert list(dstatus.cpu().numpy()) == [0, 4, 4, 0, 4, 4]
-    out.snapshot()
-    for b in (0, 3):
-        assert np.array_equal(out.read(b), words[b]), b
-    assert out.guards_intact()
+    for form in FORMS:
+        out = Blocks(torch, n, nb, 17)
+        dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+        decode_blocks(torch, sz, dst2, tight, sizes2, nb, n, out.table, dstatus, form)
+        torch.cuda.synchronize()
+        assert list(dstatus.cpu().numpy()) == [0, 4, 4, 0, 4, 4], form
+        out.snapshot()
+        for b in (0, 3):
+            assert np.array_equal(out.read(b), words[b]), (form, b)
+        assert out.guards_intact(), form
 
 
+@pytest.mark.parametrize("form", FORMS)
 @pytest.mark.parametrize("n,nb", [(65536 * 2 + 16, 4), (1 << 20, 64)])
-def test_blocks_graph_replay(torch, sz, n, nb):
+def test_blocks_graph_replay(torch, sz, n, nb, form):
     """Both calls allocate nothing, so a graph can hold them: every replay,
     with other work between, gives the eager containers and words (both
     encode forms)."""
-    say("graph, n", n, "blocks", nb)
+    say("graph, n", n, "blocks", nb, form)
     words = [make_words("kv", n, 100 + b) for b in range(nb)]
     blk = Blocks(torch, n, nb, 18)
     blk.fill(torch, words)
@@ -305,13 +326,18 @@ def test_blocks_graph_replay(torch, sz, n, nb):
     sizes = torch.zeros(nb, dtype=torch.int64, device="cuda")
     out = Blocks(torch, n, nb, 19)
     st = torch.zeros(nb, dtype=torch.int32, device="cuda")
+    dwb = sz.sz_blocks_decode_workspace_size(n, nb)
+    dws = torch.full((dwb,), 0x5A, dtype=torch.uint8, device="cuda")
     s = torch.cuda.Stream()
     g = torch.cuda.CUDAGraph()
     torch.cuda.synchronize()
     with torch.cuda.graph(g, stream=s):
         cs = torch.cuda.current_stream()
         sz.sz_encode_blocks(blk.table, nb, n, dst, pitch, sizes, ws, wb, None, cs)
-        sz.sz_decode_blocks(dst, pitch, sizes, nb, n, out.table, st, cs)
+        if form == "tiles":
+            sz.sz_decode_blocks(dst, pitch, sizes, nb, n, out.table, st, dws, dwb, stream=cs)
+        else:
+            sz.sz_decode_blocks(dst, pitch, sizes, nb, n, out.table, st, stream=cs)
     for rep in range(3):
         out.pool.fill_(SENTINEL)
         st.fill_(-1)
@@ -358,12 +384,14 @@ def test_blocks_full_size(torch, sz):
         assert int(one_size.item()) == int(s[b]), b
         assert torch.equal(one[:int(s[b])], dst[b * pitch:b * pitch + int(s[b])]), b
     del one
-    out = Blocks(torch, n, nb, 22)
-    dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
-    sz.sz_decode_blocks(dst, pitch, sizes, nb, n, out.table, dstatus)
-    torch.cuda.synchronize()
-    assert (dstatus.cpu().numpy() == 0).all()
-    out.snapshot()
-    for b in range(nb):
-        assert np.array_equal(out.read(b), blocks[b]), b
-    assert out.guards_intact()
+    for form in FORMS:
+        out = Blocks(torch, n, nb, 22)
+        dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+        ws = decode_blocks(torch, sz, dst, pitch, sizes, nb, n, out.table, dstatus, form)
+        torch.cuda.synchronize()
+        assert (dstatus.cpu().numpy() == 0).all(), form
+        out.snapshot()
+        for b in range(nb):
+            assert np.array_equal(out.read(b), blocks[b]), (form, b)
+        assert out.guards_intact(), form
+        del out, ws

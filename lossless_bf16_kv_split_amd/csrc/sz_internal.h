@@ -271,11 +271,12 @@ struct PagedWords {
 
 // Several tensors of the same length ("blocks") in one launch, one
 // container each: blockIdx.y is the block.  Its words are at blocks[y]; its
-// encode workspace lies y * ws_stride bytes after block 0's, its container
-// y * pitch bytes after block 0's, and its container size is sizes[y]
-// (written by the encode, read by the decode).  flags[y] is
-// kBlockInvalid when the block's address failed its check (the encode keeps
-// the flags in its workspace; the decode uses its per-block statuses).
+// workspace (the encode's, or the tile decode's index) lies y * ws_stride
+// bytes after block 0's, its container y * pitch bytes after block 0's,
+// and its container size is sizes[y] (written by the encode, read by the
+// decode).  flags[y] is kBlockInvalid when the block's address failed its
+// check (the encode keeps the flags in its workspace; the decode uses its
+// per-block statuses).
 constexpr int32_t kBlockInvalid = 1;  // SZ_ERR_INVALID_ARGUMENT
 struct BlockWords {
     static constexpr bool kPaged = false;

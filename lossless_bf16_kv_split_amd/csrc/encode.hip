@@ -722,7 +722,11 @@ __device__ __forceinline__ uint32_t write_escapes(const ThreadWords& r, const ui
                                                   int parity, const EscapeOut& out) {
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int wave = t >> 6;
+    // the wave index as a scalar: "v < wave" below is then one scalar
+    // compare per v, not a lane mask per v kept in scalar registers across
+    // the tile loop (sixteen 64-bit masks, which pushed the finish kernel's
+    // pack loop into reloading spilled registers on every tile)
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const uint32_t cnt = r.count;
     uint32_t lane_prefix = 0, wave_total = 0;
     if (__ballot(cnt > 1) == 0) {

@@ -31,7 +31,7 @@ __all__ = [
     "sz_encode_pages", "sz_decode_pages", "sz_blocks_workspace_size", "sz_encode_blocks",
     "sz_decode_blocks", "sz_blocks_decode_workspace_size", "sz_ship_to_host", "sz_ship_from_host", "ShipContext",
     "sz_status_string", "encode",
-    "decode",
+    "decode", "encode_blocks", "decode_blocks", "BlockContainers",
     "PREFIX_BYTES", "MAX_ELEMENTS", "NOALLOC_WORKSPACE_BYTES",
 ]
 
@@ -375,3 +375,73 @@ def decode(container, n_elements: int, dtype=None, stream=None, check: bool = Tr
         if st != SZ_OK:
             raise SplitZipError(st, "sz_decode (device check)")
     return out
+
+
+class BlockContainers:
+    """Containers of equal-length blocks as sz_encode_blocks leaves them:
+    block b's container is ``data[b * pitch : b * pitch + sizes[b]]``, and
+    ``sizes`` stays on the device (a uint64 array held as an int64 tensor)."""
+
+    def __init__(self, data, pitch: int, sizes, block_elems: int):
+        self.data, self.pitch, self.sizes, self.block_elems = data, pitch, sizes, block_elems
+
+    def __len__(self) -> int:
+        return self.sizes.numel()
+
+    def container(self, b: int):
+        """Block b's container, trimmed (reads its size back: synchronises)."""
+        return self.data[b * self.pitch: b * self.pitch + int(self.sizes[b].item())]
+
+
+def _block_table(tensors):
+    import torch
+    if not tensors:
+        raise ValueError("no blocks")
+    n = tensors[0].numel()
+    for t in tensors:
+        if t.element_size() != 2 or not t.is_cuda or t.numel() != n or not t.is_contiguous():
+            raise ValueError("blocks must be contiguous CUDA tensors of 16-bit elements, "
+                             "all of the same length")
+    return torch.tensor([t.data_ptr() for t in tensors], dtype=torch.int64,
+                        device=tensors[0].device), n
+
+
+def encode_blocks(tensors, stream=None) -> BlockContainers:
+    """Compress equal-length CUDA tensors (one per layer, say), one container
+    each, in one launch per pass (sz_encode_blocks); nothing is read back."""
+    import torch
+    table, n = _block_table(tensors)
+    nb = len(tensors)
+    dev = tensors[0].device
+    pitch = (sz_max_compressed_size(n) + 15) // 16 * 16
+    data = torch.empty(nb * pitch, dtype=torch.uint8, device=dev)
+    sizes = torch.zeros(nb, dtype=torch.int64, device=dev)
+    wb = sz_blocks_workspace_size(n, nb)
+    ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+    sz_encode_blocks(table, nb, n, data, pitch, sizes, ws, wb, None, stream)
+    return BlockContainers(data, pitch, sizes, n)
+
+
+def decode_blocks(blocks: BlockContainers, outputs, stream=None, check: bool = True):
+    """Decompress every container into the matching output tensor (same
+    count and length as encoded), with the tile form's workspace; with
+    ``check`` the per-block statuses are read back (synchronising) and any
+    failure raises, naming the first block that failed."""
+    import torch
+    table, n = _block_table(outputs)
+    nb = len(outputs)
+    if nb != len(blocks) or n != blocks.block_elems:
+        raise ValueError("outputs do not match the containers' block count and length")
+    dev = outputs[0].device
+    status = torch.zeros(nb, dtype=torch.int32, device=dev)
+    wb = sz_blocks_decode_workspace_size(n, nb)
+    ws = torch.empty(wb, dtype=torch.uint8, device=dev)
+    sz_decode_blocks(blocks.data, blocks.pitch, blocks.sizes, nb, n, table, status, ws, wb,
+                     stream)
+    if check:
+        st = status.cpu()
+        bad = (st != SZ_OK).nonzero()
+        if bad.numel():
+            b = int(bad[0])
+            raise SplitZipError(int(st[b]), f"sz_decode_blocks (block {b})")
+    return outputs

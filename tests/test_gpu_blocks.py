@@ -59,6 +59,14 @@ class Blocks:
             if w.size:
                 self.pool[s:s + w.size] = torch.from_numpy(w.view(np.int16)).cuda()
 
+    def fill_bulk(self, torch, blocks):
+        """All blocks in one copy (for many short blocks)."""
+        host = np.full(self.pool.numel(), SENTINEL, dtype=np.uint16)
+        for b, w in enumerate(blocks):
+            s = int(self.slot[b]) * self.stride
+            host[s:s + w.size] = w
+        self.pool.copy_(torch.from_numpy(host.view(np.int16)))
+
     def read(self, b: int) -> np.ndarray:
         s = int(self.slot[b]) * self.stride
         return self.host[s:s + self.n]
@@ -395,3 +403,81 @@ def test_blocks_full_size(torch, sz):
             assert np.array_equal(out.read(b), blocks[b]), (form, b)
         assert out.guards_intact(), form
         del out, ws
+
+
+def test_blocks_helpers(torch, sz):
+    """encode_blocks / decode_blocks on a list of layer tensors: each
+    container is the oracle's, the words come back, a corrupt container
+    raises naming its block."""
+    n, nb = 3 * 65536 + 40, 5
+    words = [make_words(KIND_MIX[b % len(KIND_MIX)], n, 110 + b) for b in range(nb)]
+    layers = [torch.from_numpy(w.view(np.int16)).cuda() for w in words]
+    bc = sz.encode_blocks(layers)
+    assert len(bc) == nb
+    for b in range(nb):
+        assert np.array_equal(bc.container(b).cpu().numpy(), oracle.encode(words[b])), b
+    outs = [torch.empty(n, dtype=torch.int16, device="cuda") for _ in range(nb)]
+    sz.decode_blocks(bc, outs)
+    for b in range(nb):
+        assert torch.equal(outs[b], layers[b]), b
+    bc.data[3 * bc.pitch + 16] ^= 1  # block 3's header E
+    with pytest.raises(sz.SplitZipError) as e:
+        sz.decode_blocks(bc, outs)
+    assert e.value.status == 4 and "block 3" in str(e.value)
+
+
+def test_blocks_maximum_count(torch, sz):
+    """The largest block count a launch takes (65535, the grid's height), of
+    short blocks with every distribution: every container is the oracle's
+    and both decode forms give every block back."""
+    n, nb = 40, 65535
+    say("maximum block count", nb)
+    rng = np.random.default_rng(120)
+    kinds = rng.integers(0, len(KIND_MIX), nb)
+    words = [make_words(KIND_MIX[int(k)], n, 121 + b) for b, k in enumerate(kinds)]
+    blk = Blocks(torch, n, nb, 23)
+    blk.fill_bulk(torch, words)
+    status = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    dst, pitch, sizes = encode_blocks(torch, sz, blk, status=status)
+    torch.cuda.synchronize()
+    assert (status.cpu().numpy() == 0).all()
+    check_containers(dst, pitch, sizes, words)
+    for form in FORMS:
+        out = Blocks(torch, n, nb, 24)
+        dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+        decode_blocks(torch, sz, dst, pitch, sizes, nb, n, out.table, dstatus, form)
+        torch.cuda.synchronize()
+        assert (dstatus.cpu().numpy() == 0).all(), form
+        out.snapshot()
+        got = out.host[:nb * out.stride].reshape(nb, out.stride)
+        for b in range(nb):
+            assert np.array_equal(got[out.slot[b], :n], words[b]), (form, b)
+        assert out.guards_intact(), form
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_blocks_random(torch, sz, seed):
+    """Random block counts, lengths (ragged, aligned or not), distributions
+    and decode forms, each block against the oracle."""
+    rng = np.random.default_rng([130, seed])
+    nb = int(rng.integers(1, 40))
+    n = int(rng.choice([int(rng.integers(1, 5000)), int(rng.integers(5000, 300000)),
+                        32 * int(rng.integers(1, 9000))]))
+    kinds = [KIND_MIX[int(k)] for k in rng.integers(0, len(KIND_MIX), nb)]
+    say("random blocks", seed, "n", n, "blocks", nb)
+    words = [make_words(k, n, 140 + 97 * seed + b) for b, k in enumerate(kinds)]
+    blk = Blocks(torch, n, nb, 30 + seed)
+    blk.fill(torch, words)
+    dst, pitch, sizes = encode_blocks(torch, sz, blk, ws_fill=int(rng.integers(0, 256)))
+    torch.cuda.synchronize()
+    check_containers(dst, pitch, sizes, words)
+    form = FORMS[seed % 2]
+    out = Blocks(torch, n, nb, 40 + seed)
+    dstatus = torch.full((nb,), -1, dtype=torch.int32, device="cuda")
+    decode_blocks(torch, sz, dst, pitch, sizes, nb, n, out.table, dstatus, form)
+    torch.cuda.synchronize()
+    assert (dstatus.cpu().numpy() == 0).all(), form
+    out.snapshot()
+    for b in range(nb):
+        assert np.array_equal(out.read(b), words[b]), (form, b)
+    assert out.guards_intact()

@@ -288,17 +288,48 @@ __device__ __forceinline__ uint64_t wave_inclusive_sum(uint64_t v) {
 // 255 - exponent: larger key, earlier code; the keys are distinct), as the
 // number of larger keys; four groups of 256 threads each compare against
 // 64 of the keys.  The caller synchronises after writing the keys.  Returns
-// the rank of exponent t to threads t < 256.
+// the rank of exponent t to threads t < 256.  key is 16-byte aligned: two
+// keys a 16-byte LDS load.
 __device__ __forceinline__ uint32_t rank_exponents(const uint64_t* key, uint32_t (*part)[256]) {
     const int t = threadIdx.x;
     const int bin = t & 255, grp = t >> 8;  // 0..3
     const uint64_t kx = key[bin];
+    const uint4* k2 = reinterpret_cast<const uint4*>(key + grp * 64);
     uint32_t r = 0;
-#pragma unroll 16
-    for (int y = grp * 64; y < grp * 64 + 64; y++) r += key[y] > kx ? 1u : 0u;
+#pragma unroll
+    for (int y = 0; y < 32; y++) {
+        const uint4 v = k2[y];
+        r += ((uint64_t)v.y << 32 | v.x) > kx ? 1u : 0u;
+        r += ((uint64_t)v.w << 32 | v.z) > kx ? 1u : 0u;
+    }
     part[grp][bin] = r;
     __syncthreads();
     return t < 256 ? part[0][t] + part[1][t] + part[2][t] + part[3][t] : 0u;
+}
+
+// The same rank for 32-bit keys, four keys a 16-byte LDS load (key 16-byte
+// aligned).
+__device__ __forceinline__ uint32_t rank_keys32(const uint32_t* key, uint32_t (*part)[256]) {
+    const int t = threadIdx.x;
+    const int bin = t & 255, grp = t >> 8;  // 0..3
+    const uint32_t kx = key[bin];
+    const uint4* k4 = reinterpret_cast<const uint4*>(key + grp * 64);
+    uint32_t r = 0;
+#pragma unroll
+    for (int y = 0; y < 16; y++) {
+        const uint4 v = k4[y];
+        r += (v.x > kx ? 1u : 0u) + (v.y > kx ? 1u : 0u) + (v.z > kx ? 1u : 0u) +
+             (v.w > kx ? 1u : 0u);
+    }
+    part[grp][bin] = r;
+    __syncthreads();
+    return t < 256 ? part[0][t] + part[1][t] + part[2][t] + part[3][t] : 0u;
+}
+
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
 }
 
 // Escape counts of chunks per * t .. per * t + per - 1 (per = ceil(chunks /
@@ -441,7 +472,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
     Words src, uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
     uint64_t* __restrict__ hist, SampleArea* __restrict__ sample, uint64_t* __restrict__ chunk_base,
     uint8_t* __restrict__ dst, uint64_t* d_size) {
-    __shared__ uint64_t key[256];
+    __shared__ alignas(16) uint64_t key[256];
     __shared__ uint32_t rank_part[4][256];
     __shared__ uint32_t codebook[16];
     __shared__ uint64_t wave_sum[kSelectWaves];
@@ -1038,6 +1069,8 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
 
 // Workgroups of the finish pass: two per CU of MI355X.
 constexpr uint32_t kFinishGroups = 512;
+// Escape records a finish thread moves per round of loads.
+constexpr int kFinishBatch = 4;
 constexpr uint32_t kFinishChunks = kMaxChunks / kFinishGroups;  // chunks per workgroup, at most
 static_assert(kFinishChunks * kFinishGroups == kMaxChunks, "whole chunks per finish workgroup");
 static_assert(kPackThreads == kSelectThreads, "the finish pass ranks and scans as the codebook pass");
@@ -1072,7 +1105,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
     uint64_t* d_size) {
     __shared__ PackLds lds;
     __shared__ uint8_t remap[256];  // provisional code pair -> exact code pair
-    __shared__ uint64_t key[256];
+    __shared__ alignas(16) uint64_t key[256];
     __shared__ uint32_t rank_part[4][256];
     __shared__ uint32_t codebook[16];
     __shared__ uint64_t wave_sum[kSelectWaves];
@@ -1080,6 +1113,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
     __shared__ uint64_t my_first[kFinishChunks];  // this workgroup's chunks' first slots
     __shared__ uint32_t my_count[kFinishChunks];  // and record counts (copy case)
     __shared__ uint32_t mismatch;
+    __shared__ uint32_t reranked;  // the provisional codebook failed its check
     if constexpr (Words::kBlocks) {
         const uint64_t off = block_ws(src);
         counts = byte_offset(counts, off);
@@ -1126,9 +1160,36 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
         for (int k = 0; k < (int)kTotalCopies; k++) c += totals[k * 256 + t];
         key[t] = (c << 8) | (255u - (uint32_t)t);
     }
+    if (t == 0) {
+        mismatch = 0;
+        reranked = 0;
+    }
     __syncthreads();
-    if (t == 0) mismatch = 0;
+    // The provisional codebook is the exact one when its 16 keys descend and
+    // every other exponent's key lies below its last (the keys are
+    // distinct): two keys a thread to compare instead of a ranking of all
+    // 256, which runs only when this check fails.
+    const uint32_t pw[4] = {prov.x, prov.y, prov.z, prov.w};
     {
+        bool bad = false;
+        if (t < 15) {
+            bad = key[byte_at(pw, t)] <= key[byte_at(pw, t + 1)];
+        } else if (t >= 256 && t < 512) {
+            const uint32_t e = t - 256;
+            bool found = false;
+#pragma unroll
+            for (int k = 0; k < 4; k++) {
+                const uint32_t v = pw[k] ^ (0x01010101u * e);
+                found |= ((v - 0x01010101u) & ~v & 0x80808080u) != 0;
+            }
+            bad = !found && key[e] > key[byte_at(pw, 15)];
+        }
+        if (bad) reranked = 1;
+    }
+    __syncthreads();
+    if (reranked == 0) {
+        if (t < 16) codebook[t] = byte_at(pw, t);
+    } else {
         const uint32_t r = rank_exponents(key, rank_part);
         if (t < 256 && r < 16) codebook[r] = (uint32_t)t;
     }
@@ -1196,16 +1257,32 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
 
     if (keep) {
         // the records of this workgroup's chunks move in one sweep,
-        // consecutive threads on consecutive records of a chunk
+        // consecutive threads on consecutive records of a chunk, and
+        // kFinishBatch records a thread per round, all loaded before any is
+        // stored (one memory round trip a round)
         const uint32_t* spos = reinterpret_cast<const uint32_t*>(dst + scratch_pos);
         const uint8_t* sexp = dst + scratch_exp;
         uint32_t count = 0;
         for (uint32_t j = 0; j < mine; j++) count += my_count[j];
-        for (uint32_t r = t; r < count; r += kPackThreads) {
-            uint32_t j = 0, q = r;
-            while (q >= my_count[j]) q -= my_count[j++];
-            const uint64_t from = (uint64_t)(blockIdx.x + j * gridDim.x) * spec_cap + q;
-            put_escape(esc_out, my_first[j] + q, spos[from], sexp[from]);
+        for (uint32_t r0 = 0; r0 < count; r0 += kFinishBatch * kPackThreads) {
+            uint32_t pos[kFinishBatch], ex[kFinishBatch];
+            uint64_t slot[kFinishBatch];
+#pragma unroll
+            for (int k = 0; k < kFinishBatch; k++) {
+                const uint32_t r = r0 + t + k * kPackThreads;
+                slot[k] = ~uint64_t{0};
+                if (r < count) {
+                    uint32_t j = 0, q = r;
+                    while (q >= my_count[j]) q -= my_count[j++];
+                    const uint64_t from = (uint64_t)(blockIdx.x + j * gridDim.x) * spec_cap + q;
+                    pos[k] = spos[from];
+                    ex[k] = sexp[from];
+                    slot[k] = my_first[j] + q;
+                }
+            }
+#pragma unroll
+            for (int k = 0; k < kFinishBatch; k++)
+                if (slot[k] != ~uint64_t{0}) put_escape(esc_out, slot[k], pos[k], ex[k]);
         }
         if (same_order) return;
 
@@ -1369,10 +1446,11 @@ constexpr uint32_t sample_groups() {
 // be ranked from part of the sample: a slower finish, never another
 // container).  The last workgroup reads the totals back, zeroing them, and
 // ranks the 256 exponents by the codebook rule (count descending, exponent
-// ascending); it leaves the provisional code table, decides whether the
-// first pass packs (at most one escape in 32 sampled words), clears the
-// first pass's overflow flag, and zeroes what the codebook pass counts up
-// (the whole input's counts and its workgroups done).
+// ascending); it leaves the provisional code table and decides whether the
+// first pass packs (at most one escape in 32 sampled words).  Workgroup 0
+// first clears what the later passes count up from zero (the first pass's
+// counts and overflow flag, the codebook pass's counts and workgroups
+// done), off the last workgroup's path.
 template <class Words>
 __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n,
                                                            SampleArea* __restrict__ area,
@@ -1383,8 +1461,8 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
     constexpr uint32_t kLoadsPerBlock = kSampleBlockWords / 8;
     __shared__ uint32_t h[kSpecCopies * kSpecPitch];
     __shared__ uint32_t part[4][256];
-    __shared__ uint64_t key[256];
-    __shared__ uint32_t sums[2];
+    __shared__ alignas(16) uint32_t key[256];
+    __shared__ uint32_t sums[2][4];
     __shared__ uint32_t last;
     if constexpr (Words::kBlocks) {
         const uint64_t off = block_ws(src);
@@ -1394,6 +1472,17 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
     }
     if (src.invalid()) return;
     const int t = threadIdx.x;
+    if (blockIdx.x == 0) {
+        // what the later passes count up from zero: the codebook pass's
+        // whole-input counts and arrivals, the first pass's counts and its
+        // overflow flag
+        if (t < 256) hist[t] = 0;
+        for (uint32_t i = t; i < kTotalCopies * 256; i += kSampleThreads) totals[i] = 0;
+        if (t == 0) {
+            area->overflow = 0;
+            area->arrivals = 0;
+        }
+    }
     for (int i = t; i < kSpecCopies * kSpecPitch; i += kSampleThreads) h[i] = 0;
     __syncthreads();
     uint32_t* mine = h + (t % kSpecCopies) * kSpecPitch;
@@ -1429,31 +1518,31 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
     __syncthreads();
     if (!last) return;
 
-    if (t < 2) sums[t] = 0;
+    uint32_t c = 0;
     if (t < 256) {
-        const uint32_t c = __hip_atomic_exchange(area->sample_hist + t, 0u, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT);
-        key[t] = ((uint64_t)c << 8) | (255u - (uint32_t)t);  // distinct keys
+        c = __hip_atomic_exchange(area->sample_hist + t, 0u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        // 32-bit keys: a sample count is below 2^24 (a workspace that came
+        // in with other counts is clamped there; the keys stay distinct)
+        key[t] = (min(c, (1u << 24) - 1) << 8) | (255u - (uint32_t)t);
     }
     __syncthreads();
-    const uint32_t r = rank_exponents(key, part);
+    const uint32_t r = rank_keys32(key, part);
     if (t < 256) {
-        const uint32_t c = (uint32_t)(key[t] >> 8);
         area->lut[t] = r < 16 ? (uint8_t)r : (uint8_t)0x10;
-        if (r < 16) {
-            area->cb[r] = (uint8_t)t;
-            atomicAdd(&sums[1], c);
+        if (r < 16) area->cb[r] = (uint8_t)t;
+        const uint32_t all = wave_sum_u32(c), top = wave_sum_u32(r < 16 ? c : 0u);
+        if ((t & 63) == 0) {
+            sums[0][t >> 6] = all;
+            sums[1][t >> 6] = top;
         }
-        atomicAdd(&sums[0], c);
     }
     __syncthreads();
     if (t == 0) {
-        area->spec_on = sums[0] > 0 && (uint64_t)(sums[0] - sums[1]) * 32 <= sums[0] ? 1u : 0u;
-        area->overflow = 0;
-        area->arrivals = 0;
+        const uint32_t all = sums[0][0] + sums[0][1] + sums[0][2] + sums[0][3];
+        const uint32_t top = sums[1][0] + sums[1][1] + sums[1][2] + sums[1][3];
+        area->spec_on = all > 0 && (uint64_t)(all - top) * 32 <= all ? 1u : 0u;
     }
-    if (t < 256) hist[t] = 0;  // the codebook pass adds the whole input's counts
-    for (uint32_t i = t; i < kTotalCopies * 256; i += kSampleThreads) totals[i] = 0;  // and the first pass
 }
 
 template <class Words>

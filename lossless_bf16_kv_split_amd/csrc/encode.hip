@@ -453,6 +453,10 @@ __device__ __forceinline__ uint64_t scan_chunk_escapes(const uint64_t (&esc)[kSe
     return wave_off[wave] + incl - mine;
 }
 
+// Up to this many chunks (tensors of up to 2^22 words) the codebook pass is
+// one workgroup.
+constexpr uint32_t kSmallCodebookChunks = 256;
+
 // The codebook pass, one launch of 256 workgroups: workgroup b sums bin b's
 // counts over the chunks (every load in flight at once, bin-major layout)
 // and adds the total to hist[b], which the pass before zeroed; device-wide
@@ -466,7 +470,9 @@ __device__ __forceinline__ uint64_t scan_chunk_escapes(const uint64_t (&esc)[kSe
 // in step for the next sample pass.  For blocks, one workgroup per block,
 // each on its block's workspace and container: the count pass has already
 // added up the whole block's counts, so the workgroup goes straight to the
-// ranking.
+// ranking.  With at most kSmallCodebookChunks chunks one workgroup sums the
+// 256 rows itself and ranks them, with no device-wide adds, arrivals or
+// read-back in between.
 template <class Words>
 __global__ __launch_bounds__(kSelectThreads) void k_codebook(
     Words src, uint64_t n, uint32_t chunk_log2, uint32_t chunks, const uint32_t* __restrict__ counts,
@@ -493,6 +499,59 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
         if (src.invalid()) {  // the same for every thread: no counts to read
             if (t == 0) *d_size = 0;
             return;
+        }
+    } else if (gridDim.x == 1) {
+        // at most kSmallCodebookChunks chunks: this one workgroup reads every
+        // count itself (no device-wide adds, arrivals or read-back between
+        // the counts and the ranking).  Wave w sums bins 16w .. 16w + 15,
+        // consecutive lanes on consecutive chunks of a row, 128 chunks of
+        // each of its rows per round of loads; then halving exchanges leave
+        // bin 16w + i's sum in lanes 4i .. 4i + 3 (i's bits from lane bits
+        // 5, 4, 3, 2), as in a reduce-scatter.
+        const uint32_t w = __builtin_amdgcn_readfirstlane(t >> 6);  // scalar row addresses
+        const uint32_t* rows = counts + (uint64_t)16 * w * chunks;
+        uint32_t part[16];
+#pragma unroll
+        for (int i = 0; i < 16; i++) part[i] = 0;
+        for (uint32_t c0 = 0; c0 < chunks; c0 += 128) {
+            uint32_t v[2][16];
+            if (c0 + 128 <= chunks) {  // a whole round: no per-load checks
+#pragma unroll
+                for (int h = 0; h < 2; h++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++)
+                        v[h][i] = rows[(uint64_t)i * chunks + c0 + 64 * h + lane];
+            } else {
+#pragma unroll
+                for (int h = 0; h < 2; h++)
+#pragma unroll
+                    for (int i = 0; i < 16; i++) {
+                        const uint32_t c = c0 + 64 * h + lane;
+                        v[h][i] = c < chunks ? rows[(uint64_t)i * chunks + c] : 0u;
+                    }
+            }
+#pragma unroll
+            for (int i = 0; i < 16; i++) part[i] += v[0][i] + v[1][i];
+        }
+#pragma unroll
+        for (int half = 8; half >= 1; half >>= 1) {
+            // lanes with bit log2(4 * half) set keep the upper half of
+            // their bins and send the lower, the others the reverse
+            // (mask arithmetic rather than a select of two elements, which
+            // the compiler turns into a dynamic index over the array)
+            const uint32_t upper = (lane & (4 * half)) != 0 ? ~0u : 0u;
+#pragma unroll
+            for (int i = 0; i < half; i++) {
+                const uint32_t a = part[i], b = part[half + i], flip = (a ^ b) & upper;
+                part[i] = (a ^ flip) + __shfl_xor(b ^ flip, 4 * half, 64);
+            }
+        }
+        uint32_t sum = part[0];
+        sum += __shfl_xor(sum, 1, 64);
+        sum += __shfl_xor(sum, 2, 64);
+        if ((lane & 3) == 0) {
+            const uint32_t bin = 16 * w + ((lane >> 2) & 15);
+            key[bin] = ((uint64_t)sum << 8) | (255u - bin);
         }
     } else {
         const uint32_t bin = blockIdx.x;
@@ -529,7 +588,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
     // the last workgroup: key(x) = count << 8 | (255 - x) turns "more
     // frequent, then smaller exponent" into one unsigned comparison (counts
     // stay below 2^37)
-    if (t < 256)
+    if (t < 256 && (Words::kBlocks || gridDim.x > 1))
         key[t] = (__hip_atomic_fetch_add(hist + t, uint64_t{0}, __ATOMIC_RELAXED,
                                          __HIP_MEMORY_SCOPE_AGENT) << 8) | (255u - t);
     __syncthreads();
@@ -589,8 +648,8 @@ hipError_t launch_codebook(Words src, const EncodePlan& p, uint8_t* ws, uint8_t*
     const uint32_t* counts = reinterpret_cast<const uint32_t*>(ws + p.counts_off);
     uint64_t* hist = reinterpret_cast<uint64_t*>(ws + p.hist_off);
     SampleArea* sample = reinterpret_cast<SampleArea*>(ws + p.sample_off);
-    k_codebook<Words><<<dim3(Words::kBlocks ? 1 : 256, grid_blocks(src)), kSelectThreads, 0,
-                        stream>>>(
+    const uint32_t groups = Words::kBlocks || p.chunks <= kSmallCodebookChunks ? 1 : 256;
+    k_codebook<Words><<<dim3(groups, grid_blocks(src)), kSelectThreads, 0, stream>>>(
         src, p.n, p.chunk_log2, p.chunks, counts, hist, sample,
         reinterpret_cast<uint64_t*>(ws + p.base_off), dst, d_size);
     return hipGetLastError();

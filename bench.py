@@ -50,9 +50,13 @@ KERNEL_SOURCES = ["lossless_bf16_kv_split_amd/csrc/encode.hip",
                   "lossless_bf16_kv_split_amd/csrc/decode.hip",
                   "lossless_bf16_kv_split_amd/csrc/sz_internal.h"]
 TWO_READ_PASSES = ["histogram", "codebook", "pack"]
+# up to this many chunks the two-read encode is two launches: the pack
+# workgroups rank the counts themselves (sz_encode_pack_ranked)
+RANKED_CHUNKS = 128
+RANKED_PASSES = ["histogram", "ranked"]
 SINGLE_READ_PASSES = ["sample", "first", "finish"]
 KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_codebook",
-                "pack": "k_pack", "sample": "k_sample",
+                "pack": "k_pack", "ranked": "k_pack(ranked)", "sample": "k_sample",
                 "first": "k_pack(first pass)", "finish": "k_finish",
                 "fused": "k_decode_fused", "dense": "k_decode_dense",
                 "index": "k_tile_index", "tiles": "k_decode_tiles",
@@ -113,6 +117,7 @@ def algorithmic_bytes(n: int, e: int, case: str | None = None) -> dict:
         "histogram": 2 * n,                        # read every word once
         "codebook": 0,                             # O(chunks) metadata only
         "pack": 2 * n + nib + sm + esc + pre,      # read words, write container
+        "ranked": 2 * n + nib + sm + esc + pre,    # the same (the counts are metadata)
         "sample": 2 * SAMPLE_BLOCKS * SAMPLE_BLOCK_WORDS,
         # read words, write streams + records; only count when the sample
         # predicts many escapes
@@ -623,7 +628,9 @@ def main() -> int:
     container = dst[:total]
     e = int.from_bytes(container[16:24].cpu().numpy().tobytes(), "little")
     single = sz.sz_encode_single_read(n)
-    encode_passes = SINGLE_READ_PASSES if single else TWO_READ_PASSES
+    ranked = not single and 1 <= -(-n >> chunk_log2(n)) <= RANKED_CHUNKS
+    encode_passes = (SINGLE_READ_PASSES if single else
+                     RANKED_PASSES if ranked else TWO_READ_PASSES)
     case = single_read_case(words, container[160:176].cpu().tolist()) if single else None
 
     # the decode passes sz_decode runs for this container (same rule), and
@@ -650,6 +657,8 @@ def main() -> int:
             sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size, st)
         elif p == "pack":
             sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap, st)
+        elif p == "ranked":
+            sz.sz_encode_pack_ranked(x, n, ws, ws_bytes, dst, cap, size, st)
         elif p == "sample":
             sz.sz_encode_sample(x, n, ws, ws_bytes, st)
         elif p == "first":
@@ -871,9 +880,10 @@ def main() -> int:
         "encode_alg_bytes": enc_alg,
         "decode_alg_bytes": dec_alg,
         "encode_form": ("single read (sampled codebook), finish case " + case) if single
-                       else "two reads (histogram, then pack)",
+                       else ("two reads (histogram, then pack with its own ranking)" if ranked
+                             else "two reads (histogram, codebook, pack)"),
         "other_encode_form": None if not other_enc else
-                             ("two reads (histogram, then pack)" if single else "single read"),
+                             ("two reads (histogram, codebook, pack)" if single else "single read"),
         "other_encode_form_GBps": None if other_enc_ms is None else
                                   round(2 * n / (other_enc_ms * 1e-3) / 1e9, 2),
         "decode_form": form,

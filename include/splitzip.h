@@ -176,6 +176,20 @@ sz_status sz_encode_pack(const void *d_src, uint64_t n_elements,
                          const void *d_workspace, uint64_t workspace_bytes,
                          void *d_dst, uint64_t dst_capacity, hipStream_t stream);
 
+/* Passes 2 and 3 in one launch, after sz_encode_histogram, for
+ * 1 <= n_elements <= 2^21 (at most 128 chunks of the plan; otherwise
+ * SZ_ERR_INVALID_ARGUMENT): every pack workgroup sums and ranks the chunk
+ * counts itself (the selection of section "3. La strategie SplitZip") and
+ * works out its chunk's first escape slot, so no codebook pass runs between
+ * the two launches.  Writes the same container as sz_encode_codebook then
+ * sz_encode_pack, and the container size to *d_compressed_size (optional);
+ * sz_encode takes this form for such n.  Same arguments and checks as
+ * sz_encode_pack. */
+sz_status sz_encode_pack_ranked(const void *d_src, uint64_t n_elements,
+                                const void *d_workspace, uint64_t workspace_bytes,
+                                void *d_dst, uint64_t dst_capacity,
+                                uint64_t *d_compressed_size, hipStream_t stream);
+
 /* ---- staged form of the single-read encode (n >= 2^20) -----------------
  * sz_encode_sample; sz_encode_first_pass; sz_encode_finish on one stream,
  * one workspace, gives the container of sz_encode.  Not part of the pages'

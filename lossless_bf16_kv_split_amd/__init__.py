@@ -25,7 +25,7 @@ import os
 __all__ = [
     "SplitZipError", "lib_path", "sz_max_compressed_size", "sz_workspace_size", "sz_encode",
     "sz_decode", "sz_encode_noalloc", "sz_encode_histogram", "sz_encode_codebook", "sz_encode_pack",
-    "sz_encode_single_read", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
+    "sz_encode_pack_ranked", "sz_encode_single_read", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
     "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused", "sz_decode_dense",
     "sz_decode_workspace_size", "sz_decode_index", "sz_decode_tiles",
     "sz_encode_pages", "sz_decode_pages", "sz_blocks_workspace_size", "sz_encode_blocks",
@@ -73,6 +73,7 @@ def _load() -> ctypes.CDLL:
     L.sz_encode_histogram.argtypes = [p, u64, p, u64, p]
     L.sz_encode_codebook.argtypes = [u64, p, u64, p, u64, p, p]
     L.sz_encode_pack.argtypes = [p, u64, p, u64, p, u64, p]
+    L.sz_encode_pack_ranked.argtypes = [p, u64, p, u64, p, u64, p, p]
     L.sz_encode_single_read.argtypes = [u64]
     L.sz_encode_single_read.restype = i32
     L.sz_encode_sample.argtypes = [p, u64, p, u64, p]
@@ -102,7 +103,8 @@ def _load() -> ctypes.CDLL:
     L.sz_ship_to_host_ctx.argtypes = [p, p, u64, p, u64, p, p]
     L.sz_ship_from_host_ctx.argtypes = [p, p, p, u64, p, p, p]
     for name in ("sz_encode", "sz_decode", "sz_encode_noalloc", "sz_encode_histogram", "sz_encode_codebook",
-                 "sz_encode_pack", "sz_encode_sample", "sz_encode_first_pass", "sz_encode_finish",
+                 "sz_encode_pack", "sz_encode_pack_ranked", "sz_encode_sample",
+                 "sz_encode_first_pass", "sz_encode_finish",
                  "sz_decode_unpack", "sz_decode_scatter", "sz_decode_fused",
                  "sz_decode_dense", "sz_decode_index", "sz_decode_tiles", "sz_encode_pages",
                  "sz_decode_pages", "sz_encode_blocks", "sz_decode_blocks", "sz_ship_to_host",
@@ -190,6 +192,13 @@ def sz_encode_pack(src, n_elements: int, workspace, workspace_bytes: int, dst,
                    dst_capacity: int, stream=None) -> None:
     _check(_lib.sz_encode_pack(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
                                _ptr(dst), dst_capacity, _stream(stream)), "sz_encode_pack")
+
+
+def sz_encode_pack_ranked(src, n_elements: int, workspace, workspace_bytes: int, dst,
+                          dst_capacity: int, d_compressed_size=None, stream=None) -> None:
+    _check(_lib.sz_encode_pack_ranked(_ptr(src), n_elements, _ptr(workspace), workspace_bytes,
+                                      _ptr(dst), dst_capacity, _ptr(d_compressed_size),
+                                      _stream(stream)), "sz_encode_pack_ranked")
 
 
 def sz_encode_single_read(n_elements: int) -> bool:

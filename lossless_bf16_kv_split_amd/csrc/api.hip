@@ -131,6 +131,13 @@ sz_status encode_passes(Words src, uint64_t n, const sz::EncodePlan& p, uint8_t*
         if (st == SZ_OK) st = hip_status(sz::launch_first_pass(src, p, w, out, dst_capacity, stream));
         if (st == SZ_OK)
             st = hip_status(sz::launch_finish(src, p, w, out, dst_capacity, d_compressed_size, stream));
+    } else if (p.chunks >= 1 && p.chunks <= sz::kRankedChunks) {
+        // few chunks: the pack workgroups rank the counts themselves, with
+        // no codebook pass between the two launches
+        st = hip_status(sz::launch_histogram(src, p, w, stream));
+        if (st == SZ_OK)
+            st = hip_status(sz::launch_pack_ranked(src, p, w, out, dst_capacity,
+                                                   d_compressed_size, stream));
     } else {
         st = hip_status(sz::launch_histogram(src, p, w, stream));
         // the codebook pass reads counts only, not the words
@@ -331,6 +338,19 @@ sz_status sz_encode_pack(const void* d_src, uint64_t n, const void* d_workspace,
                                       static_cast<const uint8_t*>(d_workspace),
                                       static_cast<uint8_t*>(d_dst), dst_capacity, num_cus(dev),
                                       stream));
+}
+
+sz_status sz_encode_pack_ranked(const void* d_src, uint64_t n, const void* d_workspace,
+                                uint64_t workspace_bytes, void* d_dst, uint64_t dst_capacity,
+                                uint64_t* d_compressed_size, hipStream_t stream) {
+    if (sz_status s = check_encode_args(d_src, n, d_dst, dst_capacity)) return s;
+    const sz::EncodePlan p = sz::plan_encode(n);
+    if (p.chunks < 1 || p.chunks > sz::kRankedChunks) return SZ_ERR_INVALID_ARGUMENT;
+    if (sz_status s = check_workspace(d_workspace, workspace_bytes, p)) return s;
+    return hip_status(sz::launch_pack_ranked(flat(d_src), p,
+                                             static_cast<const uint8_t*>(d_workspace),
+                                             static_cast<uint8_t*>(d_dst), dst_capacity,
+                                             d_compressed_size, stream));
 }
 
 int sz_encode_single_read(uint64_t n) {

@@ -284,46 +284,110 @@ __device__ __forceinline__ uint64_t wave_inclusive_sum(uint64_t v) {
     return v;
 }
 
-// Rank of each exponent among the 256 by its key in LDS (count << 8 |
-// 255 - exponent: larger key, earlier code; the keys are distinct), as the
-// number of larger keys; four groups of 256 threads each compare against
-// 64 of the keys.  The caller synchronises after writing the keys.  Returns
-// the rank of exponent t to threads t < 256.  key is 16-byte aligned: two
-// keys a 16-byte LDS load.
-__device__ __forceinline__ uint32_t rank_exponents(const uint64_t* key, uint32_t (*part)[256]) {
-    const int t = threadIdx.x;
-    const int bin = t & 255, grp = t >> 8;  // 0..3
-    const uint64_t kx = key[bin];
-    const uint4* k2 = reinterpret_cast<const uint4*>(key + grp * 64);
-    uint32_t r = 0;
-#pragma unroll
-    for (int y = 0; y < 32; y++) {
-        const uint4 v = k2[y];
-        r += ((uint64_t)v.y << 32 | v.x) > kx ? 1u : 0u;
-        r += ((uint64_t)v.w << 32 | v.z) > kx ? 1u : 0u;
-    }
-    part[grp][bin] = r;
-    __syncthreads();
-    return t < 256 ? part[0][t] + part[1][t] + part[2][t] + part[3][t] : 0u;
+// Rank of this lane's bits among lower lanes: popcount of mask below lane.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// The same rank for 32-bit keys, four keys a 16-byte LDS load (key 16-byte
-// aligned).
-__device__ __forceinline__ uint32_t rank_keys32(const uint32_t* key, uint32_t (*part)[256]) {
+// LDS of top16_ranks (keys of type K: 64-bit, or 32-bit where every count
+// is below 2^24).
+template <class K>
+struct alignas(16) RankLds {
+    uint32_t full[4][256];   // partial counts of the full ranking
+    K gmax[4][16];           // per wave of the first four, each group's largest key
+    K cand[64];              // the candidates' keys
+    uint32_t wave_cand[4];   // candidates per wave
+};
+
+template <class K>
+__device__ __forceinline__ K max_key(K a, K b) {
+    return a > b ? a : b;
+}
+template <class K>
+__device__ __forceinline__ K min_key(K a, K b) {
+    return a < b ? a : b;
+}
+
+// Every exponent's rank as the number of larger keys, four groups of 256
+// threads each comparing against 64 of the keys, 16-byte LDS loads (key
+// 16-byte aligned).  Returns the rank of exponent t to threads t < 256.
+template <class K>
+__device__ __forceinline__ uint32_t full_rank(const K* key, RankLds<K>& s) {
     const int t = threadIdx.x;
     const int bin = t & 255, grp = t >> 8;  // 0..3
-    const uint32_t kx = key[bin];
+    const K kx = key[bin];
     const uint4* k4 = reinterpret_cast<const uint4*>(key + grp * 64);
     uint32_t r = 0;
 #pragma unroll
-    for (int y = 0; y < 16; y++) {
+    for (int y = 0; y < (int)(64 * sizeof(K) / 16); y++) {
         const uint4 v = k4[y];
-        r += (v.x > kx ? 1u : 0u) + (v.y > kx ? 1u : 0u) + (v.z > kx ? 1u : 0u) +
-             (v.w > kx ? 1u : 0u);
+        if constexpr (sizeof(K) == 8) {
+            r += ((uint64_t)v.y << 32 | v.x) > kx ? 1u : 0u;
+            r += ((uint64_t)v.w << 32 | v.z) > kx ? 1u : 0u;
+        } else {
+            r += (v.x > kx ? 1u : 0u) + (v.y > kx ? 1u : 0u) + (v.z > kx ? 1u : 0u) +
+                 (v.w > kx ? 1u : 0u);
+        }
     }
-    part[grp][bin] = r;
+    s.full[grp][bin] = r;
     __syncthreads();
-    return t < 256 ? part[0][t] + part[1][t] + part[2][t] + part[3][t] : 0u;
+    return t < 256 ? s.full[0][t] + s.full[1][t] + s.full[2][t] + s.full[3][t] : 0u;
+}
+
+// The 16 most frequent exponents' ranks (the codebook rule: key = count << 8
+// | 255 - exponent, larger key earlier; the keys are distinct), from the
+// keys in LDS, which the caller has synchronised.  Returns to thread t < 256
+// the number of keys larger than exponent t's when that is below 16, and 16
+// or more otherwise.  Candidates first: with the exponents in 16 interleaved
+// groups (e, e + 16, ..., e + 240), the smallest of the groups' largest
+// keys, L, has at least 16 keys at or above it (those maxima), so the top 16
+// are among the keys >= L, and a candidate's rank counts candidates only.
+// The exponents of real data crowd into one run of consecutive bins, one
+// bin of it per group, so about 16 keys are candidates; with more than 64
+// every key is ranked against all 256 instead.
+template <class K>
+__device__ __forceinline__ uint32_t top16_ranks(const K* key, RankLds<K>& s) {
+    const int t = threadIdx.x;
+    const int lane = t & 63, w = t >> 6;
+    K kx = 0;
+    if (t < 256) {
+        // lanes l, l ^ 16, l ^ 32, l ^ 48 of a wave hold one group's bins
+        kx = key[t];
+        K m = max_key<K>(kx, __shfl_xor(kx, 16, 64));
+        m = max_key<K>(m, __shfl_xor(m, 32, 64));
+        if (lane < 16) s.gmax[w][lane] = m;
+    }
+    __syncthreads();
+    bool cand = false;
+    uint32_t in_wave = 0;
+    if (t < 256) {
+        // each of the four waves works out L itself
+        const int g = lane & 15;
+        K l = max_key<K>(max_key<K>(s.gmax[0][g], s.gmax[1][g]),
+                         max_key<K>(s.gmax[2][g], s.gmax[3][g]));
+#pragma unroll
+        for (int d = 1; d < 16; d <<= 1) l = min_key<K>(l, __shfl_xor(l, d, 64));
+        cand = kx >= l;
+        const uint64_t bits = __ballot(cand);
+        in_wave = lanes_below(bits);
+        if (lane == 0) s.wave_cand[w] = (uint32_t)__popcll(bits);
+    }
+    __syncthreads();
+    const uint32_t total = s.wave_cand[0] + s.wave_cand[1] + s.wave_cand[2] + s.wave_cand[3];
+    if (total > 64) return full_rank(key, s);  // the same for every thread
+    if (cand) {
+        uint32_t before = 0;
+        for (int v = 0; v < w; v++) before += s.wave_cand[v];
+        s.cand[before + in_wave] = kx;
+    }
+    __syncthreads();
+    uint32_t r = 16;  // below every candidate: not in the top 16
+    if (cand) {
+        r = 0;
+        for (uint32_t i = 0; i < total; i++) r += s.cand[i] > kx ? 1u : 0u;
+    }
+    return t < 256 ? r : 0u;
 }
 
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
@@ -479,7 +543,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
     uint64_t* __restrict__ hist, SampleArea* __restrict__ sample, uint64_t* __restrict__ chunk_base,
     uint8_t* __restrict__ dst, uint64_t* d_size) {
     __shared__ alignas(16) uint64_t key[256];
-    __shared__ uint32_t rank_part[4][256];
+    __shared__ RankLds<uint64_t> rank_lds;
     __shared__ uint32_t codebook[16];
     __shared__ uint64_t wave_sum[kSelectWaves];
     __shared__ uint64_t wave_off[kSelectWaves];
@@ -593,7 +657,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
                                          __HIP_MEMORY_SCOPE_AGENT) << 8) | (255u - t);
     __syncthreads();
     {
-        const uint32_t r = rank_exponents(key, rank_part);
+        const uint32_t r = top16_ranks(key, rank_lds);
         if (t < 256 && r < 16) codebook[r] = (uint32_t)t;
     }
     __syncthreads();
@@ -677,12 +741,6 @@ static_assert((1u << kMinChunkLog2) % kPackTile == 0, "chunks hold whole tiles")
 static_assert(kPackTile <= 65536, "tile offsets fit in 16 bits");
 static_assert(kPackThreads >= 256, "one LUT entry per thread");
 static_assert(kSelectChunks * kSelectThreads == kMaxChunks, "whole chunks per select thread");
-
-// Rank of this lane's bits among lower lanes: popcount of mask below lane.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
-                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
 
 // byte k of a little-endian run of dwords (k known at compile time after
 // unrolling, so the array stays in registers)
@@ -899,15 +957,114 @@ __device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0,
     return write_escapes(r, w, t0, slot_base, lds, parity, esc);
 }
 
-// The pack kernel serves two passes:
+// The pack kernel serves three passes:
 //   kClassic  codes from the exact codebook in the header; escape records to
 //             their final slots (chunk_base).
+//   kRanked   the same for at most kRankedChunks chunks, with no codebook
+//             pass before it: every workgroup ranks the histogram pass's
+//             counts itself and works out its chunk's first escape slot
+//             (ranked_codebook, below); workgroup 0 writes the header.
 //   kFirst    first pass of the single-read encode: the exact exponent counts
 //             of the chunk (as the histogram pass gives them) and, when the
 //             sample predicts few escapes, the streams under the provisional
 //             codebook, escape records to the chunk's scratch slots.
 // k_finish (below) completes the single-read encode.
-enum class PackRole { kClassic, kFirst };
+enum class PackRole { kClassic, kRanked, kFirst };
+
+
+// LDS of ranked_codebook.
+struct RankedLds {
+    alignas(16) uint32_t key[256];
+    RankLds<uint32_t> rank;
+    uint32_t codebook[16];
+    uint32_t kept[kRankedChunks];  // per chunk: words whose exponent is in the codebook
+    uint8_t lut[256];              // exponent -> code, 16 = escape
+    uint64_t sums[2][2];           // escapes of all chunks and of those below, per wave
+};
+
+// The exact codebook from every chunk's counts (bin-major, as the histogram
+// pass leaves them; counts below 2^24), the escapes below chunk `chunk` (its
+// first escape slot, returned) and E.  Wave w loads bins 16w .. 16w + 15
+// with consecutive lanes on consecutive chunks (all 32 loads a lane in
+// flight at once) and sums them across lanes by halving exchanges (bin
+// 16w + i's sum in lanes 4i .. 4i + 3); after the ranking the same
+// registers give each chunk's count of codebook exponents.
+__device__ __forceinline__ uint64_t ranked_codebook(const uint32_t* __restrict__ counts, uint64_t n,
+                                                    uint32_t chunk_log2, uint32_t chunks,
+                                                    uint32_t chunk, RankedLds& o, uint64_t& E) {
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const uint32_t w = __builtin_amdgcn_readfirstlane(t >> 6);  // scalar row addresses
+    const uint32_t* rows = counts + (uint64_t)16 * w * chunks;
+    uint32_t v[2][16];
+#pragma unroll
+    for (int h = 0; h < 2; h++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+            const uint32_t c = 64 * h + lane;
+            v[h][i] = c < chunks ? rows[(uint64_t)i * chunks + c] : 0u;
+        }
+    uint32_t part[16];
+#pragma unroll
+    for (int i = 0; i < 16; i++) part[i] = v[0][i] + v[1][i];
+#pragma unroll
+    for (int half = 8; half >= 1; half >>= 1) {
+        // mask arithmetic rather than a select of two elements, which the
+        // compiler turns into a dynamic index over the array
+        const uint32_t upper = (lane & (4 * half)) != 0 ? ~0u : 0u;
+#pragma unroll
+        for (int i = 0; i < half; i++) {
+            const uint32_t a = part[i], b = part[half + i], flip = (a ^ b) & upper;
+            part[i] = (a ^ flip) + __shfl_xor(b ^ flip, 4 * half, 64);
+        }
+    }
+    uint32_t sum = part[0];
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    if ((lane & 3) == 0) {
+        const uint32_t bin = 16 * w + ((lane >> 2) & 15);
+        o.key[bin] = (min(sum, (1u << 24) - 1) << 8) | (255u - bin);
+    }
+    if (t < (int)kRankedChunks) o.kept[t] = 0;
+    __syncthreads();
+    const uint32_t r = top16_ranks(o.key, o.rank);
+    if (t < 256) {
+        o.lut[t] = r < 16 ? (uint8_t)r : (uint8_t)16;
+        if (r < 16) o.codebook[r] = (uint32_t)t;
+    }
+    __syncthreads();
+    uint32_t k0 = 0, k1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+        if (o.lut[16 * w + i] < 16) {  // the same for the wave
+            k0 += v[0][i];
+            k1 += v[1][i];
+        }
+    }
+    if (k0) atomicAdd(&o.kept[lane], k0);  // nonzero only for chunks that exist
+    if (k1) atomicAdd(&o.kept[64 + lane], k1);
+    __syncthreads();
+    uint64_t all = 0, below = 0;
+    if ((uint32_t)t < chunks) {
+        const uint64_t start = (uint64_t)t << chunk_log2;
+        all = min_u64(uint64_t{1} << chunk_log2, n - start) - o.kept[t];
+        below = (uint32_t)t < chunk ? all : 0;
+    }
+    if (t < 128) {
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            all += __shfl_xor(all, d, 64);
+            below += __shfl_xor(below, d, 64);
+        }
+        if (lane == 0) {
+            o.sums[w][0] = all;
+            o.sums[w][1] = below;
+        }
+    }
+    __syncthreads();
+    E = o.sums[0][0] + o.sums[1][0];
+    return o.sums[0][1] + o.sums[1][1];
+}
 
 constexpr int kSpecCopies = 16;    // exponent sub-histograms of the first pass
 constexpr int kSpecPitch = 257;
@@ -1056,10 +1213,12 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     uint8_t* __restrict__ dst, uint64_t dst_capacity, uint32_t* __restrict__ counts,
     uint64_t* __restrict__ totals, uint32_t* __restrict__ chunk_esc,
     SampleArea* __restrict__ area, uint64_t spec_cap, uint64_t scratch_pos,
-    uint64_t scratch_exp) {
+    uint64_t scratch_exp, uint64_t* d_size) {
     constexpr bool kFirst = kRole == PackRole::kFirst;
+    constexpr bool kRanked = kRole == PackRole::kRanked;
     __shared__ PackLds lds;
     __shared__ uint32_t hist[kFirst ? kSpecCopies * kSpecPitch : 1];
+    __shared__ std::conditional_t<kRanked, RankedLds, char> ranked;
     if (src.invalid()) return;  // the same for every thread
     if constexpr (Words::kBlocks) {
         const uint64_t off = block_ws(src);
@@ -1097,6 +1256,29 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
         esc.limit = spec_cap;
         esc.pos_aligned = true;
         slot_base = 0;
+    } else if constexpr (kRanked) {
+        uint64_t E;
+        slot_base = ranked_codebook(counts, n, chunk_log2, gridDim.x, chunk, ranked, E);
+        if (chunk == 0) {
+            // the header, as the codebook pass writes it (n < 2^32: every
+            // seg_end entry is E)
+            const uint64_t total = kPrefixBytes + (n + 1) / 2 + n + 5 * E;
+            if (t == 0) {
+                *reinterpret_cast<uint32_t*>(dst + 0) = kMagic;
+                *reinterpret_cast<uint16_t*>(dst + 4) = kVersion;
+                *reinterpret_cast<uint16_t*>(dst + 6) = kElementBf16;
+                *reinterpret_cast<uint64_t*>(dst + 8) = n;
+                *reinterpret_cast<uint64_t*>(dst + 16) = E;
+                *reinterpret_cast<uint64_t*>(dst + 24) = total;
+                if (d_size) *d_size = total;
+            }
+            if (t < 16) {
+                *reinterpret_cast<uint64_t*>(dst + 32 + 8 * t) = E;
+                dst[kHeaderBytes + t] = (uint8_t)ranked.codebook[t];
+            }
+        }
+        code_table(ranked.codebook, lds);
+        esc = escape_slots(dst, n, dst_capacity, E);
     } else {
         exact_code_table(dst, lds);
         esc = final_slots(dst, n, dst_capacity);
@@ -1165,7 +1347,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
     __shared__ PackLds lds;
     __shared__ uint8_t remap[256];  // provisional code pair -> exact code pair
     __shared__ alignas(16) uint64_t key[256];
-    __shared__ uint32_t rank_part[4][256];
+    __shared__ RankLds<uint64_t> rank_lds;
     __shared__ uint32_t codebook[16];
     __shared__ uint64_t wave_sum[kSelectWaves];
     __shared__ uint64_t wave_off[kSelectWaves];
@@ -1249,7 +1431,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
     if (reranked == 0) {
         if (t < 16) codebook[t] = byte_at(pw, t);
     } else {
-        const uint32_t r = rank_exponents(key, rank_part);
+        const uint32_t r = top16_ranks(key, rank_lds);
         if (t < 256 && r < 16) codebook[r] = (uint32_t)t;
     }
     __syncthreads();
@@ -1407,7 +1589,7 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
 
 template <class Words, PackRole kRole>
 hipError_t launch_pack_role(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
-                            uint64_t dst_capacity, hipStream_t stream) {
+                            uint64_t dst_capacity, uint64_t* d_size, hipStream_t stream) {
     if (p.chunks == 0) return hipSuccess;
     const uint64_t* base = reinterpret_cast<const uint64_t*>(ws + p.base_off);
     uint32_t* counts = reinterpret_cast<uint32_t*>(const_cast<uint8_t*>(ws) + p.counts_off);
@@ -1420,24 +1602,34 @@ hipError_t launch_pack_role(Words src, const EncodePlan& p, const uint8_t* ws, u
     if (aligned)
         k_pack<true, Words, kRole><<<dim3(p.chunks, grid_blocks(src)), kPackThreads, 0, stream>>>(
             src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, totals, chunk_esc, area,
-            p.spec_cap, p.scratch_pos, p.scratch_exp);
+            p.spec_cap, p.scratch_pos, p.scratch_exp, d_size);
     else
         k_pack<false, Words, kRole><<<dim3(p.chunks, grid_blocks(src)), kPackThreads, 0, stream>>>(
             src, p.n, p.chunk_log2, base, dst, dst_capacity, counts, totals, chunk_esc, area,
-            p.spec_cap, p.scratch_pos, p.scratch_exp);
+            p.spec_cap, p.scratch_pos, p.scratch_exp, d_size);
     return hipGetLastError();
 }
 
 template <class Words>
 hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
                        uint64_t dst_capacity, int /*num_cus*/, hipStream_t stream) {
-    return launch_pack_role<Words, PackRole::kClassic>(src, p, ws, dst, dst_capacity, stream);
+    return launch_pack_role<Words, PackRole::kClassic>(src, p, ws, dst, dst_capacity, nullptr,
+                                                       stream);
+}
+
+template <class Words>
+hipError_t launch_pack_ranked(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
+                              uint64_t dst_capacity, uint64_t* d_size, hipStream_t stream) {
+    if (p.chunks == 0 || p.chunks > kRankedChunks) return hipErrorInvalidValue;
+    return launch_pack_role<Words, PackRole::kRanked>(src, p, ws, dst, dst_capacity, d_size,
+                                                      stream);
 }
 
 template <class Words>
 hipError_t launch_first_pass(Words src, const EncodePlan& p, uint8_t* ws, uint8_t* dst,
                              uint64_t dst_capacity, hipStream_t stream) {
-    return launch_pack_role<Words, PackRole::kFirst>(src, p, ws, dst, dst_capacity, stream);
+    return launch_pack_role<Words, PackRole::kFirst>(src, p, ws, dst, dst_capacity, nullptr,
+                                                     stream);
 }
 
 template <class Words>
@@ -1519,7 +1711,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
     constexpr uint32_t kBlocksPerGroup = kSampleBlocksPerGroup;
     constexpr uint32_t kLoadsPerBlock = kSampleBlockWords / 8;
     __shared__ uint32_t h[kSpecCopies * kSpecPitch];
-    __shared__ uint32_t part[4][256];
+    __shared__ RankLds<uint32_t> rank_lds;
     __shared__ alignas(16) uint32_t key[256];
     __shared__ uint32_t sums[2][4];
     __shared__ uint32_t last;
@@ -1586,7 +1778,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
         key[t] = (min(c, (1u << 24) - 1) << 8) | (255u - (uint32_t)t);
     }
     __syncthreads();
-    const uint32_t r = rank_keys32(key, part);
+    const uint32_t r = top16_ranks(key, rank_lds);
     if (t < 256) {
         area->lut[t] = r < 16 ? (uint8_t)r : (uint8_t)0x10;
         if (r < 16) area->cb[r] = (uint8_t)t;
@@ -1625,5 +1817,9 @@ SZ_ENCODE_INSTANCES(FlatWords)
 SZ_ENCODE_INSTANCES(PagedWords)
 SZ_ENCODE_INSTANCES(BlockWords)
 #undef SZ_ENCODE_INSTANCES
+template hipError_t launch_pack_ranked<FlatWords>(FlatWords, const EncodePlan&, const uint8_t*,
+                                                  uint8_t*, uint64_t, uint64_t*, hipStream_t);
+template hipError_t launch_pack_ranked<PagedWords>(PagedWords, const EncodePlan&, const uint8_t*,
+                                                   uint8_t*, uint64_t, uint64_t*, hipStream_t);
 
 }  // namespace sz

@@ -339,6 +339,13 @@ hipError_t launch_codebook(Words src, const EncodePlan& p, uint8_t* ws, uint8_t*
 template <class Words>
 hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
                        uint64_t dst_capacity, int num_cus, hipStream_t stream);
+// the codebook and pack passes in one launch, for 1 to kRankedChunks chunks
+// (FlatWords and PagedWords): every workgroup ranks the counts itself;
+// writes the header and *d_size
+constexpr uint32_t kRankedChunks = 128;
+template <class Words>
+hipError_t launch_pack_ranked(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
+                              uint64_t dst_capacity, uint64_t* d_size, hipStream_t stream);
 // single-read encode: sample (ranks the provisional codebook), the first
 // pass (exact per-chunk and whole-input counts, and the streams under the
 // provisional codebook), then the finish pass (takes the exact codebook and

@@ -141,6 +141,14 @@ def test_staged_host_checks(sz):
     assert status_of(sz.sz_encode_codebook, n, W, ws - 256, D, cap, None, 0) == 1
     assert status_of(sz.sz_encode_pack, A, n, W, ws, D, cap - 1, 0) == 2
     assert status_of(sz.sz_encode_pack, A, n, None, ws, D, cap, 0) == 1
+    # the one-launch codebook and pack: 1 to 2^21 words only
+    assert status_of(sz.sz_encode_pack_ranked, A, n, W, ws, D, cap - 1, None, 0) == 2
+    assert status_of(sz.sz_encode_pack_ranked, A, n, None, ws, D, cap, None, 0) == 1
+    big = (1 << 21) + 1
+    assert status_of(sz.sz_encode_pack_ranked, A, big, W, sz.sz_workspace_size(big), D,
+                     sz.sz_max_compressed_size(big), None, 0) == 1
+    assert status_of(sz.sz_encode_pack_ranked, A, 0, W, sz.sz_workspace_size(0), D,
+                     sz.sz_max_compressed_size(0), None, 0) == 1
 
 
 def test_single_read_host_checks(sz):

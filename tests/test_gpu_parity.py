@@ -107,6 +107,11 @@ def make_words(kind: str, n: int, seed: int) -> np.ndarray:
         e = rng.integers(100, 140, n, dtype=np.uint16)
         return ((rng.integers(0, 2, n, dtype=np.uint16) << 15) | (e << 7) |
                 rng.integers(0, 128, n, dtype=np.uint16)).astype(np.uint16)
+    if kind == "gapped":          # 240 exponents, none = 1 (mod 16): most keys are candidates
+        e = rng.integers(0, 240, n, dtype=np.uint16)
+        e = (e + e // 15 + 2) % 256  # skips 1, 17, 33, ..., 241
+        return ((rng.integers(0, 2, n, dtype=np.uint16) << 15) | (e << 7) |
+                rng.integers(0, 128, n, dtype=np.uint16)).astype(np.uint16)
     if kind == "ties":            # 20 exponents, equal counts: tie-break decides
         e = (np.arange(n) % 20 + 110).astype(np.uint16)
         rng.shuffle(e)
@@ -127,7 +132,7 @@ def make_words(kind: str, n: int, seed: int) -> np.ndarray:
 SIZES = [0, 1, 2, 3, 5, 7, 8, 9, 15, 16, 17, 31, 32, 33, 63, 64, 65, 100, 255, 256, 257,
          1000, 2047, 2048, 2049, 4095, 4096, 4097, 8191, 8192, 8193, 12345, 65535, 65536,
          65537, (1 << 20) - 1, (1 << 20) + 1, 3 * (1 << 20) + 17]
-KINDS = ["kv", "random", "narrow", "wide40", "ties", "special"]
+KINDS = ["kv", "random", "narrow", "wide40", "ties", "special", "gapped"]
 
 
 def check_case(torch, sz, words: np.ndarray, label: str):
@@ -184,6 +189,15 @@ def test_many_chunks_ragged(torch, sz):
         check_case(torch, sz, make_words("kv", n, 7), "many chunks kv")
 
 
+@pytest.mark.parametrize("n", [(1 << 22) + 16385, (1 << 26) + 3 * 16384 + 1])
+def test_gapped_exponents(torch, sz, n):
+    """Exponents of 240 values, none of them 1 modulo 16, in a 256-workgroup
+    codebook pass (257 chunks) and in the single-read encode (sample, first
+    pass, finish): the ranking's shortcut (about 16 keys near the top) does
+    not apply and every key is ranked against all 256."""
+    check_case(torch, sz, make_words("gapped", n, 11), "gapped")
+
+
 @pytest.mark.timeout(300)
 @pytest.mark.parametrize("n", [1280 * (1 << 18) - 3, 1537 * (1 << 18) - 1, (1 << 29) - 3])
 def test_halved_chunk_plans(torch, sz, n):
@@ -227,6 +241,31 @@ def two_read_encode(torch, sz, x, n):
     sz.sz_encode_codebook(n, ws, ws_bytes, dst, cap, size)
     sz.sz_encode_pack(x, n, ws, ws_bytes, dst, cap)
     return dst[:int(size.item())]
+
+
+@pytest.mark.parametrize("kind", ["kv", "random", "ties", "gapped", "narrow"])
+def test_staged_ranked_pack(torch, sz, kind):
+    """sz_encode_histogram then sz_encode_pack_ranked (the two-launch encode
+    sz_encode takes for 1 to 2^21 words) over a workspace that comes in
+    filled with other bytes, twice in a row on it: the oracle's container
+    and size each time, and the same as the three staged passes."""
+    for i, n in enumerate([1, 17, 16384, 16385, 3 * 16384 + 7, (1 << 20) + 5, 1 << 21]):
+        words = make_words(kind, n, 300 + i)
+        want = oracle.encode(words)
+        x = to_dev(torch, words)
+        ws_bytes = sz.sz_workspace_size(n)
+        ws = torch.full((ws_bytes,), 0xA5, dtype=torch.uint8, device="cuda")
+        cap = sz.sz_max_compressed_size(n)
+        for rep in range(2):
+            dst = torch.full((cap,), 0x3C, dtype=torch.uint8, device="cuda")
+            size = torch.zeros(1, dtype=torch.int64, device="cuda")
+            sz.sz_encode_histogram(x, n, ws, ws_bytes)
+            sz.sz_encode_pack_ranked(x, n, ws, ws_bytes, dst, cap, size)
+            total = int(size.item())
+            assert total == want.size, (kind, n, rep, total, want.size)
+            assert np.array_equal(dst[:total].cpu().numpy(), want), (kind, n, rep)
+        three = two_read_encode(torch, sz, x, n).cpu().numpy()
+        assert np.array_equal(three, want), (kind, n)
 
 
 @pytest.mark.timeout(600)

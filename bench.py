@@ -407,7 +407,9 @@ def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
             "container_pitch": pitch, "chunk_elems": 1 << c, "steps": args.steps,
             "encode_form": ("single read, finish cases " +
                             json.dumps({k: cases.count(k) for k in sorted(set(cases))}))
-                           if single else "two reads (counts, codebook, pack)",
+                           if single else
+                           ("two reads (counts, then the ranked pack)"
+                            if 1 <= -(-b >> c) <= RANKED_CHUNKS else "two reads (counts, codebook, pack)"),
             "decode_form": "tile index, then tiles (decode_blocks); single pass without a "
                            "workspace (decode_blocks_single_pass)",
             "ms": {k: round(v, 5) for k, v in ms.items()},

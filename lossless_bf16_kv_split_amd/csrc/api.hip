@@ -587,6 +587,13 @@ sz_status sz_encode_blocks(const void* const* d_blocks, uint64_t n_blocks, uint6
         return st;
     }
     st = hip_status(sz::launch_histogram(src, l.plan, ws, stream));
+    if (l.plan.chunks >= 1 && l.plan.chunks <= sz::kRankedChunks) {
+        // few chunks a block: no codebook pass, each pack workgroup ranks
+        if (st == SZ_OK)
+            st = hip_status(sz::launch_pack_ranked(src, l.plan, ws, out, dst_pitch, nullptr,
+                                                   stream));
+        return st;
+    }
     if (st == SZ_OK) st = hip_status(sz::launch_codebook(src, l.plan, ws, out, nullptr, stream));
     if (st == SZ_OK)
         st = hip_status(sz::launch_pack(src, l.plan, ws, out, dst_pitch, num_cus(dev), stream));

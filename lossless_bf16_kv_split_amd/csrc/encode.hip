@@ -1219,6 +1219,14 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
     __shared__ PackLds lds;
     __shared__ uint32_t hist[kFirst ? kSpecCopies * kSpecPitch : 1];
     __shared__ std::conditional_t<kRanked, RankedLds, char> ranked;
+    if constexpr (kRanked && Words::kBlocks) {
+        // this pass writes the block's size: 0 for a block it cannot read
+        d_size = src.sizes + blockIdx.y;
+        if (src.invalid()) {  // the same for every thread
+            if (blockIdx.x == 0 && threadIdx.x == 0) *d_size = 0;
+            return;
+        }
+    }
     if (src.invalid()) return;  // the same for every thread
     if constexpr (Words::kBlocks) {
         const uint64_t off = block_ws(src);
@@ -1820,6 +1828,8 @@ SZ_ENCODE_INSTANCES(BlockWords)
 template hipError_t launch_pack_ranked<FlatWords>(FlatWords, const EncodePlan&, const uint8_t*,
                                                   uint8_t*, uint64_t, uint64_t*, hipStream_t);
 template hipError_t launch_pack_ranked<PagedWords>(PagedWords, const EncodePlan&, const uint8_t*,
+                                                   uint8_t*, uint64_t, uint64_t*, hipStream_t);
+template hipError_t launch_pack_ranked<BlockWords>(BlockWords, const EncodePlan&, const uint8_t*,
                                                    uint8_t*, uint64_t, uint64_t*, hipStream_t);
 
 }  // namespace sz

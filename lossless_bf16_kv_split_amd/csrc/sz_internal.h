@@ -340,8 +340,9 @@ template <class Words>
 hipError_t launch_pack(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,
                        uint64_t dst_capacity, int num_cus, hipStream_t stream);
 // the codebook and pack passes in one launch, for 1 to kRankedChunks chunks
-// (FlatWords and PagedWords): every workgroup ranks the counts itself;
-// writes the header and *d_size
+// (a tensor's or, for BlockWords, each block's): every workgroup ranks the
+// counts itself; writes the header and *d_size (for blocks, each block's
+// size to src.sizes, 0 for a block it cannot read)
 constexpr uint32_t kRankedChunks = 128;
 template <class Words>
 hipError_t launch_pack_ranked(Words src, const EncodePlan& p, const uint8_t* ws, uint8_t* dst,

@@ -390,6 +390,31 @@ __device__ __forceinline__ uint32_t top16_ranks(const K* key, RankLds<K>& s) {
     return t < 256 ? r : 0u;
 }
 
+// The sums over the 64 lanes of each of the 16 values part[0..15] a lane
+// holds, by halving exchanges, as in a reduce-scatter: at each of four
+// steps the lanes whose bit log2(4 * half) is set keep the upper half of
+// their values and send the lower, the others the reverse; two more
+// exchanges add the four lanes that end up with the same value.  Value i's
+// sum is returned to lanes 4i .. 4i + 3, i's bits taken from lane bits
+// 5, 4, 3, 2; part is overwritten.  (Mask arithmetic picks the halves: a
+// select of two array elements is turned by the compiler into a dynamic
+// index over the array, a chain of hundreds of selects.)
+__device__ __forceinline__ uint32_t sum16_across_lanes(uint32_t (&part)[16], int lane) {
+#pragma unroll
+    for (int half = 8; half >= 1; half >>= 1) {
+        const uint32_t upper = (lane & (4 * half)) != 0 ? ~0u : 0u;
+#pragma unroll
+        for (int i = 0; i < half; i++) {
+            const uint32_t a = part[i], b = part[half + i], flip = (a ^ b) & upper;
+            part[i] = (a ^ flip) + __shfl_xor(b ^ flip, 4 * half, 64);
+        }
+    }
+    uint32_t sum = part[0];
+    sum += __shfl_xor(sum, 1, 64);
+    sum += __shfl_xor(sum, 2, 64);
+    return sum;
+}
+
 __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
@@ -569,9 +594,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
         // count itself (no device-wide adds, arrivals or read-back between
         // the counts and the ranking).  Wave w sums bins 16w .. 16w + 15,
         // consecutive lanes on consecutive chunks of a row, 128 chunks of
-        // each of its rows per round of loads; then halving exchanges leave
-        // bin 16w + i's sum in lanes 4i .. 4i + 3 (i's bits from lane bits
-        // 5, 4, 3, 2), as in a reduce-scatter.
+        // each of its rows per round of loads; then the sums across lanes.
         const uint32_t w = __builtin_amdgcn_readfirstlane(t >> 6);  // scalar row addresses
         const uint32_t* rows = counts + (uint64_t)16 * w * chunks;
         uint32_t part[16];
@@ -597,22 +620,7 @@ __global__ __launch_bounds__(kSelectThreads) void k_codebook(
 #pragma unroll
             for (int i = 0; i < 16; i++) part[i] += v[0][i] + v[1][i];
         }
-#pragma unroll
-        for (int half = 8; half >= 1; half >>= 1) {
-            // lanes with bit log2(4 * half) set keep the upper half of
-            // their bins and send the lower, the others the reverse
-            // (mask arithmetic rather than a select of two elements, which
-            // the compiler turns into a dynamic index over the array)
-            const uint32_t upper = (lane & (4 * half)) != 0 ? ~0u : 0u;
-#pragma unroll
-            for (int i = 0; i < half; i++) {
-                const uint32_t a = part[i], b = part[half + i], flip = (a ^ b) & upper;
-                part[i] = (a ^ flip) + __shfl_xor(b ^ flip, 4 * half, 64);
-            }
-        }
-        uint32_t sum = part[0];
-        sum += __shfl_xor(sum, 1, 64);
-        sum += __shfl_xor(sum, 2, 64);
+        const uint32_t sum = sum16_across_lanes(part, lane);
         if ((lane & 3) == 0) {
             const uint32_t bin = 16 * w + ((lane >> 2) & 15);
             key[bin] = ((uint64_t)sum << 8) | (255u - bin);
@@ -971,7 +979,6 @@ __device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0,
 // k_finish (below) completes the single-read encode.
 enum class PackRole { kClassic, kRanked, kFirst };
 
-
 // LDS of ranked_codebook.
 struct RankedLds {
     alignas(16) uint32_t key[256];
@@ -986,8 +993,7 @@ struct RankedLds {
 // pass leaves them; counts below 2^24), the escapes below chunk `chunk` (its
 // first escape slot, returned) and E.  Wave w loads bins 16w .. 16w + 15
 // with consecutive lanes on consecutive chunks (all 32 loads a lane in
-// flight at once) and sums them across lanes by halving exchanges (bin
-// 16w + i's sum in lanes 4i .. 4i + 3); after the ranking the same
+// flight at once) and sums them across lanes; after the ranking the same
 // registers give each chunk's count of codebook exponents.
 __device__ __forceinline__ uint64_t ranked_codebook(const uint32_t* __restrict__ counts, uint64_t n,
                                                     uint32_t chunk_log2, uint32_t chunks,
@@ -1007,20 +1013,7 @@ __device__ __forceinline__ uint64_t ranked_codebook(const uint32_t* __restrict__
     uint32_t part[16];
 #pragma unroll
     for (int i = 0; i < 16; i++) part[i] = v[0][i] + v[1][i];
-#pragma unroll
-    for (int half = 8; half >= 1; half >>= 1) {
-        // mask arithmetic rather than a select of two elements, which the
-        // compiler turns into a dynamic index over the array
-        const uint32_t upper = (lane & (4 * half)) != 0 ? ~0u : 0u;
-#pragma unroll
-        for (int i = 0; i < half; i++) {
-            const uint32_t a = part[i], b = part[half + i], flip = (a ^ b) & upper;
-            part[i] = (a ^ flip) + __shfl_xor(b ^ flip, 4 * half, 64);
-        }
-    }
-    uint32_t sum = part[0];
-    sum += __shfl_xor(sum, 1, 64);
-    sum += __shfl_xor(sum, 2, 64);
+    const uint32_t sum = sum16_across_lanes(part, lane);
     if ((lane & 3) == 0) {
         const uint32_t bin = 16 * w + ((lane >> 2) & 15);
         o.key[bin] = (min(sum, (1u << 24) - 1) << 8) | (255u - bin);

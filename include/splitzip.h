@@ -217,10 +217,10 @@ int sz_encode_single_read(uint64_t n_elements);
 sz_status sz_encode_sample(const void *d_src, uint64_t n_elements, void *d_workspace,
                            uint64_t workspace_bytes, hipStream_t stream);
 
-/* The first pass: the exact per-chunk exponent counts to the workspace (as
- * sz_encode_histogram leaves them) and, when the sample predicts few
- * escapes, the nibble and sign|mantissa streams plus each chunk's escape
- * records (to the scratch area). */
+/* The first pass: the exact per-chunk exponent counts to the workspace (laid
+ * out for sz_encode_finish, not for sz_encode_codebook) and, when the sample
+ * predicts few escapes, the nibble and sign|mantissa streams plus each
+ * chunk's escape records (to the scratch area). */
 sz_status sz_encode_first_pass(const void *d_src, uint64_t n_elements,
                                void *d_workspace, uint64_t workspace_bytes,
                                void *d_dst, uint64_t dst_capacity, hipStream_t stream);

@@ -495,9 +495,30 @@ __device__ __forceinline__ void exact_chunk_escapes(const uint32_t* __restrict__
     }
 }
 
-// The same escape counts from the first pass's chunk-major counts (chunk
-// b's 256 at counts + 256 b), one chunk at a time (its 16 codebook counts
-// in flight together), for a kernel held to 64 registers a lane.
+// The same escape counts one chunk at a time (its 16 codebook rows in
+// flight together), for a kernel held to 64 registers a lane.
+__device__ __forceinline__ void exact_chunk_escapes_narrow(const uint32_t* __restrict__ counts,
+                                                           uint32_t chunks, uint32_t chunk_log2,
+                                                           uint64_t n, const uint32_t* codebook,
+                                                           uint64_t (&esc)[kSelectChunks]) {
+    const int t = threadIdx.x;
+    const uint32_t per = (chunks + kSelectThreads - 1) / kSelectThreads;  // <= kSelectChunks
+#pragma unroll
+    for (int j = 0; j < kSelectChunks; j++) {
+        const uint32_t b = per * t + j;
+        if ((uint32_t)j < per && b < chunks) {
+            uint64_t kept = 0;
+#pragma unroll
+            for (int c = 0; c < 16; c++) kept += counts[(uint64_t)codebook[c] * chunks + b];
+            const uint64_t start = (uint64_t)b << chunk_log2;
+            esc[j] = min_u64(uint64_t{1} << chunk_log2, n - start) - kept;
+        }
+    }
+}
+
+// The same from chunk-major counts (chunk b's 256 at counts + 256 b): a
+// lane's 16 loads hit its own chunk's row, so they do not coalesce across
+// the wave; for the rare case that needs them.
 __device__ __forceinline__ void exact_chunk_escapes_chunk_major(const uint32_t* __restrict__ counts,
                                                                 uint32_t chunks, uint32_t chunk_log2,
                                                                 uint64_t n, const uint32_t* codebook,
@@ -975,7 +996,7 @@ __device__ __forceinline__ uint32_t pack_tile(const uint32_t* w, uint64_t t0,
 //             counts itself and works out its chunk's first escape slot
 //             (ranked_codebook, below); workgroup 0 writes the header.
 //   kFirst    first pass of the single-read encode: the exact exponent counts
-//             of the chunk (chunk-major, for the finish pass) and, when the
+//             of the chunk (for the finish pass) and, when the
 //             sample predicts few escapes, the streams under the provisional
 //             codebook, escape records to the chunk's scratch slots.
 // k_finish (below) completes the single-read encode.
@@ -1294,15 +1315,18 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_pack(
                                                             slot_base, write, hmine, lds, parity);
     if (kFirst) {
         __syncthreads();
-        // the chunk's exact counts, chunk-major: its 256 counts in one
-        // stretch, a single coalesced store (bin-major, as the histogram
-        // pass lays them, they were 256 words on 256 lines shared with other
-        // chunks' workgroups, 5-6 us of the 1 GiB pass)
+        // the chunk's exact counts: when the streams were written (the
+        // finish then rarely needs them), chunk-major, its 256 counts in one
+        // coalesced store (bin-major they are 256 words on 256 lines shared
+        // with other chunks' workgroups: 5-6 us of the 1 GiB pass); when the
+        // pass only counted, bin-major as the histogram pass lays them, so
+        // that the finish, which then needs every chunk's escape count,
+        // reads a codebook row of them with one coalesced load
         for (int b = t; b < 256; b += kPackThreads) {
             uint32_t s = 0;
 #pragma unroll
             for (int c = 0; c < kSpecCopies; c++) s += hist[c * kSpecPitch + b];
-            counts[(uint64_t)chunk * 256 + b] = s;
+            counts[write ? (uint64_t)chunk * 256 + b : (uint64_t)b * gridDim.x + chunk] = s;
             // and into the whole input's counts (nothing waits for the add:
             // the finish pass, a later launch, reads the sums)
             __hip_atomic_fetch_add(totals + (chunk % kTotalCopies) * 256 + b, (uint64_t)s,
@@ -1460,7 +1484,14 @@ __attribute__((amdgpu_waves_per_eu(8))) void k_finish(
     __syncthreads();
     const bool same_order = (mismatch & 2u) == 0;
     const bool keep = spec_on != 0 && overflow == 0 && (mismatch & 1u) == 0;
-    if (!keep) exact_chunk_escapes_chunk_major(counts, chunks, chunk_log2, n, codebook, esc);
+    if (!keep) {
+        // the first pass left chunk-major counts when it wrote the streams,
+        // bin-major when it only counted
+        if (spec_on)
+            exact_chunk_escapes_chunk_major(counts, chunks, chunk_log2, n, codebook, esc);
+        else
+            exact_chunk_escapes_narrow(counts, chunks, chunk_log2, n, codebook, esc);
+    }
     uint64_t E;
     uint64_t excl = scan_chunk_escapes(esc, wave_sum, wave_off, E);
     const uint32_t seg_shift = 32 - chunk_log2;  // chunks per 2^32 elements: 2^seg_shift

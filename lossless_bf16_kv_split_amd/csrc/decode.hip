@@ -891,7 +891,7 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
         if (t == 0 && status) *status = out.invalid() ? kStatusInvalid : (any ? kStatusCorrupt : 0);
         return;
     }
-    if constexpr (!Words::kBlocks) {
+    if constexpr (!Words::kBlocks && !Words::kPaged) {
         if (out.invalid()) return;  // the same for every thread
     }
     // blocks: the block's address, a scalar load first waited for at the
@@ -937,6 +937,11 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
         const uint64_t i0 = t0 + (uint64_t)t * 8;
         // every load of the tile goes out before anything waits on one
         const uint32_t sv = lane < kSlotWords ? slots[tile * kSlotWords + lane] : 0u;
+        // a paged tensor's table check, read with the tile's loads and
+        // tested only at the store (the empty asm there keeps the compiler
+        // from testing, and so waiting for, it any earlier)
+        int32_t table_flag = 0;
+        if constexpr (Words::kPaged) table_flag = *out.bad;
 
         if (tile < whole) {
             const uint32_t codes = *reinterpret_cast<const uint32_t*>(nib + i0 / 2);
@@ -962,7 +967,10 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
                 const uintptr_t a = reinterpret_cast<uintptr_t>(words.base);
                 write = a != 0 && (a & 15) == 0;
                 words_out = words.at(i0);
-            } else if constexpr (!Words::kPaged) {
+            } else if constexpr (Words::kPaged) {
+                asm volatile("" : "+v"(table_flag));
+                write = table_flag == 0;
+            } else {
                 words_out = out.at_wave(i0);
             }
             // written past the caches: a decode's output is larger than they
@@ -983,6 +991,10 @@ __global__ __launch_bounds__(kTileThreads) void k_decode_tiles(
             uint32_t e0 = ex[0] | (ex[1] << 8) | (ex[2] << 16) | (ex[3] << 24);
             uint32_t e1 = ex[4] | (ex[5] << 8) | (ex[6] << 16) | (ex[7] << 24);
             patch(tile, t0, sv, e0, e1);
+            if constexpr (Words::kPaged) {
+                asm volatile("" : "+v"(table_flag));
+                if (table_flag != 0) return;  // the same for every thread
+            }
             for (uint32_t k = 0; k < 8 && i0 + k < n; k++) {
                 const uint32_t x = ((k < 4 ? e0 : e1) >> (8 * (k & 3))) & 0xFFu;
                 *words.at(i0 + k) = (uint16_t)recombine(sm[i0 + k], x);

@@ -63,7 +63,16 @@ KERNEL_NAMES = {"histogram": "k_histogram", "codebook": "k_codebook",
                 "unpack": "k_unpack", "scatter": "k_scatter"}
 # the sample of the single-read encode: 512 blocks of 2048 words (32 for
 # each of several blocks encoded together)
-SAMPLE_BLOCKS, SAMPLE_BLOCK_WORDS, BLOCK_SAMPLE_BLOCKS = 512, 2048, 32
+SAMPLE_BLOCKS, SAMPLE_BLOCK_WORDS = 512, 2048
+
+
+def block_sample_blocks(block_elems: int) -> int:
+    """The sample of each of several blocks: 8 runs of 2048 words per 2^19
+    words of the block, in a power of two of groups from 4 to 32."""
+    g = 4
+    while g < 32 and (2 * g) << 19 <= block_elems:
+        g *= 2
+    return 8 * g
 MIN_CHUNK_LOG2, PLAN_CHUNKS, RESIDENT_PACK_GROUPS = 14, 2048, 512
 
 
@@ -392,9 +401,9 @@ def blocks_bench(args, w, n, words, x, torch, np, sz) -> int:
     for i, e_ in enumerate(es):
         if single:
             cb = dst[i * pitch + 160:i * pitch + 176].cpu().tolist()
-            case = single_read_case(words[i * b:(i + 1) * b], cb, BLOCK_SAMPLE_BLOCKS, c)
+            case = single_read_case(words[i * b:(i + 1) * b], cb, block_sample_blocks(b), c)
             a = algorithmic_bytes(b, e_, case)
-            enc_alg += 2 * BLOCK_SAMPLE_BLOCKS * SAMPLE_BLOCK_WORDS + a["first"] + a["finish"]
+            enc_alg += 2 * block_sample_blocks(b) * SAMPLE_BLOCK_WORDS + a["first"] + a["finish"]
             cases.append(case)
         else:
             a = algorithmic_bytes(b, e_)

@@ -1710,24 +1710,34 @@ static_assert(kSampleBlocks % kSampleGroups == 0, "whole blocks per workgroup");
 static_assert(kSingleReadMin / kSampleBlocks >= kSampleBlockWords, "blocks do not overlap");
 static_assert(kSampleThreads == 1024, "four groups of 256 threads rank the exponents");
 static_assert((kSampleGroups & (kSampleGroups - 1)) == 0, "tickets wrap at a multiple of a run");
-// Per-layer blocks are sampled by fewer workgroups each, so that the sample
-// stays a small share of a small block (32 blocks of 2048 words: 1/32 of a
-// 2^21-word block).
+// Per-layer blocks are sampled in proportion to their length: one
+// workgroup (8 runs of 2048 words) per 2^19 words of a block, a power of two
+// from 4 to 32, so about 1/32 of every block (a fixed 32 runs made 1/256 of
+// a 2^24-word block, whose finish then rewrote the codes of 13 of 32 blocks
+// and packed one again; 256 runs, 6 and none).
 constexpr uint32_t kBlockSampleGroups = 4;
+constexpr uint32_t kBlockSampleGroupsMax = 32;
 static_assert((kBlockSampleGroups & (kBlockSampleGroups - 1)) == 0, "tickets wrap at a multiple of a run");
 static_assert(kSingleReadMin / (kBlockSampleGroups * kSampleBlocksPerGroup) >= kSampleBlockWords,
               "blocks do not overlap");
 
 template <class Words>
-constexpr uint32_t sample_groups() {
-    return Words::kBlocks ? kBlockSampleGroups : kSampleGroups;
+uint32_t sample_groups(uint64_t n) {
+    if constexpr (!Words::kBlocks) {
+        return kSampleGroups;
+    } else {
+        // groups * 2^19 <= n keeps the runs apart: n / (groups * 8) >= 2^16
+        uint32_t g = kBlockSampleGroups;
+        while (g < kBlockSampleGroupsMax && (uint64_t{2} * g << 19) <= n) g *= 2;
+        return g;
+    }
 }
 
 // The sample pass, one launch.  Each workgroup counts its blocks, adds the
 // counts into area->sample_hist (device-wide atomics whose returned values
 // a barrier waits for) and then takes a ticket.  Tickets count on from run
-// to run, kSampleGroups a run (kBlockSampleGroups for each of several
-// blocks, each on its own area), so the workgroup whose ticket completes a
+// to run, a run being the launch's workgroups per tensor or block (a power of
+// two; each block on its own area), so the workgroup whose ticket completes a
 // multiple of the run arrives last; the codebook pass puts tickets and
 // counts back to zero, so a workspace that came in with other values is in
 // step from its second encode on (until then the provisional codebook may
@@ -1744,7 +1754,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
                                                            SampleArea* __restrict__ area,
                                                            uint64_t* __restrict__ hist,
                                                            uint64_t* __restrict__ totals) {
-    constexpr uint32_t kGroups = sample_groups<Words>();
+    const uint32_t kGroups = gridDim.x;  // a power of two
     constexpr uint32_t kBlocksPerGroup = kSampleBlocksPerGroup;
     constexpr uint32_t kLoadsPerBlock = kSampleBlockWords / 8;
     __shared__ uint32_t h[kSpecCopies * kSpecPitch];
@@ -1836,7 +1846,7 @@ __global__ __launch_bounds__(kSampleThreads) void k_sample(Words src, uint64_t n
 template <class Words>
 hipError_t launch_sample(Words src, const EncodePlan& p, uint8_t* ws, hipStream_t stream) {
     SampleArea* area = reinterpret_cast<SampleArea*>(ws + p.sample_off);
-    k_sample<Words><<<dim3(sample_groups<Words>(), grid_blocks(src)), kSampleThreads, 0, stream>>>(
+    k_sample<Words><<<dim3(sample_groups<Words>(p.n), grid_blocks(src)), kSampleThreads, 0, stream>>>(
         src, p.n, area, reinterpret_cast<uint64_t*>(ws + p.hist_off),
         reinterpret_cast<uint64_t*>(ws + p.totals_off));
     return hipGetLastError();
